@@ -1,0 +1,243 @@
+/*
+ * moe.h — C ABI of the MI355X (gfx950) Mixture-of-Experts layer library (libmoe_mi355x.so).
+ *
+ * One GPU runs the whole layer on its tokens: router logits, top-K, optional token rounding,
+ * per-expert counts and offsets, the token permutation, grouped SwiGLU expert GEMMs with the row
+ * gather fused into operand staging, the gate-weighted combine, and the backward pass.
+ *
+ * Where the operations come from (the pages this library implements):
+ *  - cloud.baidu.com, "MoE架构的物理瓶颈与扩展限制解析", section "工作原理": the forward is
+ *    gate network -> top-k -> dispatch -> local expert compute -> combine back to the tokens.
+ *    With every expert on one GPU, dispatch and combine are a local row gather and a local sum.
+ *  - apxml.com, "硬件加速的考量", section "自定义核与核融合": the five fused steps
+ *    (gate scores, top-k, gather of the selected experts, expert matmuls, weighted combine).
+ *  - hebangwen.github.io, "SonicMoE: 加速 MoE 模型的 IO 与 Tile 感知优化": gather fused into
+ *    the GEMM's operand load ("Gather 与加载融合"; contiguous-packed or gathered inputs),
+ *    SwiGLU fused into the GEMM, the router-score gradient computed without caching expert
+ *    outputs, no separate scatter kernel (kernel-comparison table), recompute in the backward
+ *    (optimization 1), and token rounding of per-expert counts to tile multiples
+ *    (optimization 3).
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers unless the comment says "host".  Tensors are dense row-major,
+ *    with the shapes given below.  Every device pointer must be 16-byte aligned.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the legacy default stream).  All work is
+ *    enqueued on it asynchronously; no call synchronises with the device, and data-dependent
+ *    sizes (rows per expert, the total row count R) stay on the device.
+ *  - The caller owns all memory: inputs, outputs, the routing plan and the workspace.  The
+ *    library never allocates or frees device memory and keeps no state between calls, apart from
+ *    a thread-local error message and, when enabled, the stage-timing records (moe_timing_*).
+ *    Outputs are fully overwritten, never accumulated into.
+ *  - Arguments are validated on the host before anything is enqueued.  An invalid call returns
+ *    MOE_EINVAL / MOE_ENOTSUP / MOE_EWORKSPACE and enqueues nothing; a failed launch returns
+ *    MOE_EHIP.  Faults inside kernels surface at the caller's next synchronisation, as in HIP.
+ *    moe_last_error() returns a message describing the last failure on the calling thread.
+ *  - Results are deterministic: the same inputs give bitwise-identical outputs (no floating-point
+ *    atomics; every sum has a fixed order).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,     /* a pointer is NULL/misaligned or a size is out of range */
+  MOE_ENOTSUP = -2,    /* valid but unsupported shape or dtype (see moe_dims) */
+  MOE_EWORKSPACE = -3, /* ws_bytes smaller than moe_workspace_bytes() */
+  MOE_EHIP = -4        /* the HIP runtime reported an error when launching */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Token rounding (SonicMoE page, optimization 3).  Each expert's token count c is moved to a
+ * multiple of tile_m: NEAREST drops r = c mod tile_m tokens when r < tile_m/2 and otherwise adds
+ * tile_m - r (half a tile rounds up); UP always adds; DOWN always drops; an addition that would
+ * need more than T tokens drops instead.  An expert drops its lowest-ranked members and adds its
+ * highest-ranked non-members, ranking tokens by (logit descending, token id ascending). */
+typedef enum {
+  MOE_ROUND_NONE = 0,
+  MOE_ROUND_NEAREST = 1,
+  MOE_ROUND_UP = 2,
+  MOE_ROUND_DOWN = 3
+} moe_round;
+
+/* Layer shape (host struct).
+ *  T tokens (1 .. 2^24), d model width, n expert FFN width (d and n multiples of 64,
+ *  64 .. 65536), E experts (1 .. 1024), K experts per token (1 .. min(E, 16)).
+ *  dtype: type of X, W_r, W_gate, W_up, W_down, dY, out, dX, dW_*, H and Y_perm.  Logits, gate
+ *  weights, dS and dLogits are always fp32; accumulation is always fp32.
+ *  round_mode / tile_m: token rounding (tile_m 1 .. 1024; ignored for MOE_ROUND_NONE).
+ *  flags: reserved, must be 0. */
+typedef struct moe_dims {
+  int64_t T;
+  int64_t d;
+  int64_t n;
+  int32_t E;
+  int32_t K;
+  int32_t dtype;
+  int32_t round_mode;
+  int32_t tile_m;
+  int32_t flags;
+} moe_dims;
+
+/* The routing plan: device arrays the caller allocates with the sizes given here, written by
+ * moe_route and read by the other calls.  R is the number of (token, expert) rows after token
+ * rounding; R_max = moe_max_rows(dims) bounds it.  Row r of the permuted ("expert-major") layout
+ * belongs to expert e when expert_off[e] <= r < expert_off[e+1]; an expert's rows are its tokens
+ * in ascending token id.
+ *   topk_idx   int32 [T*K]   plain top-K expert ids per token, best first (ties: lower id)
+ *   topk_w     fp32  [T*K]   softmax of the token's K selected logits (plain top-K weights)
+ *   counts     int32 [E]     rows per expert after token rounding
+ *   expert_off int32 [E+1]   exclusive prefix sum of counts; expert_off[E] = R
+ *   row_token  int32 [R_max] token of row r (entries r >= R are unspecified)
+ *   row_w      fp32  [R_max] gate weight of row r: softmax over the token's final experts
+ *   tok_off    int32 [T+1]   token t owns tok_row[tok_off[t] .. tok_off[t+1])
+ *   tok_row    int32 [R_max] rows of each token, in ascending expert id
+ *   meta       int32 [16]    meta[0] = R; the other entries are reserved */
+typedef struct moe_plan {
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t* counts;
+  int32_t* expert_off;
+  int32_t* row_token;
+  float* row_w;
+  int32_t* tok_off;
+  int32_t* tok_row;
+  int32_t* meta;
+} moe_plan;
+
+/* Operation codes for moe_workspace_bytes(). */
+enum {
+  MOE_OP_ROUTE = 0,
+  MOE_OP_PERMUTE = 1,
+  MOE_OP_FFN = 2,
+  MOE_OP_COMBINE = 3,
+  MOE_OP_FORWARD = 4,
+  MOE_OP_BACKWARD = 5
+};
+
+/* Host: upper bound on R for these dims (T*K without rounding; rounding can add at most
+ * tile_m - 1 rows per expert, and never more than T*E rows in total).  0 if dims are invalid. */
+int64_t moe_max_rows(const moe_dims* dims);
+
+/* Host: workspace bytes the call `op` needs for these dims (0 if none; 0 for invalid dims, with
+ * moe_last_error() set).  A workspace may be reused by calls that are ordered on one stream. */
+size_t moe_workspace_bytes(const moe_dims* dims, int op);
+
+/* moe_route — gate network, top-K, token rounding, counts, offsets and the permutation indices.
+ * cloud.baidu.com "工作原理" steps 1 (gate_network, top_k); apxml.com fused steps 1-2; SonicMoE
+ * optimization 3 (token rounding).
+ *  X      [T,d] dtype, W_r [E,d] dtype, bias [E] fp32 or NULL: if X != NULL, the library computes
+ *         logits = X W_r^T + bias (fp32 accumulation) and writes them to `logits`.
+ *         If X == NULL, `logits` is an INPUT: caller-computed fp32 logits (bias already added).
+ *  logits [T,E] fp32.  Must be finite.
+ *  plan   all arrays written (see moe_plan).
+ * Selection compares fp32 logits exactly: the K largest per token (ties to the lower expert id);
+ * the gate weights are the softmax over the token's final expert set.  A token that token
+ * rounding leaves with no expert has no rows. */
+moe_status moe_route(const moe_dims* dims, const void* X, const void* W_r, const float* bias,
+                     float* logits, const moe_plan* plan, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* moe_permute — materialise the expert-major copy of the tokens ("contiguous packed" input):
+ * X_perm[r] = X[row_token[r]] for r < R.  X [T,d] dtype, X_perm [R_max,d] dtype (rows >= R are
+ * left untouched).  Bit-exact copies.  Needs a plan from moe_route. */
+moe_status moe_permute(const moe_dims* dims, const moe_plan* plan, const void* X, void* X_perm,
+                       void* stream);
+
+/* moe_grouped_ffn — every expert's SwiGLU FFN on its rows, as grouped GEMMs.
+ *  A_in     gathered != 0: X [T,d]; row r reads X[row_token[r]] straight into the GEMM's operand
+ *           staging (no permuted copy).  gathered == 0: X_perm [R_max,d] from moe_permute.
+ *  W_gate, W_up [E,n,d] dtype;  W_down [E,d,n] dtype.
+ *  H_cache  [R_max,2n] dtype or NULL: if given, row r receives [G_r | U_r] with
+ *           G = x W_gate[e]^T and U = x W_up[e]^T (the pre-activations the backward reuses).
+ *  Y_perm   [R_max,d] dtype: Y_r = (silu(G_r) * U_r) W_down[e]^T.
+ * silu(g) = g / (1 + exp(-g)).  fp32 accumulation; the SwiGLU output is rounded to dtype between
+ * the two GEMMs. */
+moe_status moe_grouped_ffn(const moe_dims* dims, const moe_plan* plan, const void* A_in,
+                           int gathered, const void* W_gate, const void* W_up,
+                           const void* W_down, void* H_cache, void* Y_perm, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/* moe_combine — scatter-free combine: out[t] = sum over the token's rows r (ascending expert)
+ * of w_r * Y_perm[r], with w_r = row_w[r] if weighted != 0, else 1.  fp32 accumulation, one
+ * rounding to dtype.  A token with no rows gets zeros.  Y_perm [R_max,d], out [T,d] dtype. */
+moe_status moe_combine(const moe_dims* dims, const moe_plan* plan, const void* Y_perm,
+                       int weighted, void* out, void* stream);
+
+/* moe_forward — the whole layer: moe_route (logits from X, W_r, bias), the grouped FFN on
+ * gathered rows, and the weighted combine.
+ *  logits [T,E] fp32 output; plan output; H_cache [R_max,2n] or NULL (see moe_grouped_ffn);
+ *  out [T,d] dtype. */
+moe_status moe_forward(const moe_dims* dims, const void* X, const void* W_r, const float* bias,
+                       const void* W_gate, const void* W_up, const void* W_down, float* logits,
+                       const moe_plan* plan, void* H_cache, void* out, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* moe_backward — gradients of the layer for the routing in `plan` (selection and token rounding
+ * held fixed; the bias is a constant).  SonicMoE optimization 1 and "反向传播优化".
+ *  dY [T,d] dtype: gradient of the loss with respect to out.
+ *  X, W_gate, W_up, W_down: the forward's inputs.  plan: the forward's plan.
+ *  H_cache [R_max,2n] from the forward, or NULL: then [G|U] is recomputed from X first.
+ *  The SwiGLU output A = silu(G) * U is recomputed from H; expert outputs Y are never needed:
+ *  dS_r = <dY[t_r] W_down[e], A_r> equals <dY[t_r], Y_r>.
+ *  Outputs (all overwritten):
+ *   dX [T,d] dtype           expert-path gradient plus, if W_r != NULL, dLogits W_r
+ *   dW_gate, dW_up [E,n,d], dW_down [E,d,n] dtype  (zero for experts without rows)
+ *   dS [R_max] fp32          dLoss/dw_r per row (rows >= R unspecified)
+ *   dLogits [T,E] fp32       w_j (dS_j - sum_k w_k dS_k) on the token's experts, 0 elsewhere
+ *   dW_r [E,d] dtype or NULL (requires W_r): dLogits^T X */
+moe_status moe_backward(const moe_dims* dims, const void* dY, const void* X, const void* W_r,
+                        const void* W_gate, const void* W_up, const void* W_down,
+                        const moe_plan* plan, const void* H_cache, void* dX, void* dW_gate,
+                        void* dW_up, void* dW_down, float* dS, float* dLogits, void* dW_r,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* Stages of the layer, for the timing facility below.  Each stage is one kernel, except ROUTE
+ * (top-K, counts, token rounding, offsets, placement) and DWR_GEMM (GEMM + slice reduction). */
+typedef enum {
+  MOE_STAGE_ROUTER_GEMM = 0, /* logits = X W_r^T + bias */
+  MOE_STAGE_ROUTE = 1,       /* top-K ... placement */
+  MOE_STAGE_TILES = 2,       /* grouped-GEMM tile offsets */
+  MOE_STAGE_UP_GEMM = 3,     /* gate/up GEMM + SwiGLU (also the backward's recompute) */
+  MOE_STAGE_DOWN_GEMM = 4,   /* down GEMM */
+  MOE_STAGE_PERMUTE = 5,     /* materialised permute */
+  MOE_STAGE_COMBINE = 6,     /* weighted combine */
+  MOE_STAGE_DACT_GEMM = 7,   /* backward dAct GEMM + SwiGLU backward + dS partials */
+  MOE_STAGE_DW_DOWN_GEMM = 8,
+  MOE_STAGE_DW_GU_GEMM = 9,
+  MOE_STAGE_DX_GEMM = 10,
+  MOE_STAGE_ROUTER_BWD = 11, /* dS, dLogits and the dX gather-sum */
+  MOE_STAGE_DWR_GEMM = 12,
+  MOE_STAGE_COUNT = 13
+} moe_stage;
+
+/* Host: stage timing for measurement tools (not thread-safe; for a single host thread).
+ * moe_timing_enable(1) makes every later call record a hipEvent pair around each stage it
+ * enqueues, on the call's stream, up to 4096 stage launches; moe_timing_enable(0) stops
+ * recording and releases the events (it synchronises with them first).  Returns MOE_OK or
+ * MOE_EHIP.  moe_timing_read(stage, ms, max) waits for the recorded events and writes the
+ * durations of that stage's launches (in launch order, milliseconds) to ms[0..]; it returns how
+ * many it wrote (at most max), or a negative moe_status.  Recording starts empty at every
+ * moe_timing_enable(1). */
+int moe_timing_enable(int on);
+int moe_timing_read(int stage, float* ms, int max);
+
+/* Host: static text for a status code. */
+const char* moe_status_string(int status);
+/* Host: message of the last failed call on this thread ("" if none). */
+const char* moe_last_error(void);
+/* Host: library version string. */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

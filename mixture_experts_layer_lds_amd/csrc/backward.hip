@@ -1,0 +1,521 @@
+// Backward of the MoE layer: dAct GEMM with the SwiGLU backward and router-score partials in its
+// epilogue, the weight-gradient GEMMs that reduce over each expert's rows, the dX GEMM, and the
+// router backward fused with the scatter-free dX gather-sum.
+//
+// Pages: SonicMoE page, optimization 1 (nothing the router gradient needs is cached; A is
+// recomputed from the cached pre-activations), section "反向传播优化" (dW1 reads gathered X,
+// dW2 and dH read gathered dO, each gather fused into the GEMM's operand load), and the
+// kernel-comparison table ("dS computation": dS_r = <dY_t W_down[e], A_r>, which equals
+// <dY_t, Y_r> without the expert output Y ever being stored).
+#include "gemm_core.h"
+#include "internal.h"
+
+namespace moe {
+
+static inline int grid8(int64_t n) { return (int)((n + 7) / 8 * 8); }
+
+// Adapter: a ColLoader bound to its k -> row-pointer functor.
+template <typename T, class KPtr>
+struct ColOp {
+  ColLoader<T> c;
+  KPtr f;
+  __device__ ColOp(KPtr f_, int mn_base, int mn_valid) : f(f_) { c.init(mn_base, mn_valid); }
+  __device__ void load(int kt) { c.load(kt, f); }
+  __device__ void store(char* lds) const { c.store(lds); }
+};
+template <typename T, class KPtr>
+__device__ ColOp<T, KPtr> make_col(KPtr f, int mn_base, int mn_valid) {
+  return ColOp<T, KPtr>(f, mn_base, mn_valid);
+}
+
+// ---------------------------------------------------------------------------------------------
+// dAct: dA'[r][j] = sum_c dY[t_r][c] W_down[e][c][j]  (M = rows of e, N = n, K = d).
+// Epilogue per (r, j), with G, U read from H and w = row_w[r]:
+//   A = silu(G) U;  dS partial += dA' A;  dA = w dA'
+//   dG = dA U sigmoid(G) (1 + G (1 - sigmoid(G)));  dU = dA silu(G)
+//   dH[r] = [dG | dU];  wA[r][j] = w A   (the down-weight gradient's operand)
+// dS partials are reduced over the tile's 128 columns in registers, lanes and LDS, and written
+// per column tile: dS_part[nt][r].
+// ---------------------------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(GEMM_THREADS, 2) void k_dact(
+    const int32_t* __restrict__ mtile_off, const int32_t* __restrict__ expert_off,
+    const int32_t* __restrict__ row_token, const float* __restrict__ row_w,
+    const T* __restrict__ dY, const T* __restrict__ Wd, const T* __restrict__ H,
+    T* __restrict__ dH, T* __restrict__ wA, float* __restrict__ dS_part, int64_t R_max, int d,
+    int n, int E, int NT) {
+  __shared__ __attribute__((aligned(16))) char lds[GEMM_LDS];
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int mt = lin / NT, nt = lin % NT;
+  GroupTile g;
+  if (!find_group_tile(mt, mtile_off, expert_off, E, g)) return;
+  const int n0 = nt * BN;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t rowb = (int64_t)d * sizeof(T);
+  RowLoader la;
+  la.init([&](int i) -> const char* {
+    return i < g.mrows ? reinterpret_cast<const char*>(dY) + (int64_t)row_token[g.m0 + i] * rowb : nullptr;
+  });
+  const char* wd = reinterpret_cast<const char*>(Wd) + (int64_t)g.e * d * n * sizeof(T) + n0 * sizeof(T);
+  auto lb = make_col<T>([&](int k) -> const char* {
+    return k < d ? wd + (int64_t)k * n * sizeof(T) : nullptr;
+  }, n0, n);
+  f32x16 acc[2][2];
+  gemm_mainloop<T>(la, lb, (int)(rowb / KB), acc, lds, wm, [&](int j) { return wn * 64 + j * 32; });
+
+  float part[2][16];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) part[i][v] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = acc_row(wm, i, v);
+      if (m >= g.mrows) continue;
+      const int64_t r = g.m0 + m;
+      const float w = row_w[r];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+        if (col >= n) continue;
+        const float G = to_f32(H[r * 2 * n + col]);
+        const float U = to_f32(H[r * 2 * n + n + col]);
+        const float sg = sigmoid_f32(G);
+        const float silu = G * sg;
+        const float A = silu * U;
+        const float dAp = acc[i][j][v];
+        part[i][v] += dAp * A;
+        const float dA = w * dAp;
+        dH[r * 2 * n + col] = from_f32<T>(dA * U * sg * (1.0f + G * (1.0f - sg)));
+        dH[r * 2 * n + n + col] = from_f32<T>(dA * silu);
+        wA[r * n + col] = from_f32<T>(w * A);
+      }
+    }
+  // reduce over the 32 columns held by lanes with equal (lane / 32)
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      float x = part[i][v];
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) x += __shfl_xor(x, o, 64);
+      part[i][v] = x;
+    }
+  float* red = reinterpret_cast<float*>(lds);  // [2 (wn)][128 rows]; LDS is free after the loop
+  if ((lane & 31) == 0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) red[wn * 128 + acc_row(wm, i, v)] = part[i][v];
+  }
+  __syncthreads();
+  if (threadIdx.x < 128 && (int)threadIdx.x < g.mrows)
+    dS_part[(int64_t)nt * R_max + g.m0 + threadIdx.x] = red[threadIdx.x] + red[128 + threadIdx.x];
+}
+
+int dact_ntiles(int64_t n) { return (int)cdiv(n, BN); }
+
+hipError_t launch_dact_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off,
+                            const void* dY, const void* W_down, const void* H, void* dH, void* wA,
+                            float* dS_part, hipStream_t st) {
+  const int NT = dact_ntiles(s.n);
+  const int grid = grid8(max_mtiles(s.R_max, s.E) * NT);
+  if (s.bf16)
+    k_dact<bf16><<<grid, GEMM_THREADS, 0, st>>>(mtile_off, p.expert_off, p.row_token, p.row_w,
+                                                (const bf16*)dY, (const bf16*)W_down, (const bf16*)H,
+                                                (bf16*)dH, (bf16*)wA, dS_part, s.R_max, (int)s.d,
+                                                (int)s.n, s.E, NT);
+  else
+    k_dact<float><<<grid, GEMM_THREADS, 0, st>>>(mtile_off, p.expert_off, p.row_token, p.row_w,
+                                                 (const float*)dY, (const float*)W_down, (const float*)H,
+                                                 (float*)dH, (float*)wA, dS_part, s.R_max, (int)s.d,
+                                                 (int)s.n, s.E, NT);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// dX_perm[r][c] = sum_j dG[r][j] W_gate[e][j][c] + dU[r][j] W_up[e][j][c]
+// (M = rows of e, N = d, K = 2n: k < n walks W_gate, k >= n walks W_up).
+// ---------------------------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(GEMM_THREADS, 2) void k_dx(
+    const int32_t* __restrict__ mtile_off, const int32_t* __restrict__ expert_off,
+    const T* __restrict__ dH, const T* __restrict__ Wg, const T* __restrict__ Wu,
+    T* __restrict__ dXp, int d, int n, int E, int NT) {
+  __shared__ __attribute__((aligned(16))) char lds[GEMM_LDS];
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int mt = lin / NT, nt = lin % NT;
+  GroupTile g;
+  if (!find_group_tile(mt, mtile_off, expert_off, E, g)) return;
+  const int n0 = nt * BN;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t rowb = (int64_t)2 * n * sizeof(T);
+  RowLoader la;
+  la.init([&](int i) -> const char* {
+    return i < g.mrows ? reinterpret_cast<const char*>(dH) + (int64_t)(g.m0 + i) * rowb : nullptr;
+  });
+  const int64_t wrow = (int64_t)d * sizeof(T);
+  const char* wg = reinterpret_cast<const char*>(Wg) + (int64_t)g.e * n * wrow + n0 * sizeof(T);
+  const char* wu = reinterpret_cast<const char*>(Wu) + (int64_t)g.e * n * wrow + n0 * sizeof(T);
+  auto lb = make_col<T>([&](int k) -> const char* {
+    if (k >= 2 * n) return nullptr;
+    return k < n ? wg + (int64_t)k * wrow : wu + (int64_t)(k - n) * wrow;
+  }, n0, d);
+  f32x16 acc[2][2];
+  gemm_mainloop<T>(la, lb, (int)(rowb / KB), acc, lds, wm, [&](int j) { return wn * 64 + j * 32; });
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = n0 + wn * 64 + j * 32 + (lane & 31);
+    if (c >= d) continue;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = acc_row(wm, i, v);
+        if (m < g.mrows) dXp[(int64_t)(g.m0 + m) * d + c] = from_f32<T>(acc[i][j][v]);
+      }
+  }
+}
+
+hipError_t launch_dx_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off,
+                          const void* dH, const void* W_gate, const void* W_up, void* dX_perm,
+                          hipStream_t st) {
+  const int NT = (int)cdiv(s.d, BN);
+  const int grid = grid8(max_mtiles(s.R_max, s.E) * NT);
+  if (s.bf16)
+    k_dx<bf16><<<grid, GEMM_THREADS, 0, st>>>(mtile_off, p.expert_off, (const bf16*)dH,
+                                              (const bf16*)W_gate, (const bf16*)W_up, (bf16*)dX_perm,
+                                              (int)s.d, (int)s.n, s.E, NT);
+  else
+    k_dx<float><<<grid, GEMM_THREADS, 0, st>>>(mtile_off, p.expert_off, (const float*)dH,
+                                               (const float*)W_gate, (const float*)W_up, (float*)dX_perm,
+                                               (int)s.d, (int)s.n, s.E, NT);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Weight gradients: one output tile of one expert per workgroup; K runs over the expert's rows.
+//   dW_down[e][c][j] = sum_r dY[t_r][c] wA[r][j]          (M = d, N = n)
+//   dW_gu[e][j][c]   = sum_r dH[r][j] X[t_r][c]           (M = 2n, N = d; j < n -> gate)
+// Both operands are MN-contiguous in memory and are transposed while staged.  Experts without
+// rows get zero tiles.
+// ---------------------------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(GEMM_THREADS, 2) void k_dw_down(
+    const int32_t* __restrict__ expert_off, const int32_t* __restrict__ row_token,
+    const T* __restrict__ dY, const T* __restrict__ wA, T* __restrict__ dWd, int d, int n,
+    int E, int MT, int NT) {
+  __shared__ __attribute__((aligned(16))) char lds[GEMM_LDS];
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int per = MT * NT;
+  const int e = lin / per;
+  if (e >= E) return;
+  const int rem = lin % per;
+  const int m0 = (rem / NT) * BM, n0 = (rem % NT) * BN;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int off = expert_off[e];
+  const int cnt = expert_off[e + 1] - off;
+  const char* dyb = reinterpret_cast<const char*>(dY) + m0 * sizeof(T);
+  const char* wab = reinterpret_cast<const char*>(wA) + n0 * sizeof(T);
+  auto la = make_col<T>([&](int k) -> const char* {
+    return k < cnt ? dyb + (int64_t)row_token[off + k] * d * sizeof(T) : nullptr;
+  }, m0, d);
+  auto lb = make_col<T>([&](int k) -> const char* {
+    return k < cnt ? wab + (int64_t)(off + k) * n * sizeof(T) : nullptr;
+  }, n0, n);
+  f32x16 acc[2][2];
+  gemm_mainloop<T>(la, lb, (int)cdiv(cnt, Mma<T>::BK), acc, lds, wm,
+                   [&](int j) { return wn * 64 + j * 32; });
+  T* out = dWd + (int64_t)e * d * n;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = n0 + wn * 64 + j * 32 + (lane & 31);
+    if (c >= n) continue;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + acc_row(wm, i, v);
+        if (m < d) out[(int64_t)m * n + c] = from_f32<T>(acc[i][j][v]);
+      }
+  }
+}
+
+hipError_t launch_dw_down_gemm(const Shape& s, const PlanPtrs& p, const void* dY, const void* wA,
+                               void* dW_down, hipStream_t st) {
+  const int MT = (int)cdiv(s.d, BM), NT = (int)cdiv(s.n, BN);
+  const int grid = grid8((int64_t)s.E * MT * NT);
+  if (s.bf16)
+    k_dw_down<bf16><<<grid, GEMM_THREADS, 0, st>>>(p.expert_off, p.row_token, (const bf16*)dY,
+                                                   (const bf16*)wA, (bf16*)dW_down, (int)s.d,
+                                                   (int)s.n, s.E, MT, NT);
+  else
+    k_dw_down<float><<<grid, GEMM_THREADS, 0, st>>>(p.expert_off, p.row_token, (const float*)dY,
+                                                    (const float*)wA, (float*)dW_down, (int)s.d,
+                                                    (int)s.n, s.E, MT, NT);
+  return hipGetLastError();
+}
+
+
+template <typename T>
+__global__ __launch_bounds__(GEMM_THREADS, 2) void k_dw_gu(
+    const int32_t* __restrict__ expert_off, const int32_t* __restrict__ row_token,
+    const T* __restrict__ dH, const T* __restrict__ X, T* __restrict__ dWg, T* __restrict__ dWu,
+    int d, int n, int E, int MT, int NT) {
+  __shared__ __attribute__((aligned(16))) char lds[GEMM_LDS];
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int per = MT * NT;
+  const int e = lin / per;
+  if (e >= E) return;
+  const int rem = lin % per;
+  const int m0 = (rem / NT) * BM, n0 = (rem % NT) * BN;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int off = expert_off[e];
+  const int cnt = expert_off[e + 1] - off;
+  const char* dhb = reinterpret_cast<const char*>(dH) + m0 * sizeof(T);
+  const char* xb = reinterpret_cast<const char*>(X) + n0 * sizeof(T);
+  auto la = make_col<T>([&](int k) -> const char* {
+    return k < cnt ? dhb + (int64_t)(off + k) * 2 * n * sizeof(T) : nullptr;
+  }, m0, 2 * n);
+  auto lb = make_col<T>([&](int k) -> const char* {
+    return k < cnt ? xb + (int64_t)row_token[off + k] * d * sizeof(T) : nullptr;
+  }, n0, d);
+  f32x16 acc[2][2];
+  gemm_mainloop<T>(la, lb, (int)cdiv(cnt, Mma<T>::BK), acc, lds, wm,
+                   [&](int j) { return wn * 64 + j * 32; });
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = n0 + wn * 64 + j * 32 + (lane & 31);
+    if (c >= d) continue;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + acc_row(wm, i, v);
+        if (m >= 2 * n) continue;
+        T* out = m < n ? dWg + ((int64_t)e * n + m) * d : dWu + ((int64_t)e * n + (m - n)) * d;
+        out[c] = from_f32<T>(acc[i][j][v]);
+      }
+  }
+}
+
+hipError_t launch_dw_gu_gemm(const Shape& s, const PlanPtrs& p, const void* dH, const void* X,
+                             void* dW_gate, void* dW_up, hipStream_t st) {
+  const int MT = (int)cdiv(2 * s.n, BM), NT = (int)cdiv(s.d, BN);
+  const int grid = grid8((int64_t)s.E * MT * NT);
+  if (s.bf16)
+    k_dw_gu<bf16><<<grid, GEMM_THREADS, 0, st>>>(p.expert_off, p.row_token, (const bf16*)dH,
+                                                 (const bf16*)X, (bf16*)dW_gate, (bf16*)dW_up,
+                                                 (int)s.d, (int)s.n, s.E, MT, NT);
+  else
+    k_dw_gu<float><<<grid, GEMM_THREADS, 0, st>>>(p.expert_off, p.row_token, (const float*)dH,
+                                                  (const float*)X, (float*)dW_gate, (float*)dW_up,
+                                                  (int)s.d, (int)s.n, s.E, MT, NT);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Router backward fused with the dX gather-sum; one wave per token (4 tokens per block).
+//   dS_r = sum over column tiles of dS_part;  s = sum_r w_r dS_r;  dL_r = w_r (dS_r - s)
+//   dLogits[t][:] = dL on the token's experts, 0 elsewhere (dLop: the same row in the GEMM dtype,
+//   padded to E_pad columns, the operand of the router weight gradient)
+//   dX[t] = sum_r dX_perm[r] + dL_r W_r[e_r]      (rows in ascending expert order)
+// ---------------------------------------------------------------------------------------------
+constexpr int RB_MAX_E = 1024;
+
+__device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ expert_off, int E, int r) {
+  int lo = 0, hi = E;  // expert_off[lo] <= r < expert_off[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (expert_off[mid] <= r) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_router_bwd(
+    const int32_t* __restrict__ tok_off, const int32_t* __restrict__ tok_row,
+    const int32_t* __restrict__ expert_off, const float* __restrict__ row_w,
+    const float* __restrict__ dS_part, int ntiles, int64_t R_max, const T* __restrict__ dXp,
+    const T* __restrict__ Wr, float* __restrict__ dS, float* __restrict__ dLogits,
+    T* __restrict__ dLop, int E_pad, T* __restrict__ dX, int T_, int d, int E) {
+  __shared__ float s_dl[4][RB_MAX_E];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T_) return;
+  const int base = tok_off[t], cnt = tok_off[t + 1] - base;
+  float* sdl = s_dl[wave];
+  for (int e = lane; e < E_pad; e += 64) sdl[e] = 0.0f;
+  // pass 1: s = sum_r w_r dS_r
+  float part = 0.0f;
+  for (int i = lane; i < cnt; i += 64) {
+    const int r = tok_row[base + i];
+    float ds = 0.0f;
+    for (int q = 0; q < ntiles; ++q) ds += dS_part[(int64_t)q * R_max + r];
+    part += row_w[r] * ds;
+  }
+  const float ssum = wave_sum(part);
+  // pass 2: dL per row, dS out, dense dL row in LDS
+  for (int i = lane; i < cnt; i += 64) {
+    const int r = tok_row[base + i];
+    float ds = 0.0f;
+    for (int q = 0; q < ntiles; ++q) ds += dS_part[(int64_t)q * R_max + r];
+    dS[r] = ds;
+    sdl[expert_of_row(expert_off, E, r)] = row_w[r] * (ds - ssum);
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  for (int e = lane; e < E_pad; e += 64) {
+    const float v = sdl[e];
+    if (e < E) dLogits[(int64_t)t * E + e] = v;
+    if (dLop) dLop[(int64_t)t * E_pad + e] = from_f32<T>(v);
+  }
+  // dX[t]: lanes own 16-byte column chunks; rows broadcast from LDS-free registers per chunk.
+  constexpr int VEC = 16 / sizeof(T);
+  const int nch = d / VEC;
+  for (int ch = lane; ch < nch; ch += 64) {
+    float acc[VEC];
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) acc[k] = 0.0f;
+    for (int i = 0; i < cnt; ++i) {
+      const int r = tok_row[base + i];
+      float f[VEC];
+      unpack16<T>(ld16(dXp + (int64_t)r * d + ch * VEC), f);
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) acc[k] += f[k];
+      if (Wr) {
+        const int e = expert_of_row(expert_off, E, r);
+        const float dl = sdl[e];
+        float wv[VEC];
+        unpack16<T>(ld16(Wr + (int64_t)e * d + ch * VEC), wv);
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) acc[k] += dl * wv[k];
+      }
+    }
+    st16(dX + (int64_t)t * d + ch * VEC, pack16<T>(acc));
+  }
+}
+
+hipError_t launch_router_bwd(const Shape& s, const PlanPtrs& p, const float* dS_part, int ntiles,
+                             const void* dX_perm, const void* W_r, float* dS, float* dLogits,
+                             void* dLop, int E_pad, void* dX, hipStream_t st) {
+  const int grid = (int)cdiv(s.T, 4);
+  if (s.bf16)
+    k_router_bwd<bf16><<<grid, 256, 0, st>>>(p.tok_off, p.tok_row, p.expert_off, p.row_w, dS_part, ntiles,
+                                             s.R_max, (const bf16*)dX_perm, (const bf16*)W_r, dS, dLogits,
+                                             (bf16*)dLop, E_pad, (bf16*)dX, (int)s.T, (int)s.d, s.E);
+  else
+    k_router_bwd<float><<<grid, 256, 0, st>>>(p.tok_off, p.tok_row, p.expert_off, p.row_w, dS_part, ntiles,
+                                              s.R_max, (const float*)dX_perm, (const float*)W_r, dS, dLogits,
+                                              (float*)dLop, E_pad, (float*)dX, (int)s.T, (int)s.d, s.E);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Router weight gradient dW_r[e][c] = sum_t dL[t][e] X[t][c]  (M = E, N = d, K = T).  The token
+// range is split into S contiguous slices so that the few output tiles still fill the chip;
+// each slice writes fp32 partials and a second kernel sums the slices in a fixed order.
+// ---------------------------------------------------------------------------------------------
+struct DwrPlan {
+  int MT, NT, S, TS;  // tiles, slices, tokens per slice (multiple of the stage depth)
+};
+static DwrPlan dwr_plan(const Shape& s) {
+  DwrPlan q;
+  q.MT = (int)cdiv(s.E, BM);
+  q.NT = (int)cdiv(s.d, BN);
+  const int bk = s.bf16 ? Mma<bf16>::BK : Mma<float>::BK;
+  const int tiles = q.MT * q.NT;
+  int S = (int)cdiv(2048, tiles);
+  const int max_s = (int)cdiv(s.T, bk);
+  if (S > max_s) S = max_s;
+  if (S > 64) S = 64;
+  if (S < 1) S = 1;
+  q.TS = (int)(cdiv(cdiv(s.T, S), bk) * bk);
+  q.S = (int)cdiv(s.T, q.TS);
+  return q;
+}
+
+size_t dwr_workspace_bytes(const Shape& s) {
+  const DwrPlan q = dwr_plan(s);
+  return q.S > 1 ? (size_t)q.S * s.E * s.d * sizeof(float) : 0;
+}
+
+template <typename T>
+__global__ __launch_bounds__(GEMM_THREADS, 2) void k_dwr(
+    const T* __restrict__ dLop, int E_pad, const T* __restrict__ X, float* __restrict__ part,
+    T* __restrict__ dWr, int T_, int d, int E, int MT, int NT, int S, int TS) {
+  __shared__ __attribute__((aligned(16))) char lds[GEMM_LDS];
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int per = MT * NT;
+  const int sl = lin / per;
+  if (sl >= S) return;
+  const int rem = lin % per;
+  const int m0 = (rem / NT) * BM, n0 = (rem % NT) * BN;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int t0 = sl * TS;
+  const int klen = min(TS, T_ - t0);
+  const char* ab = reinterpret_cast<const char*>(dLop) + m0 * sizeof(T);
+  const char* xb = reinterpret_cast<const char*>(X) + n0 * sizeof(T);
+  auto la = make_col<T>([&](int k) -> const char* {
+    return k < klen ? ab + (int64_t)(t0 + k) * E_pad * sizeof(T) : nullptr;
+  }, m0, E_pad);
+  auto lb = make_col<T>([&](int k) -> const char* {
+    return k < klen ? xb + (int64_t)(t0 + k) * d * sizeof(T) : nullptr;
+  }, n0, d);
+  f32x16 acc[2][2];
+  gemm_mainloop<T>(la, lb, (int)cdiv(klen, Mma<T>::BK), acc, lds, wm,
+                   [&](int j) { return wn * 64 + j * 32; });
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = n0 + wn * 64 + j * 32 + (lane & 31);
+    if (c >= d) continue;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + acc_row(wm, i, v);
+        if (m >= E) continue;
+        if (S == 1) dWr[(int64_t)m * d + c] = from_f32<T>(acc[i][j][v]);
+        else part[((int64_t)sl * E + m) * d + c] = acc[i][j][v];
+      }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_dwr_reduce(const float* __restrict__ part, int S,
+                                                    int64_t n, T* __restrict__ dWr) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.0f;
+  for (int q = 0; q < S; ++q) s += part[(int64_t)q * n + i];
+  dWr[i] = from_f32<T>(s);
+}
+
+hipError_t launch_dwr_gemm(const Shape& s, const void* dLop, int E_pad, const void* X, void* dW_r,
+                           void* ws, hipStream_t st) {
+  const DwrPlan q = dwr_plan(s);
+  const int grid = grid8((int64_t)q.S * q.MT * q.NT);
+  float* part = static_cast<float*>(ws);
+  const int64_t nout = (int64_t)s.E * s.d;
+  if (s.bf16) {
+    k_dwr<bf16><<<grid, GEMM_THREADS, 0, st>>>((const bf16*)dLop, E_pad, (const bf16*)X, part,
+                                               (bf16*)dW_r, (int)s.T, (int)s.d, s.E, q.MT, q.NT, q.S, q.TS);
+    if (q.S > 1) k_dwr_reduce<bf16><<<(int)cdiv(nout, 256), 256, 0, st>>>(part, q.S, nout, (bf16*)dW_r);
+  } else {
+    k_dwr<float><<<grid, GEMM_THREADS, 0, st>>>((const float*)dLop, E_pad, (const float*)X, part,
+                                                (float*)dW_r, (int)s.T, (int)s.d, s.E, q.MT, q.NT, q.S, q.TS);
+    if (q.S > 1) k_dwr_reduce<float><<<(int)cdiv(nout, 256), 256, 0, st>>>(part, q.S, nout, (float*)dW_r);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,97 @@
+// Permute (materialised expert-major copy of the tokens) and the scatter-free weighted combine.
+//
+// Pages: cloud.baidu.com "工作原理" steps 2 and 4 (dispatch tokens to their experts, return the
+// results to the tokens' positions; on one GPU both are local row movements); apxml.com
+// "自定义核与核融合" step 5 (combine the expert outputs weighted by the gate scores); SonicMoE page
+// kernel-comparison table (no separate scatter kernel: each token gathers its own rows, so no
+// two workgroups ever write the same output row and no atomics are needed).
+//
+// Both kernels stream whole rows with 16-byte accesses, one 64-lane wave per row (permute) or
+// per token (combine); the combine accumulates in fp32 over the token's rows in ascending expert
+// order and rounds once.
+#include "internal.h"
+
+namespace moe {
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_permute(const int32_t* __restrict__ meta,
+                                                 const int32_t* __restrict__ row_token,
+                                                 const T* __restrict__ X, T* __restrict__ Xp, int d) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= meta[0]) return;
+  const int64_t src = row_token[r];
+  constexpr int VEC = 16 / sizeof(T);
+  const int nch = d / VEC;
+  const T* s = X + src * d;
+  T* o = Xp + (int64_t)r * d;
+  for (int c = lane; c < nch; c += 64) st16_nt(o + c * VEC, ld16(s + c * VEC));
+}
+
+hipError_t launch_permute(const Shape& s, const PlanPtrs& p, const void* X, void* X_perm, hipStream_t st) {
+  const int grid = (int)cdiv(s.R_max, 4);
+  if (s.bf16) k_permute<bf16><<<grid, 256, 0, st>>>(p.meta, p.row_token, (const bf16*)X, (bf16*)X_perm, (int)s.d);
+  else k_permute<float><<<grid, 256, 0, st>>>(p.meta, p.row_token, (const float*)X, (float*)X_perm, (int)s.d);
+  return hipGetLastError();
+}
+
+// out[t] = sum_{r in rows(t)} w_r Y[r].  Lanes own 16-byte column chunks; up to 4 rows are
+// loaded before they are accumulated so that several loads are in flight per lane.
+template <typename T, bool WEIGHTED>
+__global__ __launch_bounds__(256) void k_combine(const int32_t* __restrict__ tok_off,
+                                                 const int32_t* __restrict__ tok_row,
+                                                 const float* __restrict__ row_w,
+                                                 const T* __restrict__ Y, T* __restrict__ out,
+                                                 int T_, int d) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T_) return;
+  const int base = tok_off[t], cnt = tok_off[t + 1] - base;
+  constexpr int VEC = 16 / sizeof(T);
+  const int nch = d / VEC;
+  for (int c = lane; c < nch; c += 64) {
+    float acc[VEC];
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) acc[k] = 0.0f;
+    int i = 0;
+    for (; i + 4 <= cnt; i += 4) {
+      u32x4 v[4];
+      float w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = tok_row[base + i + q];
+        v[q] = ld16_nt(Y + (int64_t)r * d + c * VEC);
+        w[q] = WEIGHTED ? row_w[r] : 1.0f;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float f[VEC];
+        unpack16<T>(v[q], f);
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) acc[k] += w[q] * f[k];
+      }
+    }
+    for (; i < cnt; ++i) {
+      const int r = tok_row[base + i];
+      const float w = WEIGHTED ? row_w[r] : 1.0f;
+      float f[VEC];
+      unpack16<T>(ld16_nt(Y + (int64_t)r * d + c * VEC), f);
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) acc[k] += w * f[k];
+    }
+    st16(out + (int64_t)t * d + c * VEC, pack16<T>(acc));
+  }
+}
+
+hipError_t launch_combine(const Shape& s, const PlanPtrs& p, const void* Y_perm, bool weighted,
+                          void* out, hipStream_t st) {
+  const int grid = (int)cdiv(s.T, 4);
+#define MOE_COMB(TT, W) k_combine<TT, W><<<grid, 256, 0, st>>>(p.tok_off, p.tok_row, p.row_w, \
+      (const TT*)Y_perm, (TT*)out, (int)s.T, (int)s.d)
+  if (s.bf16) { if (weighted) MOE_COMB(bf16, true); else MOE_COMB(bf16, false); }
+  else { if (weighted) MOE_COMB(float, true); else MOE_COMB(float, false); }
+#undef MOE_COMB
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,217 @@
+// Forward GEMMs: router logits, grouped gate/up projection with the SwiGLU epilogue, grouped
+// down projection.
+//
+// Pages: apxml.com "自定义核与核融合" steps 1 and 4 (gate scores; the experts' dense matmuls);
+// SonicMoE page "Gather 与加载融合" (the grouped GEMM reads either packed rows or rows gathered
+// by index during its operand load) and the kernel-comparison table (SwiGLU fused into the GEMM);
+// apxml.com "条件参数加载" (only experts that received tokens have their weights read: the tile
+// list holds no tile for an empty expert).
+#include "gemm_core.h"
+#include "internal.h"
+
+namespace moe {
+
+// mtile_off[E+1]: exclusive scan over experts of ceil(counts[e] / BM).  One block, E <= 1024.
+__global__ __launch_bounds__(1024) void k_tile_offsets(const int32_t* __restrict__ counts, int E,
+                                                       int32_t* __restrict__ mtile_off) {
+  __shared__ int sh[16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int x = threadIdx.x < E ? (counts[threadIdx.x] + BM - 1) / BM : 0;
+  int inc = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) sh[wave] = inc;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int w = 0; w < 16; ++w) {
+    base += (w < wave) ? sh[w] : 0;
+    tot += sh[w];
+  }
+  if (threadIdx.x < E) mtile_off[threadIdx.x] = base + inc - x;
+  if (threadIdx.x == 0) mtile_off[E] = tot;
+}
+
+hipError_t launch_tile_offsets(const int32_t* counts, int E, int32_t* mtile_off, hipStream_t st) {
+  k_tile_offsets<<<1, 1024, 0, st>>>(counts, E, mtile_off);
+  return hipGetLastError();
+}
+
+int64_t max_mtiles(int64_t R_max, int E) { return R_max / BM + E; }
+
+static inline int grid8(int64_t n) { return (int)((n + 7) / 8 * 8); }
+
+// ---------------------------------------------------------------------------------------------
+// Router: logits[t][e] = sum_i X[t][i] W_r[e][i] + bias[e]
+// ---------------------------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(GEMM_THREADS, 2) void k_router(const T* __restrict__ X,
+                                                           const T* __restrict__ Wr,
+                                                           const float* __restrict__ bias,
+                                                           float* __restrict__ logits, int T_, int d,
+                                                           int E, int NT) {
+  __shared__ __attribute__((aligned(16))) char lds[GEMM_LDS];
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int mt = lin / NT, nt = lin % NT;
+  const int m0 = mt * BM, n0 = nt * BN;
+  if (m0 >= T_) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t rowb = (int64_t)d * sizeof(T);
+  RowLoader la, lb;
+  la.init([&](int i) -> const char* {
+    return m0 + i < T_ ? reinterpret_cast<const char*>(X) + (m0 + i) * rowb : nullptr;
+  });
+  lb.init([&](int i) -> const char* {
+    return n0 + i < E ? reinterpret_cast<const char*>(Wr) + (n0 + i) * rowb : nullptr;
+  });
+  f32x16 acc[2][2];
+  gemm_mainloop<T>(la, lb, (int)(rowb / KB), acc, lds, wm, [&](int j) { return wn * 64 + j * 32; });
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+    if (n >= E) continue;
+    const float b = bias ? bias[n] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + acc_row(wm, i, v);
+        if (m < T_) logits[(int64_t)m * E + n] = acc[i][j][v] + b;
+      }
+  }
+}
+
+hipError_t launch_router_gemm(const Shape& s, const void* X, const void* W_r, const float* bias,
+                              float* logits, hipStream_t st) {
+  const int NT = (int)cdiv(s.E, BN);
+  const int n = grid8(cdiv(s.T, BM) * NT);
+  if (s.bf16)
+    k_router<bf16><<<n, GEMM_THREADS, 0, st>>>((const bf16*)X, (const bf16*)W_r, bias, logits,
+                                                (int)s.T, (int)s.d, s.E, NT);
+  else
+    k_router<float><<<n, GEMM_THREADS, 0, st>>>((const float*)X, (const float*)W_r, bias, logits,
+                                                 (int)s.T, (int)s.d, s.E, NT);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Gate/up projection.  Tile = 128 rows of one expert x 64 output columns j0..j0+63; the B tile
+// stacks W_gate[e] rows j0..j0+63 over W_up[e] rows j0..j0+63, and wave column wn takes gate
+// block wn*32 and up block 64 + wn*32, so each lane holds G and U of the same (row, column) in
+// matching accumulators.  Epilogue: A = silu(G) * U (fp32, rounded once), optional H = [G | U].
+// ---------------------------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(GEMM_THREADS, 2) void k_up(
+    const int32_t* __restrict__ mtile_off, const int32_t* __restrict__ expert_off,
+    const int32_t* __restrict__ row_token, const T* __restrict__ A_in, int gathered,
+    const T* __restrict__ Wg, const T* __restrict__ Wu, T* __restrict__ act, T* __restrict__ H,
+    int d, int n, int E, int NT) {
+  __shared__ __attribute__((aligned(16))) char lds[GEMM_LDS];
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int mt = lin / NT, nt = lin % NT;
+  GroupTile g;
+  if (!find_group_tile(mt, mtile_off, expert_off, E, g)) return;
+  const int j0 = nt * 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t rowb = (int64_t)d * sizeof(T);
+  RowLoader la, lb;
+  la.init([&](int i) -> const char* {
+    if (i >= g.mrows) return nullptr;
+    const int64_t src = gathered ? row_token[g.m0 + i] : (int64_t)(g.m0 + i);
+    return reinterpret_cast<const char*>(A_in) + src * rowb;
+  });
+  const char* wg = reinterpret_cast<const char*>(Wg) + ((int64_t)g.e * n + j0) * rowb;
+  const char* wu = reinterpret_cast<const char*>(Wu) + ((int64_t)g.e * n + j0) * rowb;
+  lb.init([&](int i) -> const char* { return i < 64 ? wg + i * rowb : wu + (i - 64) * rowb; });
+  f32x16 acc[2][2];
+  gemm_mainloop<T>(la, lb, (int)(rowb / KB), acc, lds, wm, [&](int j) { return j * 64 + wn * 32; });
+  const int col = j0 + wn * 32 + (lane & 31);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = acc_row(wm, i, v);
+      if (m >= g.mrows) continue;
+      const int64_t r = g.m0 + m;
+      const float gv = acc[i][0][v], uv = acc[i][1][v];
+      act[r * n + col] = from_f32<T>(gv * sigmoid_f32(gv) * uv);
+      if (H) {
+        H[r * 2 * n + col] = from_f32<T>(gv);
+        H[r * 2 * n + n + col] = from_f32<T>(uv);
+      }
+    }
+}
+
+hipError_t launch_up_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off,
+                          const void* A_in, bool gathered, const void* W_gate, const void* W_up,
+                          void* act, void* H, hipStream_t st) {
+  const int NT = (int)(s.n / 64);
+  const int grid = grid8(max_mtiles(s.R_max, s.E) * NT);
+  if (s.bf16)
+    k_up<bf16><<<grid, GEMM_THREADS, 0, st>>>(mtile_off, p.expert_off, p.row_token, (const bf16*)A_in,
+                                              gathered, (const bf16*)W_gate, (const bf16*)W_up,
+                                              (bf16*)act, (bf16*)H, (int)s.d, (int)s.n, s.E, NT);
+  else
+    k_up<float><<<grid, GEMM_THREADS, 0, st>>>(mtile_off, p.expert_off, p.row_token, (const float*)A_in,
+                                               gathered, (const float*)W_gate, (const float*)W_up,
+                                               (float*)act, (float*)H, (int)s.d, (int)s.n, s.E, NT);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Down projection: Y[r][c] = sum_j Act[r][j] W_down[e][c][j];  tile 128 rows x 128 columns of d.
+// ---------------------------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(GEMM_THREADS, 2) void k_down(
+    const int32_t* __restrict__ mtile_off, const int32_t* __restrict__ expert_off,
+    const T* __restrict__ act, const T* __restrict__ Wd, T* __restrict__ Y, int d, int n, int E,
+    int NT) {
+  __shared__ __attribute__((aligned(16))) char lds[GEMM_LDS];
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int mt = lin / NT, nt = lin % NT;
+  GroupTile g;
+  if (!find_group_tile(mt, mtile_off, expert_off, E, g)) return;
+  const int n0 = nt * BN;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t rowb = (int64_t)n * sizeof(T);
+  RowLoader la, lb;
+  la.init([&](int i) -> const char* {
+    return i < g.mrows ? reinterpret_cast<const char*>(act) + (int64_t)(g.m0 + i) * rowb : nullptr;
+  });
+  const char* wd = reinterpret_cast<const char*>(Wd) + (int64_t)g.e * d * rowb;
+  lb.init([&](int i) -> const char* { return n0 + i < d ? wd + (int64_t)(n0 + i) * rowb : nullptr; });
+  f32x16 acc[2][2];
+  gemm_mainloop<T>(la, lb, (int)(rowb / KB), acc, lds, wm, [&](int j) { return wn * 64 + j * 32; });
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = n0 + wn * 64 + j * 32 + (lane & 31);
+    if (c >= d) continue;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = acc_row(wm, i, v);
+        if (m < g.mrows) Y[(int64_t)(g.m0 + m) * d + c] = from_f32<T>(acc[i][j][v]);
+      }
+  }
+}
+
+hipError_t launch_down_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off,
+                            const void* act, const void* W_down, void* Y, hipStream_t st) {
+  const int NT = (int)cdiv(s.d, BN);
+  const int grid = grid8(max_mtiles(s.R_max, s.E) * NT);
+  if (s.bf16)
+    k_down<bf16><<<grid, GEMM_THREADS, 0, st>>>(mtile_off, p.expert_off, (const bf16*)act,
+                                                (const bf16*)W_down, (bf16*)Y, (int)s.d, (int)s.n, s.E, NT);
+  else
+    k_down<float><<<grid, GEMM_THREADS, 0, st>>>(mtile_off, p.expert_off, (const float*)act,
+                                                 (const float*)W_down, (float*)Y, (int)s.d, (int)s.n, s.E, NT);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,89 @@
+// Internal launcher interface between the C-ABI host layer (moe_api.cpp) and the kernels.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace moe {
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct PlanPtrs {
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t* counts;
+  int32_t* expert_off;
+  int32_t* row_token;
+  float* row_w;
+  int32_t* tok_off;
+  int32_t* tok_row;
+  int32_t* meta;
+};
+
+// Problem description shared by the expert-GEMM launchers.
+struct Shape {
+  int64_t T, d, n;
+  int E, K;
+  int64_t R_max;
+  bool bf16;  // element type of activations and weights (else fp32)
+};
+
+// ---- routing (route.hip) ----
+size_t route_workspace_bytes(int64_t T, int E);
+hipError_t launch_route(const float* logits, int64_t T, int E, int K, int round_mode, int tile_m,
+                        const PlanPtrs& p, void* ws, hipStream_t st);
+
+// ---- grouped GEMM tile schedule (gemm.hip) ----
+// mtile_off[E+1] = exclusive scan over experts of ceil(counts[e] / 128).
+hipError_t launch_tile_offsets(const int32_t* counts, int E, int32_t* mtile_off, hipStream_t st);
+int64_t max_mtiles(int64_t R_max, int E);
+
+// ---- forward GEMMs (gemm_fwd.hip) ----
+// logits[T,E] (fp32) = X[T,d] W_r[E,d]^T + bias
+hipError_t launch_router_gemm(const Shape& s, const void* X, const void* W_r, const float* bias,
+                              float* logits, hipStream_t st);
+// Act[R,n] = silu(G) * U with [G|U] = X[rows] [W_gate|W_up]^T; H[R,2n] optional
+hipError_t launch_up_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off,
+                          const void* A_in, bool gathered, const void* W_gate, const void* W_up,
+                          void* act, void* H, hipStream_t st);
+// Y[R,d] = Act[R,n] W_down[e]^T
+hipError_t launch_down_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off,
+                            const void* act, const void* W_down, void* Y, hipStream_t st);
+
+// ---- permute / combine (combine.hip) ----
+hipError_t launch_permute(const Shape& s, const PlanPtrs& p, const void* X, void* X_perm, hipStream_t st);
+hipError_t launch_combine(const Shape& s, const PlanPtrs& p, const void* Y_perm, bool weighted,
+                          void* out, hipStream_t st);
+
+// ---- backward (backward.hip) ----
+// dAct GEMM with the SwiGLU backward and dS partials in its epilogue:
+//   dA' = dY[rows] W_down[e]   (N = n);  dS_part[nt][r] = sum over the tile's columns of dA' * A
+//   dH[r] = [dG | dU];  wA[r] = w_r * A_r
+hipError_t launch_dact_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off,
+                            const void* dY, const void* W_down, const void* H, void* dH, void* wA,
+                            float* dS_part, hipStream_t st);
+int dact_ntiles(int64_t n);
+// dX_perm[R,d] = dG W_gate[e] + dU W_up[e]
+hipError_t launch_dx_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off,
+                          const void* dH, const void* W_gate, const void* W_up, void* dX_perm,
+                          hipStream_t st);
+// dW_down[e] = (w dY[rows])^T A = dY[rows]^T wA
+hipError_t launch_dw_down_gemm(const Shape& s, const PlanPtrs& p, const void* dY, const void* wA,
+                               void* dW_down, hipStream_t st);
+// dW_gate[e] | dW_up[e] = dH^T X[rows]
+hipError_t launch_dw_gu_gemm(const Shape& s, const PlanPtrs& p, const void* dH, const void* X,
+                             void* dW_gate, void* dW_up, hipStream_t st);
+// Router backward + dX gather-sum, one wave per token:
+//   dS[r] = sum of partials; dL = w (dS - <w, dS>); dLogits row; dLop[t][e] (GEMM operand);
+//   dX[t] = sum_r dX_perm[r] (+ sum_r dL_r W_r[e_r] if W_r)
+hipError_t launch_router_bwd(const Shape& s, const PlanPtrs& p, const float* dS_part, int ntiles,
+                             const void* dX_perm, const void* W_r, float* dS, float* dLogits,
+                             void* dLop, int E_pad, void* dX, hipStream_t st);
+// dW_r[E,d] = dL^T X (split over tokens, fp32 partials, fixed-order reduction)
+size_t dwr_workspace_bytes(const Shape& s);
+hipError_t launch_dwr_gemm(const Shape& s, const void* dLop, int E_pad, const void* X, void* dW_r,
+                           void* ws, hipStream_t st);
+
+}  // namespace moe

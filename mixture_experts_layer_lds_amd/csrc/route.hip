@@ -1,0 +1,429 @@
+// Routing kernels: top-K + softmax, per-expert membership bitmap and counts, token rounding,
+// offsets and the (token, expert) -> row placement.
+//
+// Pages: cloud.baidu.com "工作原理" (gate network, top_k), apxml.com "自定义核与核融合" steps 1-2,
+// SonicMoE page optimization 3 (token rounding), ThunderEP article section 2.2.2 (int32 row index
+// lists).  Design for gfx950: one 64-lane wave per token for selection; the membership of every
+// (token, expert) pair lives in a bitmap bits[E][ceil(T/32)] built in LDS per block, so that
+// per-expert counts, in-expert ranks (rows ordered by token id) and token rounding are popcounts
+// and scans over 32-bit words; no atomics touch global memory and every result is deterministic.
+#include "internal.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------------------------
+// top-K: one wave per token.  Lane i holds logits e = i + 64 j.  K rounds of a wave arg-max
+// under the order (logit descending, expert id ascending); -0.0 and +0.0 compare equal because
+// the comparisons are floating-point comparisons.  Then the softmax over the K winners.  The
+// winners set their bit in the block's LDS bitmap (bitwise OR is order independent).
+// ---------------------------------------------------------------------------------------------
+constexpr int TOPK_TOKENS_PER_BLOCK = 64;  // two 32-bit bitmap words per expert per block
+
+template <int EPL>
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int K,
+                                              int W, int32_t* __restrict__ topk_idx,
+                                              float* __restrict__ topk_w, uint32_t* __restrict__ bits) {
+  extern __shared__ uint32_t sbits[];  // [E][2]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * TOPK_TOKENS_PER_BLOCK;
+  for (int i = threadIdx.x; i < 2 * E; i += blockDim.x) sbits[i] = 0u;
+  __syncthreads();
+  for (int tt = wave; tt < TOPK_TOKENS_PER_BLOCK; tt += 4) {
+    const int t = t0 + tt;
+    if (t >= T) break;
+    const float* row = logits + (int64_t)t * E;
+    float v[EPL];
+    bool live[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane + 64 * j;
+      live[j] = e < E;
+      v[j] = live[j] ? row[e] : 0.0f;
+    }
+    float my_v = 0.0f;
+    int my_e = 0;
+    for (int k = 0; k < K; ++k) {
+      // lane-local best among live slots (ties: lower id = lower j)
+      float bv = 0.0f;
+      int be = 0x7fffffff;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        if (live[j] && (be == 0x7fffffff || v[j] > bv)) { bv = v[j]; be = lane + 64 * j; }
+      // wave arg-max; empty lanes carry id INT_MAX and never beat a live candidate
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oe = __shfl_xor(be, o, 64);
+        const bool take = (oe != 0x7fffffff) &&
+                          (be == 0x7fffffff || ov > bv || (ov == bv && oe < be));
+        if (take) { bv = ov; be = oe; }
+      }
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        if (be == lane + 64 * j) live[j] = false;
+      if (lane == k) { my_v = bv; my_e = be; }
+    }
+    const float vmax = __shfl(my_v, 0, 64);
+    const float ex = lane < K ? __expf(my_v - vmax) : 0.0f;
+    const float s = wave_sum(ex);
+    if (lane < K) {
+      topk_idx[(int64_t)t * K + lane] = my_e;
+      topk_w[(int64_t)t * K + lane] = ex / s;
+      atomicOr(&sbits[my_e * 2 + (tt >> 5)], 1u << (tt & 31));
+    }
+  }
+  __syncthreads();
+  const int w0 = blockIdx.x * 2;
+  for (int i = threadIdx.x; i < 2 * E; i += blockDim.x) {
+    const int e = i >> 1, w = w0 + (i & 1);
+    if (w < W) bits[(int64_t)e * W + w] = sbits[i];
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Block-wide exclusive scan helper (256 threads).  Returns the exclusive prefix of `x` and the
+// block total.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ int block_exscan_256(int x, int* total, int* sh /*[4]*/) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) sh[wave] = inc;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    base += (w < wave) ? sh[w] : 0;
+    tot += sh[w];
+  }
+  __syncthreads();
+  *total = tot;
+  return base + inc - x;
+}
+
+// Per expert (one block each): counts[e] = popcount of its bitmap row, and the exclusive prefix
+// of popcounts per word, which is the rank of a member token among the expert's earlier tokens.
+__global__ __launch_bounds__(256) void k_count(const uint32_t* __restrict__ bits, int W,
+                                               int32_t* __restrict__ wprefix,
+                                               int32_t* __restrict__ counts) {
+  __shared__ int sh[4];
+  const int e = blockIdx.x;
+  const uint32_t* b = bits + (int64_t)e * W;
+  int32_t* p = wprefix + (int64_t)e * W;
+  int carry = 0;
+  for (int w0 = 0; w0 < W; w0 += 256) {
+    const int w = w0 + threadIdx.x;
+    const int c = w < W ? __popc(b[w]) : 0;
+    int tot;
+    const int ex = block_exscan_256(c, &tot, sh);
+    if (w < W) p[w] = carry + ex;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) counts[e] = carry;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Token rounding, one 1024-thread block per expert.
+// Key of token t for expert e, larger = chosen first:
+//   adding  (best non-members): (ord(L[t,e]) << 32) | ~t      -> larger logit, then lower t
+//   dropping (worst members):   (~ord(L[t,e]) << 32) | t      -> smaller logit, then higher t
+// ord() maps fp32 to an order-preserving uint32 (with -0.0 folded onto +0.0).  Keys are unique
+// (t is), so the set of the `amount` largest keys is unique; it is found by an 8-pass radix
+// select (8-bit digits, LDS histograms with integer atomics), and the bitmap row is rewritten.
+// The expert's logit column is cached in LDS when T <= TR_LDS_TOKENS.
+// ---------------------------------------------------------------------------------------------
+constexpr int TR_THREADS = 1024;
+constexpr int TR_LDS_TOKENS = 32768;
+
+__device__ __forceinline__ uint32_t ord_f32(float x) {
+  uint32_t u = __float_as_uint(x == 0.0f ? 0.0f : x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__global__ __launch_bounds__(TR_THREADS) void k_token_round(const float* __restrict__ logits, int T,
+                                                           int E, int W, int M, int mode,
+                                                           uint32_t* __restrict__ bits,
+                                                           const int32_t* __restrict__ counts) {
+  extern __shared__ uint32_t s_ord[];  // [min(T, TR_LDS_TOKENS)] (only if cached)
+  __shared__ int hist[256];
+  __shared__ uint64_t s_prefix;
+  __shared__ int s_need;
+  const int e = blockIdx.x;
+  const int c = counts[e];
+  const int r = c % M;
+  if (r == 0) return;
+  bool add;
+  if (mode == 1) add = 2 * r >= M;
+  else if (mode == 2) add = true;
+  else add = false;
+  if (add && (int64_t)c + (M - r) > T) add = false;
+  const int amount = add ? (M - r) : r;
+  const bool cached = T <= TR_LDS_TOKENS;
+  uint32_t* brow = bits + (int64_t)e * W;
+  if (cached) {
+    for (int t = threadIdx.x; t < T; t += TR_THREADS) s_ord[t] = ord_f32(logits[(int64_t)t * E + e]);
+    __syncthreads();
+  }
+  auto key_of = [&](int t, bool& cand) -> uint64_t {
+    const bool mem = (brow[t >> 5] >> (t & 31)) & 1u;
+    cand = add ? !mem : mem;
+    const uint32_t o = cached ? s_ord[t] : ord_f32(logits[(int64_t)t * E + e]);
+    return add ? (((uint64_t)o << 32) | (uint32_t)(~(uint32_t)t))
+               : (((uint64_t)(~o) << 32) | (uint32_t)t);
+  };
+  uint64_t prefix = 0;  // digits fixed so far (high bits)
+  int need = amount;    // how many keys >= threshold still to take within the current prefix
+  for (int pass = 0; pass < 8; ++pass) {
+    const int shift = 56 - 8 * pass;
+    for (int i = threadIdx.x; i < 256; i += TR_THREADS) hist[i] = 0;
+    __syncthreads();
+    const uint64_t hi_mask = pass == 0 ? 0ull : (~0ull << (shift + 8));
+    for (int t = threadIdx.x; t < T; t += TR_THREADS) {
+      bool cand;
+      const uint64_t k = key_of(t, cand);
+      if (cand && (k & hi_mask) == prefix) atomicAdd(&hist[(k >> shift) & 255], 1);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int acc = 0, d = 255;
+      for (; d > 0; --d) {
+        if (acc + hist[d] >= need) break;
+        acc += hist[d];
+      }
+      s_prefix = prefix | ((uint64_t)d << shift);
+      s_need = need - acc;
+    }
+    __syncthreads();
+    prefix = s_prefix;
+    need = s_need;
+    __syncthreads();
+  }
+  // prefix is now the smallest chosen key: every candidate with key >= prefix flips membership.
+  const uint64_t thr = prefix;
+  for (int w = threadIdx.x; w < W; w += TR_THREADS) {
+    uint32_t word = brow[w];
+    for (int b = 0; b < 32; ++b) {
+      const int t = w * 32 + b;
+      if (t >= T) break;
+      bool cand;
+      const uint64_t k = key_of(t, cand);
+      if (cand && k >= thr) word ^= (1u << b);
+    }
+    // all reads of this word by other threads happen before any write: each word is owned by
+    // exactly one thread in this loop, and key_of only reads bits of the word it evaluates.
+    brow[w] = word;
+  }
+}
+
+// expert_off = exclusive scan of counts (E <= 1024, one block of 1024 threads); meta[0] = R.
+__global__ __launch_bounds__(1024) void k_offsets(const int32_t* __restrict__ counts, int E,
+                                                  int32_t* __restrict__ expert_off,
+                                                  int32_t* __restrict__ meta) {
+  __shared__ int sh[16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int x = threadIdx.x < E ? counts[threadIdx.x] : 0;
+  int inc = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) sh[wave] = inc;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int w = 0; w < 16; ++w) {
+    base += (w < wave) ? sh[w] : 0;
+    tot += sh[w];
+  }
+  if (threadIdx.x < E) expert_off[threadIdx.x] = base + inc - x;
+  if (threadIdx.x == 0) {
+    expert_off[E] = tot;
+    meta[0] = tot;
+  }
+}
+
+// Tokens' final expert counts after token rounding -> tok_off[t+1] (scanned afterwards).
+__global__ __launch_bounds__(256) void k_tok_count(const uint32_t* __restrict__ bits, int T, int E,
+                                                   int W, int32_t* __restrict__ tok_off) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  const int w = t >> 5;
+  const uint32_t m = 1u << (t & 31);
+  int c = 0;
+  for (int e = 0; e < E; ++e) c += (bits[(int64_t)e * W + w] & m) ? 1 : 0;
+  tok_off[t + 1] = c;
+}
+
+// Plain top-K: every token has K rows.
+__global__ __launch_bounds__(256) void k_tok_fill(int T, int K, int32_t* __restrict__ tok_off) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t <= T) tok_off[t] = t * K;
+}
+
+// In-place scan: tok_off[1..T] holds counts; afterwards tok_off[t] = sum of counts before t.
+// One block of 1024 threads, sequential over chunks of 1024 * 8 tokens.
+__global__ __launch_bounds__(1024) void k_tok_scan(int T, int32_t* __restrict__ tok_off) {
+  __shared__ int sh[16];
+  __shared__ int s_carry;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (threadIdx.x == 0) s_carry = 0;
+  __syncthreads();
+  constexpr int PER = 8;
+  for (int base0 = 0; base0 < T; base0 += 1024 * PER) {
+    int v[PER];
+    int loc = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int t = base0 + threadIdx.x * PER + i;
+      v[i] = t < T ? tok_off[t + 1] : 0;
+      loc += v[i];
+    }
+    int inc = loc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += y;
+    }
+    if (lane == 63) sh[wave] = inc;
+    __syncthreads();
+    int wb = 0, tot = 0;
+    for (int w = 0; w < 16; ++w) {
+      wb += (w < wave) ? sh[w] : 0;
+      tot += sh[w];
+    }
+    int run = s_carry + wb + inc - loc;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int t = base0 + threadIdx.x * PER + i;
+      run += v[i];
+      if (t < T) tok_off[t + 1] = run;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) s_carry += tot;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) tok_off[0] = 0;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Placement: one thread per token.  The token's final experts in ascending id (plain top-K: its
+// K ids sorted; token rounding: the set bits of its bitmap column); gate weights = softmax of
+// its final logits; row of (t, e) = expert_off[e] + (members of e before t), a popcount.
+// ---------------------------------------------------------------------------------------------
+template <bool ROUNDED>
+__global__ __launch_bounds__(256) void k_place(const float* __restrict__ logits, int T, int E,
+                                               int K, int W, const int32_t* __restrict__ topk_idx,
+                                               const uint32_t* __restrict__ bits,
+                                               const int32_t* __restrict__ wprefix,
+                                               const int32_t* __restrict__ expert_off,
+                                               const int32_t* __restrict__ tok_off,
+                                               int32_t* __restrict__ row_token,
+                                               float* __restrict__ row_w,
+                                               int32_t* __restrict__ tok_row) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  const float* L = logits + (int64_t)t * E;
+  const int w = t >> 5;
+  const uint32_t below = (1u << (t & 31)) - 1u;
+  const uint32_t me = 1u << (t & 31);
+  const int base = tok_off[t];
+  if (!ROUNDED) {
+    int ids[16];
+    for (int k = 0; k < K; ++k) ids[k] = topk_idx[(int64_t)t * K + k];
+    for (int k = 1; k < K; ++k) {  // insertion sort, K <= 16
+      const int x = ids[k];
+      int j = k - 1;
+      while (j >= 0 && ids[j] > x) { ids[j + 1] = ids[j]; --j; }
+      ids[j + 1] = x;
+    }
+    float m = L[ids[0]];
+    for (int k = 1; k < K; ++k) m = fmaxf(m, L[ids[k]]);
+    float s = 0.0f;
+    for (int k = 0; k < K; ++k) s += __expf(L[ids[k]] - m);
+    const float inv = 1.0f / s;
+    for (int k = 0; k < K; ++k) {
+      const int e = ids[k];
+      const int row = expert_off[e] + wprefix[(int64_t)e * W + w] + __popc(bits[(int64_t)e * W + w] & below);
+      row_token[row] = t;
+      row_w[row] = __expf(L[e] - m) * inv;
+      tok_row[base + k] = row;
+    }
+  } else {
+    const int cnt = tok_off[t + 1] - base;
+    if (cnt == 0) return;
+    float m = -INFINITY;
+    for (int e = 0; e < E; ++e)
+      if (bits[(int64_t)e * W + w] & me) m = fmaxf(m, L[e]);
+    float s = 0.0f;
+    for (int e = 0; e < E; ++e)
+      if (bits[(int64_t)e * W + w] & me) s += __expf(L[e] - m);
+    const float inv = 1.0f / s;
+    int i = 0;
+    for (int e = 0; e < E; ++e) {
+      const uint32_t word = bits[(int64_t)e * W + w];
+      if (!(word & me)) continue;
+      const int row = expert_off[e] + wprefix[(int64_t)e * W + w] + __popc(word & below);
+      row_token[row] = t;
+      row_w[row] = __expf(L[e] - m) * inv;
+      tok_row[base + i] = row;
+      ++i;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Host launcher for the whole routing plan from fp32 logits.
+// ---------------------------------------------------------------------------------------------
+size_t route_workspace_bytes(int64_t T, int E) {
+  const int64_t W = cdiv(T, 32);
+  return align_up((size_t)E * W * 4, 256) * 2;
+}
+
+hipError_t launch_route(const float* logits, int64_t T, int E, int K, int round_mode, int tile_m,
+                        const PlanPtrs& p, void* ws, hipStream_t st) {
+  const int W = (int)cdiv(T, 32);
+  uint32_t* bits = static_cast<uint32_t*>(ws);
+  int32_t* wprefix = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + align_up((size_t)E * W * 4, 256));
+  const int nblk = (int)cdiv(T, TOPK_TOKENS_PER_BLOCK);
+  const size_t lds = (size_t)E * 2 * sizeof(uint32_t);
+#define MOE_TOPK(EPL) k_topk<EPL><<<nblk, 256, lds, st>>>(logits, (int)T, E, K, W, p.topk_idx, p.topk_w, bits)
+  if (E <= 64) MOE_TOPK(1);
+  else if (E <= 128) MOE_TOPK(2);
+  else if (E <= 256) MOE_TOPK(4);
+  else if (E <= 512) MOE_TOPK(8);
+  else MOE_TOPK(16);
+#undef MOE_TOPK
+  k_count<<<E, 256, 0, st>>>(bits, W, wprefix, p.counts);
+  const bool rounded = round_mode != 0;
+  if (rounded) {
+    const size_t tr_lds = T <= TR_LDS_TOKENS ? (size_t)T * 4 : 0;
+    static bool lds_attr_set = false;  // dynamic LDS above 64 KiB must be opted into
+    if (!lds_attr_set) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_token_round),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               TR_LDS_TOKENS * 4);
+      if (e != hipSuccess) return e;
+      lds_attr_set = true;
+    }
+    k_token_round<<<E, TR_THREADS, tr_lds, st>>>(logits, (int)T, E, W, tile_m, round_mode, bits, p.counts);
+    k_count<<<E, 256, 0, st>>>(bits, W, wprefix, p.counts);
+  }
+  k_offsets<<<1, 1024, 0, st>>>(p.counts, E, p.expert_off, p.meta);
+  if (rounded) {
+    k_tok_count<<<(int)cdiv(T, 256), 256, 0, st>>>(bits, (int)T, E, W, p.tok_off);
+    k_tok_scan<<<1, 1024, 0, st>>>((int)T, p.tok_off);
+    k_place<true><<<(int)cdiv(T, 256), 256, 0, st>>>(logits, (int)T, E, K, W, p.topk_idx, bits, wprefix,
+                                                     p.expert_off, p.tok_off, p.row_token, p.row_w, p.tok_row);
+  } else {
+    k_tok_fill<<<(int)cdiv(T + 1, 256), 256, 0, st>>>((int)T, K, p.tok_off);
+    k_place<false><<<(int)cdiv(T, 256), 256, 0, st>>>(logits, (int)T, E, K, W, p.topk_idx, bits, wprefix,
+                                                      p.expert_off, p.tok_off, p.row_token, p.row_w, p.tok_row);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

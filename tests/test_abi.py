@@ -1,0 +1,118 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every function that
+include/moe.h declares, sizes plans and workspaces, and rejects invalid calls on the host
+before anything is enqueued (every case below fails validation, so no kernel is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_layer_lds_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 1 << 20            # a non-null, 16-byte aligned address that is never dereferenced
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "moe.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.lib()
+
+
+def test_exports_every_declared_function(lib):
+    declared = header_functions()
+    assert {"moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward",
+            "moe_backward"} <= set(declared)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(B.EXPORTS) == declared
+    assert b"gfx950" in lib.moe_version()
+
+
+def test_status_strings(lib):
+    for code, name in B.STATUS.items():
+        assert lib.moe_status_string(code).decode().startswith(name)
+
+
+def dims(**kw):
+    base = dict(T=256, d=128, n=256, E=8, K=2, dtype="bf16")
+    base.update(kw)
+    return B.make_dims(**base)
+
+
+def test_max_rows():
+    assert B.moe_max_rows(dims()) == 512
+    assert B.moe_max_rows(dims(round_mode=B.ROUND_DOWN, tile_m=64)) == 512
+    assert B.moe_max_rows(dims(round_mode=B.ROUND_NEAREST, tile_m=128)) == 512 + 8 * 127
+    assert B.moe_max_rows(dims(T=16, E=8, K=2, round_mode=B.ROUND_UP, tile_m=128)) == 16 * 8
+
+
+def test_workspace_sizes():
+    d = dims(T=32768, d=1536, n=256, E=128, K=8)
+    for op in range(6):
+        assert B.moe_workspace_bytes(d, op) >= 0
+    R = 32768 * 8
+    assert B.moe_workspace_bytes(d, B.OP_FFN) >= R * 256 * 2
+    assert B.moe_workspace_bytes(d, B.OP_FORWARD) >= R * (256 + 1536) * 2
+    assert B.moe_workspace_bytes(d, B.OP_BACKWARD) >= R * (4 * 256 + 256 + 1536) * 2
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=9), -1), (dict(K=0), -1), (dict(E=0, K=1), -1), (dict(E=2000), -1),
+    (dict(E=32, K=17), -2), (dict(d=96), -2), (dict(n=100), -2), (dict(d=32), -1), (dict(T=0), -1),
+    (dict(dtype="f32", round_mode=7), -1), (dict(round_mode=1, tile_m=0), -1),
+    (dict(round_mode=1, tile_m=4096), -1),
+])
+def test_invalid_dims_rejected(lib, kw, status):
+    d = dims(**kw)
+    plan = B.PlanStruct(*([FAKE] * 9))
+    r = lib.moe_route(ctypes.byref(d), None, None, None, FAKE, ctypes.byref(plan), FAKE, 1 << 40, None)
+    assert r == status, lib.moe_last_error()
+    assert lib.moe_last_error()
+    assert B.lib().moe_max_rows(ctypes.byref(d)) == 0
+
+
+def test_null_and_misaligned_pointers_rejected(lib):
+    d = dims()
+    plan = B.PlanStruct(*([FAKE] * 9))
+    r = lib.moe_route(ctypes.byref(d), None, None, None, None, ctypes.byref(plan), FAKE, 1 << 40, None)
+    assert r == -1 and b"logits" in lib.moe_last_error()
+    bad = B.PlanStruct(*([FAKE] * 8 + [FAKE + 4]))
+    r = lib.moe_route(ctypes.byref(d), None, None, None, FAKE, ctypes.byref(bad), FAKE, 1 << 40, None)
+    assert r == -1 and b"meta" in lib.moe_last_error()
+    r = lib.moe_route(ctypes.byref(d), None, None, None, FAKE, None, FAKE, 1 << 40, None)
+    assert r == -1 and b"plan" in lib.moe_last_error()
+    # X given without W_r
+    r = lib.moe_route(ctypes.byref(d), FAKE, None, None, FAKE, ctypes.byref(plan), FAKE, 1 << 40, None)
+    assert r == -1 and b"W_r" in lib.moe_last_error()
+    r = lib.moe_combine(ctypes.byref(d), ctypes.byref(plan), FAKE + 8, 1, FAKE, None)
+    assert r == -1 and b"Y_perm" in lib.moe_last_error()
+
+
+def test_workspace_too_small_rejected(lib):
+    d = dims()
+    plan = B.PlanStruct(*([FAKE] * 9))
+    need = B.moe_workspace_bytes(d, B.OP_FORWARD)
+    r = lib.moe_forward(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, ctypes.byref(plan),
+                        None, FAKE, FAKE, need - 1, None)
+    assert r == -3 and b"workspace" in lib.moe_last_error()
+    need_b = B.moe_workspace_bytes(d, B.OP_BACKWARD)
+    r = lib.moe_backward(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, ctypes.byref(plan), None,
+                         FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, need_b - 1, None)
+    assert r == -3
+    # dW_r without W_r is an argument error
+    r = lib.moe_backward(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, ctypes.byref(plan), None,
+                         FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need_b, None)
+    assert r == -1 and b"dW_r" in lib.moe_last_error()
+
+
+def test_binding_raises_moe_error():
+    with pytest.raises(B.MoEError) as ei:
+        B.moe_max_rows(dims(K=99))
+    assert ei.value.status == -1

@@ -1,0 +1,164 @@
+"""GPU parity: the HIP library (through its C ABI) against the float64 oracle, element by element,
+on seeded inputs small enough for the oracle but spanning several GEMM tiles with ragged tails.
+
+Routing outputs must be bit-exact given the same fp32 logits; floating-point outputs and
+gradients must satisfy max|y - y_ref| <= tol * max|y_ref| (1e-4 fp32, 2e-2 bf16).
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_layer_lds_amd import binding as B
+from mixture_experts_layer_lds_amd import workloads as wl
+from parity import (TOL, assert_close, check_backward, check_forward, check_routing, f64, run_gpu)
+
+pytestmark = pytest.mark.gpu
+
+LOG = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
+
+
+@pytest.fixture(autouse=True)
+def announce(request):
+    """Record which case is about to touch the GPU, flushed before it runs."""
+    os.makedirs(LOG, exist_ok=True)
+    with open(os.path.join(LOG, "gpu_test_progress.txt"), "a") as f:
+        f.write("START %s\n" % request.node.nodeid)
+        f.flush()
+        os.fsync(f.fileno())
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    yield
+
+
+def full_check(cfg, **kw):
+    res = run_gpu(cfg, **kw)
+    ref = check_routing(cfg, res)
+    errs, _ = check_forward(cfg, res, ref)
+    if cfg.backward:
+        errs.update(check_backward(cfg, res, ref))
+    return res, ref, errs
+
+
+def test_tiny_fp32_layer_forward_backward():
+    cfg = wl.CONFIGS[0].with_(backward=True)
+    _, ref, errs = full_check(cfg)
+    assert int(ref["counts"].sum()) == cfg.T * cfg.K
+    print(errs)
+
+
+@pytest.mark.parametrize("shape", [
+    dict(T=1000, d=192, E=4, K=2, n=320, dtype="bf16"),
+    dict(T=700, d=128, E=5, K=3, n=192, dtype="f32"),
+    dict(T=333, d=256, E=16, K=4, n=128, dtype="bf16"),
+    dict(T=129, d=64, E=3, K=1, n=64, dtype="f32"),
+])
+def test_ragged_multi_tile(shape):
+    cfg = wl.small_shape(**shape, seed=31)
+    _, _, errs = full_check(cfg)
+    print(errs)
+
+
+@pytest.mark.parametrize("mode,tile_m,dtype", [
+    (1, 128, "f32"), (1, 32, "bf16"), (2, 16, "bf16"), (3, 64, "f32"), (2, 128, "f32"), (3, 8, "bf16"),
+])
+def test_token_rounding_layer(mode, tile_m, dtype):
+    cfg = wl.small_shape(T=900, d=128, E=6, K=2, n=128, dtype=dtype, bias="zipf", round_mode=mode,
+                         tile_m=tile_m, seed=40 + mode)
+    _, ref, errs = full_check(cfg)
+    assert np.all(ref["counts"] % tile_m == 0)
+    print(errs)
+
+
+def test_single_expert_and_all_experts():
+    full_check(wl.small_shape(T=200, d=128, E=1, K=1, n=128, dtype="f32", seed=5))
+    full_check(wl.small_shape(T=200, d=128, E=4, K=4, n=64, dtype="f32", seed=6))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_empty_experts(dtype):
+    cfg = wl.small_shape(T=400, d=128, E=8, K=2, n=128, dtype=dtype, bias="normal", seed=7)
+    inp = wl.make_inputs(cfg, device="cuda")
+    inp["bias"] = torch.tensor([0, -100, 0, -100, 0, 0, -100, 0], dtype=torch.float32, device="cuda")
+    res = run_gpu(cfg, inputs=inp)
+    ref = check_routing(cfg, res)
+    assert (ref["counts"] == 0).sum() == 3
+    check_forward(cfg, res, ref)
+    check_backward(cfg, res, ref)
+    for e in (1, 3, 6):
+        assert torch.count_nonzero(res["dW_gate"][e]) == 0
+        assert torch.count_nonzero(res["dW_down"][e]) == 0
+
+
+def test_recompute_equals_cached_and_determinism():
+    cfg = wl.small_shape(T=512, d=256, E=8, K=2, n=192, dtype="bf16", seed=9)
+    inp = wl.make_inputs(cfg, device="cuda")
+    a = run_gpu(cfg, inputs=inp, cache_h=True)
+    b = run_gpu(cfg, inputs=inp, cache_h=False)
+    c = run_gpu(cfg, inputs=inp, cache_h=True)
+    for k in ("out", "logits", "dX", "dW_gate", "dW_up", "dW_down", "dLogits", "dW_r"):
+        assert torch.equal(a[k], b[k]), k
+        assert torch.equal(a[k], c[k]), k
+    R = int(a["plan"].meta[0])
+    assert torch.equal(a["dS"][:R], b["dS"][:R])
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2, 3])
+def test_route_from_given_logits_with_ties(mode):
+    """Caller-supplied logits with many exact ties (and -0.0): selection and indices bit-exact."""
+    T, E, K = 777, 40, 5
+    g = torch.Generator().manual_seed(123 + mode)
+    L = torch.randint(-3, 4, (T, E), generator=g).to(torch.float32)
+    L[::7] = 0.0
+    L[3::11, ::2] = -0.0
+    cfg = wl.small_shape(T=T, d=64, E=E, K=K, n=64, dtype="f32", round_mode=mode, tile_m=16)
+    dims = B.make_dims(T, 64, 64, E, K, "f32", mode, 16)
+    plan = B.Plan(dims)
+    logits = L.cuda()
+    ws, nb = B.workspace(dims, B.OP_ROUTE)
+    B.moe_route(dims, None, None, None, logits, plan, ws, nb)
+    torch.cuda.synchronize()
+    check_routing(cfg, dict(plan=plan), L=L.double().numpy())
+
+
+def test_permute_packed_ffn_and_combine():
+    cfg = wl.small_shape(T=600, d=192, E=6, K=3, n=128, dtype="bf16", seed=11)
+    inp = wl.make_inputs(cfg, device="cuda")
+    dims = B.make_dims(cfg.T, cfg.d, cfg.n, cfg.E, cfg.K, "bf16")
+    plan = B.Plan(dims)
+    logits = torch.empty(cfg.T, cfg.E, device="cuda")
+    ws, nb = B.workspace(dims, B.OP_ROUTE)
+    B.moe_route(dims, inp["X"], inp["W_r"], None, logits, plan, ws, nb)
+    R_max = plan.R_max
+    Xp = torch.zeros(R_max, cfg.d, dtype=torch.bfloat16, device="cuda")
+    B.moe_permute(dims, plan, inp["X"], Xp)
+    Yg = torch.empty(R_max, cfg.d, dtype=torch.bfloat16, device="cuda")
+    Yp = torch.empty_like(Yg)
+    Hg = torch.empty(R_max, 2 * cfg.n, dtype=torch.bfloat16, device="cuda")
+    Hp = torch.empty_like(Hg)
+    wsf, nbf = B.workspace(dims, B.OP_FFN)
+    B.moe_grouped_ffn(dims, plan, inp["X"], True, inp["W_gate"], inp["W_up"], inp["W_down"], Hg, Yg, wsf, nbf)
+    B.moe_grouped_ffn(dims, plan, Xp, False, inp["W_gate"], inp["W_up"], inp["W_down"], Hp, Yp, wsf, nbf)
+    out_w = torch.empty(cfg.T, cfg.d, dtype=torch.bfloat16, device="cuda")
+    out_u = torch.empty_like(out_w)
+    B.moe_combine(dims, plan, Yg, True, out_w)
+    B.moe_combine(dims, plan, Xp, False, out_u)
+    torch.cuda.synchronize()
+    hp = plan.to_host()
+    R = hp["R"]
+    # permute: bit-exact row copies; unpermute(permute(X)) is the replicated X
+    X = inp["X"].cpu()
+    assert torch.equal(Xp[:R].cpu(), X[torch.from_numpy(hp["row_token"]).long()])
+    Z = oracle.unpermute(Xp[:R].cpu().view(torch.int16).numpy(), hp["tok_row"])
+    rep = np.repeat(X.view(torch.int16).numpy(), np.diff(hp["tok_off"]), axis=0)
+    assert np.array_equal(Z, rep)
+    # packed and gathered inputs feed identical bits to the same GEMMs
+    assert torch.equal(Yg[:R], Yp[:R]) and torch.equal(Hg[:R], Hp[:R])
+    # weighted combine of the expert outputs = the layer output; unit combine of X_perm = K X
+    ref = oracle.build_plan(f64(logits), cfg.K)
+    fw = oracle.layer_forward(f64(inp["X"]), f64(inp["W_gate"]), f64(inp["W_up"]), f64(inp["W_down"]), ref)
+    assert_close("out", f64(out_w), fw["out"], TOL["bf16"])
+    assert_close("Y_perm", f64(Yg[:R]), fw["Y_perm"], TOL["bf16"])
+    assert_close("unit combine", f64(out_u), cfg.K * f64(inp["X"]), TOL["bf16"])
