@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Benchmark of the one-GPU MoE layer on MI355X: useful TFLOP/s of forward + backward.
+
+Default workload: the fine-grained 7B-style layer (T=32768 tokens, d=1536, E=128 experts, top-8,
+SwiGLU experts of width n=256, bf16), forward + backward, seeded synthetic inputs resident in HBM.
+One step = moe_forward (router GEMM, routing, gathered gate/up GEMM with SwiGLU, down GEMM,
+weighted combine) + moe_backward (dAct with SwiGLU backward and dS, dW_down, dW_gate/up, dX,
+router backward with the dX gather-sum, router weight gradient).
+
+Prints ONE JSON line.  "Useful" FLOPs count real (token, expert) rows only:
+6 R d n forward + 12 R d n backward for the experts, plus 2 T d E (router forward) and
+4 T d E (router backward).  Per-stage durations come from hipEvent pairs the library records
+around each stage on the stream it launches on, inside the timed region.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
+PEAK_FP32_TFLOPS = 157.3      # MI355X dense fp32 MFMA (published)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
+METRIC = "MoE layer fwd+bwd useful TFLOPS and % bf16 MFMA peak, T=32768 fine-grained"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="fine_grained_7b")
+    ap.add_argument("--round-mode", type=int, default=None, help="override token rounding (0..3)")
+    ap.add_argument("--no-h-cache", action="store_true", help="backward recomputes [G|U] from X")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU baseline time budget")
+    ap.add_argument("--forward-only", action="store_true")
+    return ap.parse_args()
+
+
+def stage_flops(stage, R, T, d, n, E):
+    """Algorithmic FLOPs of one launch of a GEMM stage (real rows only)."""
+    return {
+        "router_gemm": 2 * T * d * E,
+        "up_gemm": 4 * R * d * n,
+        "down_gemm": 2 * R * d * n,
+        "dact_gemm": 2 * R * d * n,
+        "dw_down_gemm": 2 * R * d * n,
+        "dw_gu_gemm": 4 * R * d * n,
+        "dx_gemm": 4 * R * d * n,
+        "dwr_gemm": 2 * T * d * E,
+    }.get(stage)
+
+
+def stage_bytes(stage, R, T, d, n, E, es):
+    """Algorithmic HBM bytes of one launch of a streaming stage."""
+    return {
+        "permute": R * d * es + T * d * es + R * 4,
+        "combine": R * d * es + T * d * es + R * 8 + (T + 1) * 4,
+        "router_bwd": R * d * es + T * d * es + T * E * 4 + R * 16,
+    }.get(stage)
+
+
+def cpu_baseline(cfg, inp, logits, budget_s):
+    """The float64 oracle, as it stands, on a bounded sample of the same layer: whole experts'
+    forward + backward, experts taken in a seeded order until the time budget is used."""
+    import torch
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    L = logits.double().cpu().numpy()
+    plan = oracle.build_plan(L, cfg.K, round_mode=cfg.round_mode, tile_m=cfg.tile_m)
+    X = inp["X"].double().cpu().numpy()
+    dY = inp["dY"].double().cpu().numpy() if "dY" in inp else None
+
+    class Lazy:
+        def __init__(self, t):
+            self.t = t
+
+        def __getitem__(self, e):
+            return self.t[e].double().cpu().numpy()
+
+    Wg, Wu, Wd = Lazy(inp["W_gate"]), Lazy(inp["W_up"]), Lazy(inp["W_down"])
+    order = np.random.default_rng(1234).permutation(cfg.E)
+    rows = 0
+    used = []
+    t_total = 0.0
+    for e in order:
+        t0 = time.perf_counter()
+        oracle.layer_forward(X, Wg, Wu, Wd, plan, experts=[int(e)])
+        if dY is not None:
+            oracle.layer_backward(dY, X, Wg, Wu, Wd, plan, experts=[int(e)])
+        t_total += time.perf_counter() - t0
+        rows += int(plan["counts"][e])
+        used.append(int(e))
+        if t_total >= budget_s:
+            break
+    mult = 18 if dY is not None else 6
+    flops = mult * rows * cfg.d * cfg.n
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": "%d of %d experts (%d token rows), expert SwiGLU FFN %s in float64 numpy, %.1f s"
+                      % (len(used), cfg.E, rows, "forward+backward" if dY is not None else "forward", t_total)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d, WORLD_SIZE=%d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from mixture_experts_layer_lds_amd import binding as B
+    from mixture_experts_layer_lds_amd import workloads as wl
+
+    cfg = wl.BY_NAME[args.config]
+    if args.round_mode is not None:
+        cfg = cfg.with_(round_mode=args.round_mode)
+    backward = cfg.backward and not args.forward_only
+    log("config", cfg)
+    inp = wl.make_inputs(cfg, device="cuda", with_grad_out=backward)
+    dims = B.make_dims(cfg.T, cfg.d, cfg.n, cfg.E, cfg.K, cfg.dtype, cfg.round_mode, cfg.tile_m)
+    dt = B.torch_dtype(dims)
+    plan = B.Plan(dims)
+    R_max = plan.R_max
+    logits = torch.empty(cfg.T, cfg.E, dtype=torch.float32, device="cuda")
+    H = torch.empty(R_max, 2 * cfg.n, dtype=dt, device="cuda") if backward else None
+    out = torch.empty(cfg.T, cfg.d, dtype=dt, device="cuda")
+    ws_f, nb_f = B.workspace(dims, B.OP_FORWARD)
+    if backward:
+        g = dict(dX=torch.empty_like(inp["X"]), dW_gate=torch.empty_like(inp["W_gate"]),
+                 dW_up=torch.empty_like(inp["W_up"]), dW_down=torch.empty_like(inp["W_down"]),
+                 dS=torch.empty(R_max, dtype=torch.float32, device="cuda"),
+                 dLogits=torch.empty(cfg.T, cfg.E, dtype=torch.float32, device="cuda"),
+                 dW_r=torch.empty_like(inp["W_r"]))
+        ws_b, nb_b = B.workspace(dims, B.OP_BACKWARD)
+    h_arg = None if args.no_h_cache else H
+
+    def step():
+        B.moe_forward(dims, inp["X"], inp["W_r"], inp["bias"], inp["W_gate"], inp["W_up"], inp["W_down"],
+                      logits, plan, H, out, ws_f, nb_f)
+        if backward:
+            B.moe_backward(dims, inp["dY"], inp["X"], inp["W_r"], inp["W_gate"], inp["W_up"], inp["W_down"],
+                           plan, h_arg, g["dX"], g["dW_gate"], g["dW_up"], g["dW_down"], g["dS"],
+                           g["dLogits"], g["dW_r"], ws_b, nb_b)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    R = int(plan.meta[0].item())
+    log("warmup done, R =", R)
+
+    B.moe_timing_enable(True)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for i in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    stages = {s: B.moe_timing_read(s) for s in B.STAGES}
+    B.moe_timing_enable(False)
+    ms_step = total_ms / args.steps
+    log("timed %d steps: %.3f ms/step" % (args.steps, ms_step))
+
+    T, d, n, E = cfg.T, cfg.d, cfg.n, cfg.E
+    es = 2 if cfg.dtype == "bf16" else 4
+    flops = 6 * R * d * n + 2 * T * d * E
+    if backward:
+        flops += 12 * R * d * n + 4 * T * d * E
+    value = flops / (ms_step * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
+
+    breakdown = {}
+    for s, v in stages.items():
+        if not v:
+            continue
+        avg = float(np.mean(v))
+        ent = {"launches_per_step": round(len(v) / args.steps, 3), "avg_ms": round(avg, 4),
+               "ms_per_step": round(float(np.sum(v)) / args.steps, 4)}
+        f = stage_flops(s, R, T, d, n, E)
+        b = stage_bytes(s, R, T, d, n, E, es)
+        if f:
+            ent["tflops"] = round(f / (avg * 1e-3) / 1e12, 1)
+            ent["pct_peak"] = round(100 * f / (avg * 1e-3) / 1e12 / peak, 1)
+        if b:
+            ent["gbs"] = round(b / (avg * 1e-3) / 1e9, 1)
+            ent["pct_hbm"] = round(100 * b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 1)
+        breakdown[s] = ent
+    gemm_stages = [s for s in breakdown if stage_flops(s, R, T, d, n, E)]
+    dom = max(breakdown, key=lambda s: breakdown[s]["ms_per_step"])
+    if stage_flops(dom, R, T, d, n, E):
+        avg = breakdown[dom]["avg_ms"]
+        ach = stage_flops(dom, R, T, d, n, E) / (avg * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4), "traffic": None, "avg_ms": avg}
+    else:
+        avg = breakdown[dom]["avg_ms"]
+        ach = stage_bytes(dom, R, T, d, n, E, es) / (avg * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "avg_ms": avg}
+    gemm_ms = sum(breakdown[s]["ms_per_step"] for s in gemm_stages)
+    expert_flops = (18 if backward else 6) * R * d * n
+    res = {
+        "metric": METRIC if (cfg.name == "fine_grained_7b" and backward) else
+        "MoE layer %s useful TFLOPS, %s" % ("fwd+bwd" if backward else "fwd", cfg.name),
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded normal inputs and random-init weights)",
+        "config": {"workload": cfg.name, "T": T, "d": d, "n": n, "E": E, "K": cfg.K,
+                   "pass": "fwd+bwd" if backward else "fwd", "round_mode": cfg.round_mode,
+                   "tile_m": cfg.tile_m, "rows": R, "h_cache": (not args.no_h_cache) if backward else None,
+                   "parallelism": "single GPU"},
+        "pct_bf16_peak": round(100 * value / peak, 2),
+        "grouped_gemm_pct_peak": round(100 * expert_flops / (gemm_ms * 1e-3) / 1e12 / peak, 2) if gemm_ms else None,
+        "roofline": roof,
+        "stages": breakdown,
+    }
+    if not args.no_cpu:
+        log("CPU oracle baseline ...")
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, logits, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
