@@ -14,31 +14,38 @@ namespace moe {
 
 static inline int grid8(int64_t n) { return (int)((n + 7) / 8 * 8); }
 
-// Adapter: a ColLoader bound to its k -> row-pointer functor.
 template <typename T, class KPtr>
-struct ColOp {
-  ColLoader<T> c;
-  KPtr f;
-  __device__ ColOp(KPtr f_, int mn_base, int mn_valid) : f(f_) { c.init(mn_base, mn_valid); }
-  __device__ void load(int kt) { c.load(kt, f); }
-  __device__ void store(char* lds) const { c.store(lds); }
-};
-template <typename T, class KPtr>
-__device__ ColOp<T, KPtr> make_col(KPtr f, int mn_base, int mn_valid) {
-  return ColOp<T, KPtr>(f, mn_base, mn_valid);
+__device__ __forceinline__ typename MNOperand<T, KPtr>::Loader make_mn(KPtr f, int mn_base, int mn_valid) {
+  return typename MNOperand<T, KPtr>::Loader(f, mn_base, mn_valid);
+}
+
+// Store a bf16 staging tile row by row through a row-pointer functor (rows without a pointer
+// are skipped); 16-byte writes.
+template <class RowPtr>
+__device__ __forceinline__ void epi_store_rows(const char* lds, RowPtr row_ptr, int mrows, int ncols,
+                                               int ncols_valid) {
+  const int cpr = ncols / 8;
+  for (int c = threadIdx.x; c < 256 * cpr; c += GEMM_THREADS) {
+    const int r = c / cpr, ch = c % cpr;
+    if (r >= mrows || ch * 8 >= ncols_valid) continue;
+    bf16* p = row_ptr(r);
+    if (p) st16(p + ch * 8, *reinterpret_cast<const u32x4*>(lds + r * EPI_ROW + ch * 16));
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
 // dAct: dA'[r][j] = sum_c dY[t_r][c] W_down[e][c][j]  (M = rows of e, N = n, K = d).
+// Wave column wn owns columns j*128 + wn*32 + (lane % 32), j = 0, 1, so that each half of the
+// 256-column tile is contiguous for the staged stores.
 // Epilogue per (r, j), with G, U read from H and w = row_w[r]:
 //   A = silu(G) U;  dS partial += dA' A;  dA = w dA'
 //   dG = dA U sigmoid(G) (1 + G (1 - sigmoid(G)));  dU = dA silu(G)
 //   dH[r] = [dG | dU];  wA[r][j] = w A   (the down-weight gradient's operand)
-// dS partials are reduced over the tile's 128 columns in registers, lanes and LDS, and written
-// per column tile: dS_part[nt][r].
+// dS partials are reduced over the tile's columns in registers, lanes and LDS, and written per
+// column tile: dS_part[nt][r].
 // ---------------------------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(GEMM_THREADS, 2) void k_dact(
+__global__ __launch_bounds__(GEMM_THREADS, 1) void k_dact(
     const int32_t* __restrict__ mtile_off, const int32_t* __restrict__ expert_off,
     const int32_t* __restrict__ row_token, const float* __restrict__ row_w,
     const T* __restrict__ dY, const T* __restrict__ Wd, const T* __restrict__ H,
@@ -51,69 +58,69 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_dact(
   if (!find_group_tile(mt, mtile_off, expert_off, E, g)) return;
   const int n0 = nt * BN;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int64_t rowb = (int64_t)d * sizeof(T);
   RowLoader la;
   la.init([&](int i) -> const char* {
     return i < g.mrows ? reinterpret_cast<const char*>(dY) + (int64_t)row_token[g.m0 + i] * rowb : nullptr;
   });
-  const char* wd = reinterpret_cast<const char*>(Wd) + (int64_t)g.e * d * n * sizeof(T) + n0 * sizeof(T);
-  auto lb = make_col<T>([&](int k) -> const char* {
-    return k < d ? wd + (int64_t)k * n * sizeof(T) : nullptr;
-  }, n0, n);
-  f32x16 acc[2][2];
-  gemm_mainloop<T>(la, lb, (int)(rowb / KB), acc, lds, wm, [&](int j) { return wn * 64 + j * 32; });
-
-  float part[2][16];
+  const char* wd = reinterpret_cast<const char*>(Wd) + ((int64_t)g.e * d * n + n0) * sizeof(T);
+  auto kp = [=](int k) -> const char* { return k < d ? wd + (int64_t)k * n * sizeof(T) : nullptr; };
+  auto lb = make_mn<T>(kp, n0, n);
+  WaveAcc acc;
+  gemm_mainloop<T, KOperand<T>, MNOperand<T, decltype(kp)>>(la, lb, (int)(rowb / KB), acc, lds, wm,
+                                                           [&](int j) { return j * 128 + wn * 32; });
+  // Epilogue, one 128-column half of the tile at a time: the wave dumps its fp32 accumulators
+  // into an LDS tile [256][128], then the block walks the half row by row in 16-byte chunks
+  // (coalesced loads of G, U and coalesced stores of dG, dU, w A), and the 16 or 32 lanes that
+  // share a row reduce its dS partial.
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int CPR = 128 / VEC;                 // chunks per half-row
+  constexpr int FROW = 128 * 4 + 16;             // fp32 staging pitch
+  float* red = reinterpret_cast<float*>(lds + 256 * FROW);  // [256] dS partials of this tile
+  const int valid = min(BN, n - n0);
+  for (int half = 0; half < 2; ++half) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) part[i][v] = 0.0f;
+      for (int v = 0; v < 16; ++v)
+        *reinterpret_cast<float*>(lds + acc_row(wm, i, v) * FROW + (wn * 32 + (lane & 31)) * 4) = acc.c[i][half][v];
+    __syncthreads();
+    for (int c = threadIdx.x; c < 256 * CPR; c += GEMM_THREADS) {
+      const int row = c / CPR, ch = c % CPR;
+      const int col = half * 128 + ch * VEC;   // column within the tile
+      float p = 0.0f;
+      if (row < g.mrows && col < valid) {
+        const int64_t r = g.m0 + row;
+        const float w = row_w[r];
+        float dAp[VEC], G[VEC], U[VEC], oG[VEC], oU[VEC], oA[VEC];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+        for (int k = 0; k < VEC; ++k) dAp[k] = *reinterpret_cast<const float*>(lds + row * FROW + (ch * VEC + k) * 4);
+        unpack16<T>(ld16(H + r * 2 * n + n0 + col), G);
+        unpack16<T>(ld16(H + r * 2 * n + n + n0 + col), U);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int m = acc_row(wm, i, v);
-      if (m >= g.mrows) continue;
-      const int64_t r = g.m0 + m;
-      const float w = row_w[r];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = n0 + wn * 64 + j * 32 + (lane & 31);
-        if (col >= n) continue;
-        const float G = to_f32(H[r * 2 * n + col]);
-        const float U = to_f32(H[r * 2 * n + n + col]);
-        const float sg = sigmoid_f32(G);
-        const float silu = G * sg;
-        const float A = silu * U;
-        const float dAp = acc[i][j][v];
-        part[i][v] += dAp * A;
-        const float dA = w * dAp;
-        dH[r * 2 * n + col] = from_f32<T>(dA * U * sg * (1.0f + G * (1.0f - sg)));
-        dH[r * 2 * n + n + col] = from_f32<T>(dA * silu);
-        wA[r * n + col] = from_f32<T>(w * A);
+        for (int k = 0; k < VEC; ++k) {
+          const float sg = sigmoid_f32(G[k]);
+          const float silu = G[k] * sg;
+          const float A = silu * U[k];
+          p += dAp[k] * A;
+          const float dA = w * dAp[k];
+          oG[k] = dA * U[k] * sg * (1.0f + G[k] * (1.0f - sg));
+          oU[k] = dA * silu;
+          oA[k] = w * A;
+        }
+        st16(dH + r * 2 * n + n0 + col, pack16<T>(oG));
+        st16(dH + r * 2 * n + n + n0 + col, pack16<T>(oU));
+        st16(wA + r * n + n0 + col, pack16<T>(oA));
       }
+#pragma unroll
+      for (int o = 1; o < CPR; o <<= 1) p += __shfl_xor(p, o, 64);
+      if (ch == 0) red[row] = half == 0 ? p : red[row] + p;
     }
-  // reduce over the 32 columns held by lanes with equal (lane / 32)
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      float x = part[i][v];
-#pragma unroll
-      for (int o = 1; o < 32; o <<= 1) x += __shfl_xor(x, o, 64);
-      part[i][v] = x;
-    }
-  float* red = reinterpret_cast<float*>(lds);  // [2 (wn)][128 rows]; LDS is free after the loop
-  if ((lane & 31) == 0) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) red[wn * 128 + acc_row(wm, i, v)] = part[i][v];
+    __syncthreads();
   }
-  __syncthreads();
-  if (threadIdx.x < 128 && (int)threadIdx.x < g.mrows)
-    dS_part[(int64_t)nt * R_max + g.m0 + threadIdx.x] = red[threadIdx.x] + red[128 + threadIdx.x];
+  if (threadIdx.x < 256 && (int)threadIdx.x < g.mrows)
+    dS_part[(int64_t)nt * R_max + g.m0 + threadIdx.x] = red[threadIdx.x];
 }
 
 int dact_ntiles(int64_t n) { return (int)cdiv(n, BN); }
@@ -138,10 +145,10 @@ hipError_t launch_dact_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mt
 
 // ---------------------------------------------------------------------------------------------
 // dX_perm[r][c] = sum_j dG[r][j] W_gate[e][j][c] + dU[r][j] W_up[e][j][c]
-// (M = rows of e, N = d, K = 2n: k < n walks W_gate, k >= n walks W_up).
+// (M = rows of e, N = d, K = 2n: k < n walks W_gate, k >= n walks W_up; B is MN-major).
 // ---------------------------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(GEMM_THREADS, 2) void k_dx(
+__global__ __launch_bounds__(GEMM_THREADS, 1) void k_dx(
     const int32_t* __restrict__ mtile_off, const int32_t* __restrict__ expert_off,
     const T* __restrict__ dH, const T* __restrict__ Wg, const T* __restrict__ Wu,
     T* __restrict__ dXp, int d, int n, int E, int NT) {
@@ -152,7 +159,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_dx(
   if (!find_group_tile(mt, mtile_off, expert_off, E, g)) return;
   const int n0 = nt * BN;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int64_t rowb = (int64_t)2 * n * sizeof(T);
   RowLoader la;
   la.init([&](int i) -> const char* {
@@ -161,23 +168,33 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_dx(
   const int64_t wrow = (int64_t)d * sizeof(T);
   const char* wg = reinterpret_cast<const char*>(Wg) + (int64_t)g.e * n * wrow + n0 * sizeof(T);
   const char* wu = reinterpret_cast<const char*>(Wu) + (int64_t)g.e * n * wrow + n0 * sizeof(T);
-  auto lb = make_col<T>([&](int k) -> const char* {
+  auto kp = [=](int k) -> const char* {
     if (k >= 2 * n) return nullptr;
     return k < n ? wg + (int64_t)k * wrow : wu + (int64_t)(k - n) * wrow;
-  }, n0, d);
-  f32x16 acc[2][2];
-  gemm_mainloop<T>(la, lb, (int)(rowb / KB), acc, lds, wm, [&](int j) { return wn * 64 + j * 32; });
+  };
+  auto lb = make_mn<T>(kp, n0, d);
+  WaveAcc acc;
+  gemm_mainloop<T, KOperand<T>, MNOperand<T, decltype(kp)>>(la, lb, (int)(rowb / KB), acc, lds, wm,
+                                                           [&](int j) { return wn * 64 + j * 32; });
+  const int valid = min(BN, d - n0);
+  if constexpr (sizeof(T) == 2) {
+    epi_stage_bf16(lds, acc, wm, [&](int j) { return wn * 64 + j * 32 + (lane & 31); },
+                   [&](int i, int j, int v) { return acc.c[i][j][v]; });
+    __syncthreads();
+    epi_store_bf16(lds, reinterpret_cast<bf16*>(dXp) + (int64_t)g.m0 * d + n0, d, g.mrows, BN, valid);
+  } else {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int c = n0 + wn * 64 + j * 32 + (lane & 31);
-    if (c >= d) continue;
+    for (int j = 0; j < 2; ++j) {
+      const int c = wn * 64 + j * 32 + (lane & 31);
+      if (c >= valid) continue;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = acc_row(wm, i, v);
-        if (m < g.mrows) dXp[(int64_t)(g.m0 + m) * d + c] = from_f32<T>(acc[i][j][v]);
-      }
+        for (int v = 0; v < 16; ++v) {
+          const int m = acc_row(wm, i, v);
+          if (m < g.mrows) dXp[(int64_t)(g.m0 + m) * d + n0 + c] = from_f32<T>(acc.c[i][j][v]);
+        }
+    }
   }
 }
 
@@ -201,11 +218,12 @@ hipError_t launch_dx_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mtil
 // Weight gradients: one output tile of one expert per workgroup; K runs over the expert's rows.
 //   dW_down[e][c][j] = sum_r dY[t_r][c] wA[r][j]          (M = d, N = n)
 //   dW_gu[e][j][c]   = sum_r dH[r][j] X[t_r][c]           (M = 2n, N = d; j < n -> gate)
-// Both operands are MN-contiguous in memory and are transposed while staged.  Experts without
-// rows get zero tiles.
+// Both operands are MN-major in memory (their rows are the expert's token rows); bf16 tiles are
+// staged as they lie and read with the transposing LDS load.  Experts without rows get zero
+// tiles.
 // ---------------------------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(GEMM_THREADS, 2) void k_dw_down(
+__global__ __launch_bounds__(GEMM_THREADS, 1) void k_dw_down(
     const int32_t* __restrict__ expert_off, const int32_t* __restrict__ row_token,
     const T* __restrict__ dY, const T* __restrict__ wA, T* __restrict__ dWd, int d, int n,
     int E, int MT, int NT) {
@@ -217,32 +235,40 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_dw_down(
   const int rem = lin % per;
   const int m0 = (rem / NT) * BM, n0 = (rem % NT) * BN;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int off = expert_off[e];
   const int cnt = expert_off[e + 1] - off;
   const char* dyb = reinterpret_cast<const char*>(dY) + m0 * sizeof(T);
   const char* wab = reinterpret_cast<const char*>(wA) + n0 * sizeof(T);
-  auto la = make_col<T>([&](int k) -> const char* {
+  auto ka = [=](int k) -> const char* {
     return k < cnt ? dyb + (int64_t)row_token[off + k] * d * sizeof(T) : nullptr;
-  }, m0, d);
-  auto lb = make_col<T>([&](int k) -> const char* {
-    return k < cnt ? wab + (int64_t)(off + k) * n * sizeof(T) : nullptr;
-  }, n0, n);
-  f32x16 acc[2][2];
-  gemm_mainloop<T>(la, lb, (int)cdiv(cnt, Mma<T>::BK), acc, lds, wm,
-                   [&](int j) { return wn * 64 + j * 32; });
+  };
+  auto kb = [=](int k) -> const char* { return k < cnt ? wab + (int64_t)(off + k) * n * sizeof(T) : nullptr; };
+  auto la = make_mn<T>(ka, m0, d);
+  auto lb = make_mn<T>(kb, n0, n);
+  WaveAcc acc;
+  gemm_mainloop<T, MNOperand<T, decltype(ka)>, MNOperand<T, decltype(kb)>>(
+      la, lb, (int)cdiv(cnt, Mma<T>::BK), acc, lds, wm, [&](int j) { return wn * 64 + j * 32; });
   T* out = dWd + (int64_t)e * d * n;
+  const int mrows = min(BM, d - m0), valid = min(BN, n - n0);
+  if constexpr (sizeof(T) == 2) {
+    epi_stage_bf16(lds, acc, wm, [&](int j) { return wn * 64 + j * 32 + (lane & 31); },
+                   [&](int i, int j, int v) { return acc.c[i][j][v]; });
+    __syncthreads();
+    epi_store_bf16(lds, reinterpret_cast<bf16*>(out) + (int64_t)m0 * n + n0, n, mrows, BN, valid);
+  } else {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int c = n0 + wn * 64 + j * 32 + (lane & 31);
-    if (c >= n) continue;
+    for (int j = 0; j < 2; ++j) {
+      const int c = wn * 64 + j * 32 + (lane & 31);
+      if (c >= valid) continue;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = m0 + acc_row(wm, i, v);
-        if (m < d) out[(int64_t)m * n + c] = from_f32<T>(acc[i][j][v]);
-      }
+        for (int v = 0; v < 16; ++v) {
+          const int m = acc_row(wm, i, v);
+          if (m < mrows) out[(int64_t)(m0 + m) * n + n0 + c] = from_f32<T>(acc.c[i][j][v]);
+        }
+    }
   }
 }
 
@@ -261,9 +287,8 @@ hipError_t launch_dw_down_gemm(const Shape& s, const PlanPtrs& p, const void* dY
   return hipGetLastError();
 }
 
-
 template <typename T>
-__global__ __launch_bounds__(GEMM_THREADS, 2) void k_dw_gu(
+__global__ __launch_bounds__(GEMM_THREADS, 1) void k_dw_gu(
     const int32_t* __restrict__ expert_off, const int32_t* __restrict__ row_token,
     const T* __restrict__ dH, const T* __restrict__ X, T* __restrict__ dWg, T* __restrict__ dWu,
     int d, int n, int E, int MT, int NT) {
@@ -275,33 +300,45 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_dw_gu(
   const int rem = lin % per;
   const int m0 = (rem / NT) * BM, n0 = (rem % NT) * BN;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int off = expert_off[e];
   const int cnt = expert_off[e + 1] - off;
   const char* dhb = reinterpret_cast<const char*>(dH) + m0 * sizeof(T);
   const char* xb = reinterpret_cast<const char*>(X) + n0 * sizeof(T);
-  auto la = make_col<T>([&](int k) -> const char* {
+  auto ka = [=](int k) -> const char* {
     return k < cnt ? dhb + (int64_t)(off + k) * 2 * n * sizeof(T) : nullptr;
-  }, m0, 2 * n);
-  auto lb = make_col<T>([&](int k) -> const char* {
+  };
+  auto kb = [=](int k) -> const char* {
     return k < cnt ? xb + (int64_t)row_token[off + k] * d * sizeof(T) : nullptr;
-  }, n0, d);
-  f32x16 acc[2][2];
-  gemm_mainloop<T>(la, lb, (int)cdiv(cnt, Mma<T>::BK), acc, lds, wm,
-                   [&](int j) { return wn * 64 + j * 32; });
+  };
+  auto la = make_mn<T>(ka, m0, 2 * n);
+  auto lb = make_mn<T>(kb, n0, d);
+  WaveAcc acc;
+  gemm_mainloop<T, MNOperand<T, decltype(ka)>, MNOperand<T, decltype(kb)>>(
+      la, lb, (int)cdiv(cnt, Mma<T>::BK), acc, lds, wm, [&](int j) { return wn * 64 + j * 32; });
+  const int mrows = min(BM, 2 * n - m0), valid = min(BN, d - n0);
+  auto row_ptr = [&](int r) -> T* {
+    const int m = m0 + r;
+    return (m < n ? dWg + ((int64_t)e * n + m) * d : dWu + ((int64_t)e * n + (m - n)) * d) + n0;
+  };
+  if constexpr (sizeof(T) == 2) {
+    epi_stage_bf16(lds, acc, wm, [&](int j) { return wn * 64 + j * 32 + (lane & 31); },
+                   [&](int i, int j, int v) { return acc.c[i][j][v]; });
+    __syncthreads();
+    epi_store_rows(lds, [&](int r) { return reinterpret_cast<bf16*>(row_ptr(r)); }, mrows, BN, valid);
+  } else {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int c = n0 + wn * 64 + j * 32 + (lane & 31);
-    if (c >= d) continue;
+    for (int j = 0; j < 2; ++j) {
+      const int c = wn * 64 + j * 32 + (lane & 31);
+      if (c >= valid) continue;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = m0 + acc_row(wm, i, v);
-        if (m >= 2 * n) continue;
-        T* out = m < n ? dWg + ((int64_t)e * n + m) * d : dWu + ((int64_t)e * n + (m - n)) * d;
-        out[c] = from_f32<T>(acc[i][j][v]);
-      }
+        for (int v = 0; v < 16; ++v) {
+          const int m = acc_row(wm, i, v);
+          if (m < mrows) row_ptr(m)[c] = from_f32<T>(acc.c[i][j][v]);
+        }
+    }
   }
 }
 
@@ -378,17 +415,43 @@ __global__ __launch_bounds__(256) void k_router_bwd(
     if (e < E) dLogits[(int64_t)t * E + e] = v;
     if (dLop) dLop[(int64_t)t * E_pad + e] = from_f32<T>(v);
   }
-  // dX[t]: lanes own 16-byte column chunks; rows broadcast from LDS-free registers per chunk.
+  // dX[t]: lanes own 16-byte column chunks; the token's rows are taken four at a time so that
+  // several row loads are in flight per lane.
   constexpr int VEC = 16 / sizeof(T);
   const int nch = d / VEC;
   for (int ch = lane; ch < nch; ch += 64) {
     float acc[VEC];
 #pragma unroll
     for (int k = 0; k < VEC; ++k) acc[k] = 0.0f;
-    for (int i = 0; i < cnt; ++i) {
+    int i = 0;
+    for (; i + 4 <= cnt; i += 4) {
+      u32x4 v[4];
+      int rr[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        rr[q] = tok_row[base + i + q];
+        v[q] = ld16_nt(dXp + (int64_t)rr[q] * d + ch * VEC);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float f[VEC];
+        unpack16<T>(v[q], f);
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) acc[k] += f[k];
+        if (Wr) {
+          const int e = expert_of_row(expert_off, E, rr[q]);
+          const float dl = sdl[e];
+          float wv[VEC];
+          unpack16<T>(ld16(Wr + (int64_t)e * d + ch * VEC), wv);
+#pragma unroll
+          for (int k = 0; k < VEC; ++k) acc[k] += dl * wv[k];
+        }
+      }
+    }
+    for (; i < cnt; ++i) {
       const int r = tok_row[base + i];
       float f[VEC];
-      unpack16<T>(ld16(dXp + (int64_t)r * d + ch * VEC), f);
+      unpack16<T>(ld16_nt(dXp + (int64_t)r * d + ch * VEC), f);
 #pragma unroll
       for (int k = 0; k < VEC; ++k) acc[k] += f[k];
       if (Wr) {
@@ -433,7 +496,7 @@ static DwrPlan dwr_plan(const Shape& s) {
   q.NT = (int)cdiv(s.d, BN);
   const int bk = s.bf16 ? Mma<bf16>::BK : Mma<float>::BK;
   const int tiles = q.MT * q.NT;
-  int S = (int)cdiv(2048, tiles);
+  int S = (int)cdiv(512, tiles);
   const int max_s = (int)cdiv(s.T, bk);
   if (S > max_s) S = max_s;
   if (S > 64) S = 64;
@@ -449,7 +512,7 @@ size_t dwr_workspace_bytes(const Shape& s) {
 }
 
 template <typename T>
-__global__ __launch_bounds__(GEMM_THREADS, 2) void k_dwr(
+__global__ __launch_bounds__(GEMM_THREADS, 1) void k_dwr(
     const T* __restrict__ dLop, int E_pad, const T* __restrict__ X, float* __restrict__ part,
     T* __restrict__ dWr, int T_, int d, int E, int MT, int NT, int S, int TS) {
   __shared__ __attribute__((aligned(16))) char lds[GEMM_LDS];
@@ -460,32 +523,30 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_dwr(
   const int rem = lin % per;
   const int m0 = (rem / NT) * BM, n0 = (rem % NT) * BN;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int t0 = sl * TS;
   const int klen = min(TS, T_ - t0);
   const char* ab = reinterpret_cast<const char*>(dLop) + m0 * sizeof(T);
   const char* xb = reinterpret_cast<const char*>(X) + n0 * sizeof(T);
-  auto la = make_col<T>([&](int k) -> const char* {
-    return k < klen ? ab + (int64_t)(t0 + k) * E_pad * sizeof(T) : nullptr;
-  }, m0, E_pad);
-  auto lb = make_col<T>([&](int k) -> const char* {
-    return k < klen ? xb + (int64_t)(t0 + k) * d * sizeof(T) : nullptr;
-  }, n0, d);
-  f32x16 acc[2][2];
-  gemm_mainloop<T>(la, lb, (int)cdiv(klen, Mma<T>::BK), acc, lds, wm,
-                   [&](int j) { return wn * 64 + j * 32; });
+  auto ka = [=](int k) -> const char* { return k < klen ? ab + (int64_t)(t0 + k) * E_pad * sizeof(T) : nullptr; };
+  auto kb = [=](int k) -> const char* { return k < klen ? xb + (int64_t)(t0 + k) * d * sizeof(T) : nullptr; };
+  auto la = make_mn<T>(ka, m0, E_pad);
+  auto lb = make_mn<T>(kb, n0, d);
+  WaveAcc acc;
+  gemm_mainloop<T, MNOperand<T, decltype(ka)>, MNOperand<T, decltype(kb)>>(
+      la, lb, (int)cdiv(klen, Mma<T>::BK), acc, lds, wm, [&](int j) { return wn * 64 + j * 32; });
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int c = n0 + wn * 64 + j * 32 + (lane & 31);
     if (c >= d) continue;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int m = m0 + acc_row(wm, i, v);
         if (m >= E) continue;
-        if (S == 1) dWr[(int64_t)m * d + c] = from_f32<T>(acc[i][j][v]);
-        else part[((int64_t)sl * E + m) * d + c] = acc[i][j][v];
+        if (S == 1) dWr[(int64_t)m * d + c] = from_f32<T>(acc.c[i][j][v]);
+        else part[((int64_t)sl * E + m) * d + c] = acc.c[i][j][v];
       }
   }
 }

@@ -44,10 +44,10 @@ int64_t max_mtiles(int64_t R_max, int E) { return R_max / BM + E; }
 static inline int grid8(int64_t n) { return (int)((n + 7) / 8 * 8); }
 
 // ---------------------------------------------------------------------------------------------
-// Router: logits[t][e] = sum_i X[t][i] W_r[e][i] + bias[e]
+// Router: logits[t][e] = sum_i X[t][i] W_r[e][i] + bias[e]   (fp32 out, direct stores)
 // ---------------------------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(GEMM_THREADS, 2) void k_router(const T* __restrict__ X,
+__global__ __launch_bounds__(GEMM_THREADS, 1) void k_router(const T* __restrict__ X,
                                                            const T* __restrict__ Wr,
                                                            const float* __restrict__ bias,
                                                            float* __restrict__ logits, int T_, int d,
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_router(const T* __restrict_
   const int m0 = mt * BM, n0 = nt * BN;
   if (m0 >= T_) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int64_t rowb = (int64_t)d * sizeof(T);
   RowLoader la, lb;
   la.init([&](int i) -> const char* {
@@ -67,19 +67,20 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_router(const T* __restrict_
   lb.init([&](int i) -> const char* {
     return n0 + i < E ? reinterpret_cast<const char*>(Wr) + (n0 + i) * rowb : nullptr;
   });
-  f32x16 acc[2][2];
-  gemm_mainloop<T>(la, lb, (int)(rowb / KB), acc, lds, wm, [&](int j) { return wn * 64 + j * 32; });
+  WaveAcc acc;
+  gemm_mainloop<T, KOperand<T>, KOperand<T>>(la, lb, (int)(rowb / KB), acc, lds, wm,
+                                             [&](int j) { return wn * 64 + j * 32; });
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int n = n0 + wn * 64 + j * 32 + (lane & 31);
     if (n >= E) continue;
     const float b = bias ? bias[n] : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int m = m0 + acc_row(wm, i, v);
-        if (m < T_) logits[(int64_t)m * E + n] = acc[i][j][v] + b;
+        if (m < T_) logits[(int64_t)m * E + n] = acc.c[i][j][v] + b;
       }
   }
 }
@@ -90,21 +91,22 @@ hipError_t launch_router_gemm(const Shape& s, const void* X, const void* W_r, co
   const int n = grid8(cdiv(s.T, BM) * NT);
   if (s.bf16)
     k_router<bf16><<<n, GEMM_THREADS, 0, st>>>((const bf16*)X, (const bf16*)W_r, bias, logits,
-                                                (int)s.T, (int)s.d, s.E, NT);
+                                                      (int)s.T, (int)s.d, s.E, NT);
   else
     k_router<float><<<n, GEMM_THREADS, 0, st>>>((const float*)X, (const float*)W_r, bias, logits,
-                                                 (int)s.T, (int)s.d, s.E, NT);
+                                                       (int)s.T, (int)s.d, s.E, NT);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------------------
-// Gate/up projection.  Tile = 128 rows of one expert x 64 output columns j0..j0+63; the B tile
-// stacks W_gate[e] rows j0..j0+63 over W_up[e] rows j0..j0+63, and wave column wn takes gate
-// block wn*32 and up block 64 + wn*32, so each lane holds G and U of the same (row, column) in
-// matching accumulators.  Epilogue: A = silu(G) * U (fp32, rounded once), optional H = [G | U].
+// Gate/up projection.  Tile = 256 rows of one expert x 128 output columns j0..j0+127; the B tile
+// stacks W_gate[e] rows j0..j0+127 over W_up[e] rows j0..j0+127, and wave column wn takes gate
+// block wn*32 (j = 0) and up block 128 + wn*32 (j = 1), so each lane holds G and U of the same
+// (row, column) in matching accumulators.  Epilogue: A = silu(G) U in fp32, rounded once;
+// optional H = [G | U].
 // ---------------------------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(GEMM_THREADS, 2) void k_up(
+__global__ __launch_bounds__(GEMM_THREADS, 1) void k_up(
     const int32_t* __restrict__ mtile_off, const int32_t* __restrict__ expert_off,
     const int32_t* __restrict__ row_token, const T* __restrict__ A_in, int gathered,
     const T* __restrict__ Wg, const T* __restrict__ Wu, T* __restrict__ act, T* __restrict__ H,
@@ -114,9 +116,9 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_up(
   const int mt = lin / NT, nt = lin % NT;
   GroupTile g;
   if (!find_group_tile(mt, mtile_off, expert_off, E, g)) return;
-  const int j0 = nt * 64;
+  const int j0 = nt * 128;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int64_t rowb = (int64_t)d * sizeof(T);
   RowLoader la, lb;
   la.init([&](int i) -> const char* {
@@ -124,49 +126,80 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_up(
     const int64_t src = gathered ? row_token[g.m0 + i] : (int64_t)(g.m0 + i);
     return reinterpret_cast<const char*>(A_in) + src * rowb;
   });
-  const char* wg = reinterpret_cast<const char*>(Wg) + ((int64_t)g.e * n + j0) * rowb;
-  const char* wu = reinterpret_cast<const char*>(Wu) + ((int64_t)g.e * n + j0) * rowb;
-  lb.init([&](int i) -> const char* { return i < 64 ? wg + i * rowb : wu + (i - 64) * rowb; });
-  f32x16 acc[2][2];
-  gemm_mainloop<T>(la, lb, (int)(rowb / KB), acc, lds, wm, [&](int j) { return j * 64 + wn * 32; });
-  const int col = j0 + wn * 32 + (lane & 31);
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int m = acc_row(wm, i, v);
-      if (m >= g.mrows) continue;
-      const int64_t r = g.m0 + m;
-      const float gv = acc[i][0][v], uv = acc[i][1][v];
-      act[r * n + col] = from_f32<T>(gv * sigmoid_f32(gv) * uv);
-      if (H) {
-        H[r * 2 * n + col] = from_f32<T>(gv);
-        H[r * 2 * n + n + col] = from_f32<T>(uv);
-      }
+  const char* wg = reinterpret_cast<const char*>(Wg) + (int64_t)g.e * n * rowb;
+  const char* wu = reinterpret_cast<const char*>(Wu) + (int64_t)g.e * n * rowb;
+  lb.init([&](int i) -> const char* {
+    const int j = j0 + (i & 127);
+    if (j >= n) return nullptr;
+    return (i < 128 ? wg : wu) + (int64_t)j * rowb;
+  });
+  WaveAcc acc;
+  gemm_mainloop<T, KOperand<T>, KOperand<T>>(la, lb, (int)(rowb / KB), acc, lds, wm,
+                                             [&](int j) { return j * 128 + wn * 32; });
+  const int ccol = wn * 32 + (lane & 31);  // act column within the tile
+  const int valid = min(128, n - j0);
+  if constexpr (sizeof(T) == 2) {
+    auto silu_u = [&](int i, int j, int v) {
+      const float gv = acc.c[i][0][v], uv = acc.c[i][1][v];
+      return gv * sigmoid_f32(gv) * uv;
+    };
+    auto colf = [&](int j) { return j == 0 ? ccol : -1; };
+    epi_stage_bf16(lds, acc, wm, colf, silu_u);
+    __syncthreads();
+    epi_store_bf16(lds, reinterpret_cast<bf16*>(act) + (int64_t)g.m0 * n + j0, n, g.mrows, 128, valid);
+    if (H) {
+      // G and U halves side by side in one staging tile: columns [0,128) G, [128,256) U
+      __syncthreads();
+      auto both = [&](int j) { return j * 128 + ccol; };
+      epi_stage_bf16(lds, acc, wm, both, [&](int i, int j, int v) { return acc.c[i][j][v]; });
+      __syncthreads();
+      bf16* hb = reinterpret_cast<bf16*>(H) + (int64_t)g.m0 * 2 * n;
+      epi_store_bf16(lds, hb + j0, 2 * n, g.mrows, 128, valid);
+      // the U half: shift the staging base by 128 columns
+      epi_store_bf16(lds + 256, hb + n + j0, 2 * n, g.mrows, 128, valid);
     }
+  } else {
+    if (ccol < valid) {
+      const int col = j0 + ccol;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = acc_row(wm, i, v);
+          if (m >= g.mrows) continue;
+          const int64_t r = g.m0 + m;
+          const float gv = acc.c[i][0][v], uv = acc.c[i][1][v];
+          act[r * n + col] = from_f32<T>(gv * sigmoid_f32(gv) * uv);
+          if (H) {
+            H[r * 2 * n + col] = from_f32<T>(gv);
+            H[r * 2 * n + n + col] = from_f32<T>(uv);
+          }
+        }
+    }
+  }
 }
 
 hipError_t launch_up_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off,
                           const void* A_in, bool gathered, const void* W_gate, const void* W_up,
                           void* act, void* H, hipStream_t st) {
-  const int NT = (int)(s.n / 64);
+  const int NT = (int)cdiv(s.n, 128);
   const int grid = grid8(max_mtiles(s.R_max, s.E) * NT);
   if (s.bf16)
     k_up<bf16><<<grid, GEMM_THREADS, 0, st>>>(mtile_off, p.expert_off, p.row_token, (const bf16*)A_in,
-                                              gathered, (const bf16*)W_gate, (const bf16*)W_up,
-                                              (bf16*)act, (bf16*)H, (int)s.d, (int)s.n, s.E, NT);
+                                                     gathered, (const bf16*)W_gate, (const bf16*)W_up,
+                                                     (bf16*)act, (bf16*)H, (int)s.d, (int)s.n, s.E, NT);
   else
     k_up<float><<<grid, GEMM_THREADS, 0, st>>>(mtile_off, p.expert_off, p.row_token, (const float*)A_in,
-                                               gathered, (const float*)W_gate, (const float*)W_up,
-                                               (float*)act, (float*)H, (int)s.d, (int)s.n, s.E, NT);
+                                                      gathered, (const float*)W_gate, (const float*)W_up,
+                                                      (float*)act, (float*)H, (int)s.d, (int)s.n, s.E, NT);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------------------
-// Down projection: Y[r][c] = sum_j Act[r][j] W_down[e][c][j];  tile 128 rows x 128 columns of d.
+// Down projection: Y[r][c] = sum_j Act[r][j] W_down[e][c][j];  tile 256 rows x 256 columns of d.
 // ---------------------------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(GEMM_THREADS, 2) void k_down(
+__global__ __launch_bounds__(GEMM_THREADS, 1) void k_down(
     const int32_t* __restrict__ mtile_off, const int32_t* __restrict__ expert_off,
     const T* __restrict__ act, const T* __restrict__ Wd, T* __restrict__ Y, int d, int n, int E,
     int NT) {
@@ -177,7 +210,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_down(
   if (!find_group_tile(mt, mtile_off, expert_off, E, g)) return;
   const int n0 = nt * BN;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int64_t rowb = (int64_t)n * sizeof(T);
   RowLoader la, lb;
   la.init([&](int i) -> const char* {
@@ -185,19 +218,28 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_down(
   });
   const char* wd = reinterpret_cast<const char*>(Wd) + (int64_t)g.e * d * rowb;
   lb.init([&](int i) -> const char* { return n0 + i < d ? wd + (int64_t)(n0 + i) * rowb : nullptr; });
-  f32x16 acc[2][2];
-  gemm_mainloop<T>(la, lb, (int)(rowb / KB), acc, lds, wm, [&](int j) { return wn * 64 + j * 32; });
+  WaveAcc acc;
+  gemm_mainloop<T, KOperand<T>, KOperand<T>>(la, lb, (int)(rowb / KB), acc, lds, wm,
+                                             [&](int j) { return wn * 64 + j * 32; });
+  const int valid = min(BN, d - n0);
+  if constexpr (sizeof(T) == 2) {
+    epi_stage_bf16(lds, acc, wm, [&](int j) { return wn * 64 + j * 32 + (lane & 31); },
+                   [&](int i, int j, int v) { return acc.c[i][j][v]; });
+    __syncthreads();
+    epi_store_bf16(lds, reinterpret_cast<bf16*>(Y) + (int64_t)g.m0 * d + n0, d, g.mrows, BN, valid);
+  } else {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int c = n0 + wn * 64 + j * 32 + (lane & 31);
-    if (c >= d) continue;
+    for (int j = 0; j < 2; ++j) {
+      const int c = wn * 64 + j * 32 + (lane & 31);
+      if (c >= valid) continue;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = acc_row(wm, i, v);
-        if (m < g.mrows) Y[(int64_t)(g.m0 + m) * d + c] = from_f32<T>(acc[i][j][v]);
-      }
+        for (int v = 0; v < 16; ++v) {
+          const int m = acc_row(wm, i, v);
+          if (m < g.mrows) Y[(int64_t)(g.m0 + m) * d + n0 + c] = from_f32<T>(acc.c[i][j][v]);
+        }
+    }
   }
 }
 
@@ -207,10 +249,10 @@ hipError_t launch_down_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mt
   const int grid = grid8(max_mtiles(s.R_max, s.E) * NT);
   if (s.bf16)
     k_down<bf16><<<grid, GEMM_THREADS, 0, st>>>(mtile_off, p.expert_off, (const bf16*)act,
-                                                (const bf16*)W_down, (bf16*)Y, (int)s.d, (int)s.n, s.E, NT);
+                                                       (const bf16*)W_down, (bf16*)Y, (int)s.d, (int)s.n, s.E, NT);
   else
     k_down<float><<<grid, GEMM_THREADS, 0, st>>>(mtile_off, p.expert_off, (const float*)act,
-                                                 (const float*)W_down, (float*)Y, (int)s.d, (int)s.n, s.E, NT);
+                                                        (const float*)W_down, (float*)Y, (int)s.d, (int)s.n, s.E, NT);
   return hipGetLastError();
 }
 
