@@ -136,7 +136,7 @@ size_t moe_workspace_bytes(const moe_dims* dims, int op);
  *  X      [T,d] dtype, W_r [E,d] dtype, bias [E] fp32 or NULL: if X != NULL, the library computes
  *         logits = X W_r^T + bias (fp32 accumulation) and writes them to `logits`.
  *         If X == NULL, `logits` is an INPUT: caller-computed fp32 logits (bias already added).
- *  logits [T,E] fp32.  Must be finite.
+ *  logits [T,E] fp32.  NaN ranks below every number (so a token still gets K distinct experts).
  *  plan   all arrays written (see moe_plan).
  * Selection compares fp32 logits exactly: the K largest per token (ties to the lower expert id);
  * the gate weights are the softmax over the token's final expert set.  A token that token

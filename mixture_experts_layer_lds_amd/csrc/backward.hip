@@ -14,25 +14,6 @@ namespace moe {
 
 static inline int grid8(int64_t n) { return (int)((n + 7) / 8 * 8); }
 
-template <typename T, class KPtr>
-__device__ __forceinline__ typename MNOperand<T, KPtr>::Loader make_mn(KPtr f, int mn_base, int mn_valid) {
-  return typename MNOperand<T, KPtr>::Loader(f, mn_base, mn_valid);
-}
-
-// Store a bf16 staging tile row by row through a row-pointer functor (rows without a pointer
-// are skipped); 16-byte writes.
-template <class RowPtr>
-__device__ __forceinline__ void epi_store_rows(const char* lds, RowPtr row_ptr, int mrows, int ncols,
-                                               int ncols_valid) {
-  const int cpr = ncols / 8;
-  for (int c = threadIdx.x; c < 256 * cpr; c += GEMM_THREADS) {
-    const int r = c / cpr, ch = c % cpr;
-    if (r >= mrows || ch * 8 >= ncols_valid) continue;
-    bf16* p = row_ptr(r);
-    if (p) st16(p + ch * 8, *reinterpret_cast<const u32x4*>(lds + r * EPI_ROW + ch * 16));
-  }
-}
-
 // ---------------------------------------------------------------------------------------------
 // dAct: dA'[r][j] = sum_c dY[t_r][c] W_down[e][c][j]  (M = rows of e, N = n, K = d).
 // Wave column wn owns columns j*128 + wn*32 + (lane % 32), j = 0, 1, so that each half of the
@@ -50,8 +31,8 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dact(
     const int32_t* __restrict__ row_token, const float* __restrict__ row_w,
     const T* __restrict__ dY, const T* __restrict__ Wd, const T* __restrict__ H,
     T* __restrict__ dH, T* __restrict__ wA, float* __restrict__ dS_part, int64_t R_max, int d,
-    int n, int E, int NT) {
-  __shared__ __attribute__((aligned(16))) char lds[GEMM_LDS];
+    int n, int E, int NT, int T_) {
+  MOE_GEMM_LDS(L);
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int mt = lin / NT, nt = lin % NT;
   GroupTile g;
@@ -60,16 +41,14 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dact(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave >> 2, wn = wave & 3;
   const int64_t rowb = (int64_t)d * sizeof(T);
-  RowLoader la;
-  la.init([&](int i) -> const char* {
-    return i < g.mrows ? reinterpret_cast<const char*>(dY) + (int64_t)row_token[g.m0 + i] * rowb : nullptr;
+  auto la = k_rows<T>([&](int i) -> const char* {
+    return i < g.mrows ? reinterpret_cast<const char*>(dY) + (int64_t)clamp_idx(row_token[g.m0 + i], T_) * rowb
+                       : nullptr;
   });
   const char* wd = reinterpret_cast<const char*>(Wd) + ((int64_t)g.e * d * n + n0) * sizeof(T);
-  auto kp = [=](int k) -> const char* { return k < d ? wd + (int64_t)k * n * sizeof(T) : nullptr; };
-  auto lb = make_mn<T>(kp, n0, n);
+  auto lb = mn_rows<T>([=](int k) { return wd + (int64_t)k * n * sizeof(T); }, d, n0, n);
   WaveAcc acc;
-  gemm_mainloop<T, KOperand<T>, MNOperand<T, decltype(kp)>>(la, lb, (int)(rowb / KB), acc, lds, wm,
-                                                           [&](int j) { return j * 128 + wn * 32; });
+  gemm_mainloop<T>(la, lb, d / Mma<T>::BK, acc, L, wm, [&](int j) { return j * 128 + wn * 32; });
   // Epilogue, one 128-column half of the tile at a time: the wave dumps its fp32 accumulators
   // into an LDS tile [256][128], then the block walks the half row by row in 16-byte chunks
   // (coalesced loads of G, U and coalesced stores of dG, dU, w A), and the 16 or 32 lanes that
@@ -77,14 +56,16 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dact(
   constexpr int VEC = 16 / sizeof(T);
   constexpr int CPR = 128 / VEC;                 // chunks per half-row
   constexpr int FROW = 128 * 4 + 16;             // fp32 staging pitch
-  float* red = reinterpret_cast<float*>(lds + 256 * FROW);  // [256] dS partials of this tile
+  static_assert(64 * FROW + 1024 <= LDS_BUF, "fp32 staging + dS partials");
+  float* red = reinterpret_cast<float*>(L.b[0] + 64 * FROW);  // [256] dS partials of this tile
+  auto frow = [&](int r) { return epi_buf(L, r) + (r & 63) * FROW; };
   const int valid = min(BN, n - n0);
   for (int half = 0; half < 2; ++half) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v)
-        *reinterpret_cast<float*>(lds + acc_row(wm, i, v) * FROW + (wn * 32 + (lane & 31)) * 4) = acc.c[i][half][v];
+        *reinterpret_cast<float*>(frow(acc_row(wm, i, v)) + (wn * 32 + (lane & 31)) * 4) = acc.c[i][half][v];
     __syncthreads();
     for (int c = threadIdx.x; c < 256 * CPR; c += GEMM_THREADS) {
       const int row = c / CPR, ch = c % CPR;
@@ -95,7 +76,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dact(
         const float w = row_w[r];
         float dAp[VEC], G[VEC], U[VEC], oG[VEC], oU[VEC], oA[VEC];
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) dAp[k] = *reinterpret_cast<const float*>(lds + row * FROW + (ch * VEC + k) * 4);
+        for (int k = 0; k < VEC; ++k) dAp[k] = *reinterpret_cast<const float*>(frow(row) + (ch * VEC + k) * 4);
         unpack16<T>(ld16(H + r * 2 * n + n0 + col), G);
         unpack16<T>(ld16(H + r * 2 * n + n + n0 + col), U);
 #pragma unroll
@@ -134,12 +115,12 @@ hipError_t launch_dact_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mt
     k_dact<bf16><<<grid, GEMM_THREADS, 0, st>>>(mtile_off, p.expert_off, p.row_token, p.row_w,
                                                 (const bf16*)dY, (const bf16*)W_down, (const bf16*)H,
                                                 (bf16*)dH, (bf16*)wA, dS_part, s.R_max, (int)s.d,
-                                                (int)s.n, s.E, NT);
+                                                (int)s.n, s.E, NT, (int)s.T);
   else
     k_dact<float><<<grid, GEMM_THREADS, 0, st>>>(mtile_off, p.expert_off, p.row_token, p.row_w,
                                                  (const float*)dY, (const float*)W_down, (const float*)H,
                                                  (float*)dH, (float*)wA, dS_part, s.R_max, (int)s.d,
-                                                 (int)s.n, s.E, NT);
+                                                 (int)s.n, s.E, NT, (int)s.T);
   return hipGetLastError();
 }
 
@@ -152,7 +133,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dx(
     const int32_t* __restrict__ mtile_off, const int32_t* __restrict__ expert_off,
     const T* __restrict__ dH, const T* __restrict__ Wg, const T* __restrict__ Wu,
     T* __restrict__ dXp, int d, int n, int E, int NT) {
-  __shared__ __attribute__((aligned(16))) char lds[GEMM_LDS];
+  MOE_GEMM_LDS(L);
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int mt = lin / NT, nt = lin % NT;
   GroupTile g;
@@ -161,27 +142,22 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dx(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave >> 2, wn = wave & 3;
   const int64_t rowb = (int64_t)2 * n * sizeof(T);
-  RowLoader la;
-  la.init([&](int i) -> const char* {
+  auto la = k_rows<T>([&](int i) -> const char* {
     return i < g.mrows ? reinterpret_cast<const char*>(dH) + (int64_t)(g.m0 + i) * rowb : nullptr;
   });
   const int64_t wrow = (int64_t)d * sizeof(T);
   const char* wg = reinterpret_cast<const char*>(Wg) + (int64_t)g.e * n * wrow + n0 * sizeof(T);
   const char* wu = reinterpret_cast<const char*>(Wu) + (int64_t)g.e * n * wrow + n0 * sizeof(T);
-  auto kp = [=](int k) -> const char* {
-    if (k >= 2 * n) return nullptr;
-    return k < n ? wg + (int64_t)k * wrow : wu + (int64_t)(k - n) * wrow;
-  };
-  auto lb = make_mn<T>(kp, n0, d);
+  auto lb = mn_rows<T>([=](int k) { return k < n ? wg + (int64_t)k * wrow : wu + (int64_t)(k - n) * wrow; },
+                       2 * n, n0, d);
   WaveAcc acc;
-  gemm_mainloop<T, KOperand<T>, MNOperand<T, decltype(kp)>>(la, lb, (int)(rowb / KB), acc, lds, wm,
-                                                           [&](int j) { return wn * 64 + j * 32; });
+  gemm_mainloop<T>(la, lb, 2 * n / Mma<T>::BK, acc, L, wm, [&](int j) { return wn * 64 + j * 32; });
   const int valid = min(BN, d - n0);
   if constexpr (sizeof(T) == 2) {
-    epi_stage_bf16(lds, acc, wm, [&](int j) { return wn * 64 + j * 32 + (lane & 31); },
+    epi_stage_bf16(L, wm, [&](int j) { return wn * 64 + j * 32 + (lane & 31); },
                    [&](int i, int j, int v) { return acc.c[i][j][v]; });
     __syncthreads();
-    epi_store_bf16(lds, reinterpret_cast<bf16*>(dXp) + (int64_t)g.m0 * d + n0, d, g.mrows, BN, valid);
+    epi_store_bf16(L, 0, reinterpret_cast<bf16*>(dXp) + (int64_t)g.m0 * d + n0, d, g.mrows, BN, valid);
   } else {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -226,8 +202,8 @@ template <typename T>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dw_down(
     const int32_t* __restrict__ expert_off, const int32_t* __restrict__ row_token,
     const T* __restrict__ dY, const T* __restrict__ wA, T* __restrict__ dWd, int d, int n,
-    int E, int MT, int NT) {
-  __shared__ __attribute__((aligned(16))) char lds[GEMM_LDS];
+    int E, int MT, int NT, int T_) {
+  MOE_GEMM_LDS(L);
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int per = MT * NT;
   const int e = lin / per;
@@ -240,22 +216,19 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dw_down(
   const int cnt = expert_off[e + 1] - off;
   const char* dyb = reinterpret_cast<const char*>(dY) + m0 * sizeof(T);
   const char* wab = reinterpret_cast<const char*>(wA) + n0 * sizeof(T);
-  auto ka = [=](int k) -> const char* {
-    return k < cnt ? dyb + (int64_t)row_token[off + k] * d * sizeof(T) : nullptr;
-  };
-  auto kb = [=](int k) -> const char* { return k < cnt ? wab + (int64_t)(off + k) * n * sizeof(T) : nullptr; };
-  auto la = make_mn<T>(ka, m0, d);
-  auto lb = make_mn<T>(kb, n0, n);
+  auto la = mn_rows<T>([=](int k) {
+    return dyb + (int64_t)clamp_idx(sload_i32(row_token + off, k), T_) * d * sizeof(T);
+  }, cnt, m0, d);
+  auto lb = mn_rows<T>([=](int k) { return wab + (int64_t)(off + k) * n * sizeof(T); }, cnt, n0, n);
   WaveAcc acc;
-  gemm_mainloop<T, MNOperand<T, decltype(ka)>, MNOperand<T, decltype(kb)>>(
-      la, lb, (int)cdiv(cnt, Mma<T>::BK), acc, lds, wm, [&](int j) { return wn * 64 + j * 32; });
+  gemm_mainloop<T>(la, lb, (int)cdiv(cnt, Mma<T>::BK), acc, L, wm, [&](int j) { return wn * 64 + j * 32; });
   T* out = dWd + (int64_t)e * d * n;
   const int mrows = min(BM, d - m0), valid = min(BN, n - n0);
   if constexpr (sizeof(T) == 2) {
-    epi_stage_bf16(lds, acc, wm, [&](int j) { return wn * 64 + j * 32 + (lane & 31); },
+    epi_stage_bf16(L, wm, [&](int j) { return wn * 64 + j * 32 + (lane & 31); },
                    [&](int i, int j, int v) { return acc.c[i][j][v]; });
     __syncthreads();
-    epi_store_bf16(lds, reinterpret_cast<bf16*>(out) + (int64_t)m0 * n + n0, n, mrows, BN, valid);
+    epi_store_bf16(L, 0, reinterpret_cast<bf16*>(out) + (int64_t)m0 * n + n0, n, mrows, BN, valid);
   } else {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -279,11 +252,11 @@ hipError_t launch_dw_down_gemm(const Shape& s, const PlanPtrs& p, const void* dY
   if (s.bf16)
     k_dw_down<bf16><<<grid, GEMM_THREADS, 0, st>>>(p.expert_off, p.row_token, (const bf16*)dY,
                                                    (const bf16*)wA, (bf16*)dW_down, (int)s.d,
-                                                   (int)s.n, s.E, MT, NT);
+                                                   (int)s.n, s.E, MT, NT, (int)s.T);
   else
     k_dw_down<float><<<grid, GEMM_THREADS, 0, st>>>(p.expert_off, p.row_token, (const float*)dY,
                                                     (const float*)wA, (float*)dW_down, (int)s.d,
-                                                    (int)s.n, s.E, MT, NT);
+                                                    (int)s.n, s.E, MT, NT, (int)s.T);
   return hipGetLastError();
 }
 
@@ -291,8 +264,8 @@ template <typename T>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dw_gu(
     const int32_t* __restrict__ expert_off, const int32_t* __restrict__ row_token,
     const T* __restrict__ dH, const T* __restrict__ X, T* __restrict__ dWg, T* __restrict__ dWu,
-    int d, int n, int E, int MT, int NT) {
-  __shared__ __attribute__((aligned(16))) char lds[GEMM_LDS];
+    int d, int n, int E, int MT, int NT, int T_) {
+  MOE_GEMM_LDS(L);
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int per = MT * NT;
   const int e = lin / per;
@@ -305,27 +278,22 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dw_gu(
   const int cnt = expert_off[e + 1] - off;
   const char* dhb = reinterpret_cast<const char*>(dH) + m0 * sizeof(T);
   const char* xb = reinterpret_cast<const char*>(X) + n0 * sizeof(T);
-  auto ka = [=](int k) -> const char* {
-    return k < cnt ? dhb + (int64_t)(off + k) * 2 * n * sizeof(T) : nullptr;
-  };
-  auto kb = [=](int k) -> const char* {
-    return k < cnt ? xb + (int64_t)row_token[off + k] * d * sizeof(T) : nullptr;
-  };
-  auto la = make_mn<T>(ka, m0, 2 * n);
-  auto lb = make_mn<T>(kb, n0, d);
+  auto la = mn_rows<T>([=](int k) { return dhb + (int64_t)(off + k) * 2 * n * sizeof(T); }, cnt, m0, 2 * n);
+  auto lb = mn_rows<T>([=](int k) {
+    return xb + (int64_t)clamp_idx(sload_i32(row_token + off, k), T_) * d * sizeof(T);
+  }, cnt, n0, d);
   WaveAcc acc;
-  gemm_mainloop<T, MNOperand<T, decltype(ka)>, MNOperand<T, decltype(kb)>>(
-      la, lb, (int)cdiv(cnt, Mma<T>::BK), acc, lds, wm, [&](int j) { return wn * 64 + j * 32; });
+  gemm_mainloop<T>(la, lb, (int)cdiv(cnt, Mma<T>::BK), acc, L, wm, [&](int j) { return wn * 64 + j * 32; });
   const int mrows = min(BM, 2 * n - m0), valid = min(BN, d - n0);
   auto row_ptr = [&](int r) -> T* {
     const int m = m0 + r;
     return (m < n ? dWg + ((int64_t)e * n + m) * d : dWu + ((int64_t)e * n + (m - n)) * d) + n0;
   };
   if constexpr (sizeof(T) == 2) {
-    epi_stage_bf16(lds, acc, wm, [&](int j) { return wn * 64 + j * 32 + (lane & 31); },
+    epi_stage_bf16(L, wm, [&](int j) { return wn * 64 + j * 32 + (lane & 31); },
                    [&](int i, int j, int v) { return acc.c[i][j][v]; });
     __syncthreads();
-    epi_store_rows(lds, [&](int r) { return reinterpret_cast<bf16*>(row_ptr(r)); }, mrows, BN, valid);
+    epi_store_rows(L, 0, [&](int r) { return reinterpret_cast<bf16*>(row_ptr(r)); }, mrows, BN, valid);
   } else {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -349,11 +317,11 @@ hipError_t launch_dw_gu_gemm(const Shape& s, const PlanPtrs& p, const void* dH, 
   if (s.bf16)
     k_dw_gu<bf16><<<grid, GEMM_THREADS, 0, st>>>(p.expert_off, p.row_token, (const bf16*)dH,
                                                  (const bf16*)X, (bf16*)dW_gate, (bf16*)dW_up,
-                                                 (int)s.d, (int)s.n, s.E, MT, NT);
+                                                 (int)s.d, (int)s.n, s.E, MT, NT, (int)s.T);
   else
     k_dw_gu<float><<<grid, GEMM_THREADS, 0, st>>>(p.expert_off, p.row_token, (const float*)dH,
                                                   (const float*)X, (float*)dW_gate, (float*)dW_up,
-                                                  (int)s.d, (int)s.n, s.E, MT, NT);
+                                                  (int)s.d, (int)s.n, s.E, MT, NT, (int)s.T);
   return hipGetLastError();
 }
 
@@ -392,8 +360,9 @@ __global__ __launch_bounds__(256) void k_router_bwd(
   for (int e = lane; e < E_pad; e += 64) sdl[e] = 0.0f;
   // pass 1: s = sum_r w_r dS_r
   float part = 0.0f;
+  const int rmax = (int)R_max;
   for (int i = lane; i < cnt; i += 64) {
-    const int r = tok_row[base + i];
+    const int r = clamp_idx(tok_row[base + i], rmax);
     float ds = 0.0f;
     for (int q = 0; q < ntiles; ++q) ds += dS_part[(int64_t)q * R_max + r];
     part += row_w[r] * ds;
@@ -401,7 +370,7 @@ __global__ __launch_bounds__(256) void k_router_bwd(
   const float ssum = wave_sum(part);
   // pass 2: dL per row, dS out, dense dL row in LDS
   for (int i = lane; i < cnt; i += 64) {
-    const int r = tok_row[base + i];
+    const int r = clamp_idx(tok_row[base + i], rmax);
     float ds = 0.0f;
     for (int q = 0; q < ntiles; ++q) ds += dS_part[(int64_t)q * R_max + r];
     dS[r] = ds;
@@ -429,7 +398,7 @@ __global__ __launch_bounds__(256) void k_router_bwd(
       int rr[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        rr[q] = tok_row[base + i + q];
+        rr[q] = clamp_idx(tok_row[base + i + q], rmax);
         v[q] = ld16_nt(dXp + (int64_t)rr[q] * d + ch * VEC);
       }
 #pragma unroll
@@ -449,7 +418,7 @@ __global__ __launch_bounds__(256) void k_router_bwd(
       }
     }
     for (; i < cnt; ++i) {
-      const int r = tok_row[base + i];
+      const int r = clamp_idx(tok_row[base + i], rmax);
       float f[VEC];
       unpack16<T>(ld16_nt(dXp + (int64_t)r * d + ch * VEC), f);
 #pragma unroll
@@ -515,7 +484,7 @@ template <typename T>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dwr(
     const T* __restrict__ dLop, int E_pad, const T* __restrict__ X, float* __restrict__ part,
     T* __restrict__ dWr, int T_, int d, int E, int MT, int NT, int S, int TS) {
-  __shared__ __attribute__((aligned(16))) char lds[GEMM_LDS];
+  MOE_GEMM_LDS(L);
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int per = MT * NT;
   const int sl = lin / per;
@@ -528,13 +497,10 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dwr(
   const int klen = min(TS, T_ - t0);
   const char* ab = reinterpret_cast<const char*>(dLop) + m0 * sizeof(T);
   const char* xb = reinterpret_cast<const char*>(X) + n0 * sizeof(T);
-  auto ka = [=](int k) -> const char* { return k < klen ? ab + (int64_t)(t0 + k) * E_pad * sizeof(T) : nullptr; };
-  auto kb = [=](int k) -> const char* { return k < klen ? xb + (int64_t)(t0 + k) * d * sizeof(T) : nullptr; };
-  auto la = make_mn<T>(ka, m0, E_pad);
-  auto lb = make_mn<T>(kb, n0, d);
+  auto la = mn_rows<T>([=](int k) { return ab + (int64_t)(t0 + k) * E_pad * sizeof(T); }, klen, m0, E_pad);
+  auto lb = mn_rows<T>([=](int k) { return xb + (int64_t)(t0 + k) * d * sizeof(T); }, klen, n0, d);
   WaveAcc acc;
-  gemm_mainloop<T, MNOperand<T, decltype(ka)>, MNOperand<T, decltype(kb)>>(
-      la, lb, (int)cdiv(klen, Mma<T>::BK), acc, lds, wm, [&](int j) { return wn * 64 + j * 32; });
+  gemm_mainloop<T>(la, lb, (int)cdiv(klen, Mma<T>::BK), acc, L, wm, [&](int j) { return wn * 64 + j * 32; });
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int c = n0 + wn * 64 + j * 32 + (lane & 31);

@@ -16,11 +16,12 @@ namespace moe {
 template <typename T>
 __global__ __launch_bounds__(256) void k_permute(const int32_t* __restrict__ meta,
                                                  const int32_t* __restrict__ row_token,
-                                                 const T* __restrict__ X, T* __restrict__ Xp, int d) {
+                                                 const T* __restrict__ X, T* __restrict__ Xp, int d,
+                                                 int T_) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (r >= meta[0]) return;
-  const int64_t src = row_token[r];
+  const int64_t src = clamp_idx(row_token[r], T_);
   constexpr int VEC = 16 / sizeof(T);
   const int nch = d / VEC;
   const T* s = X + src * d;
@@ -30,8 +31,8 @@ __global__ __launch_bounds__(256) void k_permute(const int32_t* __restrict__ met
 
 hipError_t launch_permute(const Shape& s, const PlanPtrs& p, const void* X, void* X_perm, hipStream_t st) {
   const int grid = (int)cdiv(s.R_max, 4);
-  if (s.bf16) k_permute<bf16><<<grid, 256, 0, st>>>(p.meta, p.row_token, (const bf16*)X, (bf16*)X_perm, (int)s.d);
-  else k_permute<float><<<grid, 256, 0, st>>>(p.meta, p.row_token, (const float*)X, (float*)X_perm, (int)s.d);
+  if (s.bf16) k_permute<bf16><<<grid, 256, 0, st>>>(p.meta, p.row_token, (const bf16*)X, (bf16*)X_perm, (int)s.d, (int)s.T);
+  else k_permute<float><<<grid, 256, 0, st>>>(p.meta, p.row_token, (const float*)X, (float*)X_perm, (int)s.d, (int)s.T);
   return hipGetLastError();
 }
 
@@ -42,7 +43,7 @@ __global__ __launch_bounds__(256) void k_combine(const int32_t* __restrict__ tok
                                                  const int32_t* __restrict__ tok_row,
                                                  const float* __restrict__ row_w,
                                                  const T* __restrict__ Y, T* __restrict__ out,
-                                                 int T_, int d) {
+                                                 int T_, int d, int rmax) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (t >= T_) return;
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(256) void k_combine(const int32_t* __restrict__ tok
       float w[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int r = tok_row[base + i + q];
+        const int r = clamp_idx(tok_row[base + i + q], rmax);
         v[q] = ld16_nt(Y + (int64_t)r * d + c * VEC);
         w[q] = WEIGHTED ? row_w[r] : 1.0f;
       }
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(256) void k_combine(const int32_t* __restrict__ tok
       }
     }
     for (; i < cnt; ++i) {
-      const int r = tok_row[base + i];
+      const int r = clamp_idx(tok_row[base + i], rmax);
       const float w = WEIGHTED ? row_w[r] : 1.0f;
       float f[VEC];
       unpack16<T>(ld16_nt(Y + (int64_t)r * d + c * VEC), f);
@@ -87,7 +88,7 @@ hipError_t launch_combine(const Shape& s, const PlanPtrs& p, const void* Y_perm,
                           void* out, hipStream_t st) {
   const int grid = (int)cdiv(s.T, 4);
 #define MOE_COMB(TT, W) k_combine<TT, W><<<grid, 256, 0, st>>>(p.tok_off, p.tok_row, p.row_w, \
-      (const TT*)Y_perm, (TT*)out, (int)s.T, (int)s.d)
+      (const TT*)Y_perm, (TT*)out, (int)s.T, (int)s.d, (int)s.R_max)
   if (s.bf16) { if (weighted) MOE_COMB(bf16, true); else MOE_COMB(bf16, false); }
   else { if (weighted) MOE_COMB(float, true); else MOE_COMB(float, false); }
 #undef MOE_COMB

@@ -89,6 +89,10 @@ template <> __device__ __forceinline__ u32x4 pack16<bf16>(const float* f) {
 
 __host__ __device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Clamp a gathered index into [0, n): routing indices are always in range when they come from
+// moe_route; the clamp keeps every gathered read in bounds even for a corrupted plan.
+__device__ __forceinline__ int clamp_idx(int i, int n) { return min(max(i, 0), n - 1); }
+
 // XCD-aware remap of a 1-D grid: hardware hands consecutive workgroups to the 8 XCDs in turn,
 // each with its own L2.  Remap so that each XCD walks a contiguous range of logical tiles
 // (neighbouring tiles share operands).  `n` must be a multiple of 8.

@@ -4,24 +4,35 @@
 //   * workgroup = 512 threads = 8 waves in a 2 (M) x 4 (N) grid; block tile 256 x 256;
 //   * each wave owns 128 x 64 = 4 x 2 MFMA 32x32 blocks
 //     (bf16: v_mfma_f32_32x32x16_bf16; fp32: v_mfma_f32_32x32x2_f32);
-//   * K advances in stages of 128 bytes per row (64 bf16 / 32 fp32 elements), double-buffered in
-//     LDS: the next stage's global loads are in flight while the current stage feeds the MFMAs.
+//   * LDS = four 36 KiB buffers.
 //
-// Operand staging (the SonicMoE page's "gather fused into the HBM->SMEM load", done on gfx950 with
-// 16-byte vector loads into LDS; a row pointer can come through an index, so gathered token rows
-// cost nothing extra):
-//   * K-major operand (each row's K elements contiguous in memory, e.g. activations or
-//     [out][in] weights): LDS tile [256 rows][128 B + 16 B pad]; an MFMA fragment is one
-//     ds_read_b128 (32 lanes on 32 rows: the 144-byte pitch puts them on distinct banks).
-//   * MN-major bf16 operand (each k-row contiguous along M or N, e.g. dY / X / dH rows feeding a
-//     weight gradient, or weights read transposed): staged untransposed as LDS [64 k][256 mn]
-//     with a 576-byte pitch, and read with the gfx950 transposing LDS load ds_read_b64_tr_b16.
-//     Within a 16-lane group, lane i supplies 4 consecutive 16-bit elements and lane j receives
-//     element j%4 of lanes j/4, j/4+4, j/4+8, j/4+12 (verified on gfx950).  Lane i therefore
-//     points at k-row i/4 and column 4(i%4): lane j receives 4 consecutive k of column j.  Two
-//     such loads give the 8 k-values of an MFMA fragment.  The 576-byte pitch (= 16 banks mod 64)
-//     puts the four k-rows one half-wave touches on disjoint banks.
-//   * MN-major fp32 operands (small fp32 layers only) are transposed in registers while staged.
+// bf16 path — a four-deep ring of K stages (32 k per stage) filled by direct global->LDS loads
+// (global_load_lds_dwordx4: each lane moves 16 bytes straight into LDS, no registers), issued
+// three stages ahead of the MFMAs.  This is the gfx950 form of the SonicMoE page's asynchronous
+// "Gather+Load -> GEMM" (its kernels overlap IO with MMA through cp.async; section "Gather
+// 与加载融合"): the gathered row pointers feed the DMA directly.  One wave instruction fills
+// 1 KiB of contiguous LDS (lane l -> byte 16 l), so tiles are unpadded and XOR-swizzled:
+//   * K-major operand (rows with contiguous K: activations, [out][in] weights): [256][64 B];
+//     16-byte chunk c of row r sits at slot c ^ ((r >> 2) & 3).  An MFMA fragment is one
+//     ds_read_b128 per lane; 16 consecutive rows hit 16 distinct bank groups.
+//   * MN-major operand (rows indexed by k, contiguous along M or N: dY / X / dH rows feeding a
+//     weight gradient, or weights read transposed): [32 k][256 mn = 512 B]; chunk c of k-row k
+//     sits at slot c ^ (4 (k & 3)), and fragments are read with the transposing LDS load
+//     ds_read_b64_tr_b16.  Within a 16-lane group, lane i supplies 4 consecutive 16-bit
+//     elements and lane j receives element j%4 of lanes j/4, j/4+4, j/4+8, j/4+12 (verified on
+//     gfx950): lane i points at k-row i/4, column 4 (i%4), so lane j receives 4 consecutive k of
+//     column j; two such loads make the 8 k-values of an MFMA fragment.
+//   Invalid rows / columns are loaded from a zero page, so padding contributes zeros.
+//   Waits: each thread issues 4 DMA instructions per stage, in order; before a stage is read it
+//   waits until at most 4 * (stages issued after it) are outstanding, then a plain s_barrier (no
+//   fence) publishes every wave's DMA writes.  Each ring slot is its own __shared__ array and the
+//   loop is unrolled by the ring depth, so the compiler can tell that reading one slot does not
+//   conflict with the DMAs still in flight into the others.  Fragment reads are double-buffered
+//   in registers so that LDS latency hides behind the previous k-step's MFMAs.
+//
+// fp32 path (small fp32 layers only) — register-staged double buffer: stage j uses buffers
+// 2j (A) and 2j+1 (B) as [256][128 B + 16 B pad]; MN-major fp32 operands are transposed in
+// registers while staged.
 //
 // Accumulator layout (32x32 MFMA, verified on gfx950): register v of lane l holds
 //   row (v / 4) * 8 + (l / 32) * 4 + (v % 4), column l % 32.
@@ -34,19 +45,35 @@ namespace moe {
 constexpr int BM = 256;
 constexpr int BN = 256;
 constexpr int GEMM_THREADS = 512;
-constexpr int KB = 128;                     // bytes of K per stage and row
-constexpr int KROW = KB + 16;               // K-major LDS row pitch
-constexpr int MNROW = 256 * 2 + 64;         // MN-major (bf16) LDS row pitch
-constexpr int STAGE_BYTES = 256 * KROW;     // one operand, one stage (= 64 * MNROW)
-static_assert(STAGE_BYTES == 64 * MNROW, "operand stage sizes must agree");
-constexpr int GEMM_LDS = 4 * STAGE_BYTES;   // A and B, two stages each: 147456 bytes
+constexpr int LDS_BUF = 36864;              // bytes per LDS buffer (four per workgroup)
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void gmem_void;
+
+// Read-only int32 at base[i] through the scalar cache (i made wave-uniform): used for gathered row
+// indices inside the DMA loop, where a vector load would be counted by vmcnt and force the wait
+// on every outstanding DMA.
+__device__ __forceinline__ int sload_i32(const int32_t* base, int i) {
+  typedef const __attribute__((address_space(4))) int32_t cint;
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const int u = __builtin_amdgcn_readfirstlane(i);
+  return *((cint*)(((uint64_t)hi << 32) | lo) + u);
+}
+
+// Zero-filled global memory that invalid operand rows are loaded from.
+static __device__ __attribute__((aligned(1024))) char g_zero_page[1024];
+
+struct LdsBufs {
+  char* b[4];
+};
 
 template <typename T> struct Mma;
 template <> struct Mma<bf16> {
-  static constexpr int BK = KB / 2;              // 64 elements per stage
+  static constexpr int BK = 32;                  // k per stage (DMA ring)
   static constexpr int STEPS = BK / 16;
   typedef bf16x8 frag;
   __device__ static f32x16 mma(frag a, frag b, f32x16 c) {
@@ -54,7 +81,7 @@ template <> struct Mma<bf16> {
   }
 };
 template <> struct Mma<float> {
-  static constexpr int BK = KB / 4;              // 32 elements per stage
+  static constexpr int BK = 32;                  // 128 bytes per row per stage
   static constexpr int STEPS = BK / 2;
   typedef float frag;
   __device__ static f32x16 mma(frag a, frag b, f32x16 c) {
@@ -62,31 +89,111 @@ template <> struct Mma<float> {
   }
 };
 
-// ---------------------------------------------------------------------------------------------
-// Fragment readers.  row0 / mn0: first of the 32 rows (M or N) of the fragment; s: k-step.
-// ---------------------------------------------------------------------------------------------
-template <typename T> struct KFrag;
-template <> struct KFrag<bf16> {
-  __device__ static bf16x8 read(const char* lds, int row0, int s) {
+struct WaveAcc {
+  f32x16 c[4][2];
+};
+
+__device__ __forceinline__ void zero_acc(WaveAcc& acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc.c[i][j][v] = 0.0f;
+}
+
+// ===============================================================================================
+// bf16: DMA ring
+// ===============================================================================================
+constexpr int DMA_B_OFF = 16384;            // B tile offset inside a ring slot (A tile at 0)
+
+// s_waitcnt with only vmcnt <= n (n < 16).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+__device__ __forceinline__ void dma16(const void* g, char* lds_uniform) {
+  __builtin_amdgcn_global_load_lds((gmem_void*)g, (lds_void*)lds_uniform, 16, 0, 0);
+}
+
+// K-major operand: tile row i of the stage <- 64 bytes of row_ptr(i) at K offset 64 s.  Wave w
+// instruction q fills rows R0 = (8 q + w) * 16 .. R0 + 15; lane l takes row R0 + l/4 and the
+// chunk that lands in its slot: (l & 3) ^ (l >> 4).  row_ptr returns null for an invalid row.
+struct KDma {
+  const char* g[2];
+  int step[2];
+  template <class RowPtr>
+  __device__ void init(RowPtr row_ptr) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int chunk = (lane & 3) ^ (lane >> 4);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const char* p = row_ptr((8 * q + w) * 16 + (lane >> 2));
+      g[q] = p ? p + chunk * 16 : g_zero_page + chunk * 16;
+      step[q] = p ? 64 : 0;
+    }
+  }
+  __device__ void issue(int s, char* dst) const {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) dma16(g[q] + (int64_t)s * step[q], dst + (8 * q + w) * 1024);
+  }
+  __device__ static bf16x8 frag(const char* t, int row0, int s) {
     const int lane = threadIdx.x & 63;
-    return *reinterpret_cast<const bf16x8*>(lds + (row0 + (lane & 31)) * KROW + s * 32 + (lane >> 5) * 16);
+    const int r = row0 + (lane & 31);
+    const int slot = (s * 2 + (lane >> 5)) ^ ((r >> 2) & 3);
+    return *reinterpret_cast<const bf16x8*>(t + r * 64 + slot * 16);
   }
 };
-template <> struct KFrag<float> {
-  __device__ static float read(const char* lds, int row0, int s) {
-    const int lane = threadIdx.x & 63;
-    return *reinterpret_cast<const float*>(lds + (row0 + (lane & 31)) * KROW + s * 8 + (lane >> 5) * 4);
+
+// MN-major operand: stage k-rows 32 s .. 32 s + 31.  kbase(k) returns the global address of
+// element (mn_base, k) for 0 <= k < klim; it is only ever called with k clamped into that range
+// (so a gathered row index is always read in bounds), and rows k >= klim load zeros.  Wave w
+// instruction q fills k-rows K0 = (8 q + w) * 2 and K0 + 1: lanes 0-31 the first, 32-63 the
+// second; lane slot l % 32 holds chunk (l % 32) ^ (4 (k & 3)).  The address math is branch-free.
+template <class KBase>
+struct MNDma {
+  KBase kbase;
+  int klim;
+  int chunk[2];
+  bool mn_ok[2];
+  __device__ MNDma(KBase f, int klim_, int mn_base, int mn_valid) : kbase(f), klim(klim_) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int k = (8 * q + w) * 2 + (lane >> 5);
+      chunk[q] = (lane & 31) ^ (4 * (k & 3));
+      mn_ok[q] = mn_base + chunk[q] * 8 < mn_valid;
+    }
   }
-};
-struct MNFrag {  // bf16 only
-  __device__ static bf16x8 read(const char* lds, int mn0, int s) {
+  __device__ void issue(int s, char* dst) const {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int lim = __builtin_amdgcn_readfirstlane(klim);
+      const int k0 = __builtin_amdgcn_readfirstlane(s * 32 + (8 * q + w) * 2);
+      const int c0 = __builtin_amdgcn_readfirstlane(min(k0, lim - 1));
+      const int c1 = __builtin_amdgcn_readfirstlane(min(k0 + 1, lim - 1));
+      const uint64_t p0 = reinterpret_cast<uint64_t>(kbase(c0));
+      const uint64_t p1 = reinterpret_cast<uint64_t>(kbase(c1));
+      const bool hi = lane >= 32;
+      const bool ok = mn_ok[q] && (hi ? k0 + 1 < lim : k0 < lim);
+      const uint64_t row = hi ? p1 : p0;
+      const uint64_t zero = reinterpret_cast<uint64_t>(g_zero_page) + (lane & 31) * 16;
+      const uint64_t src = ok ? row + chunk[q] * 16 : zero;
+      dma16(reinterpret_cast<const void*>(src), dst + (8 * q + w) * 1024);
+    }
+  }
+  __device__ static bf16x8 frag(const char* t, int mn0, int s) {
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4, i = lane & 15;
     const int k = s * 16 + (g >> 1) * 8 + (i >> 2);
     const int mn = mn0 + (g & 1) * 16 + 4 * (i & 3);
-    const char* p = lds + k * MNROW + mn * 2;
-    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
-    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 4 * MNROW));
+    const int col = ((mn >> 3) ^ (4 * (k & 3))) * 16 + (mn & 7) * 2;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(t + k * 512 + col));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(t + (k + 4) * 512 + col));
     const v4i16 both[2] = {lo, hi};
     bf16x8 r;
     __builtin_memcpy(&r, both, 16);
@@ -94,12 +201,104 @@ struct MNFrag {  // bf16 only
   }
 };
 
-// ---------------------------------------------------------------------------------------------
-// Loaders: load(kt) issues the global loads of stage kt into registers, store(lds) writes them.
-// ---------------------------------------------------------------------------------------------
-// K-major rows: LDS row i <- 128 bytes of global row rp_i at stage kt.  Thread owns rows
-// tid/8 + 64 q (q = 0..3), chunk tid % 8.  A null row stages zeros.
-struct RowLoader {
+// Fragments of one MFMA k-step for this wave: 4 A blocks (its 128 rows) and 2 B blocks.
+struct FragSet {
+  bf16x8 a[4], b[2];
+};
+
+template <class AL, class BL, class BSub>
+__device__ __forceinline__ void load_frags(const char* slot, int ks, int wm, BSub bsub, FragSet& F) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) F.b[j] = BL::frag(slot + DMA_B_OFF, bsub(j), ks);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) F.a[i] = AL::frag(slot, wm * 128 + i * 32, ks);
+}
+
+__device__ __forceinline__ void mma_frags(const FragSet& F, WaveAcc& acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc.c[i][j] = Mma<bf16>::mma(F.a[i], F.b[j], acc.c[i][j]);
+}
+
+// Scheduling hint for a block of 6 fragment reads and 8 MFMAs: alternate one LDS read with one
+// MFMA so that the reads of the next k-step hide behind the current k-step's matrix work.
+__device__ __forceinline__ void interleave_reads_mfma() {
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);    // the remaining MFMAs
+}
+
+// Workgroup barrier without a memory fence (the DMA waits are explicit); the empty asm keeps the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One ring step for stage s (two MFMA k-steps).  On entry F0 holds stage s's k-step 0 fragments.
+//   1. read stage s's k-step 1 fragments into F1 while the k-step 0 MFMAs run;
+//   2. wait for stage s + 1 (only stage s + 2, four DMA instructions, was issued after it) and
+//      barrier: every wave is now done with stage s - 1, whose slot is refilled with stage s + 3
+//      (past the end: the last stage again, never computed, so the DMA count per step is fixed
+//      and the waits stay exact);
+//   3. issue the k-step 1 MFMAs, then read stage s + 1's k-step 0 fragments into F0 while they
+//      run.
+// The DMA issue is unconditional and its address never comes from a pointer select: a DMA under
+// a branch makes the compiler's wait tracking fall back to draining everything.
+template <class AL, class BL, class BSub>
+__device__ __forceinline__ void dma_step(const AL& la, const BL& lb, int s, int nkt, const char* cur,
+                                         const char* next, char* refill, FragSet& F0, FragSet& F1,
+                                         WaveAcc& acc, int wm, BSub bsub) {
+  const bool live = s < nkt;
+  if (live) {
+    load_frags<AL, BL>(cur, 1, wm, bsub, F1);
+    mma_frags(F0, acc);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<4>();
+  ring_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  const int r = min(s + 3, nkt - 1);
+  la.issue(r, refill);
+  lb.issue(r, refill + DMA_B_OFF);
+  if (live) mma_frags(F1, acc);
+  if (s + 1 < nkt) load_frags<AL, BL>(next, 0, wm, bsub, F0);
+}
+
+template <class AL, class BL, class BSub>
+__device__ __forceinline__ void gemm_mainloop_dma(const AL& la, const BL& lb, int nkt, WaveAcc& acc,
+                                                  LdsBufs L, int wm, BSub bsub) {
+  zero_acc(acc);
+  if (nkt <= 0) return;
+  la.issue(0, L.b[0]);
+  lb.issue(0, L.b[0] + DMA_B_OFF);
+  la.issue(min(1, nkt - 1), L.b[1]);
+  lb.issue(min(1, nkt - 1), L.b[1] + DMA_B_OFF);
+  la.issue(min(2, nkt - 1), L.b[2]);
+  lb.issue(min(2, nkt - 1), L.b[2] + DMA_B_OFF);
+  wait_vmcnt<8>();
+  ring_barrier();
+  FragSet F0, F1;
+  load_frags<AL, BL>(L.b[0], 0, wm, bsub, F0);
+  for (int s = 0; s < nkt; s += 4) {
+    dma_step(la, lb, s, nkt, L.b[0], L.b[1], L.b[3], F0, F1, acc, wm, bsub);
+    dma_step(la, lb, s + 1, nkt, L.b[1], L.b[2], L.b[0], F0, F1, acc, wm, bsub);
+    dma_step(la, lb, s + 2, nkt, L.b[2], L.b[3], L.b[1], F0, F1, acc, wm, bsub);
+    dma_step(la, lb, s + 3, nkt, L.b[3], L.b[0], L.b[2], F0, F1, acc, wm, bsub);
+  }
+  __syncthreads();  // drains the trailing loads; the LDS is free for the epilogue
+}
+
+// ===============================================================================================
+// fp32: register-staged double buffer
+// ===============================================================================================
+constexpr int KROW = 128 + 16;              // padded K-major row pitch (bytes)
+
+struct RowLoaderF32 {                       // K-major rows: thread owns rows tid/8 + 64 q
   const char* rp[4];
   u32x4 v[4];
   template <class RowPtr>
@@ -111,7 +310,7 @@ struct RowLoader {
     const int chunk = threadIdx.x & 7;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      if (rp[q]) v[q] = ld16(rp[q] + (int64_t)kt * KB + chunk * 16);
+      if (rp[q]) v[q] = ld16(rp[q] + (int64_t)kt * 128 + chunk * 16);
       else v[q] = u32x4{0u, 0u, 0u, 0u};
     }
   }
@@ -121,52 +320,28 @@ struct RowLoader {
     for (int q = 0; q < 4; ++q)
       *reinterpret_cast<u32x4*>(lds + ((threadIdx.x >> 3) + 64 * q) * KROW + chunk * 16) = v[q];
   }
-};
-
-// MN-major bf16 tile, staged untransposed: LDS [64 k][256 mn].  kptr(k) returns the global
-// address of element (mn_base, k) or null (zeros).  Thread owns k-rows tid/32 + 16 q, chunk
-// tid % 32 (8 mn elements); chunks at or beyond mn_valid stage zeros.
-template <class KPtr>
-struct TileLoaderMN {
-  KPtr kptr;
-  u32x4 v[4];
-  bool ok;
-  __device__ TileLoaderMN(KPtr f, int mn_base, int mn_valid) : kptr(f) {
-    ok = mn_base + (int)(threadIdx.x & 31) * 8 < mn_valid;
-  }
-  __device__ void load(int kt) {
-    const int chunk = threadIdx.x & 31;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const char* p = ok ? kptr(kt * 64 + (int)(threadIdx.x >> 5) + 16 * q) : nullptr;
-      if (p) v[q] = ld16(p + chunk * 16);
-      else v[q] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  __device__ void store(char* lds) const {
-    const int chunk = threadIdx.x & 31;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<u32x4*>(lds + ((threadIdx.x >> 5) + 16 * q) * MNROW + chunk * 16) = v[q];
+  __device__ static float frag(const char* lds, int row0, int s) {
+    const int lane = threadIdx.x & 63;
+    return *reinterpret_cast<const float*>(lds + (row0 + (lane & 31)) * KROW + s * 8 + (lane >> 5) * 4);
   }
 };
 
-// MN-major fp32 operand, transposed in registers into the K-major LDS layout: thread owns a
-// 4 (k) x 4 (mn) block, mn = 4 (tid % 64), k = 4 (tid / 64).
-template <class KPtr>
+// MN-major fp32 operand, transposed in registers into the K-major layout: thread owns a 4 (k) x
+// 4 (mn) block, mn = 4 (tid % 64), k = 4 (tid / 64).  kbase / klim as for MNDma.
+template <class KBase>
 struct ColLoaderF32 {
-  KPtr kptr;
+  KBase kbase;
+  int klim;
   u32x4 v[4];
   bool ok;
-  __device__ ColLoaderF32(KPtr f, int mn_base, int mn_valid) : kptr(f) {
+  __device__ ColLoaderF32(KBase f, int klim_, int mn_base, int mn_valid) : kbase(f), klim(klim_) {
     ok = mn_base + (int)(threadIdx.x & 63) * 4 < mn_valid;
   }
   __device__ void load(int kt) {
-    const int k0 = kt * Mma<float>::BK + (int)(threadIdx.x >> 6) * 4;
+    const int k0 = kt * 32 + (int)(threadIdx.x >> 6) * 4;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const char* p = ok ? kptr(k0 + kk) : nullptr;
-      if (p) v[kk] = ld16(p + (threadIdx.x & 63) * 16);
+      if (ok && k0 + kk < klim) v[kk] = ld16(kbase(k0 + kk) + (threadIdx.x & 63) * 16);
       else v[kk] = u32x4{0u, 0u, 0u, 0u};
     }
   }
@@ -178,77 +353,80 @@ struct ColLoaderF32 {
       *reinterpret_cast<u32x4*>(lds + (mn0 + e) * KROW + kq * 16) = o;
     }
   }
+  __device__ static float frag(const char* lds, int row0, int s) { return RowLoaderF32::frag(lds, row0, s); }
 };
 
-// The MN-major operand kind for element type T: loader type and fragment reader.
-template <typename T, class KPtr> struct MNOperand;
-template <class KPtr> struct MNOperand<bf16, KPtr> {
-  typedef TileLoaderMN<KPtr> Loader;
-  __device__ static bf16x8 frag(const char* lds, int mn0, int s) { return MNFrag::read(lds, mn0, s); }
-};
-template <class KPtr> struct MNOperand<float, KPtr> {
-  typedef ColLoaderF32<KPtr> Loader;
-  __device__ static float frag(const char* lds, int mn0, int s) { return KFrag<float>::read(lds, mn0, s); }
-};
-template <typename T> struct KOperand {
-  typedef RowLoader Loader;
-  __device__ static typename Mma<T>::frag frag(const char* lds, int row0, int s) {
-    return KFrag<T>::read(lds, row0, s);
-  }
-};
-
-// ---------------------------------------------------------------------------------------------
-// Main loop.  AOp / BOp provide frag(lds, first_row, kstep); la / lb the loaders.  bsub(j) is the
-// first LDS row (N index) of the wave's j-th B block.  Accumulators acc[i][j]: M block i of the
-// wave's 128 rows, N block j of its two 32-column blocks.
-// ---------------------------------------------------------------------------------------------
-struct WaveAcc {
-  f32x16 c[4][2];
-};
-
-template <typename T, class AOp, class BOp, class LA, class LB, class BSub>
-__device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nkt, WaveAcc& acc, char* lds,
-                                              int wm, BSub bsub) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc.c[i][j][v] = 0.0f;
+template <class LA, class LB, class BSub>
+__device__ __forceinline__ void gemm_mainloop_reg(LA& la, LB& lb, int nkt, WaveAcc& acc, LdsBufs L,
+                                                  int wm, BSub bsub) {
+  zero_acc(acc);
   if (nkt <= 0) return;
   la.load(0);
   lb.load(0);
-  la.store(lds);
-  lb.store(lds + STAGE_BYTES);
+  la.store(L.b[0]);
+  lb.store(L.b[1]);
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
-    const char* As = lds + (kt & 1) * 2 * STAGE_BYTES;
-    const char* Bs = As + STAGE_BYTES;
+    const char* As = (kt & 1) ? L.b[2] : L.b[0];
+    const char* Bs = (kt & 1) ? L.b[3] : L.b[1];
     const bool more = kt + 1 < nkt;
     if (more) {
       la.load(kt + 1);
       lb.load(kt + 1);
     }
 #pragma unroll
-    for (int s = 0; s < Mma<T>::STEPS; ++s) {
-      typename Mma<T>::frag a[4], b[2];
+    for (int s = 0; s < Mma<float>::STEPS; ++s) {
+      float a[4], b[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = BOp::frag(Bs, bsub(j), s);
+      for (int j = 0; j < 2; ++j) b[j] = LB::frag(Bs, bsub(j), s);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = AOp::frag(As, wm * 128 + i * 32, s);
+      for (int i = 0; i < 4; ++i) a[i] = LA::frag(As, wm * 128 + i * 32, s);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc.c[i][j] = Mma<T>::mma(a[i], b[j], acc.c[i][j]);
+        for (int j = 0; j < 2; ++j) acc.c[i][j] = Mma<float>::mma(a[i], b[j], acc.c[i][j]);
     }
     if (more) {
-      char* Ad = lds + ((kt + 1) & 1) * 2 * STAGE_BYTES;
-      la.store(Ad);
-      lb.store(Ad + STAGE_BYTES);
+      la.store((kt & 1) ? L.b[0] : L.b[2]);
+      lb.store((kt & 1) ? L.b[1] : L.b[3]);
     }
     __syncthreads();
   }
 }
+
+// ===============================================================================================
+// Operand builders: one call site per operand kind works for both element types.
+//   k_rows<T>(row_ptr)                  K-major rows (row_ptr(i) -> row start or null)
+//   mn_rows<T>(kbase, klim, mn_base, mn_valid)
+//                                       MN-major rows (kbase(k) -> element (mn_base, k), k < klim)
+// and the main loop dispatch gemm_mainloop<T>(la, lb, nkt, acc, L, wm, bsub).
+// ===============================================================================================
+template <typename T> struct KRowsOf;
+template <> struct KRowsOf<bf16> { typedef KDma type; };
+template <> struct KRowsOf<float> { typedef RowLoaderF32 type; };
+
+template <typename T, class RowPtr>
+__device__ __forceinline__ typename KRowsOf<T>::type k_rows(RowPtr row_ptr) {
+  typename KRowsOf<T>::type l;
+  l.init(row_ptr);
+  return l;
+}
+
+template <typename T, class KBase>
+__device__ __forceinline__ auto mn_rows(KBase kbase, int klim, int mn_base, int mn_valid) {
+  if constexpr (sizeof(T) == 2) return MNDma<KBase>(kbase, klim, mn_base, mn_valid);
+  else return ColLoaderF32<KBase>(kbase, klim, mn_base, mn_valid);
+}
+
+template <typename T, class LA, class LB, class BSub>
+__device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nkt, WaveAcc& acc, LdsBufs L, int wm,
+                                              BSub bsub) {
+  if constexpr (sizeof(T) == 2) gemm_mainloop_dma(la, lb, nkt, acc, L, wm, bsub);
+  else gemm_mainloop_reg(la, lb, nkt, acc, L, wm, bsub);
+}
+
+// K stages for a K extent of `k` elements.
+template <typename T> __host__ __device__ constexpr int stage_k() { return Mma<T>::BK; }
 
 // Tile row of accumulator register v for M block i of wave row wm.
 __device__ __forceinline__ int acc_row(int wm, int i, int v) {
@@ -257,15 +435,21 @@ __device__ __forceinline__ int acc_row(int wm, int i, int v) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Epilogue through LDS for 2-byte outputs: the wave writes val(i, j, v) at (acc_row, col(j)) of a
-// [256][ncols] bf16 staging tile, then the block stores rows < mrows and columns < ncols_valid
-// with 16-byte writes: out + r * ld (elements) + c.  Requires the LDS to be free (after the
-// main loop) and ncols <= 256.
+// Epilogue through LDS for 2-byte outputs.  Tile row r lives in buffer r / 64 at row r % 64 of a
+// [64][256 bf16 + 16 B] staging array.  epi_stage_bf16 writes val(i, j, v) at (acc_row, col(j))
+// (col < 0 skips), epi_store_bf16 stores rows < mrows and columns < ncols_valid with 16-byte
+// writes through row_ptr(r) (null skips).  Requires the LDS to be free.
 // ---------------------------------------------------------------------------------------------
 constexpr int EPI_ROW = 256 * 2 + 16;
+static_assert(64 * EPI_ROW <= LDS_BUF, "staging rows per buffer");
+
+__device__ __forceinline__ char* epi_buf(LdsBufs L, int r) {
+  return r < 128 ? (r < 64 ? L.b[0] : L.b[1]) : (r < 192 ? L.b[2] : L.b[3]);
+}
+__device__ __forceinline__ char* epi_row(LdsBufs L, int r) { return epi_buf(L, r) + (r & 63) * EPI_ROW; }
 
 template <class Col, class Val>
-__device__ __forceinline__ void epi_stage_bf16(char* lds, const WaveAcc& acc, int wm, Col col, Val val) {
+__device__ __forceinline__ void epi_stage_bf16(LdsBufs L, int wm, Col col, Val val) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int c = col(j);
@@ -274,18 +458,25 @@ __device__ __forceinline__ void epi_stage_bf16(char* lds, const WaveAcc& acc, in
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v)
-        *reinterpret_cast<bf16*>(lds + acc_row(wm, i, v) * EPI_ROW + c * 2) = (bf16)val(i, j, v);
+        *reinterpret_cast<bf16*>(epi_row(L, acc_row(wm, i, v)) + c * 2) = (bf16)val(i, j, v);
   }
 }
 
-__device__ __forceinline__ void epi_store_bf16(const char* lds, bf16* out, int64_t ld, int mrows,
-                                               int ncols, int ncols_valid) {
+template <class RowPtr>
+__device__ __forceinline__ void epi_store_rows(LdsBufs L, int col0, RowPtr row_ptr, int mrows, int ncols,
+                                               int ncols_valid) {
   const int cpr = ncols / 8;  // 16-byte chunks per row
   for (int c = threadIdx.x; c < 256 * cpr; c += GEMM_THREADS) {
     const int r = c / cpr, ch = c % cpr;
-    if (r < mrows && ch * 8 < ncols_valid)
-      st16(out + (int64_t)r * ld + ch * 8, *reinterpret_cast<const u32x4*>(lds + r * EPI_ROW + ch * 16));
+    if (r >= mrows || ch * 8 >= ncols_valid) continue;
+    bf16* p = row_ptr(r);
+    if (p) st16(p + ch * 8, *reinterpret_cast<const u32x4*>(epi_row(L, r) + col0 * 2 + ch * 16));
   }
+}
+
+__device__ __forceinline__ void epi_store_bf16(LdsBufs L, int col0, bf16* out, int64_t ld, int mrows,
+                                               int ncols, int ncols_valid) {
+  epi_store_rows(L, col0, [&](int r) { return out + (int64_t)r * ld; }, mrows, ncols, ncols_valid);
 }
 
 // Grouped M tiles: tile mt of the concatenation of the experts' ceil(rows / BM) tiles.
@@ -307,5 +498,13 @@ __device__ __forceinline__ bool find_group_tile(int mt, const int32_t* __restric
   g.mrows = min(BM, expert_off[lo + 1] - g.m0);
   return true;
 }
+
+// The four LDS buffers of a GEMM workgroup.
+#define MOE_GEMM_LDS(L)                                              \
+  __shared__ __attribute__((aligned(1024))) char L##_0[LDS_BUF];     \
+  __shared__ __attribute__((aligned(1024))) char L##_1[LDS_BUF];     \
+  __shared__ __attribute__((aligned(1024))) char L##_2[LDS_BUF];     \
+  __shared__ __attribute__((aligned(1024))) char L##_3[LDS_BUF];     \
+  const LdsBufs L{{L##_0, L##_1, L##_2, L##_3}}
 
 }  // namespace moe

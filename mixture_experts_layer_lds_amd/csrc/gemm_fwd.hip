@@ -52,7 +52,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_router(const T* __restrict_
                                                            const float* __restrict__ bias,
                                                            float* __restrict__ logits, int T_, int d,
                                                            int E, int NT) {
-  __shared__ __attribute__((aligned(16))) char lds[GEMM_LDS];
+  MOE_GEMM_LDS(L);
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int mt = lin / NT, nt = lin % NT;
   const int m0 = mt * BM, n0 = nt * BN;
@@ -60,16 +60,14 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_router(const T* __restrict_
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave >> 2, wn = wave & 3;
   const int64_t rowb = (int64_t)d * sizeof(T);
-  RowLoader la, lb;
-  la.init([&](int i) -> const char* {
+  auto la = k_rows<T>([&](int i) -> const char* {
     return m0 + i < T_ ? reinterpret_cast<const char*>(X) + (m0 + i) * rowb : nullptr;
   });
-  lb.init([&](int i) -> const char* {
+  auto lb = k_rows<T>([&](int i) -> const char* {
     return n0 + i < E ? reinterpret_cast<const char*>(Wr) + (n0 + i) * rowb : nullptr;
   });
   WaveAcc acc;
-  gemm_mainloop<T, KOperand<T>, KOperand<T>>(la, lb, (int)(rowb / KB), acc, lds, wm,
-                                             [&](int j) { return wn * 64 + j * 32; });
+  gemm_mainloop<T>(la, lb, d / Mma<T>::BK, acc, L, wm, [&](int j) { return wn * 64 + j * 32; });
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int n = n0 + wn * 64 + j * 32 + (lane & 31);
@@ -110,8 +108,8 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_up(
     const int32_t* __restrict__ mtile_off, const int32_t* __restrict__ expert_off,
     const int32_t* __restrict__ row_token, const T* __restrict__ A_in, int gathered,
     const T* __restrict__ Wg, const T* __restrict__ Wu, T* __restrict__ act, T* __restrict__ H,
-    int d, int n, int E, int NT) {
-  __shared__ __attribute__((aligned(16))) char lds[GEMM_LDS];
+    int d, int n, int E, int NT, int T_) {
+  MOE_GEMM_LDS(L);
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int mt = lin / NT, nt = lin % NT;
   GroupTile g;
@@ -120,22 +118,20 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_up(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave >> 2, wn = wave & 3;
   const int64_t rowb = (int64_t)d * sizeof(T);
-  RowLoader la, lb;
-  la.init([&](int i) -> const char* {
+  auto la = k_rows<T>([&](int i) -> const char* {
     if (i >= g.mrows) return nullptr;
-    const int64_t src = gathered ? row_token[g.m0 + i] : (int64_t)(g.m0 + i);
+    const int64_t src = gathered ? clamp_idx(row_token[g.m0 + i], T_) : (int64_t)(g.m0 + i);
     return reinterpret_cast<const char*>(A_in) + src * rowb;
   });
   const char* wg = reinterpret_cast<const char*>(Wg) + (int64_t)g.e * n * rowb;
   const char* wu = reinterpret_cast<const char*>(Wu) + (int64_t)g.e * n * rowb;
-  lb.init([&](int i) -> const char* {
+  auto lb = k_rows<T>([&](int i) -> const char* {
     const int j = j0 + (i & 127);
     if (j >= n) return nullptr;
     return (i < 128 ? wg : wu) + (int64_t)j * rowb;
   });
   WaveAcc acc;
-  gemm_mainloop<T, KOperand<T>, KOperand<T>>(la, lb, (int)(rowb / KB), acc, lds, wm,
-                                             [&](int j) { return j * 128 + wn * 32; });
+  gemm_mainloop<T>(la, lb, d / Mma<T>::BK, acc, L, wm, [&](int j) { return j * 128 + wn * 32; });
   const int ccol = wn * 32 + (lane & 31);  // act column within the tile
   const int valid = min(128, n - j0);
   if constexpr (sizeof(T) == 2) {
@@ -144,19 +140,18 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_up(
       return gv * sigmoid_f32(gv) * uv;
     };
     auto colf = [&](int j) { return j == 0 ? ccol : -1; };
-    epi_stage_bf16(lds, acc, wm, colf, silu_u);
+    epi_stage_bf16(L, wm, colf, silu_u);
     __syncthreads();
-    epi_store_bf16(lds, reinterpret_cast<bf16*>(act) + (int64_t)g.m0 * n + j0, n, g.mrows, 128, valid);
+    epi_store_bf16(L, 0, reinterpret_cast<bf16*>(act) + (int64_t)g.m0 * n + j0, n, g.mrows, 128, valid);
     if (H) {
       // G and U halves side by side in one staging tile: columns [0,128) G, [128,256) U
       __syncthreads();
       auto both = [&](int j) { return j * 128 + ccol; };
-      epi_stage_bf16(lds, acc, wm, both, [&](int i, int j, int v) { return acc.c[i][j][v]; });
+      epi_stage_bf16(L, wm, both, [&](int i, int j, int v) { return acc.c[i][j][v]; });
       __syncthreads();
       bf16* hb = reinterpret_cast<bf16*>(H) + (int64_t)g.m0 * 2 * n;
-      epi_store_bf16(lds, hb + j0, 2 * n, g.mrows, 128, valid);
-      // the U half: shift the staging base by 128 columns
-      epi_store_bf16(lds + 256, hb + n + j0, 2 * n, g.mrows, 128, valid);
+      epi_store_bf16(L, 0, hb + j0, 2 * n, g.mrows, 128, valid);
+      epi_store_bf16(L, 128, hb + n + j0, 2 * n, g.mrows, 128, valid);
     }
   } else {
     if (ccol < valid) {
@@ -187,11 +182,11 @@ hipError_t launch_up_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mtil
   if (s.bf16)
     k_up<bf16><<<grid, GEMM_THREADS, 0, st>>>(mtile_off, p.expert_off, p.row_token, (const bf16*)A_in,
                                                      gathered, (const bf16*)W_gate, (const bf16*)W_up,
-                                                     (bf16*)act, (bf16*)H, (int)s.d, (int)s.n, s.E, NT);
+                                                     (bf16*)act, (bf16*)H, (int)s.d, (int)s.n, s.E, NT, (int)s.T);
   else
     k_up<float><<<grid, GEMM_THREADS, 0, st>>>(mtile_off, p.expert_off, p.row_token, (const float*)A_in,
                                                       gathered, (const float*)W_gate, (const float*)W_up,
-                                                      (float*)act, (float*)H, (int)s.d, (int)s.n, s.E, NT);
+                                                      (float*)act, (float*)H, (int)s.d, (int)s.n, s.E, NT, (int)s.T);
   return hipGetLastError();
 }
 
@@ -203,7 +198,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_down(
     const int32_t* __restrict__ mtile_off, const int32_t* __restrict__ expert_off,
     const T* __restrict__ act, const T* __restrict__ Wd, T* __restrict__ Y, int d, int n, int E,
     int NT) {
-  __shared__ __attribute__((aligned(16))) char lds[GEMM_LDS];
+  MOE_GEMM_LDS(L);
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int mt = lin / NT, nt = lin % NT;
   GroupTile g;
@@ -212,21 +207,19 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_down(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave >> 2, wn = wave & 3;
   const int64_t rowb = (int64_t)n * sizeof(T);
-  RowLoader la, lb;
-  la.init([&](int i) -> const char* {
+  auto la = k_rows<T>([&](int i) -> const char* {
     return i < g.mrows ? reinterpret_cast<const char*>(act) + (int64_t)(g.m0 + i) * rowb : nullptr;
   });
   const char* wd = reinterpret_cast<const char*>(Wd) + (int64_t)g.e * d * rowb;
-  lb.init([&](int i) -> const char* { return n0 + i < d ? wd + (int64_t)(n0 + i) * rowb : nullptr; });
+  auto lb = k_rows<T>([&](int i) -> const char* { return n0 + i < d ? wd + (int64_t)(n0 + i) * rowb : nullptr; });
   WaveAcc acc;
-  gemm_mainloop<T, KOperand<T>, KOperand<T>>(la, lb, (int)(rowb / KB), acc, lds, wm,
-                                             [&](int j) { return wn * 64 + j * 32; });
+  gemm_mainloop<T>(la, lb, n / Mma<T>::BK, acc, L, wm, [&](int j) { return wn * 64 + j * 32; });
   const int valid = min(BN, d - n0);
   if constexpr (sizeof(T) == 2) {
-    epi_stage_bf16(lds, acc, wm, [&](int j) { return wn * 64 + j * 32 + (lane & 31); },
+    epi_stage_bf16(L, wm, [&](int j) { return wn * 64 + j * 32 + (lane & 31); },
                    [&](int i, int j, int v) { return acc.c[i][j][v]; });
     __syncthreads();
-    epi_store_bf16(lds, reinterpret_cast<bf16*>(Y) + (int64_t)g.m0 * d + n0, d, g.mrows, BN, valid);
+    epi_store_bf16(L, 0, reinterpret_cast<bf16*>(Y) + (int64_t)g.m0 * d + n0, d, g.mrows, BN, valid);
   } else {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {

@@ -13,11 +13,22 @@ namespace moe {
 
 // ---------------------------------------------------------------------------------------------
 // top-K: one wave per token.  Lane i holds logits e = i + 64 j.  K rounds of a wave arg-max
-// under the order (logit descending, expert id ascending); -0.0 and +0.0 compare equal because
-// the comparisons are floating-point comparisons.  Then the softmax over the K winners.  The
-// winners set their bit in the block's LDS bitmap (bitwise OR is order independent).
+// under the order (logit descending, expert id ascending), compared on order_key; then the
+// softmax over the K winners.  The winners set their bit in the block's LDS bitmap (bitwise OR
+// is order independent).
 // ---------------------------------------------------------------------------------------------
 constexpr int TOPK_TOKENS_PER_BLOCK = 64;  // two 32-bit bitmap words per expert per block
+
+// Order-preserving integer key of an fp32 logit: a > b as floats <=> key(a) > key(b), -0.0 and
+// +0.0 share a key, and NaN takes the smallest key (it ranks below every number).  Selecting on
+// keys makes every comparison a total order, so all 64 lanes of a wave agree on each winner
+// even for NaN inputs (float comparisons with NaN are not an order, and lanes could then pick
+// the same expert twice).
+__device__ __forceinline__ uint32_t order_key(float x) {
+  if (x != x) return 0u;
+  const uint32_t u = __float_as_uint(x == 0.0f ? 0.0f : x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
 
 template <int EPL>
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int K,
@@ -33,30 +44,34 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
     if (t >= T) break;
     const float* row = logits + (int64_t)t * E;
     float v[EPL];
+    uint32_t key[EPL];
     bool live[EPL];
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
       const int e = lane + 64 * j;
       live[j] = e < E;
       v[j] = live[j] ? row[e] : 0.0f;
+      key[j] = order_key(v[j]);
     }
     float my_v = 0.0f;
     int my_e = 0;
     for (int k = 0; k < K; ++k) {
       // lane-local best among live slots (ties: lower id = lower j)
+      uint32_t bk = 0u;
       float bv = 0.0f;
       int be = 0x7fffffff;
 #pragma unroll
       for (int j = 0; j < EPL; ++j)
-        if (live[j] && (be == 0x7fffffff || v[j] > bv)) { bv = v[j]; be = lane + 64 * j; }
+        if (live[j] && (be == 0x7fffffff || key[j] > bk)) { bk = key[j]; bv = v[j]; be = lane + 64 * j; }
       // wave arg-max; empty lanes carry id INT_MAX and never beat a live candidate
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t ok = __shfl_xor(bk, o, 64);
         const float ov = __shfl_xor(bv, o, 64);
         const int oe = __shfl_xor(be, o, 64);
         const bool take = (oe != 0x7fffffff) &&
-                          (be == 0x7fffffff || ov > bv || (ov == bv && oe < be));
-        if (take) { bv = ov; be = oe; }
+                          (be == 0x7fffffff || ok > bk || (ok == bk && oe < be));
+        if (take) { bk = ok; bv = ov; be = oe; }
       }
 #pragma unroll
       for (int j = 0; j < EPL; ++j)
@@ -131,7 +146,7 @@ __global__ __launch_bounds__(256) void k_count(const uint32_t* __restrict__ bits
 // Key of token t for expert e, larger = chosen first:
 //   adding  (best non-members): (ord(L[t,e]) << 32) | ~t      -> larger logit, then lower t
 //   dropping (worst members):   (~ord(L[t,e]) << 32) | t      -> smaller logit, then higher t
-// ord() maps fp32 to an order-preserving uint32 (with -0.0 folded onto +0.0).  Keys are unique
+// ord() is order_key (-0.0 folded onto +0.0, NaN lowest).  Keys are unique
 // (t is), so the set of the `amount` largest keys is unique; it is found by an 8-pass radix
 // select (8-bit digits, LDS histograms with integer atomics), and the bitmap row is rewritten.
 // The expert's logit column is cached in LDS when T <= TR_LDS_TOKENS.
@@ -139,10 +154,6 @@ __global__ __launch_bounds__(256) void k_count(const uint32_t* __restrict__ bits
 constexpr int TR_THREADS = 1024;
 constexpr int TR_LDS_TOKENS = 32768;
 
-__device__ __forceinline__ uint32_t ord_f32(float x) {
-  uint32_t u = __float_as_uint(x == 0.0f ? 0.0f : x);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
 
 __global__ __launch_bounds__(TR_THREADS) void k_token_round(const float* __restrict__ logits, int T,
                                                            int E, int W, int M, int mode,
@@ -165,13 +176,13 @@ __global__ __launch_bounds__(TR_THREADS) void k_token_round(const float* __restr
   const bool cached = T <= TR_LDS_TOKENS;
   uint32_t* brow = bits + (int64_t)e * W;
   if (cached) {
-    for (int t = threadIdx.x; t < T; t += TR_THREADS) s_ord[t] = ord_f32(logits[(int64_t)t * E + e]);
+    for (int t = threadIdx.x; t < T; t += TR_THREADS) s_ord[t] = order_key(logits[(int64_t)t * E + e]);
     __syncthreads();
   }
   auto key_of = [&](int t, bool& cand) -> uint64_t {
     const bool mem = (brow[t >> 5] >> (t & 31)) & 1u;
     cand = add ? !mem : mem;
-    const uint32_t o = cached ? s_ord[t] : ord_f32(logits[(int64_t)t * E + e]);
+    const uint32_t o = cached ? s_ord[t] : order_key(logits[(int64_t)t * E + e]);
     return add ? (((uint64_t)o << 32) | (uint32_t)(~(uint32_t)t))
                : (((uint64_t)(~o) << 32) | (uint32_t)t);
   };

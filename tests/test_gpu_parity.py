@@ -162,3 +162,29 @@ def test_permute_packed_ffn_and_combine():
     assert_close("out", f64(out_w), fw["out"], TOL["bf16"])
     assert_close("Y_perm", f64(Yg[:R]), fw["Y_perm"], TOL["bf16"])
     assert_close("unit combine", f64(out_u), cfg.K * f64(inp["X"]), TOL["bf16"])
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_route_nan_and_inf_logits(mode):
+    """Non-finite logits still give K distinct experts per token and a valid permutation, with the
+    same selection as the oracle (NaN ranks below every number, ties to the lower expert id)."""
+    T, E, K = 500, 70, 6
+    g = torch.Generator().manual_seed(7 + mode)
+    L = torch.randn(T, E, generator=g)
+    L[torch.rand(T, E, generator=g) < 0.2] = float("nan")
+    L[torch.rand(T, E, generator=g) < 0.05] = float("inf")
+    L[torch.rand(T, E, generator=g) < 0.05] = float("-inf")
+    L[3, :] = float("nan")
+    dims = B.make_dims(T, 64, 64, E, K, "f32", mode, 16)
+    plan = B.Plan(dims)
+    ws, nb = B.workspace(dims, B.OP_ROUTE)
+    B.moe_route(dims, None, None, None, L.cuda(), plan, ws, nb)
+    torch.cuda.synchronize()
+    got = plan.to_host()
+    ref = oracle.build_plan(L.double().numpy(), K, round_mode=mode, tile_m=16)
+    for k in ("counts", "expert_off", "row_token", "tok_off", "tok_row"):
+        assert np.array_equal(got[k], ref[k]), k
+    assert np.array_equal(got["topk_idx"].reshape(T, K), ref["topk_idx"])
+    idx = got["topk_idx"].reshape(T, K)
+    assert all(len(set(r.tolist())) == K for r in idx)
+    assert sorted(got["tok_row"].tolist()) == list(range(got["R"]))
