@@ -16,8 +16,8 @@ static inline int grid8(int64_t n) { return (int)((n + 7) / 8 * 8); }
 
 // ---------------------------------------------------------------------------------------------
 // dAct: dA'[r][j] = sum_c dY[t_r][c] W_down[e][c][j]  (M = rows of e, N = n, K = d).
-// Wave column wn owns columns j*128 + wn*32 + (lane % 32), j = 0, 1, so that each half of the
-// 256-column tile is contiguous for the staged stores.
+// Wave column wn owns columns (j/2)*128 + wn*64 + (j%2)*32 + (lane % 32), j = 0..3, so that
+// each 128-column half of the tile holds two of its blocks and can be finished on its own.
 // Epilogue per (r, j), with G, U read from H and w = row_w[r]:
 //   A = silu(G) U;  dS partial += dA' A;  dA = w dA'
 //   dG = dA U sigmoid(G) (1 + G (1 - sigmoid(G)));  dU = dA silu(G)
@@ -34,12 +34,12 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dact(
     int n, int E, int NT, int T_) {
   MOE_GEMM_LDS(L);
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int mt = lin / NT, nt = lin % NT;
   GroupTile g;
-  if (!find_group_tile(mt, mtile_off, expert_off, E, g)) return;
+  if (!find_group_tile(lin, NT, mtile_off, expert_off, E, g)) return;
+  const int nt = g.nt;
   const int n0 = nt * BN;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave >> 1, wn = wave & 1;
   const int64_t rowb = (int64_t)d * sizeof(T);
   auto la = k_rows<T>([&](int i) -> const char* {
     return i < g.mrows ? reinterpret_cast<const char*>(dY) + (int64_t)clamp_idx(row_token[g.m0 + i], T_) * rowb
@@ -48,7 +48,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dact(
   const char* wd = reinterpret_cast<const char*>(Wd) + ((int64_t)g.e * d * n + n0) * sizeof(T);
   auto lb = mn_rows<T>([=](int k) { return wd + (int64_t)k * n * sizeof(T); }, d, n0, n);
   WaveAcc acc;
-  gemm_mainloop<T>(la, lb, d / Mma<T>::BK, acc, L, wm, [&](int j) { return j * 128 + wn * 32; });
+  gemm_mainloop<T>(la, lb, d / Mma<T>::BK, acc, L, wm, [&](int j) { return bsub_halved(wn, j); });
   // Epilogue, one 128-column half of the tile at a time: the wave dumps its fp32 accumulators
   // into an LDS tile [256][128], then the block walks the half row by row in 16-byte chunks
   // (coalesced loads of G, U and coalesced stores of dG, dU, w A), and the 16 or 32 lanes that
@@ -60,12 +60,16 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dact(
   float* red = reinterpret_cast<float*>(L.b[0] + 64 * FROW);  // [256] dS partials of this tile
   auto frow = [&](int r) { return epi_buf(L, r) + (r & 63) * FROW; };
   const int valid = min(BN, n - n0);
+#pragma unroll
   for (int half = 0; half < 2; ++half) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        *reinterpret_cast<float*>(frow(acc_row(wm, i, v)) + (wn * 32 + (lane & 31)) * 4) = acc.c[i][half][v];
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          *reinterpret_cast<float*>(frow(acc_row(wm, i, v)) + (wn * 64 + jj * 32 + (lane & 31)) * 4) =
+              acc.c[i][2 * half + jj][v];
     __syncthreads();
     for (int c = threadIdx.x; c < 256 * CPR; c += GEMM_THREADS) {
       const int row = c / CPR, ch = c % CPR;
@@ -135,12 +139,12 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dx(
     T* __restrict__ dXp, int d, int n, int E, int NT) {
   MOE_GEMM_LDS(L);
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int mt = lin / NT, nt = lin % NT;
   GroupTile g;
-  if (!find_group_tile(mt, mtile_off, expert_off, E, g)) return;
+  if (!find_group_tile(lin, NT, mtile_off, expert_off, E, g)) return;
+  const int nt = g.nt;
   const int n0 = nt * BN;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave >> 1, wn = wave & 1;
   const int64_t rowb = (int64_t)2 * n * sizeof(T);
   auto la = k_rows<T>([&](int i) -> const char* {
     return i < g.mrows ? reinterpret_cast<const char*>(dH) + (int64_t)(g.m0 + i) * rowb : nullptr;
@@ -151,17 +155,17 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dx(
   auto lb = mn_rows<T>([=](int k) { return k < n ? wg + (int64_t)k * wrow : wu + (int64_t)(k - n) * wrow; },
                        2 * n, n0, d);
   WaveAcc acc;
-  gemm_mainloop<T>(la, lb, 2 * n / Mma<T>::BK, acc, L, wm, [&](int j) { return wn * 64 + j * 32; });
+  gemm_mainloop<T>(la, lb, 2 * n / Mma<T>::BK, acc, L, wm, [&](int j) { return bsub_plain(wn, j); });
   const int valid = min(BN, d - n0);
   if constexpr (sizeof(T) == 2) {
-    epi_stage_bf16(L, wm, [&](int j) { return wn * 64 + j * 32 + (lane & 31); },
+    epi_stage_bf16(L, wm, [&](int j) { return bsub_plain(wn, j) + (lane & 31); },
                    [&](int i, int j, int v) { return acc.c[i][j][v]; });
     __syncthreads();
     epi_store_bf16(L, 0, reinterpret_cast<bf16*>(dXp) + (int64_t)g.m0 * d + n0, d, g.mrows, BN, valid);
   } else {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int c = wn * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < 4; ++j) {
+      const int c = bsub_plain(wn, j) + (lane & 31);
       if (c >= valid) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -211,7 +215,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dw_down(
   const int rem = lin % per;
   const int m0 = (rem / NT) * BM, n0 = (rem % NT) * BN;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave >> 1, wn = wave & 1;
   const int off = expert_off[e];
   const int cnt = expert_off[e + 1] - off;
   const char* dyb = reinterpret_cast<const char*>(dY) + m0 * sizeof(T);
@@ -221,18 +225,18 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dw_down(
   }, cnt, m0, d);
   auto lb = mn_rows<T>([=](int k) { return wab + (int64_t)(off + k) * n * sizeof(T); }, cnt, n0, n);
   WaveAcc acc;
-  gemm_mainloop<T>(la, lb, (int)cdiv(cnt, Mma<T>::BK), acc, L, wm, [&](int j) { return wn * 64 + j * 32; });
+  gemm_mainloop<T>(la, lb, (int)cdiv(cnt, Mma<T>::BK), acc, L, wm, [&](int j) { return bsub_plain(wn, j); });
   T* out = dWd + (int64_t)e * d * n;
   const int mrows = min(BM, d - m0), valid = min(BN, n - n0);
   if constexpr (sizeof(T) == 2) {
-    epi_stage_bf16(L, wm, [&](int j) { return wn * 64 + j * 32 + (lane & 31); },
+    epi_stage_bf16(L, wm, [&](int j) { return bsub_plain(wn, j) + (lane & 31); },
                    [&](int i, int j, int v) { return acc.c[i][j][v]; });
     __syncthreads();
     epi_store_bf16(L, 0, reinterpret_cast<bf16*>(out) + (int64_t)m0 * n + n0, n, mrows, BN, valid);
   } else {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int c = wn * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < 4; ++j) {
+      const int c = bsub_plain(wn, j) + (lane & 31);
       if (c >= valid) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -273,7 +277,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dw_gu(
   const int rem = lin % per;
   const int m0 = (rem / NT) * BM, n0 = (rem % NT) * BN;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave >> 1, wn = wave & 1;
   const int off = expert_off[e];
   const int cnt = expert_off[e + 1] - off;
   const char* dhb = reinterpret_cast<const char*>(dH) + m0 * sizeof(T);
@@ -283,21 +287,21 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dw_gu(
     return xb + (int64_t)clamp_idx(sload_i32(row_token + off, k), T_) * d * sizeof(T);
   }, cnt, n0, d);
   WaveAcc acc;
-  gemm_mainloop<T>(la, lb, (int)cdiv(cnt, Mma<T>::BK), acc, L, wm, [&](int j) { return wn * 64 + j * 32; });
+  gemm_mainloop<T>(la, lb, (int)cdiv(cnt, Mma<T>::BK), acc, L, wm, [&](int j) { return bsub_plain(wn, j); });
   const int mrows = min(BM, 2 * n - m0), valid = min(BN, d - n0);
   auto row_ptr = [&](int r) -> T* {
     const int m = m0 + r;
     return (m < n ? dWg + ((int64_t)e * n + m) * d : dWu + ((int64_t)e * n + (m - n)) * d) + n0;
   };
   if constexpr (sizeof(T) == 2) {
-    epi_stage_bf16(L, wm, [&](int j) { return wn * 64 + j * 32 + (lane & 31); },
+    epi_stage_bf16(L, wm, [&](int j) { return bsub_plain(wn, j) + (lane & 31); },
                    [&](int i, int j, int v) { return acc.c[i][j][v]; });
     __syncthreads();
     epi_store_rows(L, 0, [&](int r) { return reinterpret_cast<bf16*>(row_ptr(r)); }, mrows, BN, valid);
   } else {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int c = wn * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < 4; ++j) {
+      const int c = bsub_plain(wn, j) + (lane & 31);
       if (c >= valid) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -492,7 +496,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dwr(
   const int rem = lin % per;
   const int m0 = (rem / NT) * BM, n0 = (rem % NT) * BN;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave >> 1, wn = wave & 1;
   const int t0 = sl * TS;
   const int klen = min(TS, T_ - t0);
   const char* ab = reinterpret_cast<const char*>(dLop) + m0 * sizeof(T);
@@ -500,10 +504,10 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dwr(
   auto la = mn_rows<T>([=](int k) { return ab + (int64_t)(t0 + k) * E_pad * sizeof(T); }, klen, m0, E_pad);
   auto lb = mn_rows<T>([=](int k) { return xb + (int64_t)(t0 + k) * d * sizeof(T); }, klen, n0, d);
   WaveAcc acc;
-  gemm_mainloop<T>(la, lb, (int)cdiv(klen, Mma<T>::BK), acc, L, wm, [&](int j) { return wn * 64 + j * 32; });
+  gemm_mainloop<T>(la, lb, (int)cdiv(klen, Mma<T>::BK), acc, L, wm, [&](int j) { return bsub_plain(wn, j); });
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int c = n0 + wn * 64 + j * 32 + (lane & 31);
+  for (int j = 0; j < 4; ++j) {
+    const int c = n0 + bsub_plain(wn, j) + (lane & 31);
     if (c >= d) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i)

@@ -1,8 +1,10 @@
 // MFMA GEMM engine for gfx950, shared by every expert and router GEMM of the layer.
 //
 // C[m][n] = sum_k A(m,k) B(k,n), fp32 accumulation in MFMA accumulators.
-//   * workgroup = 512 threads = 8 waves in a 2 (M) x 4 (N) grid; block tile 256 x 256;
-//   * each wave owns 128 x 64 = 4 x 2 MFMA 32x32 blocks
+//   * workgroup = 256 threads = 4 waves in a 2 (M) x 2 (N) grid; block tile 256 x 256;
+//   * each wave owns 128 x 128 = 4 x 4 MFMA 32x32 blocks (the accumulators live in AGPRs); per
+//     MFMA k-step a wave reads 8 fragments for 16 MFMAs, which keeps the LDS traffic of fragment
+//     reads plus DMA writes within the LDS bandwidth at full MFMA rate
 //     (bf16: v_mfma_f32_32x32x16_bf16; fp32: v_mfma_f32_32x32x2_f32);
 //   * LDS = four 36 KiB buffers.
 //
@@ -23,8 +25,8 @@
 //     gfx950): lane i points at k-row i/4, column 4 (i%4), so lane j receives 4 consecutive k of
 //     column j; two such loads make the 8 k-values of an MFMA fragment.
 //   Invalid rows / columns are loaded from a zero page, so padding contributes zeros.
-//   Waits: each thread issues 4 DMA instructions per stage, in order; before a stage is read it
-//   waits until at most 4 * (stages issued after it) are outstanding, then a plain s_barrier (no
+//   Waits: each thread issues 8 DMA instructions per stage, in order; before a stage is read it
+//   waits until at most 8 * (stages issued after it) are outstanding, then a plain s_barrier (no
 //   fence) publishes every wave's DMA writes.  Each ring slot is its own __shared__ array and the
 //   loop is unrolled by the ring depth, so the compiler can tell that reading one slot does not
 //   conflict with the DMAs still in flight into the others.  Fragment reads are double-buffered
@@ -44,7 +46,7 @@ namespace moe {
 
 constexpr int BM = 256;
 constexpr int BN = 256;
-constexpr int GEMM_THREADS = 512;
+constexpr int GEMM_THREADS = 256;
 constexpr int LDS_BUF = 36864;              // bytes per LDS buffer (four per workgroup)
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -90,14 +92,14 @@ template <> struct Mma<float> {
 };
 
 struct WaveAcc {
-  f32x16 c[4][2];
+  f32x16 c[4][4];
 };
 
 __device__ __forceinline__ void zero_acc(WaveAcc& acc) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc.c[i][j][v] = 0.0f;
 }
@@ -107,11 +109,11 @@ __device__ __forceinline__ void zero_acc(WaveAcc& acc) {
 // ===============================================================================================
 constexpr int DMA_B_OFF = 16384;            // B tile offset inside a ring slot (A tile at 0)
 
-// s_waitcnt with only vmcnt <= n (n < 16).
+// s_waitcnt with only vmcnt <= N (vmcnt is 6 bits: low 4 in [3:0], high 2 in [15:14]).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 __device__ __forceinline__ void dma16(const void* g, char* lds_uniform) {
@@ -119,18 +121,18 @@ __device__ __forceinline__ void dma16(const void* g, char* lds_uniform) {
 }
 
 // K-major operand: tile row i of the stage <- 64 bytes of row_ptr(i) at K offset 64 s.  Wave w
-// instruction q fills rows R0 = (8 q + w) * 16 .. R0 + 15; lane l takes row R0 + l/4 and the
+// instruction q fills rows R0 = (4 q + w) * 16 .. R0 + 15; lane l takes row R0 + l/4 and the
 // chunk that lands in its slot: (l & 3) ^ (l >> 4).  row_ptr returns null for an invalid row.
 struct KDma {
-  const char* g[2];
-  int step[2];
+  const char* g[4];
+  int step[4];
   template <class RowPtr>
   __device__ void init(RowPtr row_ptr) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int chunk = (lane & 3) ^ (lane >> 4);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const char* p = row_ptr((8 * q + w) * 16 + (lane >> 2));
+    for (int q = 0; q < 4; ++q) {
+      const char* p = row_ptr((4 * q + w) * 16 + (lane >> 2));
       g[q] = p ? p + chunk * 16 : g_zero_page + chunk * 16;
       step[q] = p ? 64 : 0;
     }
@@ -138,7 +140,7 @@ struct KDma {
   __device__ void issue(int s, char* dst) const {
     const int w = threadIdx.x >> 6;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) dma16(g[q] + (int64_t)s * step[q], dst + (8 * q + w) * 1024);
+    for (int q = 0; q < 4; ++q) dma16(g[q] + (int64_t)s * step[q], dst + (4 * q + w) * 1024);
   }
   __device__ static bf16x8 frag(const char* t, int row0, int s) {
     const int lane = threadIdx.x & 63;
@@ -151,19 +153,19 @@ struct KDma {
 // MN-major operand: stage k-rows 32 s .. 32 s + 31.  kbase(k) returns the global address of
 // element (mn_base, k) for 0 <= k < klim; it is only ever called with k clamped into that range
 // (so a gathered row index is always read in bounds), and rows k >= klim load zeros.  Wave w
-// instruction q fills k-rows K0 = (8 q + w) * 2 and K0 + 1: lanes 0-31 the first, 32-63 the
+// instruction q fills k-rows K0 = (4 q + w) * 2 and K0 + 1: lanes 0-31 the first, 32-63 the
 // second; lane slot l % 32 holds chunk (l % 32) ^ (4 (k & 3)).  The address math is branch-free.
 template <class KBase>
 struct MNDma {
   KBase kbase;
   int klim;
-  int chunk[2];
-  bool mn_ok[2];
+  int chunk[4];
+  bool mn_ok[4];
   __device__ MNDma(KBase f, int klim_, int mn_base, int mn_valid) : kbase(f), klim(klim_) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int k = (8 * q + w) * 2 + (lane >> 5);
+    for (int q = 0; q < 4; ++q) {
+      const int k = (4 * q + w) * 2 + (lane >> 5);
       chunk[q] = (lane & 31) ^ (4 * (k & 3));
       mn_ok[q] = mn_base + chunk[q] * 8 < mn_valid;
     }
@@ -171,9 +173,9 @@ struct MNDma {
   __device__ void issue(int s, char* dst) const {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < 4; ++q) {
       const int lim = __builtin_amdgcn_readfirstlane(klim);
-      const int k0 = __builtin_amdgcn_readfirstlane(s * 32 + (8 * q + w) * 2);
+      const int k0 = __builtin_amdgcn_readfirstlane(s * 32 + (4 * q + w) * 2);
       const int c0 = __builtin_amdgcn_readfirstlane(min(k0, lim - 1));
       const int c1 = __builtin_amdgcn_readfirstlane(min(k0 + 1, lim - 1));
       const uint64_t p0 = reinterpret_cast<uint64_t>(kbase(c0));
@@ -183,7 +185,7 @@ struct MNDma {
       const uint64_t row = hi ? p1 : p0;
       const uint64_t zero = reinterpret_cast<uint64_t>(g_zero_page) + (lane & 31) * 16;
       const uint64_t src = ok ? row + chunk[q] * 16 : zero;
-      dma16(reinterpret_cast<const void*>(src), dst + (8 * q + w) * 1024);
+      dma16(reinterpret_cast<const void*>(src), dst + (4 * q + w) * 1024);
     }
   }
   __device__ static bf16x8 frag(const char* t, int mn0, int s) {
@@ -201,35 +203,31 @@ struct MNDma {
   }
 };
 
-// Fragments of one MFMA k-step for this wave: 4 A blocks (its 128 rows) and 2 B blocks.
+// Fragments of one MFMA k-step for this wave: 4 A blocks (its 128 rows) and 4 B blocks.
 struct FragSet {
-  bf16x8 a[4], b[2];
+  bf16x8 a[4], b[4];
 };
 
 template <class AL, class BL, class BSub>
 __device__ __forceinline__ void load_frags(const char* slot, int ks, int wm, BSub bsub, FragSet& F) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) F.b[j] = BL::frag(slot + DMA_B_OFF, bsub(j), ks);
+  for (int j = 0; j < 4; ++j) F.b[j] = BL::frag(slot + DMA_B_OFF, bsub(j), ks);
 #pragma unroll
   for (int i = 0; i < 4; ++i) F.a[i] = AL::frag(slot, wm * 128 + i * 32, ks);
 }
 
-__device__ __forceinline__ void mma_frags(const FragSet& F, WaveAcc& acc) {
+// The 16 MFMAs of one k-step, split so that a batch of fragment reads can be issued after the
+// first one: the compiler waits for all outstanding LDS reads before an MFMA that needs
+// fragments, so reads issued after that first MFMA never delay the current k-step.
+__device__ __forceinline__ void mma_first(const FragSet& F, WaveAcc& acc) {
+  acc.c[0][0] = Mma<bf16>::mma(F.a[0], F.b[0], acc.c[0][0]);
+}
+__device__ __forceinline__ void mma_rest(const FragSet& F, WaveAcc& acc) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc.c[i][j] = Mma<bf16>::mma(F.a[i], F.b[j], acc.c[i][j]);
-}
-
-// Scheduling hint for a block of 6 fragment reads and 8 MFMAs: alternate one LDS read with one
-// MFMA so that the reads of the next k-step hide behind the current k-step's matrix work.
-__device__ __forceinline__ void interleave_reads_mfma() {
-#pragma unroll
-  for (int i = 0; i < 6; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);    // the remaining MFMAs
+    for (int j = 0; j < 4; ++j)
+      if (i | j) acc.c[i][j] = Mma<bf16>::mma(F.a[i], F.b[j], acc.c[i][j]);
 }
 
 // Workgroup barrier without a memory fence (the DMA waits are explicit); the empty asm keeps the
@@ -239,34 +237,41 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// One ring step for stage s (two MFMA k-steps).  On entry F0 holds stage s's k-step 0 fragments.
-//   1. read stage s's k-step 1 fragments into F1 while the k-step 0 MFMAs run;
-//   2. wait for stage s + 1 (only stage s + 2, four DMA instructions, was issued after it) and
-//      barrier: every wave is now done with stage s - 1, whose slot is refilled with stage s + 3
-//      (past the end: the last stage again, never computed, so the DMA count per step is fixed
-//      and the waits stay exact);
-//   3. issue the k-step 1 MFMAs, then read stage s + 1's k-step 0 fragments into F0 while they
-//      run.
+// One ring step for stage s (two MFMA k-steps).  On entry F0 holds stage s's k-step 0 fragment
+// reads, issued during the previous step.
+//   1. first k-step 0 MFMA (waits for F0), then read k-step 1 into F1 behind the other 15;
+//   2. wait for stage s + 1 (only stage s + 2, eight DMA instructions per wave, was issued after
+//      it) and barrier: every wave is now done with stage s - 1, whose slot is refilled with
+//      stage s + 3 (past the end: the last stage again, never computed, so the DMA count per step
+//      is fixed and the waits stay exact);
+//   3. first k-step 1 MFMA (waits for F1), then read stage s + 1's k-step 0 into F0 (on the last
+//      step this reads a valid slot whose contents go unused) and issue the refill behind the
+//      other 15.
 // The DMA issue is unconditional and its address never comes from a pointer select: a DMA under
-// a branch makes the compiler's wait tracking fall back to draining everything.
+// a branch makes the compiler's wait tracking fall back to draining everything.  With one wave
+// per SIMD nothing else hides a stall, so sched_barrier fences pin this order.
 template <class AL, class BL, class BSub>
 __device__ __forceinline__ void dma_step(const AL& la, const BL& lb, int s, int nkt, const char* cur,
                                          const char* next, char* refill, FragSet& F0, FragSet& F1,
                                          WaveAcc& acc, int wm, BSub bsub) {
-  const bool live = s < nkt;
-  if (live) {
-    load_frags<AL, BL>(cur, 1, wm, bsub, F1);
-    mma_frags(F0, acc);
-  }
+  mma_first(F0, acc);
   __builtin_amdgcn_sched_barrier(0);
-  wait_vmcnt<4>();
+  load_frags<AL, BL>(cur, 1, wm, bsub, F1);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_rest(F0, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<8>();
   ring_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  mma_first(F1, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  load_frags<AL, BL>(next, 0, wm, bsub, F0);
   __builtin_amdgcn_sched_barrier(0);
   const int r = min(s + 3, nkt - 1);
   la.issue(r, refill);
   lb.issue(r, refill + DMA_B_OFF);
-  if (live) mma_frags(F1, acc);
-  if (s + 1 < nkt) load_frags<AL, BL>(next, 0, wm, bsub, F0);
+  mma_rest(F1, acc);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <class AL, class BL, class BSub>
@@ -280,16 +285,21 @@ __device__ __forceinline__ void gemm_mainloop_dma(const AL& la, const BL& lb, in
   lb.issue(min(1, nkt - 1), L.b[1] + DMA_B_OFF);
   la.issue(min(2, nkt - 1), L.b[2]);
   lb.issue(min(2, nkt - 1), L.b[2] + DMA_B_OFF);
-  wait_vmcnt<8>();
+  wait_vmcnt<16>();
   ring_barrier();
   FragSet F0, F1;
   load_frags<AL, BL>(L.b[0], 0, wm, bsub, F0);
-  for (int s = 0; s < nkt; s += 4) {
+  int s = 0;
+  for (; s + 4 <= nkt; s += 4) {  // full groups: no branches between the steps
     dma_step(la, lb, s, nkt, L.b[0], L.b[1], L.b[3], F0, F1, acc, wm, bsub);
     dma_step(la, lb, s + 1, nkt, L.b[1], L.b[2], L.b[0], F0, F1, acc, wm, bsub);
     dma_step(la, lb, s + 2, nkt, L.b[2], L.b[3], L.b[1], F0, F1, acc, wm, bsub);
     dma_step(la, lb, s + 3, nkt, L.b[3], L.b[0], L.b[2], F0, F1, acc, wm, bsub);
   }
+  // 0 to 3 remaining stages; the ring position is again at slot 0
+  if (s < nkt) dma_step(la, lb, s, nkt, L.b[0], L.b[1], L.b[3], F0, F1, acc, wm, bsub);
+  if (s + 1 < nkt) dma_step(la, lb, s + 1, nkt, L.b[1], L.b[2], L.b[0], F0, F1, acc, wm, bsub);
+  if (s + 2 < nkt) dma_step(la, lb, s + 2, nkt, L.b[2], L.b[3], L.b[1], F0, F1, acc, wm, bsub);
   __syncthreads();  // drains the trailing loads; the LDS is free for the epilogue
 }
 
@@ -298,18 +308,18 @@ __device__ __forceinline__ void gemm_mainloop_dma(const AL& la, const BL& lb, in
 // ===============================================================================================
 constexpr int KROW = 128 + 16;              // padded K-major row pitch (bytes)
 
-struct RowLoaderF32 {                       // K-major rows: thread owns rows tid/8 + 64 q
-  const char* rp[4];
-  u32x4 v[4];
+struct RowLoaderF32 {                       // K-major rows: thread owns rows tid/8 + 32 q
+  const char* rp[8];
+  u32x4 v[8];
   template <class RowPtr>
   __device__ void init(RowPtr row_ptr) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) rp[q] = row_ptr((threadIdx.x >> 3) + 64 * q);
+    for (int q = 0; q < 8; ++q) rp[q] = row_ptr((threadIdx.x >> 3) + 32 * q);
   }
   __device__ void load(int kt) {
     const int chunk = threadIdx.x & 7;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 8; ++q) {
       if (rp[q]) v[q] = ld16(rp[q] + (int64_t)kt * 128 + chunk * 16);
       else v[q] = u32x4{0u, 0u, 0u, 0u};
     }
@@ -317,8 +327,8 @@ struct RowLoaderF32 {                       // K-major rows: thread owns rows ti
   __device__ void store(char* lds) const {
     const int chunk = threadIdx.x & 7;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<u32x4*>(lds + ((threadIdx.x >> 3) + 64 * q) * KROW + chunk * 16) = v[q];
+    for (int q = 0; q < 8; ++q)
+      *reinterpret_cast<u32x4*>(lds + ((threadIdx.x >> 3) + 32 * q) * KROW + chunk * 16) = v[q];
   }
   __device__ static float frag(const char* lds, int row0, int s) {
     const int lane = threadIdx.x & 63;
@@ -326,31 +336,39 @@ struct RowLoaderF32 {                       // K-major rows: thread owns rows ti
   }
 };
 
-// MN-major fp32 operand, transposed in registers into the K-major layout: thread owns a 4 (k) x
-// 4 (mn) block, mn = 4 (tid % 64), k = 4 (tid / 64).  kbase / klim as for MNDma.
+// MN-major fp32 operand, transposed in registers into the K-major layout: thread owns two 4 (k)
+// x 4 (mn) blocks, mn = 4 (tid % 64), k = 4 (tid / 64) and 4 (tid / 64 + 4).  kbase / klim as
+// for MNDma.
 template <class KBase>
 struct ColLoaderF32 {
   KBase kbase;
   int klim;
-  u32x4 v[4];
+  u32x4 v[2][4];
   bool ok;
   __device__ ColLoaderF32(KBase f, int klim_, int mn_base, int mn_valid) : kbase(f), klim(klim_) {
     ok = mn_base + (int)(threadIdx.x & 63) * 4 < mn_valid;
   }
   __device__ void load(int kt) {
-    const int k0 = kt * 32 + (int)(threadIdx.x >> 6) * 4;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      if (ok && k0 + kk < klim) v[kk] = ld16(kbase(k0 + kk) + (threadIdx.x & 63) * 16);
-      else v[kk] = u32x4{0u, 0u, 0u, 0u};
+    for (int h = 0; h < 2; ++h) {
+      const int k0 = kt * 32 + ((int)(threadIdx.x >> 6) + 4 * h) * 4;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        if (ok && k0 + kk < klim) v[h][kk] = ld16(kbase(k0 + kk) + (threadIdx.x & 63) * 16);
+        else v[h][kk] = u32x4{0u, 0u, 0u, 0u};
+      }
     }
   }
   __device__ void store(char* lds) const {
-    const int mn0 = (threadIdx.x & 63) * 4, kq = threadIdx.x >> 6;
+    const int mn0 = (threadIdx.x & 63) * 4;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      u32x4 o{v[0][e], v[1][e], v[2][e], v[3][e]};
-      *reinterpret_cast<u32x4*>(lds + (mn0 + e) * KROW + kq * 16) = o;
+    for (int h = 0; h < 2; ++h) {
+      const int kq = (threadIdx.x >> 6) + 4 * h;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        u32x4 o{v[h][0][e], v[h][1][e], v[h][2][e], v[h][3][e]};
+        *reinterpret_cast<u32x4*>(lds + (mn0 + e) * KROW + kq * 16) = o;
+      }
     }
   }
   __device__ static float frag(const char* lds, int row0, int s) { return RowLoaderF32::frag(lds, row0, s); }
@@ -376,15 +394,15 @@ __device__ __forceinline__ void gemm_mainloop_reg(LA& la, LB& lb, int nkt, WaveA
     }
 #pragma unroll
     for (int s = 0; s < Mma<float>::STEPS; ++s) {
-      float a[4], b[2];
+      float a[4], b[4];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = LB::frag(Bs, bsub(j), s);
+      for (int j = 0; j < 4; ++j) b[j] = LB::frag(Bs, bsub(j), s);
 #pragma unroll
       for (int i = 0; i < 4; ++i) a[i] = LA::frag(As, wm * 128 + i * 32, s);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc.c[i][j] = Mma<float>::mma(a[i], b[j], acc.c[i][j]);
+        for (int j = 0; j < 4; ++j) acc.c[i][j] = Mma<float>::mma(a[i], b[j], acc.c[i][j]);
     }
     if (more) {
       la.store((kt & 1) ? L.b[0] : L.b[2]);
@@ -428,6 +446,14 @@ __device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nkt, WaveAcc& 
 // K stages for a K extent of `k` elements.
 template <typename T> __host__ __device__ constexpr int stage_k() { return Mma<T>::BK; }
 
+// Column (within the 256-wide tile) of N block j of wave column wn, for lane l:
+//   plain:  wn * 128 + j * 32 + l % 32
+//   halved: (j / 2) * 128 + wn * 64 + (j % 2) * 32 + l % 32   (each 128-column half of the tile
+//           holds two of the wave's blocks: used where the tile's halves are gate and up, or where
+//           the epilogue works one half at a time)
+__device__ __forceinline__ int bsub_plain(int wn, int j) { return wn * 128 + j * 32; }
+__device__ __forceinline__ int bsub_halved(int wn, int j) { return (j >> 1) * 128 + wn * 64 + (j & 1) * 32; }
+
 // Tile row of accumulator register v for M block i of wave row wm.
 __device__ __forceinline__ int acc_row(int wm, int i, int v) {
   const int lane = threadIdx.x & 63;
@@ -451,7 +477,7 @@ __device__ __forceinline__ char* epi_row(LdsBufs L, int r) { return epi_buf(L, r
 template <class Col, class Val>
 __device__ __forceinline__ void epi_stage_bf16(LdsBufs L, int wm, Col col, Val val) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < 4; ++j) {
     const int c = col(j);
     if (c < 0) continue;
 #pragma unroll
@@ -479,22 +505,34 @@ __device__ __forceinline__ void epi_store_bf16(LdsBufs L, int col0, bf16* out, i
   epi_store_rows(L, col0, [&](int r) { return out + (int64_t)r * ld; }, mrows, ncols, ncols_valid);
 }
 
-// Grouped M tiles: tile mt of the concatenation of the experts' ceil(rows / BM) tiles.
+// Grouped tiles.  The experts' ceil(rows / BM) m-tiles are concatenated (mtile_off is their
+// exclusive scan), and each m-tile has NT n-tiles.  Tile `lin` is found expert by expert; inside
+// an expert the tiles run in groups of RASTER_M m-tiles, n-tile outer and m-tile inner, so that
+// the workgroups an XCD runs side by side (consecutive `lin`, see xcd_remap) share both their
+// weight columns (same n-tile) and their token rows (same group) through that XCD's L2.
 struct GroupTile {
-  int e, m0, mrows;
+  int e, m0, mrows, nt;
 };
-__device__ __forceinline__ bool find_group_tile(int mt, const int32_t* __restrict__ mtile_off,
+constexpr int RASTER_M = 8;
+__device__ __forceinline__ bool find_group_tile(int lin, int NT, const int32_t* __restrict__ mtile_off,
                                                 const int32_t* __restrict__ expert_off, int E,
                                                 GroupTile& g) {
-  if (mt >= mtile_off[E]) return false;
-  int lo = 0, hi = E;  // mtile_off[lo] <= mt < mtile_off[hi]
+  if (lin >= mtile_off[E] * NT) return false;
+  int lo = 0, hi = E;  // mtile_off[lo] * NT <= lin < mtile_off[hi] * NT
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (mtile_off[mid] <= mt) lo = mid;
+    if (mtile_off[mid] * NT <= lin) lo = mid;
     else hi = mid;
   }
+  const int me = mtile_off[lo + 1] - mtile_off[lo];  // >= 1: tile lin lies in this expert
+  const int local = lin - mtile_off[lo] * NT;
+  const int grp = local / (RASTER_M * NT);
+  const int idx = local - grp * RASTER_M * NT;
+  const int gm = min(RASTER_M, me - grp * RASTER_M);
+  const int mt = grp * RASTER_M + idx % gm;
+  g.nt = idx / gm;
   g.e = lo;
-  g.m0 = expert_off[lo] + (mt - mtile_off[lo]) * BM;
+  g.m0 = expert_off[lo] + mt * BM;
   g.mrows = min(BM, expert_off[lo + 1] - g.m0);
   return true;
 }

@@ -58,7 +58,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_router(const T* __restrict_
   const int m0 = mt * BM, n0 = nt * BN;
   if (m0 >= T_) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave >> 1, wn = wave & 1;
   const int64_t rowb = (int64_t)d * sizeof(T);
   auto la = k_rows<T>([&](int i) -> const char* {
     return m0 + i < T_ ? reinterpret_cast<const char*>(X) + (m0 + i) * rowb : nullptr;
@@ -67,10 +67,10 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_router(const T* __restrict_
     return n0 + i < E ? reinterpret_cast<const char*>(Wr) + (n0 + i) * rowb : nullptr;
   });
   WaveAcc acc;
-  gemm_mainloop<T>(la, lb, d / Mma<T>::BK, acc, L, wm, [&](int j) { return wn * 64 + j * 32; });
+  gemm_mainloop<T>(la, lb, d / Mma<T>::BK, acc, L, wm, [&](int j) { return bsub_plain(wn, j); });
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + bsub_plain(wn, j) + (lane & 31);
     if (n >= E) continue;
     const float b = bias ? bias[n] : 0.0f;
 #pragma unroll
@@ -99,8 +99,8 @@ hipError_t launch_router_gemm(const Shape& s, const void* X, const void* W_r, co
 // ---------------------------------------------------------------------------------------------
 // Gate/up projection.  Tile = 256 rows of one expert x 128 output columns j0..j0+127; the B tile
 // stacks W_gate[e] rows j0..j0+127 over W_up[e] rows j0..j0+127, and wave column wn takes gate
-// block wn*32 (j = 0) and up block 128 + wn*32 (j = 1), so each lane holds G and U of the same
-// (row, column) in matching accumulators.  Epilogue: A = silu(G) U in fp32, rounded once;
+// blocks wn*64 + {0, 32} (j = 0, 1) and the up blocks 128 + wn*64 + {0, 32} (j = 2, 3), so each
+// lane holds G and U of the same (row, column) in accumulators j and j + 2.  Epilogue: A = silu(G) U in fp32, rounded once;
 // optional H = [G | U].
 // ---------------------------------------------------------------------------------------------
 template <typename T>
@@ -111,12 +111,12 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_up(
     int d, int n, int E, int NT, int T_) {
   MOE_GEMM_LDS(L);
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int mt = lin / NT, nt = lin % NT;
   GroupTile g;
-  if (!find_group_tile(mt, mtile_off, expert_off, E, g)) return;
+  if (!find_group_tile(lin, NT, mtile_off, expert_off, E, g)) return;
+  const int nt = g.nt;
   const int j0 = nt * 128;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave >> 1, wn = wave & 1;
   const int64_t rowb = (int64_t)d * sizeof(T);
   auto la = k_rows<T>([&](int i) -> const char* {
     if (i >= g.mrows) return nullptr;
@@ -131,22 +131,22 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_up(
     return (i < 128 ? wg : wu) + (int64_t)j * rowb;
   });
   WaveAcc acc;
-  gemm_mainloop<T>(la, lb, d / Mma<T>::BK, acc, L, wm, [&](int j) { return j * 128 + wn * 32; });
-  const int ccol = wn * 32 + (lane & 31);  // act column within the tile
+  // B blocks j = 0, 1 are gate columns, j = 2, 3 the up columns of the same act columns
+  gemm_mainloop<T>(la, lb, d / Mma<T>::BK, acc, L, wm, [&](int j) { return bsub_halved(wn, j); });
   const int valid = min(128, n - j0);
   if constexpr (sizeof(T) == 2) {
     auto silu_u = [&](int i, int j, int v) {
-      const float gv = acc.c[i][0][v], uv = acc.c[i][1][v];
+      const float gv = acc.c[i][j & 1][v], uv = acc.c[i][(j & 1) + 2][v];
       return gv * sigmoid_f32(gv) * uv;
     };
-    auto colf = [&](int j) { return j == 0 ? ccol : -1; };
+    auto colf = [&](int j) { return j < 2 ? bsub_halved(wn, j) + (lane & 31) : -1; };
     epi_stage_bf16(L, wm, colf, silu_u);
     __syncthreads();
     epi_store_bf16(L, 0, reinterpret_cast<bf16*>(act) + (int64_t)g.m0 * n + j0, n, g.mrows, 128, valid);
     if (H) {
       // G and U halves side by side in one staging tile: columns [0,128) G, [128,256) U
       __syncthreads();
-      auto both = [&](int j) { return j * 128 + ccol; };
+      auto both = [&](int j) { return bsub_halved(wn, j) + (lane & 31); };
       epi_stage_bf16(L, wm, both, [&](int i, int j, int v) { return acc.c[i][j][v]; });
       __syncthreads();
       bf16* hb = reinterpret_cast<bf16*>(H) + (int64_t)g.m0 * 2 * n;
@@ -154,7 +154,10 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_up(
       epi_store_bf16(L, 128, hb + n + j0, 2 * n, g.mrows, 128, valid);
     }
   } else {
-    if (ccol < valid) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int ccol = bsub_halved(wn, j) + (lane & 31);  // act column within the tile
+      if (ccol >= valid) continue;
       const int col = j0 + ccol;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -163,7 +166,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_up(
           const int m = acc_row(wm, i, v);
           if (m >= g.mrows) continue;
           const int64_t r = g.m0 + m;
-          const float gv = acc.c[i][0][v], uv = acc.c[i][1][v];
+          const float gv = acc.c[i][j][v], uv = acc.c[i][j + 2][v];
           act[r * n + col] = from_f32<T>(gv * sigmoid_f32(gv) * uv);
           if (H) {
             H[r * 2 * n + col] = from_f32<T>(gv);
@@ -200,12 +203,12 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_down(
     int NT) {
   MOE_GEMM_LDS(L);
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int mt = lin / NT, nt = lin % NT;
   GroupTile g;
-  if (!find_group_tile(mt, mtile_off, expert_off, E, g)) return;
+  if (!find_group_tile(lin, NT, mtile_off, expert_off, E, g)) return;
+  const int nt = g.nt;
   const int n0 = nt * BN;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave >> 1, wn = wave & 1;
   const int64_t rowb = (int64_t)n * sizeof(T);
   auto la = k_rows<T>([&](int i) -> const char* {
     return i < g.mrows ? reinterpret_cast<const char*>(act) + (int64_t)(g.m0 + i) * rowb : nullptr;
@@ -213,17 +216,17 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_down(
   const char* wd = reinterpret_cast<const char*>(Wd) + (int64_t)g.e * d * rowb;
   auto lb = k_rows<T>([&](int i) -> const char* { return n0 + i < d ? wd + (int64_t)(n0 + i) * rowb : nullptr; });
   WaveAcc acc;
-  gemm_mainloop<T>(la, lb, n / Mma<T>::BK, acc, L, wm, [&](int j) { return wn * 64 + j * 32; });
+  gemm_mainloop<T>(la, lb, n / Mma<T>::BK, acc, L, wm, [&](int j) { return bsub_plain(wn, j); });
   const int valid = min(BN, d - n0);
   if constexpr (sizeof(T) == 2) {
-    epi_stage_bf16(L, wm, [&](int j) { return wn * 64 + j * 32 + (lane & 31); },
+    epi_stage_bf16(L, wm, [&](int j) { return bsub_plain(wn, j) + (lane & 31); },
                    [&](int i, int j, int v) { return acc.c[i][j][v]; });
     __syncthreads();
     epi_store_bf16(L, 0, reinterpret_cast<bf16*>(Y) + (int64_t)g.m0 * d + n0, d, g.mrows, BN, valid);
   } else {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int c = wn * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < 4; ++j) {
+      const int c = bsub_plain(wn, j) + (lane & 31);
       if (c >= valid) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
