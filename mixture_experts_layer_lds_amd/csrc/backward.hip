@@ -220,9 +220,8 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dw_down(
   const int cnt = expert_off[e + 1] - off;
   const char* dyb = reinterpret_cast<const char*>(dY) + m0 * sizeof(T);
   const char* wab = reinterpret_cast<const char*>(wA) + n0 * sizeof(T);
-  auto la = mn_rows<T>([=](int k) {
-    return dyb + (int64_t)clamp_idx(sload_i32(row_token + off, k), T_) * d * sizeof(T);
-  }, cnt, m0, d);
+  auto la = mn_rows_idx<T>([=](int k) { return clamp_idx(sload_i32(row_token + off, k), T_); },
+                          [=](int t) { return dyb + (int64_t)t * d * sizeof(T); }, cnt, m0, d);
   auto lb = mn_rows<T>([=](int k) { return wab + (int64_t)(off + k) * n * sizeof(T); }, cnt, n0, n);
   WaveAcc acc;
   gemm_mainloop<T>(la, lb, (int)cdiv(cnt, Mma<T>::BK), acc, L, wm, [&](int j) { return bsub_plain(wn, j); });
@@ -283,9 +282,8 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dw_gu(
   const char* dhb = reinterpret_cast<const char*>(dH) + m0 * sizeof(T);
   const char* xb = reinterpret_cast<const char*>(X) + n0 * sizeof(T);
   auto la = mn_rows<T>([=](int k) { return dhb + (int64_t)(off + k) * 2 * n * sizeof(T); }, cnt, m0, 2 * n);
-  auto lb = mn_rows<T>([=](int k) {
-    return xb + (int64_t)clamp_idx(sload_i32(row_token + off, k), T_) * d * sizeof(T);
-  }, cnt, n0, d);
+  auto lb = mn_rows_idx<T>([=](int k) { return clamp_idx(sload_i32(row_token + off, k), T_); },
+                          [=](int t) { return xb + (int64_t)t * d * sizeof(T); }, cnt, n0, d);
   WaveAcc acc;
   gemm_mainloop<T>(la, lb, (int)cdiv(cnt, Mma<T>::BK), acc, L, wm, [&](int j) { return bsub_plain(wn, j); });
   const int mrows = min(BM, 2 * n - m0), valid = min(BN, d - n0);

@@ -137,6 +137,7 @@ struct KDma {
       step[q] = p ? 64 : 0;
     }
   }
+  __device__ void fetch(int) {}
   __device__ void issue(int s, char* dst) const {
     const int w = threadIdx.x >> 6;
 #pragma unroll
@@ -150,42 +151,67 @@ struct KDma {
   }
 };
 
-// MN-major operand: stage k-rows 32 s .. 32 s + 31.  kbase(k) returns the global address of
-// element (mn_base, k) for 0 <= k < klim; it is only ever called with k clamped into that range
-// (so a gathered row index is always read in bounds), and rows k >= klim load zeros.  Wave w
-// instruction q fills k-rows K0 = (4 q + w) * 2 and K0 + 1: lanes 0-31 the first, 32-63 the
-// second; lane slot l % 32 holds chunk (l % 32) ^ (4 (k & 3)).  The address math is branch-free.
-template <class KBase>
+// MN-major operand: stage k-rows 32 s .. 32 s + 31.  Row k of the operand lives at
+// kptr(kidx(k)): kidx maps k to a (uniform) row id, either k itself or a gathered token id read
+// with a scalar load, and kptr turns the row id into the global address of element (mn_base, k).
+// Both are only ever called with k clamped into [0, klim) (so a gathered index is always read in
+// bounds); rows k >= klim load zeros.  Wave w instruction q fills k-rows K0 = (4 q + w) * 2 and
+// K0 + 1: lanes 0-31 the first, 32-63 the second; lane slot l % 32 holds chunk
+// (l % 32) ^ (4 (k & 3)).
+//
+// fetch(s) reads the row ids of stage s and issue(s, dst) starts its DMA; the main loop calls
+// fetch half a ring step before issue, so that the scalar loads of a gathered operand land behind
+// 15 MFMAs and no refill waits for them.  Everything per lane is a select on a scalar lane mask:
+// both row addresses sit in scalar registers, and the choice between the row and the zero page is
+// one v_cndmask per half (written out, so that the compiler cannot turn it into a branch and push
+// the MFMAs behind the address math).
+template <class KIdx, class KPtr>
 struct MNDma {
-  KBase kbase;
+  KIdx kidx;
+  KPtr kptr;
   int klim;
-  int chunk[4];
-  bool mn_ok[4];
-  __device__ MNDma(KBase f, int klim_, int mn_base, int mn_valid) : kbase(f), klim(klim_) {
+  uint32_t off[4];      // lane byte offset of its chunk in the row
+  uint64_t okmask[4];   // lanes whose columns are inside the operand
+  int nid[4][2];        // row ids of the fetched stage: k-rows K0 and K0 + 1 of each instruction
+  __device__ MNDma(KIdx fi, KPtr fp, int klim_, int mn_base, int mn_valid)
+      : kidx(fi), kptr(fp), klim(klim_) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int k = (4 * q + w) * 2 + (lane >> 5);
-      chunk[q] = (lane & 31) ^ (4 * (k & 3));
-      mn_ok[q] = mn_base + chunk[q] * 8 < mn_valid;
+      const int chunk = (lane & 31) ^ (4 * (k & 3));
+      off[q] = chunk * 16;
+      okmask[q] = __builtin_amdgcn_ballot_w64(mn_base + chunk * 8 < mn_valid);
     }
   }
-  __device__ void issue(int s, char* dst) const {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __device__ void fetch(int s) {
+    const int w = threadIdx.x >> 6;
+    const int lim = __builtin_amdgcn_readfirstlane(klim);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int lim = __builtin_amdgcn_readfirstlane(klim);
       const int k0 = __builtin_amdgcn_readfirstlane(s * 32 + (4 * q + w) * 2);
-      const int c0 = __builtin_amdgcn_readfirstlane(min(k0, lim - 1));
-      const int c1 = __builtin_amdgcn_readfirstlane(min(k0 + 1, lim - 1));
-      const uint64_t p0 = reinterpret_cast<uint64_t>(kbase(c0));
-      const uint64_t p1 = reinterpret_cast<uint64_t>(kbase(c1));
-      const bool hi = lane >= 32;
-      const bool ok = mn_ok[q] && (hi ? k0 + 1 < lim : k0 < lim);
-      const uint64_t row = hi ? p1 : p0;
-      const uint64_t zero = reinterpret_cast<uint64_t>(g_zero_page) + (lane & 31) * 16;
-      const uint64_t src = ok ? row + chunk[q] * 16 : zero;
-      dma16(reinterpret_cast<const void*>(src), dst + (4 * q + w) * 1024);
+      nid[q][0] = kidx(min(k0, lim - 1));
+      nid[q][1] = kidx(min(k0 + 1, lim - 1));
+    }
+  }
+  __device__ void issue(int s, char* dst) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lim = __builtin_amdgcn_readfirstlane(klim);
+    const bool hi = lane >= 32;
+    const uint64_t zero = reinterpret_cast<uint64_t>(g_zero_page) + (lane & 31) * 16;
+    const uint32_t zl = (uint32_t)zero, zh = (uint32_t)(zero >> 32);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int k0 = __builtin_amdgcn_readfirstlane(s * 32 + (4 * q + w) * 2);
+      const uint64_t p0 = reinterpret_cast<uint64_t>(kptr(nid[q][0]));
+      const uint64_t p1 = reinterpret_cast<uint64_t>(kptr(nid[q][1]));
+      const uint64_t row = (hi ? p1 : p0) + off[q];
+      const uint64_t kmask = (k0 < lim ? 0x00000000FFFFFFFFull : 0ull) | (k0 + 1 < lim ? 0xFFFFFFFF00000000ull : 0ull);
+      const uint64_t m = okmask[q] & kmask;
+      uint32_t sl = (uint32_t)row, sh = (uint32_t)(row >> 32);
+      asm("v_cndmask_b32_e64 %0, %1, %0, %2" : "+v"(sl) : "v"(zl), "s"(m));
+      asm("v_cndmask_b32_e64 %0, %1, %0, %2" : "+v"(sh) : "v"(zh), "s"(m));
+      dma16(reinterpret_cast<const void*>(((uint64_t)sh << 32) | sl), dst + (4 * q + w) * 1024);
     }
   }
   __device__ static bf16x8 frag(const char* t, int mn0, int s) {
@@ -239,24 +265,29 @@ __device__ __forceinline__ void ring_barrier() {
 
 // One ring step for stage s (two MFMA k-steps).  On entry F0 holds stage s's k-step 0 fragment
 // reads, issued during the previous step.
-//   1. first k-step 0 MFMA (waits for F0), then read k-step 1 into F1 behind the other 15;
+//   1. first k-step 0 MFMA (waits for F0), then read k-step 1 into F1 and fetch the row ids of
+//      the refill stage behind the other 15;
 //   2. wait for stage s + 1 (only stage s + 2, eight DMA instructions per wave, was issued after
 //      it) and barrier: every wave is now done with stage s - 1, whose slot is refilled with
 //      stage s + 3 (past the end: the last stage again, never computed, so the DMA count per step
 //      is fixed and the waits stay exact);
-//   3. first k-step 1 MFMA (waits for F1), then read stage s + 1's k-step 0 into F0 (on the last
-//      step this reads a valid slot whose contents go unused) and issue the refill behind the
-//      other 15.
+//   3. first k-step 1 MFMA (waits for F1 and the ids), then read stage s + 1's k-step 0 into F0
+//      (on the last step this reads a valid slot whose contents go unused) and issue the refill,
+//      spread over the other 15.
 // The DMA issue is unconditional and its address never comes from a pointer select: a DMA under
 // a branch makes the compiler's wait tracking fall back to draining everything.  With one wave
-// per SIMD nothing else hides a stall, so sched_barrier fences pin this order.
+// per SIMD nothing else hides a stall, so sched_barrier fences and scheduling groups pin this
+// order.
 template <class AL, class BL, class BSub>
-__device__ __forceinline__ void dma_step(const AL& la, const BL& lb, int s, int nkt, const char* cur,
+__device__ __forceinline__ void dma_step(AL& la, BL& lb, int s, int nkt, const char* cur,
                                          const char* next, char* refill, FragSet& F0, FragSet& F1,
                                          WaveAcc& acc, int wm, BSub bsub) {
+  const int r = min(s + 3, nkt - 1);
   mma_first(F0, acc);
   __builtin_amdgcn_sched_barrier(0);
   load_frags<AL, BL>(cur, 1, wm, bsub, F1);
+  la.fetch(r);
+  lb.fetch(r);
   __builtin_amdgcn_sched_barrier(0);
   mma_rest(F0, acc);
   __builtin_amdgcn_sched_barrier(0);
@@ -267,24 +298,32 @@ __device__ __forceinline__ void dma_step(const AL& la, const BL& lb, int s, int 
   __builtin_amdgcn_sched_barrier(0);
   load_frags<AL, BL>(next, 0, wm, bsub, F0);
   __builtin_amdgcn_sched_barrier(0);
-  const int r = min(s + 3, nkt - 1);
   la.issue(r, refill);
   lb.issue(r, refill + DMA_B_OFF);
   mma_rest(F1, acc);
+  // spread the refill's address arithmetic and DMA issue between the 15 MFMAs
+#pragma unroll
+  for (int i = 0; i < 15; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x006, 12, 0);  // up to 12 VALU / SALU
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one DMA
+  }
   __builtin_amdgcn_sched_barrier(0);
 }
 
 template <class AL, class BL, class BSub>
-__device__ __forceinline__ void gemm_mainloop_dma(const AL& la, const BL& lb, int nkt, WaveAcc& acc,
+__device__ __forceinline__ void gemm_mainloop_dma(AL& la, BL& lb, int nkt, WaveAcc& acc,
                                                   LdsBufs L, int wm, BSub bsub) {
   zero_acc(acc);
   if (nkt <= 0) return;
-  la.issue(0, L.b[0]);
-  lb.issue(0, L.b[0] + DMA_B_OFF);
-  la.issue(min(1, nkt - 1), L.b[1]);
-  lb.issue(min(1, nkt - 1), L.b[1] + DMA_B_OFF);
-  la.issue(min(2, nkt - 1), L.b[2]);
-  lb.issue(min(2, nkt - 1), L.b[2] + DMA_B_OFF);
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int r = min(i, nkt - 1);
+    la.fetch(r);
+    lb.fetch(r);
+    la.issue(r, L.b[i]);
+    lb.issue(r, L.b[i] + DMA_B_OFF);
+  }
   wait_vmcnt<16>();
   ring_barrier();
   FragSet F0, F1;
@@ -430,10 +469,25 @@ __device__ __forceinline__ typename KRowsOf<T>::type k_rows(RowPtr row_ptr) {
   return l;
 }
 
+struct KIdentity {
+  __device__ int operator()(int k) const { return k; }
+};
+
 template <typename T, class KBase>
 __device__ __forceinline__ auto mn_rows(KBase kbase, int klim, int mn_base, int mn_valid) {
-  if constexpr (sizeof(T) == 2) return MNDma<KBase>(kbase, klim, mn_base, mn_valid);
+  if constexpr (sizeof(T) == 2) return MNDma<KIdentity, KBase>(KIdentity{}, kbase, klim, mn_base, mn_valid);
   else return ColLoaderF32<KBase>(kbase, klim, mn_base, mn_valid);
+}
+
+// MN-major rows through an index: row k at kptr(kidx(k)), kidx returning a uniform row id.
+template <typename T, class KIdx, class KPtr>
+__device__ __forceinline__ auto mn_rows_idx(KIdx kidx, KPtr kptr, int klim, int mn_base, int mn_valid) {
+  if constexpr (sizeof(T) == 2) {
+    return MNDma<KIdx, KPtr>(kidx, kptr, klim, mn_base, mn_valid);
+  } else {
+    auto kbase = [=](int k) { return kptr(kidx(k)); };
+    return ColLoaderF32<decltype(kbase)>(kbase, klim, mn_base, mn_valid);
+  }
 }
 
 template <typename T, class LA, class LB, class BSub>
