@@ -63,9 +63,13 @@ def stage_flops(stage, R, T, d, n, E):
     }.get(stage)
 
 
-def stage_bytes(stage, R, T, d, n, E, es):
-    """Algorithmic HBM bytes of one launch of a streaming stage."""
+def stage_bytes(stage, R, T, d, n, E, es, K=None):
+    """Algorithmic HBM bytes of one launch of a streaming stage.  Routing reads the fp32 logits
+    and writes the plan: top-K ids and weights, expert-major rows (token, weight) and the
+    token-major inverse (offsets, rows)."""
+    K = K if K is not None else max(1, R // max(T, 1))
     return {
+        "route": T * E * 4 + T * K * 8 + R * 12 + (T + 1) * 4,
         "permute": R * d * es + T * d * es + R * 4,
         "combine": R * d * es + T * d * es + R * 8 + (T + 1) * 4,
         "router_bwd": R * d * es + T * d * es + T * E * 4 + R * 16,
@@ -243,6 +247,9 @@ def main():
     value = flops / (ms_step * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
 
+    # the counter record is per exact workload: shape, pass, token rounding and H cache
+    workload_key = "%s:%s:round%d:%s" % (cfg.name, "fwd+bwd" if backward else "fwd", cfg.round_mode,
+                                         ("h_cache" if not args.no_h_cache else "recompute") if backward else "-")
     breakdown = {}
     for s, v in stages.items():
         if not v:
@@ -251,7 +258,7 @@ def main():
         ent = {"launches_per_step": round(len(v) / args.steps, 3), "avg_ms": round(avg, 4),
                "ms_per_step": round(float(np.sum(v)) / args.steps, 4)}
         f = stage_flops(s, R, T, d, n, E)
-        b = stage_bytes(s, R, T, d, n, E, es)
+        b = stage_bytes(s, R, T, d, n, E, es, cfg.K)
         if f:
             ent["tflops"] = round(f / (avg * 1e-3) / 1e12, 1)
             ent["pct_peak"] = round(100 * f / (avg * 1e-3) / 1e12 / peak, 1)
@@ -260,19 +267,20 @@ def main():
             ent["pct_hbm"] = round(100 * b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 1)
         breakdown[s] = ent
     gemm_stages = [s for s in breakdown if stage_flops(s, R, T, d, n, E)]
-    dom = max(breakdown, key=lambda s: breakdown[s]["ms_per_step"])
+    modelled = [s for s in breakdown if stage_flops(s, R, T, d, n, E) or stage_bytes(s, R, T, d, n, E, es, cfg.K)]
+    dom = max(modelled, key=lambda s: breakdown[s]["ms_per_step"])
     if stage_flops(dom, R, T, d, n, E):
         avg = breakdown[dom]["avg_ms"]
         ach = stage_flops(dom, R, T, d, n, E) / (avg * 1e-3) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(ach / peak, 4), "traffic": measured_traffic(cfg.name, dom), "avg_ms": avg,
+                "frac": round(ach / peak, 4), "traffic": measured_traffic(workload_key, dom), "avg_ms": avg,
                 "algorithmic_bytes": stage_min_bytes(dom, R, T, d, n, E, es)}
     else:
         avg = breakdown[dom]["avg_ms"]
-        ach = stage_bytes(dom, R, T, d, n, E, es) / (avg * 1e-3) / 1e9
+        ach = stage_bytes(dom, R, T, d, n, E, es, cfg.K) / (avg * 1e-3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": measured_traffic(cfg.name, dom), "avg_ms": avg,
-                "algorithmic_bytes": stage_bytes(dom, R, T, d, n, E, es)}
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": measured_traffic(workload_key, dom), "avg_ms": avg,
+                "algorithmic_bytes": stage_bytes(dom, R, T, d, n, E, es, cfg.K)}
     gemm_ms = sum(breakdown[s]["ms_per_step"] for s in gemm_stages)
     expert_flops = (18 if backward else 6) * R * d * n
     res = {
@@ -289,7 +297,7 @@ def main():
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic (seeded normal inputs and random-init weights)",
-        "config": {"workload": cfg.name, "T": T, "d": d, "n": n, "E": E, "K": cfg.K,
+        "config": {"workload": cfg.name, "key": workload_key, "T": T, "d": d, "n": n, "E": E, "K": cfg.K,
                    "pass": "fwd+bwd" if backward else "fwd", "round_mode": cfg.round_mode,
                    "tile_m": cfg.tile_m, "rows": R, "h_cache": (not args.no_h_cache) if backward else None,
                    "parallelism": "single GPU"},

@@ -212,8 +212,9 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dw_down(
   const int per = MT * NT;
   const int e = lin / per;
   if (e >= E) return;
-  const int rem = lin % per;
-  const int m0 = (rem / NT) * BM, n0 = (rem % NT) * BN;
+  int mt, nt;
+  raster_tile(lin % per, MT, NT, mt, nt);
+  const int m0 = mt * BM, n0 = nt * BN;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const int off = expert_off[e];
@@ -273,8 +274,9 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dw_gu(
   const int per = MT * NT;
   const int e = lin / per;
   if (e >= E) return;
-  const int rem = lin % per;
-  const int m0 = (rem / NT) * BM, n0 = (rem % NT) * BN;
+  int mt, nt;
+  raster_tile(lin % per, MT, NT, mt, nt);
+  const int m0 = mt * BM, n0 = nt * BN;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const int off = expert_off[e];
@@ -491,8 +493,9 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dwr(
   const int per = MT * NT;
   const int sl = lin / per;
   if (sl >= S) return;
-  const int rem = lin % per;
-  const int m0 = (rem / NT) * BM, n0 = (rem % NT) * BN;
+  int mt, nt;
+  raster_tile(lin % per, MT, NT, mt, nt);
+  const int m0 = mt * BM, n0 = nt * BN;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const int t0 = sl * TS;

@@ -94,11 +94,19 @@ __host__ __device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return 
 __device__ __forceinline__ int clamp_idx(int i, int n) { return min(max(i, 0), n - 1); }
 
 // XCD-aware remap of a 1-D grid: hardware hands consecutive workgroups to the 8 XCDs in turn,
-// each with its own L2.  Remap so that each XCD walks a contiguous range of logical tiles
-// (neighbouring tiles share operands).  `n` must be a multiple of 8.
-__device__ __forceinline__ int xcd_remap(int bid, int n) {
-  const int per = n >> 3;
-  return (bid & 7) * per + (bid >> 3);
+// each with its own L2.  The logical tiles are cut into chunks of XCD_CHUNK consecutive tiles
+// (one per CU of an XCD) and the chunks are dealt to the XCDs in turn, so that the tiles an XCD
+// runs side by side are neighbours (they share operands in its L2) while every XCD still gets an
+// even share of the whole range (tiles late in the list can carry more work than early ones).
+// The tail that does not fill a chunk per XCD is split evenly.  `n` must be a multiple of 8; the
+// map is a bijection of [0, n).
+constexpr int XCD_CHUNK = 32;
+__host__ __device__ __forceinline__ int xcd_remap(int bid, int n) {
+  const int per = n >> 3;           // workgroups per XCD
+  const int xcd = bid & 7, j = bid >> 3;
+  const int full = per / XCD_CHUNK; // whole chunks per XCD
+  if (j < full * XCD_CHUNK) return ((j / XCD_CHUNK) * 8 + xcd) * XCD_CHUNK + j % XCD_CHUNK;
+  const int rem = per - full * XCD_CHUNK;
+  return full * 8 * XCD_CHUNK + xcd * rem + (j - full * XCD_CHUNK);
 }
-
 }  // namespace moe

@@ -568,6 +568,16 @@ struct GroupTile {
   int e, m0, mrows, nt;
 };
 constexpr int RASTER_M = 8;
+// Tile `local` of an MT x NT grid in the grouped order: groups of RASTER_M m-tiles (the last one
+// possibly smaller), n-tile outer and m-tile inner inside a group.  Requires local < MT * NT.
+__device__ __forceinline__ void raster_tile(int local, int MT, int NT, int& mt, int& nt) {
+  const int grp = local / (RASTER_M * NT);
+  const int idx = local - grp * RASTER_M * NT;
+  const int gm = min(RASTER_M, MT - grp * RASTER_M);
+  mt = grp * RASTER_M + idx % gm;
+  nt = idx / gm;
+}
+
 __device__ __forceinline__ bool find_group_tile(int lin, int NT, const int32_t* __restrict__ mtile_off,
                                                 const int32_t* __restrict__ expert_off, int E,
                                                 GroupTile& g) {
@@ -579,12 +589,8 @@ __device__ __forceinline__ bool find_group_tile(int lin, int NT, const int32_t* 
     else hi = mid;
   }
   const int me = mtile_off[lo + 1] - mtile_off[lo];  // >= 1: tile lin lies in this expert
-  const int local = lin - mtile_off[lo] * NT;
-  const int grp = local / (RASTER_M * NT);
-  const int idx = local - grp * RASTER_M * NT;
-  const int gm = min(RASTER_M, me - grp * RASTER_M);
-  const int mt = grp * RASTER_M + idx % gm;
-  g.nt = idx / gm;
+  int mt;
+  raster_tile(lin - mtile_off[lo] * NT, me, NT, mt, g.nt);
   g.e = lo;
   g.m0 = expert_off[lo] + mt * BM;
   g.mrows = min(BM, expert_off[lo + 1] - g.m0);

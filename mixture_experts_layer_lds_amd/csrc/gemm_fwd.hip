@@ -100,8 +100,8 @@ hipError_t launch_router_gemm(const Shape& s, const void* X, const void* W_r, co
 // Gate/up projection.  Tile = 256 rows of one expert x 128 output columns j0..j0+127; the B tile
 // stacks W_gate[e] rows j0..j0+127 over W_up[e] rows j0..j0+127, and wave column wn takes gate
 // blocks wn*64 + {0, 32} (j = 0, 1) and the up blocks 128 + wn*64 + {0, 32} (j = 2, 3), so each
-// lane holds G and U of the same (row, column) in accumulators j and j + 2.  Epilogue: A = silu(G) U in fp32, rounded once;
-// optional H = [G | U].
+// lane holds G and U of the same (row, column) in accumulators j and j + 2.  Epilogue:
+// A = silu(G) U in fp32, rounded once; optional H = [G | U].
 // ---------------------------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void k_up(

@@ -12,12 +12,14 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------------------------
-// top-K: one wave per token.  Lane i holds logits e = i + 64 j.  K rounds of a wave arg-max
-// under the order (logit descending, expert id ascending), compared on order_key; then the
-// softmax over the K winners.  The winners set their bit in the block's LDS bitmap (bitwise OR
-// is order independent).
+// top-K: one wave per token, 16 waves per block of 64 tokens.  Lane i holds logits e = i + 64 j
+// as composite keys (order_key(L) << 32) | ~e, so that one unsigned maximum orders by logit
+// descending and then by expert id ascending; K rounds of a wave maximum pick the winners, whose
+// logits are re-read for the softmax over the K of them.  The winners set their bit in the
+// block's LDS bitmap (bitwise OR is order independent).
 // ---------------------------------------------------------------------------------------------
 constexpr int TOPK_TOKENS_PER_BLOCK = 64;  // two 32-bit bitmap words per expert per block
+constexpr int TOPK_THREADS = 1024;
 
 // Order-preserving integer key of an fp32 logit: a > b as floats <=> key(a) > key(b), -0.0 and
 // +0.0 share a key, and NaN takes the smallest key (it ranks below every number).  Selecting on
@@ -31,53 +33,41 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 }
 
 template <int EPL>
-__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int K,
-                                              int W, int32_t* __restrict__ topk_idx,
-                                              float* __restrict__ topk_w, uint32_t* __restrict__ bits) {
+__global__ __launch_bounds__(TOPK_THREADS) void k_topk(const float* __restrict__ logits, int T, int E,
+                                                       int K, int W, int32_t* __restrict__ topk_idx,
+                                                       float* __restrict__ topk_w,
+                                                       uint32_t* __restrict__ bits) {
   extern __shared__ uint32_t sbits[];  // [E][2]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t0 = blockIdx.x * TOPK_TOKENS_PER_BLOCK;
   for (int i = threadIdx.x; i < 2 * E; i += blockDim.x) sbits[i] = 0u;
   __syncthreads();
-  for (int tt = wave; tt < TOPK_TOKENS_PER_BLOCK; tt += 4) {
+  for (int tt = wave; tt < TOPK_TOKENS_PER_BLOCK; tt += TOPK_THREADS / 64) {
     const int t = t0 + tt;
     if (t >= T) break;
     const float* row = logits + (int64_t)t * E;
-    float v[EPL];
-    uint32_t key[EPL];
-    bool live[EPL];
+    uint64_t ck[EPL];  // 0 = no candidate (a live composite is never 0: ~e != 0)
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
       const int e = lane + 64 * j;
-      live[j] = e < E;
-      v[j] = live[j] ? row[e] : 0.0f;
-      key[j] = order_key(v[j]);
+      ck[j] = e < E ? (((uint64_t)order_key(row[e]) << 32) | (uint32_t)~(uint32_t)e) : 0ull;
     }
-    float my_v = 0.0f;
     int my_e = 0;
     for (int k = 0; k < K; ++k) {
-      // lane-local best among live slots (ties: lower id = lower j)
-      uint32_t bk = 0u;
-      float bv = 0.0f;
-      int be = 0x7fffffff;
+      uint64_t b = ck[0];
 #pragma unroll
-      for (int j = 0; j < EPL; ++j)
-        if (live[j] && (be == 0x7fffffff || key[j] > bk)) { bk = key[j]; bv = v[j]; be = lane + 64 * j; }
-      // wave arg-max; empty lanes carry id INT_MAX and never beat a live candidate
+      for (int j = 1; j < EPL; ++j) b = ck[j] > b ? ck[j] : b;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t ok = __shfl_xor(bk, o, 64);
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oe = __shfl_xor(be, o, 64);
-        const bool take = (oe != 0x7fffffff) &&
-                          (be == 0x7fffffff || ok > bk || (ok == bk && oe < be));
-        if (take) { bk = ok; bv = ov; be = oe; }
+        const uint64_t x = __shfl_xor(b, o, 64);
+        b = x > b ? x : b;
       }
 #pragma unroll
       for (int j = 0; j < EPL; ++j)
-        if (be == lane + 64 * j) live[j] = false;
-      if (lane == k) { my_v = bv; my_e = be; }
+        if (ck[j] == b) ck[j] = 0ull;
+      if (lane == k) my_e = (int)~(uint32_t)b;
     }
+    const float my_v = lane < K ? row[my_e] : 0.0f;
     const float vmax = __shfl(my_v, 0, 64);
     const float ex = lane < K ? __expf(my_v - vmax) : 0.0f;
     const float s = wave_sum(ex);
@@ -146,24 +136,34 @@ __global__ __launch_bounds__(256) void k_count(const uint32_t* __restrict__ bits
 // Key of token t for expert e, larger = chosen first:
 //   adding  (best non-members): (ord(L[t,e]) << 32) | ~t      -> larger logit, then lower t
 //   dropping (worst members):   (~ord(L[t,e]) << 32) | t      -> smaller logit, then higher t
-// ord() is order_key (-0.0 folded onto +0.0, NaN lowest).  Keys are unique
-// (t is), so the set of the `amount` largest keys is unique; it is found by an 8-pass radix
-// select (8-bit digits, LDS histograms with integer atomics), and the bitmap row is rewritten.
-// The expert's logit column is cached in LDS when T <= TR_LDS_TOKENS.
+// ord() is order_key (-0.0 folded onto +0.0, NaN lowest).  Keys are unique (t is), so the set of
+// the `amount` largest keys is unique; it is found by an 8-pass radix select over 8-bit digits
+// and the bitmap row is rewritten.  Most candidates share their top digits (those of the logit's
+// sign and exponent), so the lanes of a wave that hit its first participant's bin add their
+// count with one LDS atomic; one wave then locates the digit with a suffix scan.  Once every
+// candidate left under the chosen prefix is taken, the threshold is their minimum and the
+// remaining passes are skipped.
+// When T <= TR_LDS_TOKENS the expert's logit keys and bitmap row are cached in LDS.
 // ---------------------------------------------------------------------------------------------
 constexpr int TR_THREADS = 1024;
 constexpr int TR_LDS_TOKENS = 32768;
 
+__host__ __device__ __forceinline__ size_t tr_lds_bytes(int64_t T, int W) {
+  return T <= TR_LDS_TOKENS ? (size_t)(T + W) * 4 : 0;
+}
 
 __global__ __launch_bounds__(TR_THREADS) void k_token_round(const float* __restrict__ logits, int T,
                                                            int E, int W, int M, int mode,
                                                            uint32_t* __restrict__ bits,
                                                            const int32_t* __restrict__ counts) {
-  extern __shared__ uint32_t s_ord[];  // [min(T, TR_LDS_TOKENS)] (only if cached)
+  extern __shared__ uint32_t s_dyn[];  // cached: [T] logit keys, then [W] bitmap words
   __shared__ int hist[256];
   __shared__ uint64_t s_prefix;
+  __shared__ unsigned long long s_min;
   __shared__ int s_need;
+  __shared__ bool s_all;
   const int e = blockIdx.x;
+  const int lane = threadIdx.x & 63;
   const int c = counts[e];
   const int r = c % M;
   if (r == 0) return;
@@ -175,17 +175,23 @@ __global__ __launch_bounds__(TR_THREADS) void k_token_round(const float* __restr
   const int amount = add ? (M - r) : r;
   const bool cached = T <= TR_LDS_TOKENS;
   uint32_t* brow = bits + (int64_t)e * W;
+  uint32_t* s_ord = s_dyn;
+  uint32_t* s_bits = s_dyn + T;
   if (cached) {
+#pragma unroll 8
     for (int t = threadIdx.x; t < T; t += TR_THREADS) s_ord[t] = order_key(logits[(int64_t)t * E + e]);
+    for (int w = threadIdx.x; w < W; w += TR_THREADS) s_bits[w] = brow[w];
     __syncthreads();
   }
   auto key_of = [&](int t, bool& cand) -> uint64_t {
-    const bool mem = (brow[t >> 5] >> (t & 31)) & 1u;
+    const uint32_t word = cached ? s_bits[t >> 5] : brow[t >> 5];
+    const bool mem = (word >> (t & 31)) & 1u;
     cand = add ? !mem : mem;
     const uint32_t o = cached ? s_ord[t] : order_key(logits[(int64_t)t * E + e]);
     return add ? (((uint64_t)o << 32) | (uint32_t)(~(uint32_t)t))
                : (((uint64_t)(~o) << 32) | (uint32_t)t);
   };
+  const int iters = (T + TR_THREADS - 1) / TR_THREADS;  // uniform trip count: ballots see every lane
   uint64_t prefix = 0;  // digits fixed so far (high bits)
   int need = amount;    // how many keys >= threshold still to take within the current prefix
   for (int pass = 0; pass < 8; ++pass) {
@@ -193,39 +199,92 @@ __global__ __launch_bounds__(TR_THREADS) void k_token_round(const float* __restr
     for (int i = threadIdx.x; i < 256; i += TR_THREADS) hist[i] = 0;
     __syncthreads();
     const uint64_t hi_mask = pass == 0 ? 0ull : (~0ull << (shift + 8));
-    for (int t = threadIdx.x; t < T; t += TR_THREADS) {
-      bool cand;
-      const uint64_t k = key_of(t, cand);
-      if (cand && (k & hi_mask) == prefix) atomicAdd(&hist[(k >> shift) & 255], 1);
+    for (int it = 0; it < iters; ++it) {
+      const int t = it * TR_THREADS + threadIdx.x;
+      bool part = false;
+      int dig = 0;
+      if (t < T) {
+        bool cand;
+        const uint64_t k = key_of(t, cand);
+        part = cand && (k & hi_mask) == prefix;
+        dig = (int)((k >> shift) & 255);
+      }
+      const uint64_t act = __builtin_amdgcn_ballot_w64(part);
+      if (act) {  // uniform: the first participant's bin takes one merged atomic
+        const int leader = (int)__builtin_ctzll(act);
+        const int ld = __shfl(dig, leader, 64);
+        const uint64_t same = __builtin_amdgcn_ballot_w64(part && dig == ld);
+        if (lane == leader) atomicAdd(&hist[ld], (int)__builtin_popcountll(same));
+        else if (part && dig != ld) atomicAdd(&hist[dig], 1);
+      }
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-      int acc = 0, d = 255;
-      for (; d > 0; --d) {
-        if (acc + hist[d] >= need) break;
-        acc += hist[d];
+    if (threadIdx.x < 64) {
+      // lane l holds bins 4l .. 4l+3; suffix sums over lanes find the digit where the running
+      // count (from the top bin down) first reaches `need`.
+      int h[4], s4 = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        h[j] = hist[4 * lane + j];
+        s4 += h[j];
       }
-      s_prefix = prefix | ((uint64_t)d << shift);
-      s_need = need - acc;
+      int suf = s4;  // sum of s4 over lanes lane .. 63
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_down(suf, o, 64);
+        if (lane + o < 64) suf += v;
+      }
+      const int above = suf - s4;  // candidates in bins above 4 lane + 3
+      if (above < need && need <= suf) {
+        int acc = above, dsel = 4 * lane;
+        for (int j = 3; j >= 0; --j) {
+          if (acc + h[j] >= need) {
+            dsel = 4 * lane + j;
+            break;
+          }
+          acc += h[j];
+        }
+        s_prefix = prefix | ((uint64_t)dsel << shift);
+        s_need = need - acc;
+        s_all = (need - acc) == h[dsel - 4 * lane];
+      }
     }
     __syncthreads();
     prefix = s_prefix;
     need = s_need;
+    const bool all = s_all;
     __syncthreads();
+    if (all && pass < 7) {
+      // every candidate under the new prefix is taken: the threshold is the smallest of them
+      const uint64_t pmask = ~0ull << shift;
+      if (threadIdx.x == 0) s_min = ~0ull;
+      __syncthreads();
+      for (int t = threadIdx.x; t < T; t += TR_THREADS) {
+        bool cand;
+        const uint64_t k = key_of(t, cand);
+        if (cand && (k & pmask) == prefix) atomicMin(&s_min, k);
+      }
+      __syncthreads();
+      prefix = s_min;
+      break;
+    }
   }
   // prefix is now the smallest chosen key: every candidate with key >= prefix flips membership.
+  // Each word is owned by one thread, which reads only its own word's bits.
   const uint64_t thr = prefix;
   for (int w = threadIdx.x; w < W; w += TR_THREADS) {
-    uint32_t word = brow[w];
+    uint32_t word = cached ? s_bits[w] : brow[w];
+    const uint32_t orig = word;
     for (int b = 0; b < 32; ++b) {
       const int t = w * 32 + b;
       if (t >= T) break;
-      bool cand;
-      const uint64_t k = key_of(t, cand);
+      const bool mem = (orig >> b) & 1u;
+      const bool cand = add ? !mem : mem;
+      const uint32_t o = cached ? s_ord[t] : order_key(logits[(int64_t)t * E + e]);
+      const uint64_t k = add ? (((uint64_t)o << 32) | (uint32_t)(~(uint32_t)t))
+                             : (((uint64_t)(~o) << 32) | (uint32_t)t);
       if (cand && k >= thr) word ^= (1u << b);
     }
-    // all reads of this word by other threads happen before any write: each word is owned by
-    // exactly one thread in this loop, and key_of only reads bits of the word it evaluates.
     brow[w] = word;
   }
 }
@@ -257,15 +316,31 @@ __global__ __launch_bounds__(1024) void k_offsets(const int32_t* __restrict__ co
   }
 }
 
+// Stage the bitmap words of a 256-token block (8 words per expert) in LDS: sb[e * 8 + j] is word
+// blockIdx.x * 8 + j of expert e (0 past the end).  Coalesced 32-byte pieces replace E strided
+// loads per token.
+__device__ __forceinline__ void stage_block_bits(const uint32_t* __restrict__ bits, int E, int W,
+                                                 uint32_t* sb) {
+  const int w0 = blockIdx.x * 8;
+  for (int i = threadIdx.x; i < E * 8; i += blockDim.x) {
+    const int e = i >> 3, w = w0 + (i & 7);
+    sb[i] = w < W ? bits[(int64_t)e * W + w] : 0u;
+  }
+  __syncthreads();
+}
+
 // Tokens' final expert counts after token rounding -> tok_off[t+1] (scanned afterwards).
+// 256 threads per block, one token each; dynamic LDS E * 8 words.
 __global__ __launch_bounds__(256) void k_tok_count(const uint32_t* __restrict__ bits, int T, int E,
                                                    int W, int32_t* __restrict__ tok_off) {
+  extern __shared__ uint32_t sb[];
+  stage_block_bits(bits, E, W, sb);
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= T) return;
-  const int w = t >> 5;
+  const int wl = threadIdx.x >> 5;
   const uint32_t m = 1u << (t & 31);
   int c = 0;
-  for (int e = 0; e < E; ++e) c += (bits[(int64_t)e * W + w] & m) ? 1 : 0;
+  for (int e = 0; e < E; ++e) c += (sb[e * 8 + wl] & m) ? 1 : 0;
   tok_off[t + 1] = c;
 }
 
@@ -335,10 +410,13 @@ __global__ __launch_bounds__(256) void k_place(const float* __restrict__ logits,
                                                int32_t* __restrict__ row_token,
                                                float* __restrict__ row_w,
                                                int32_t* __restrict__ tok_row) {
+  extern __shared__ uint32_t sb[];  // ROUNDED: the block's bitmap words, E * 8
+  if (ROUNDED) stage_block_bits(bits, E, W, sb);
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= T) return;
   const float* L = logits + (int64_t)t * E;
   const int w = t >> 5;
+  const int wl = threadIdx.x >> 5;
   const uint32_t below = (1u << (t & 31)) - 1u;
   const uint32_t me = 1u << (t & 31);
   const int base = tok_off[t];
@@ -368,14 +446,14 @@ __global__ __launch_bounds__(256) void k_place(const float* __restrict__ logits,
     if (cnt == 0) return;
     float m = -INFINITY;
     for (int e = 0; e < E; ++e)
-      if (bits[(int64_t)e * W + w] & me) m = fmaxf(m, L[e]);
+      if (sb[e * 8 + wl] & me) m = fmaxf(m, L[e]);
     float s = 0.0f;
     for (int e = 0; e < E; ++e)
-      if (bits[(int64_t)e * W + w] & me) s += __expf(L[e] - m);
+      if (sb[e * 8 + wl] & me) s += __expf(L[e] - m);
     const float inv = 1.0f / s;
     int i = 0;
     for (int e = 0; e < E; ++e) {
-      const uint32_t word = bits[(int64_t)e * W + w];
+      const uint32_t word = sb[e * 8 + wl];
       if (!(word & me)) continue;
       const int row = expert_off[e] + wprefix[(int64_t)e * W + w] + __popc(word & below);
       row_token[row] = t;
@@ -401,7 +479,7 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int K, int round_
   int32_t* wprefix = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + align_up((size_t)E * W * 4, 256));
   const int nblk = (int)cdiv(T, TOPK_TOKENS_PER_BLOCK);
   const size_t lds = (size_t)E * 2 * sizeof(uint32_t);
-#define MOE_TOPK(EPL) k_topk<EPL><<<nblk, 256, lds, st>>>(logits, (int)T, E, K, W, p.topk_idx, p.topk_w, bits)
+#define MOE_TOPK(EPL) k_topk<EPL><<<nblk, TOPK_THREADS, lds, st>>>(logits, (int)T, E, K, W, p.topk_idx, p.topk_w, bits)
   if (E <= 64) MOE_TOPK(1);
   else if (E <= 128) MOE_TOPK(2);
   else if (E <= 256) MOE_TOPK(4);
@@ -411,23 +489,20 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int K, int round_
   k_count<<<E, 256, 0, st>>>(bits, W, wprefix, p.counts);
   const bool rounded = round_mode != 0;
   if (rounded) {
-    const size_t tr_lds = T <= TR_LDS_TOKENS ? (size_t)T * 4 : 0;
-    static bool lds_attr_set = false;  // dynamic LDS above 64 KiB must be opted into
-    if (!lds_attr_set) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_token_round),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               TR_LDS_TOKENS * 4);
-      if (e != hipSuccess) return e;
-      lds_attr_set = true;
-    }
+    const size_t tr_lds = tr_lds_bytes(T, W);
+    // dynamic LDS above 64 KiB must be opted into (per device; a cheap host call)
+    const hipError_t ae = hipFuncSetAttribute(reinterpret_cast<const void*>(k_token_round),
+                                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                                              (int)tr_lds_bytes(TR_LDS_TOKENS, TR_LDS_TOKENS / 32));
+    if (ae != hipSuccess) return ae;
     k_token_round<<<E, TR_THREADS, tr_lds, st>>>(logits, (int)T, E, W, tile_m, round_mode, bits, p.counts);
     k_count<<<E, 256, 0, st>>>(bits, W, wprefix, p.counts);
   }
   k_offsets<<<1, 1024, 0, st>>>(p.counts, E, p.expert_off, p.meta);
   if (rounded) {
-    k_tok_count<<<(int)cdiv(T, 256), 256, 0, st>>>(bits, (int)T, E, W, p.tok_off);
+    k_tok_count<<<(int)cdiv(T, 256), 256, (size_t)E * 32, st>>>(bits, (int)T, E, W, p.tok_off);
     k_tok_scan<<<1, 1024, 0, st>>>((int)T, p.tok_off);
-    k_place<true><<<(int)cdiv(T, 256), 256, 0, st>>>(logits, (int)T, E, K, W, p.topk_idx, bits, wprefix,
+    k_place<true><<<(int)cdiv(T, 256), 256, (size_t)E * 32, st>>>(logits, (int)T, E, K, W, p.topk_idx, bits, wprefix,
                                                      p.expert_off, p.tok_off, p.row_token, p.row_w, p.tok_row);
   } else {
     k_tok_fill<<<(int)cdiv(T + 1, 256), 256, 0, st>>>((int)T, K, p.tok_off);
