@@ -5,7 +5,6 @@ by one: sampled tokens (their output, dX, dS, dLogits and logits rows, through t
 restricted to those tokens) and sampled experts (their weight gradients); the router weight
 gradient is checked through its defining identity dW_r = dLogits^T X at full size.
 """
-import os
 
 import numpy as np
 import pytest
@@ -13,20 +12,16 @@ import torch
 
 import oracle
 from mixture_experts_layer_lds_amd import workloads as wl
+from conftest import announce_case
 from parity import (TOL, assert_close, check_routing, f64, run_gpu, subset_plan)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
-LOG = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
 
 
 @pytest.fixture(autouse=True)
 def announce(request):
-    os.makedirs(LOG, exist_ok=True)
-    with open(os.path.join(LOG, "gpu_test_progress.txt"), "a") as f:
-        f.write("START %s\n" % request.node.nodeid)
-        f.flush()
-        os.fsync(f.fileno())
+    announce_case(request.node.nodeid)
     if not torch.cuda.is_available():
         pytest.skip("no GPU visible")
     yield

@@ -4,7 +4,6 @@ on seeded inputs small enough for the oracle but spanning several GEMM tiles wit
 Routing outputs must be bit-exact given the same fp32 logits; floating-point outputs and
 gradients must satisfy max|y - y_ref| <= tol * max|y_ref| (1e-4 fp32, 2e-2 bf16).
 """
-import os
 
 import numpy as np
 import pytest
@@ -13,21 +12,17 @@ import torch
 import oracle
 from mixture_experts_layer_lds_amd import binding as B
 from mixture_experts_layer_lds_amd import workloads as wl
+from conftest import announce_case
 from parity import (TOL, assert_close, check_backward, check_forward, check_routing, f64, run_gpu)
 
 pytestmark = pytest.mark.gpu
 
-LOG = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
 
 
 @pytest.fixture(autouse=True)
 def announce(request):
     """Record which case is about to touch the GPU, flushed before it runs."""
-    os.makedirs(LOG, exist_ok=True)
-    with open(os.path.join(LOG, "gpu_test_progress.txt"), "a") as f:
-        f.write("START %s\n" % request.node.nodeid)
-        f.flush()
-        os.fsync(f.fileno())
+    announce_case(request.node.nodeid)
     if not torch.cuda.is_available():
         pytest.skip("no GPU visible")
     yield
