@@ -137,11 +137,12 @@ struct KDma {
       step[q] = p ? 64 : 0;
     }
   }
+  int ps[4];  // stage of the last prepare_q(q)
   __device__ void fetch(int) {}
-  __device__ void issue(int s, char* dst) const {
+  __device__ void prepare_q(int s, int q) { ps[q] = s; }
+  __device__ void issue_q(int q, char* dst) const {
     const int w = threadIdx.x >> 6;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) dma16(g[q] + (int64_t)s * step[q], dst + (4 * q + w) * 1024);
+    dma16(g[q] + (int64_t)ps[q] * step[q], dst + (4 * q + w) * 1024);
   }
   __device__ static bf16x8 frag(const char* t, int row0, int s) {
     const int lane = threadIdx.x & 63;
@@ -159,8 +160,9 @@ struct KDma {
 // K0 + 1: lanes 0-31 the first, 32-63 the second; lane slot l % 32 holds chunk
 // (l % 32) ^ (4 (k & 3)).
 //
-// fetch(s) reads the row ids of stage s and issue(s, dst) starts its DMA; the main loop calls
-// fetch half a ring step before issue, so that the scalar loads of a gathered operand land behind
+// fetch(s) reads the row ids of stage s, prepare_q(s, q) turns them into this lane's source for
+// instruction q and issue_q(q, dst) starts it; the main loop calls fetch half a ring step before
+// the first prepare_q, so that the scalar loads of a gathered operand land behind
 // 15 MFMAs and no refill waits for them.  Everything per lane is a select on a scalar lane mask:
 // both row addresses sit in scalar registers, and the choice between the row and the zero page is
 // one v_cndmask per half (written out, so that the compiler cannot turn it into a branch and push
@@ -194,25 +196,27 @@ struct MNDma {
       nid[q][1] = kidx(min(k0 + 1, lim - 1));
     }
   }
-  __device__ void issue(int s, char* dst) {
+  uint64_t src[4];  // per-lane DMA sources of the last prepare_q(q)
+  __device__ void prepare_q(int s, int q) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int lim = __builtin_amdgcn_readfirstlane(klim);
     const bool hi = lane >= 32;
     const uint64_t zero = reinterpret_cast<uint64_t>(g_zero_page) + (lane & 31) * 16;
     const uint32_t zl = (uint32_t)zero, zh = (uint32_t)(zero >> 32);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int k0 = __builtin_amdgcn_readfirstlane(s * 32 + (4 * q + w) * 2);
-      const uint64_t p0 = reinterpret_cast<uint64_t>(kptr(nid[q][0]));
-      const uint64_t p1 = reinterpret_cast<uint64_t>(kptr(nid[q][1]));
-      const uint64_t row = (hi ? p1 : p0) + off[q];
-      const uint64_t kmask = (k0 < lim ? 0x00000000FFFFFFFFull : 0ull) | (k0 + 1 < lim ? 0xFFFFFFFF00000000ull : 0ull);
-      const uint64_t m = okmask[q] & kmask;
-      uint32_t sl = (uint32_t)row, sh = (uint32_t)(row >> 32);
-      asm("v_cndmask_b32_e64 %0, %1, %0, %2" : "+v"(sl) : "v"(zl), "s"(m));
-      asm("v_cndmask_b32_e64 %0, %1, %0, %2" : "+v"(sh) : "v"(zh), "s"(m));
-      dma16(reinterpret_cast<const void*>(((uint64_t)sh << 32) | sl), dst + (4 * q + w) * 1024);
-    }
+    const int k0 = __builtin_amdgcn_readfirstlane(s * 32 + (4 * q + w) * 2);
+    const uint64_t p0 = reinterpret_cast<uint64_t>(kptr(nid[q][0]));
+    const uint64_t p1 = reinterpret_cast<uint64_t>(kptr(nid[q][1]));
+    const uint64_t row = (hi ? p1 : p0) + off[q];
+    const uint64_t kmask = (k0 < lim ? 0x00000000FFFFFFFFull : 0ull) | (k0 + 1 < lim ? 0xFFFFFFFF00000000ull : 0ull);
+    const uint64_t m = okmask[q] & kmask;
+    uint32_t sl = (uint32_t)row, sh = (uint32_t)(row >> 32);
+    asm("v_cndmask_b32_e64 %0, %1, %0, %2" : "+v"(sl) : "v"(zl), "s"(m));
+    asm("v_cndmask_b32_e64 %0, %1, %0, %2" : "+v"(sh) : "v"(zh), "s"(m));
+    src[q] = ((uint64_t)sh << 32) | sl;
+  }
+  __device__ void issue_q(int q, char* dst) const {
+    const int w = threadIdx.x >> 6;
+    dma16(reinterpret_cast<const void*>(src[q]), dst + (4 * q + w) * 1024);
   }
   __device__ static bf16x8 frag(const char* t, int mn0, int s) {
     const int lane = threadIdx.x & 63;
@@ -242,18 +246,13 @@ __device__ __forceinline__ void load_frags(const char* slot, int ks, int wm, BSu
   for (int i = 0; i < 4; ++i) F.a[i] = AL::frag(slot, wm * 128 + i * 32, ks);
 }
 
-// The 16 MFMAs of one k-step, split so that a batch of fragment reads can be issued after the
-// first one: the compiler waits for all outstanding LDS reads before an MFMA that needs
-// fragments, so reads issued after that first MFMA never delay the current k-step.
-__device__ __forceinline__ void mma_first(const FragSet& F, WaveAcc& acc) {
-  acc.c[0][0] = Mma<bf16>::mma(F.a[0], F.b[0], acc.c[0][0]);
-}
-__device__ __forceinline__ void mma_rest(const FragSet& F, WaveAcc& acc) {
+// MFMA blocks p = FROM .. TO-1 of one k-step, block p = (i, j) = (p / 4, p % 4).  Block 0 goes
+// first on its own: the compiler waits for all outstanding LDS reads before an MFMA that needs
+// fragments, so reads issued after it never delay the current k-step.
+template <int FROM, int TO>
+__device__ __forceinline__ void mma_range(const FragSet& F, WaveAcc& acc) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (i | j) acc.c[i][j] = Mma<bf16>::mma(F.a[i], F.b[j], acc.c[i][j]);
+  for (int p = FROM; p < TO; ++p) acc.c[p >> 2][p & 3] = Mma<bf16>::mma(F.a[p >> 2], F.b[p & 3], acc.c[p >> 2][p & 3]);
 }
 
 // Workgroup barrier without a memory fence (the DMA waits are explicit); the empty asm keeps the
@@ -263,44 +262,142 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// One ring step for stage s (two MFMA k-steps).  On entry F0 holds stage s's k-step 0 fragment
-// reads, issued during the previous step.
-//   1. first k-step 0 MFMA (waits for F0), then read k-step 1 into F1 and fetch the row ids of
-//      the refill stage behind the other 15;
-//   2. wait for stage s + 1 (only stage s + 2, eight DMA instructions per wave, was issued after
-//      it) and barrier: every wave is now done with stage s - 1, whose slot is refilled with
-//      stage s + 3 (past the end: the last stage again, never computed, so the DMA count per step
-//      is fixed and the waits stay exact);
-//   3. first k-step 1 MFMA (waits for F1 and the ids), then read stage s + 1's k-step 0 into F0
-//      (on the last step this reads a valid slot whose contents go unused) and issue the refill,
-//      spread over the other 15.
+// The 15 MFMA blocks p = 1..15 of a k-step in four chunks, with one piece of DMA work per
+// operand pair before each chunk, fenced so that at most one DMA instruction goes out per four
+// MFMAs: a CU takes about 64 bytes per clock of direct-to-LDS loads, and four waves issuing
+// back to back would queue behind that and hold up the MFMAs that follow them.
+//   half 1 (k-step 0): chunk c issues instruction 2 + c/2 of the previous stage's refill (A for
+//     even c, B for odd c) and prepares instruction c of the next refill stage r, once the
+//     previous source of that instruction has gone out;
+//   half 2 (k-step 1): chunk c issues instruction c/2 of stage r (A for even c, B for odd c).
+template <class AL, class BL>
+__device__ __forceinline__ void mma_half1(const FragSet& F, WaveAcc& acc, AL& la, BL& lb, int r,
+                                          char* slot) {
+  la.issue_q(2, slot);
+  la.prepare_q(r, 0);
+  lb.prepare_q(r, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_range<1, 5>(F, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  lb.issue_q(2, slot + DMA_B_OFF);
+  la.prepare_q(r, 1);
+  lb.prepare_q(r, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_range<5, 9>(F, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  la.issue_q(3, slot);
+  la.prepare_q(r, 2);
+  lb.prepare_q(r, 2);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_range<9, 13>(F, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  lb.issue_q(3, slot + DMA_B_OFF);
+  la.prepare_q(r, 3);
+  lb.prepare_q(r, 3);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_range<13, 16>(F, acc);
+  __builtin_amdgcn_sched_barrier(0);
+}
+template <class AL, class BL>
+__device__ __forceinline__ void mma_half2(const FragSet& F, WaveAcc& acc, const AL& la,
+                                          const BL& lb, char* slot) {
+  la.issue_q(0, slot);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_range<1, 5>(F, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  lb.issue_q(0, slot + DMA_B_OFF);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_range<5, 9>(F, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  la.issue_q(1, slot);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_range<9, 13>(F, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  lb.issue_q(1, slot + DMA_B_OFF);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_range<13, 16>(F, acc);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One ring step for stage s (two MFMA k-steps).  Each stage's refill is split in two halves of
+// four DMA instructions per wave (q = 0, 1 and q = 2, 3 of both operands), issued in the second
+// half of step s - 3 and the first half of step s - 2; the slot is free in both (its previous
+// stage was consumed before the barrier of step s - 3).  On entry F0 holds stage s's k-step 0
+// fragment reads, issued during the previous step, and the row ids of stage s + 3 have been
+// fetched during the previous step.
+//   1. first k-step 0 MFMA (waits for F0); read k-step 1 into F1; the other 15 MFMAs with the
+//      second half of stage s + 2's refill and the address preparation of stage s + 3;
+//   2. wait for stage s + 1 -- the DMA issued after its last instruction is stage s + 2, eight
+//      instructions per wave -- and barrier: every wave is now done with stage s - 1, whose slot
+//      takes stage s + 3 (past the end: the last stage again, never computed, so the DMA count
+//      per step is fixed and the waits stay exact);
+//   3. first k-step 1 MFMA (waits for F1); read stage s + 1's k-step 0 into F0 (on the last step
+//      this reads a valid slot whose contents go unused) and fetch the row ids of stage s + 4;
+//      the other 15 MFMAs with the first half of stage s + 3's refill.
 // The DMA issue is unconditional and its address never comes from a pointer select: a DMA under
 // a branch makes the compiler's wait tracking fall back to draining everything.  With one wave
-// per SIMD nothing else hides a stall, so sched_barrier fences and scheduling groups pin this
-// order.
+// per SIMD nothing else hides a stall, so sched_barrier fences pin this order.
 template <class AL, class BL, class BSub>
-__device__ __forceinline__ void dma_step(AL& la, BL& lb, int s, int nkt, const char* cur,
-                                         const char* next, char* refill, FragSet& F0, FragSet& F1,
-                                         WaveAcc& acc, int wm, BSub bsub) {
+__device__ __forceinline__ void dma_step_split(AL& la, BL& lb, int s, int nkt, const char* cur,
+                                               const char* next, char* half2, char* half1,
+                                               FragSet& F0, FragSet& F1, WaveAcc& acc, int wm,
+                                               BSub bsub) {
   const int r = min(s + 3, nkt - 1);
-  mma_first(F0, acc);
+  mma_range<0, 1>(F0, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  load_frags<AL, BL>(cur, 1, wm, bsub, F1);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_half1(F0, acc, la, lb, r, half2);
+  wait_vmcnt<8>();
+  ring_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  mma_range<0, 1>(F1, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  load_frags<AL, BL>(next, 0, wm, bsub, F0);
+  la.fetch(min(s + 4, nkt - 1));
+  lb.fetch(min(s + 4, nkt - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  mma_half2(F1, acc, la, lb, half1);
+}
+
+// One ring step for stage s, burst variant: the whole refill of stage s + 3 goes out in the
+// second half of step s, one DMA per MFMA, right after the barrier (three stages of prefetch
+// distance, for operands whose loads see long latency: gathered rows, MN-major tiles).
+//   1. first k-step 0 MFMA (waits for F0); read k-step 1 into F1 and fetch the row ids of stage
+//      s + 3; the other 15 MFMAs;
+//   2. wait for stage s + 1 (only stage s + 2, eight DMA instructions per wave, was issued after
+//      it) and barrier; stage s - 1's slot takes stage s + 3 (past the end: the last stage
+//      again);
+//   3. first k-step 1 MFMA (waits for F1 and the ids); read stage s + 1's k-step 0 into F0;
+//      prepare and issue the refill, spread over the other 15 MFMAs.
+template <class AL, class BL, class BSub>
+__device__ __forceinline__ void dma_step_burst(AL& la, BL& lb, int s, int nkt, const char* cur,
+                                               const char* next, char* refill, FragSet& F0,
+                                               FragSet& F1, WaveAcc& acc, int wm, BSub bsub) {
+  const int r = min(s + 3, nkt - 1);
+  mma_range<0, 1>(F0, acc);
   __builtin_amdgcn_sched_barrier(0);
   load_frags<AL, BL>(cur, 1, wm, bsub, F1);
   la.fetch(r);
   lb.fetch(r);
   __builtin_amdgcn_sched_barrier(0);
-  mma_rest(F0, acc);
+  mma_range<1, 16>(F0, acc);
   __builtin_amdgcn_sched_barrier(0);
   wait_vmcnt<8>();
   ring_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  mma_first(F1, acc);
+  mma_range<0, 1>(F1, acc);
   __builtin_amdgcn_sched_barrier(0);
   load_frags<AL, BL>(next, 0, wm, bsub, F0);
   __builtin_amdgcn_sched_barrier(0);
-  la.issue(r, refill);
-  lb.issue(r, refill + DMA_B_OFF);
-  mma_rest(F1, acc);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    la.prepare_q(r, q);
+    lb.prepare_q(r, q);
+    la.issue_q(q, refill);
+    lb.issue_q(q, refill + DMA_B_OFF);
+  }
+  mma_range<1, 16>(F1, acc);
   // spread the refill's address arithmetic and DMA issue between the 15 MFMAs
 #pragma unroll
   for (int i = 0; i < 15; ++i) {
@@ -311,34 +408,56 @@ __device__ __forceinline__ void dma_step(AL& la, BL& lb, int s, int nkt, const c
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <class AL, class BL, class BSub>
+// The bf16 main loop over nkt stages.  SPLIT selects dma_step_split (each refill in two halves,
+// one DMA per four MFMAs: for K-major operands with good cache locality) or dma_step_burst.
+template <bool SPLIT, class AL, class BL, class BSub>
 __device__ __forceinline__ void gemm_mainloop_dma(AL& la, BL& lb, int nkt, WaveAcc& acc,
                                                   LdsBufs L, int wm, BSub bsub) {
   zero_acc(acc);
   if (nkt <= 0) return;
+  // SPLIT: stages 0 and 1 whole and the first half of stage 2 (its second half goes out in
+  // step 0); burst: stages 0, 1 and 2 whole
 #pragma unroll
   for (int i = 0; i < 3; ++i) {
     const int r = min(i, nkt - 1);
     la.fetch(r);
     lb.fetch(r);
-    la.issue(r, L.b[i]);
-    lb.issue(r, L.b[i] + DMA_B_OFF);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      la.prepare_q(r, q);
+      lb.prepare_q(r, q);
+    }
+#pragma unroll
+    for (int q = 0; q < ((SPLIT && i == 2) ? 2 : 4); ++q) {
+      la.issue_q(q, L.b[i]);
+      lb.issue_q(q, L.b[i] + DMA_B_OFF);
+    }
   }
-  wait_vmcnt<16>();
-  ring_barrier();
   FragSet F0, F1;
+  if constexpr (SPLIT) {
+    la.fetch(min(3, nkt - 1));  // ids of the stage step 0 prepares
+    lb.fetch(min(3, nkt - 1));
+    wait_vmcnt<12>();  // stage 0 has landed: stage 1 (8) and half of stage 2 (4) came after it
+  } else {
+    wait_vmcnt<16>();  // stage 0 has landed: stages 1 and 2 (16) came after it
+  }
+  ring_barrier();
   load_frags<AL, BL>(L.b[0], 0, wm, bsub, F0);
+  auto step = [&](int st, char* b0, char* b1, char* b2, char* b3) {
+    if constexpr (SPLIT) dma_step_split(la, lb, st, nkt, b0, b1, b2, b3, F0, F1, acc, wm, bsub);
+    else dma_step_burst(la, lb, st, nkt, b0, b1, b3, F0, F1, acc, wm, bsub);
+  };
   int s = 0;
   for (; s + 4 <= nkt; s += 4) {  // full groups: no branches between the steps
-    dma_step(la, lb, s, nkt, L.b[0], L.b[1], L.b[3], F0, F1, acc, wm, bsub);
-    dma_step(la, lb, s + 1, nkt, L.b[1], L.b[2], L.b[0], F0, F1, acc, wm, bsub);
-    dma_step(la, lb, s + 2, nkt, L.b[2], L.b[3], L.b[1], F0, F1, acc, wm, bsub);
-    dma_step(la, lb, s + 3, nkt, L.b[3], L.b[0], L.b[2], F0, F1, acc, wm, bsub);
+    step(s, L.b[0], L.b[1], L.b[2], L.b[3]);
+    step(s + 1, L.b[1], L.b[2], L.b[3], L.b[0]);
+    step(s + 2, L.b[2], L.b[3], L.b[0], L.b[1]);
+    step(s + 3, L.b[3], L.b[0], L.b[1], L.b[2]);
   }
   // 0 to 3 remaining stages; the ring position is again at slot 0
-  if (s < nkt) dma_step(la, lb, s, nkt, L.b[0], L.b[1], L.b[3], F0, F1, acc, wm, bsub);
-  if (s + 1 < nkt) dma_step(la, lb, s + 1, nkt, L.b[1], L.b[2], L.b[0], F0, F1, acc, wm, bsub);
-  if (s + 2 < nkt) dma_step(la, lb, s + 2, nkt, L.b[2], L.b[3], L.b[1], F0, F1, acc, wm, bsub);
+  if (s < nkt) step(s, L.b[0], L.b[1], L.b[2], L.b[3]);
+  if (s + 1 < nkt) step(s + 1, L.b[1], L.b[2], L.b[3], L.b[0]);
+  if (s + 2 < nkt) step(s + 2, L.b[2], L.b[3], L.b[0], L.b[1]);
   __syncthreads();  // drains the trailing loads; the LDS is free for the epilogue
 }
 
@@ -490,10 +609,11 @@ __device__ __forceinline__ auto mn_rows_idx(KIdx kidx, KPtr kptr, int klim, int 
   }
 }
 
-template <typename T, class LA, class LB, class BSub>
+// SPLIT: see gemm_mainloop_dma (bf16 only; the fp32 path has one schedule).
+template <typename T, bool SPLIT = false, class LA, class LB, class BSub>
 __device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nkt, WaveAcc& acc, LdsBufs L, int wm,
                                               BSub bsub) {
-  if constexpr (sizeof(T) == 2) gemm_mainloop_dma(la, lb, nkt, acc, L, wm, bsub);
+  if constexpr (sizeof(T) == 2) gemm_mainloop_dma<SPLIT>(la, lb, nkt, acc, L, wm, bsub);
   else gemm_mainloop_reg(la, lb, nkt, acc, L, wm, bsub);
 }
 

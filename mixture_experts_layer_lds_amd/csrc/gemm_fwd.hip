@@ -67,7 +67,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_router(const T* __restrict_
     return n0 + i < E ? reinterpret_cast<const char*>(Wr) + (n0 + i) * rowb : nullptr;
   });
   WaveAcc acc;
-  gemm_mainloop<T>(la, lb, d / Mma<T>::BK, acc, L, wm, [&](int j) { return bsub_plain(wn, j); });
+  gemm_mainloop<T, true>(la, lb, d / Mma<T>::BK, acc, L, wm, [&](int j) { return bsub_plain(wn, j); });
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int n = n0 + bsub_plain(wn, j) + (lane & 31);
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_up(
   });
   WaveAcc acc;
   // B blocks j = 0, 1 are gate columns, j = 2, 3 the up columns of the same act columns
-  gemm_mainloop<T>(la, lb, d / Mma<T>::BK, acc, L, wm, [&](int j) { return bsub_halved(wn, j); });
+  gemm_mainloop<T, true>(la, lb, d / Mma<T>::BK, acc, L, wm, [&](int j) { return bsub_halved(wn, j); });
   const int valid = min(128, n - j0);
   if constexpr (sizeof(T) == 2) {
     auto silu_u = [&](int i, int j, int v) {
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_down(
   const char* wd = reinterpret_cast<const char*>(Wd) + (int64_t)g.e * d * rowb;
   auto lb = k_rows<T>([&](int i) -> const char* { return n0 + i < d ? wd + (int64_t)(n0 + i) * rowb : nullptr; });
   WaveAcc acc;
-  gemm_mainloop<T>(la, lb, n / Mma<T>::BK, acc, L, wm, [&](int j) { return bsub_plain(wn, j); });
+  gemm_mainloop<T, true>(la, lb, n / Mma<T>::BK, acc, L, wm, [&](int j) { return bsub_plain(wn, j); });
   const int valid = min(BN, d - n0);
   if constexpr (sizeof(T) == 2) {
     epi_stage_bf16(L, wm, [&](int j) { return bsub_plain(wn, j) + (lane & 31); },
