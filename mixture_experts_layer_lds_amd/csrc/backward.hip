@@ -60,6 +60,30 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dact(
   float* red = reinterpret_cast<float*>(L.b[0] + 64 * FROW);  // [256] dS partials of this tile
   auto frow = [&](int r) { return epi_buf(L, r) + (r & 63) * FROW; };
   const int valid = min(BN, n - n0);
+  // The block walks chunk c = row * CPR + ch in batches of UNR chunks per thread; a batch's G and
+  // U loads are all issued before any of them is used (the first batch of a half before the
+  // barrier that follows the accumulator dump), so their latency overlaps.
+  constexpr int UNR = 4;
+  constexpr int NB = 256 * CPR / (UNR * GEMM_THREADS);  // batches per half
+  static_assert(NB * UNR * GEMM_THREADS == 256 * CPR, "whole batches");
+  auto chunk_at = [&](int half, int b, int u, int& row, int& ch, int& col) {
+    const int c = (b * UNR + u) * GEMM_THREADS + threadIdx.x;
+    row = c / CPR;
+    ch = c % CPR;
+    col = half * 128 + ch * VEC;
+    return row < g.mrows && col < valid;
+  };
+  auto load_batch = [&](int half, int b, u32x4* gv, u32x4* uv) {
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      int row, ch, col;
+      if (chunk_at(half, b, u, row, ch, col)) {
+        const int64_t r = g.m0 + row;
+        gv[u] = ld16(H + r * 2 * n + n0 + col);
+        uv[u] = ld16(H + r * 2 * n + n + n0 + col);
+      }
+    }
+  };
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
 #pragma unroll
@@ -70,37 +94,42 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dact(
         for (int v = 0; v < 16; ++v)
           *reinterpret_cast<float*>(frow(acc_row(wm, i, v)) + (wn * 64 + jj * 32 + (lane & 31)) * 4) =
               acc.c[i][2 * half + jj][v];
+    u32x4 gv[UNR], uv[UNR];
+    load_batch(half, 0, gv, uv);
     __syncthreads();
-    for (int c = threadIdx.x; c < 256 * CPR; c += GEMM_THREADS) {
-      const int row = c / CPR, ch = c % CPR;
-      const int col = half * 128 + ch * VEC;   // column within the tile
-      float p = 0.0f;
-      if (row < g.mrows && col < valid) {
-        const int64_t r = g.m0 + row;
-        const float w = row_w[r];
-        float dAp[VEC], G[VEC], U[VEC], oG[VEC], oU[VEC], oA[VEC];
+    for (int b = 0; b < NB; ++b) {
+      if (b > 0) load_batch(half, b, gv, uv);
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) dAp[k] = *reinterpret_cast<const float*>(frow(row) + (ch * VEC + k) * 4);
-        unpack16<T>(ld16(H + r * 2 * n + n0 + col), G);
-        unpack16<T>(ld16(H + r * 2 * n + n + n0 + col), U);
+      for (int u = 0; u < UNR; ++u) {
+        int row, ch, col;
+        float p = 0.0f;
+        if (chunk_at(half, b, u, row, ch, col)) {
+          const int64_t r = g.m0 + row;
+          const float w = row_w[r];
+          float dAp[VEC], G[VEC], U[VEC], oG[VEC], oU[VEC], oA[VEC];
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) {
-          const float sg = sigmoid_f32(G[k]);
-          const float silu = G[k] * sg;
-          const float A = silu * U[k];
-          p += dAp[k] * A;
-          const float dA = w * dAp[k];
-          oG[k] = dA * U[k] * sg * (1.0f + G[k] * (1.0f - sg));
-          oU[k] = dA * silu;
-          oA[k] = w * A;
+          for (int k = 0; k < VEC; ++k) dAp[k] = *reinterpret_cast<const float*>(frow(row) + (ch * VEC + k) * 4);
+          unpack16<T>(gv[u], G);
+          unpack16<T>(uv[u], U);
+#pragma unroll
+          for (int k = 0; k < VEC; ++k) {
+            const float sg = sigmoid_f32(G[k]);
+            const float silu = G[k] * sg;
+            const float A = silu * U[k];
+            p += dAp[k] * A;
+            const float dA = w * dAp[k];
+            oG[k] = dA * U[k] * sg * (1.0f + G[k] * (1.0f - sg));
+            oU[k] = dA * silu;
+            oA[k] = w * A;
+          }
+          st16(dH + r * 2 * n + n0 + col, pack16<T>(oG));
+          st16(dH + r * 2 * n + n + n0 + col, pack16<T>(oU));
+          st16(wA + r * n + n0 + col, pack16<T>(oA));
         }
-        st16(dH + r * 2 * n + n0 + col, pack16<T>(oG));
-        st16(dH + r * 2 * n + n + n0 + col, pack16<T>(oU));
-        st16(wA + r * n + n0 + col, pack16<T>(oA));
-      }
 #pragma unroll
-      for (int o = 1; o < CPR; o <<= 1) p += __shfl_xor(p, o, 64);
-      if (ch == 0) red[row] = half == 0 ? p : red[row] + p;
+        for (int o = 1; o < CPR; o <<= 1) p += __shfl_xor(p, o, 64);
+        if (ch == 0) red[row] = half == 0 ? p : red[row] + p;
+      }
     }
     __syncthreads();
   }
@@ -336,8 +365,6 @@ hipError_t launch_dw_gu_gemm(const Shape& s, const PlanPtrs& p, const void* dH, 
 //   padded to E_pad columns, the operand of the router weight gradient)
 //   dX[t] = sum_r dX_perm[r] + dL_r W_r[e_r]      (rows in ascending expert order)
 // ---------------------------------------------------------------------------------------------
-constexpr int RB_MAX_E = 1024;
-
 __device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ expert_off, int E, int r) {
   int lo = 0, hi = E;  // expert_off[lo] <= r < expert_off[hi]
   while (hi - lo > 1) {
@@ -355,12 +382,15 @@ __global__ __launch_bounds__(256) void k_router_bwd(
     const float* __restrict__ dS_part, int ntiles, int64_t R_max, const T* __restrict__ dXp,
     const T* __restrict__ Wr, float* __restrict__ dS, float* __restrict__ dLogits,
     T* __restrict__ dLop, int E_pad, T* __restrict__ dX, int T_, int d, int E) {
-  __shared__ float s_dl[4][RB_MAX_E];
+  // per wave: the dense dL row [E_pad], the token's rows and their experts (at most E of each)
+  extern __shared__ char rb_lds[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T_) return;
   const int base = tok_off[t], cnt = tok_off[t + 1] - base;
-  float* sdl = s_dl[wave];
+  float* sdl = reinterpret_cast<float*>(rb_lds) + (size_t)wave * 3 * E_pad;
+  int* srow = reinterpret_cast<int*>(sdl + E_pad);
+  int* sexp = srow + E_pad;
   for (int e = lane; e < E_pad; e += 64) sdl[e] = 0.0f;
   // pass 1: s = sum_r w_r dS_r
   float part = 0.0f;
@@ -372,13 +402,16 @@ __global__ __launch_bounds__(256) void k_router_bwd(
     part += row_w[r] * ds;
   }
   const float ssum = wave_sum(part);
-  // pass 2: dL per row, dS out, dense dL row in LDS
+  // pass 2: dL per row, dS out, dense dL row in LDS; each row's expert resolved once
   for (int i = lane; i < cnt; i += 64) {
     const int r = clamp_idx(tok_row[base + i], rmax);
     float ds = 0.0f;
     for (int q = 0; q < ntiles; ++q) ds += dS_part[(int64_t)q * R_max + r];
     dS[r] = ds;
-    sdl[expert_of_row(expert_off, E, r)] = row_w[r] * (ds - ssum);
+    const int e = expert_of_row(expert_off, E, r);
+    sdl[e] = row_w[r] * (ds - ssum);
+    srow[i] = r;
+    sexp[i] = e;
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -388,52 +421,34 @@ __global__ __launch_bounds__(256) void k_router_bwd(
     if (e < E) dLogits[(int64_t)t * E + e] = v;
     if (dLop) dLop[(int64_t)t * E_pad + e] = from_f32<T>(v);
   }
-  // dX[t]: lanes own 16-byte column chunks; the token's rows are taken four at a time so that
-  // several row loads are in flight per lane.
+  // dX[t]: lanes own 16-byte column chunks; the token's rows are taken four at a time, and all
+  // their dX_perm and W_r chunks are loaded before any is used, so that several loads are in
+  // flight per lane.
   constexpr int VEC = 16 / sizeof(T);
   const int nch = d / VEC;
   for (int ch = lane; ch < nch; ch += 64) {
     float acc[VEC];
 #pragma unroll
     for (int k = 0; k < VEC; ++k) acc[k] = 0.0f;
-    int i = 0;
-    for (; i + 4 <= cnt; i += 4) {
-      u32x4 v[4];
-      int rr[4];
+    for (int i = 0; i < cnt; i += 4) {
+      u32x4 v[4], wv[4];
+      float dl[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        rr[q] = clamp_idx(tok_row[base + i + q], rmax);
-        v[q] = ld16_nt(dXp + (int64_t)rr[q] * d + ch * VEC);
+        const bool live = i + q < cnt;
+        const int r = live ? srow[i + q] : 0;
+        const int e = live ? sexp[i + q] : 0;
+        dl[q] = live ? sdl[e] : 0.0f;
+        v[q] = live ? ld16_nt(dXp + (int64_t)r * d + ch * VEC) : u32x4{0u, 0u, 0u, 0u};
+        wv[q] = (live && Wr) ? ld16(Wr + (int64_t)e * d + ch * VEC) : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        float f[VEC];
+        float f[VEC], w[VEC];
         unpack16<T>(v[q], f);
+        unpack16<T>(wv[q], w);
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) acc[k] += f[k];
-        if (Wr) {
-          const int e = expert_of_row(expert_off, E, rr[q]);
-          const float dl = sdl[e];
-          float wv[VEC];
-          unpack16<T>(ld16(Wr + (int64_t)e * d + ch * VEC), wv);
-#pragma unroll
-          for (int k = 0; k < VEC; ++k) acc[k] += dl * wv[k];
-        }
-      }
-    }
-    for (; i < cnt; ++i) {
-      const int r = clamp_idx(tok_row[base + i], rmax);
-      float f[VEC];
-      unpack16<T>(ld16_nt(dXp + (int64_t)r * d + ch * VEC), f);
-#pragma unroll
-      for (int k = 0; k < VEC; ++k) acc[k] += f[k];
-      if (Wr) {
-        const int e = expert_of_row(expert_off, E, r);
-        const float dl = sdl[e];
-        float wv[VEC];
-        unpack16<T>(ld16(Wr + (int64_t)e * d + ch * VEC), wv);
-#pragma unroll
-        for (int k = 0; k < VEC; ++k) acc[k] += dl * wv[k];
+        for (int k = 0; k < VEC; ++k) acc[k] += f[k] + dl[q] * w[k];
       }
     }
     st16(dX + (int64_t)t * d + ch * VEC, pack16<T>(acc));
@@ -444,12 +459,13 @@ hipError_t launch_router_bwd(const Shape& s, const PlanPtrs& p, const float* dS_
                              const void* dX_perm, const void* W_r, float* dS, float* dLogits,
                              void* dLop, int E_pad, void* dX, hipStream_t st) {
   const int grid = (int)cdiv(s.T, 4);
+  const size_t lds = (size_t)4 * 3 * E_pad * sizeof(float);  // <= 48 KiB for E <= 1024
   if (s.bf16)
-    k_router_bwd<bf16><<<grid, 256, 0, st>>>(p.tok_off, p.tok_row, p.expert_off, p.row_w, dS_part, ntiles,
+    k_router_bwd<bf16><<<grid, 256, lds, st>>>(p.tok_off, p.tok_row, p.expert_off, p.row_w, dS_part, ntiles,
                                              s.R_max, (const bf16*)dX_perm, (const bf16*)W_r, dS, dLogits,
                                              (bf16*)dLop, E_pad, (bf16*)dX, (int)s.T, (int)s.d, s.E);
   else
-    k_router_bwd<float><<<grid, 256, 0, st>>>(p.tok_off, p.tok_row, p.expert_off, p.row_w, dS_part, ntiles,
+    k_router_bwd<float><<<grid, 256, lds, st>>>(p.tok_off, p.tok_row, p.expert_off, p.row_w, dS_part, ntiles,
                                               s.R_max, (const float*)dX_perm, (const float*)W_r, dS, dLogits,
                                               (float*)dLop, E_pad, (float*)dX, (int)s.T, (int)s.d, s.E);
   return hipGetLastError();
