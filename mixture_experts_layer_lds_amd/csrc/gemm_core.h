@@ -662,15 +662,32 @@ __device__ __forceinline__ void epi_stage_bf16(LdsBufs L, int wm, Col col, Val v
   }
 }
 
+// Stores the staged rows 0..mrows-1, columns col0 .. col0 + ncols_valid - 1 (ncols = 128 or 256),
+// as 16-byte chunks: eight LDS reads per thread are issued before their eight stores, so the
+// stores do not each wait out an LDS read.  Streaming (non-temporal) stores: the results are
+// read back by a later kernel, not by this one.
 template <class RowPtr>
 __device__ __forceinline__ void epi_store_rows(LdsBufs L, int col0, RowPtr row_ptr, int mrows, int ncols,
                                                int ncols_valid) {
   const int cpr = ncols / 8;  // 16-byte chunks per row
-  for (int c = threadIdx.x; c < 256 * cpr; c += GEMM_THREADS) {
-    const int r = c / cpr, ch = c % cpr;
-    if (r >= mrows || ch * 8 >= ncols_valid) continue;
-    bf16* p = row_ptr(r);
-    if (p) st16(p + ch * 8, *reinterpret_cast<const u32x4*>(epi_row(L, r) + col0 * 2 + ch * 16));
+  const int total = 256 * cpr;
+  constexpr int BATCH = 8;
+  for (int c0 = threadIdx.x; c0 < total; c0 += BATCH * GEMM_THREADS) {
+    u32x4 v[BATCH];
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+      const int c = c0 + b * GEMM_THREADS;
+      const int r = c / cpr, ch = c % cpr;
+      if (c < total) v[b] = *reinterpret_cast<const u32x4*>(epi_row(L, r) + col0 * 2 + ch * 16);
+    }
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+      const int c = c0 + b * GEMM_THREADS;
+      const int r = c / cpr, ch = c % cpr;
+      if (c >= total || r >= mrows || ch * 8 >= ncols_valid) continue;
+      bf16* p = row_ptr(r);
+      if (p) st16_nt(p + ch * 8, v[b]);
+    }
   }
 }
 
