@@ -38,7 +38,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="fine_grained_7b")
-    ap.add_argument("--round-mode", type=int, default=None, help="override token rounding (0..3)")
+    ap.add_argument("--round-mode", type=int, default=None,
+                    help="override token rounding: 0 none, 1 nearest, 2 up, 3 down, 4 stochastic")
     ap.add_argument("--no-h-cache", action="store_true", help="backward recomputes [G|U] from X")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU baseline time budget")
@@ -135,7 +136,9 @@ def cpu_baseline(cfg, inp, logits, budget_s):
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
     L = logits.double().cpu().numpy()
-    plan = oracle.build_plan(L, cfg.K, round_mode=cfg.round_mode, tile_m=cfg.tile_m)
+    from mixture_experts_layer_lds_amd import workloads as wl
+    plan = oracle.build_plan(L, cfg.K, round_mode=cfg.round_mode, tile_m=cfg.tile_m,
+                             round_rand=wl.round_rand_words(inp["round_rand"]))
     X = inp["X"].double().cpu().numpy()
     dY = inp["dY"].double().cpu().numpy() if "dY" in inp else None
 
@@ -185,7 +188,8 @@ def main():
     backward = cfg.backward and not args.forward_only
     log("config", cfg)
     inp = wl.make_inputs(cfg, device="cuda", with_grad_out=backward)
-    dims = B.make_dims(cfg.T, cfg.d, cfg.n, cfg.E, cfg.K, cfg.dtype, cfg.round_mode, cfg.tile_m)
+    dims = B.make_dims(cfg.T, cfg.d, cfg.n, cfg.E, cfg.K, cfg.dtype, cfg.round_mode, cfg.tile_m,
+                       inp["round_rand"])
     dt = B.torch_dtype(dims)
     plan = B.Plan(dims)
     R_max = plan.R_max

@@ -57,14 +57,16 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 /* Token rounding (SonicMoE page, optimization 3).  Each expert's token count c is moved to a
  * multiple of tile_m: NEAREST drops r = c mod tile_m tokens when r < tile_m/2 and otherwise adds
- * tile_m - r (half a tile rounds up); UP always adds; DOWN always drops; an addition that would
- * need more than T tokens drops instead.  An expert drops its lowest-ranked members and adds its
+ * tile_m - r (half a tile rounds up); UP always adds; DOWN always drops; STOCHASTIC adds with
+ * probability r / tile_m using the caller's random words (moe_dims.round_rand), which keeps the
+ * expected count; an addition that would need more than T tokens drops instead.  An expert drops its lowest-ranked members and adds its
  * highest-ranked non-members, ranking tokens by (logit descending, token id ascending). */
 typedef enum {
   MOE_ROUND_NONE = 0,
   MOE_ROUND_NEAREST = 1,
   MOE_ROUND_UP = 2,
-  MOE_ROUND_DOWN = 3
+  MOE_ROUND_DOWN = 3,
+  MOE_ROUND_STOCHASTIC = 4
 } moe_round;
 
 /* Layer shape (host struct).
@@ -73,7 +75,12 @@ typedef enum {
  *  dtype: type of X, W_r, W_gate, W_up, W_down, dY, out, dX, dW_*, H and Y_perm.  Logits, gate
  *  weights, dS and dLogits are always fp32; accumulation is always fp32.
  *  round_mode / tile_m: token rounding (tile_m 1 .. 1024; ignored for MOE_ROUND_NONE).
- *  flags: reserved, must be 0. */
+ *  flags: reserved, must be 0.
+ *  round_rand: device array [E] of uniform 32-bit random words, read only by
+ *   MOE_ROUND_STOCHASTIC (must then be non-NULL): expert e with r = count mod tile_m != 0 rounds
+ *   up iff round_rand[e] * tile_m < r * 2^32, i.e. with probability r / tile_m, so its expected
+ *   count is unchanged (SonicMoE optimization 3 keeps the expected total); otherwise it drops r
+ *   tokens as DOWN does.  The caller draws fresh words per call; the library owns no generator. */
 typedef struct moe_dims {
   int64_t T;
   int64_t d;
@@ -84,6 +91,7 @@ typedef struct moe_dims {
   int32_t round_mode;
   int32_t tile_m;
   int32_t flags;
+  const uint32_t* round_rand;
 } moe_dims;
 
 /* The routing plan: device arrays the caller allocates with the sizes given here, written by

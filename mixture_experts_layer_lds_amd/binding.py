@@ -15,7 +15,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 
 MOE_F32, MOE_BF16 = 0, 1
-ROUND_NONE, ROUND_NEAREST, ROUND_UP, ROUND_DOWN = 0, 1, 2, 3
+ROUND_NONE, ROUND_NEAREST, ROUND_UP, ROUND_DOWN, ROUND_STOCHASTIC = 0, 1, 2, 3, 4
 OP_ROUTE, OP_PERMUTE, OP_FFN, OP_COMBINE, OP_FORWARD, OP_BACKWARD = range(6)
 STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ENOTSUP", -3: "MOE_EWORKSPACE", -4: "MOE_EHIP"}
 
@@ -36,7 +36,7 @@ class Dims(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int64), ("n", ctypes.c_int64),
                 ("E", ctypes.c_int32), ("K", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("round_mode", ctypes.c_int32), ("tile_m", ctypes.c_int32),
-                ("flags", ctypes.c_int32)]
+                ("flags", ctypes.c_int32), ("round_rand", ctypes.c_void_p)]
 
 
 PLAN_FIELDS = ["topk_idx", "topk_w", "counts", "expert_off", "row_token", "row_w", "tok_off",
@@ -83,9 +83,12 @@ def lib():
     return _lib
 
 
-def make_dims(T, d, n, E, K, dtype="bf16", round_mode=ROUND_NONE, tile_m=128):
+def make_dims(T, d, n, E, K, dtype="bf16", round_mode=ROUND_NONE, tile_m=128, round_rand=None):
+    """Layer shape; ``round_rand`` is the [E] int32/uint32 device tensor of random words that
+    stochastic token rounding reads (the caller keeps it alive while the dims are used)."""
     dt = {"bf16": MOE_BF16, "f32": MOE_F32, torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}[dtype]
-    return Dims(int(T), int(d), int(n), int(E), int(K), dt, int(round_mode), int(tile_m), 0)
+    return Dims(int(T), int(d), int(n), int(E), int(K), dt, int(round_mode), int(tile_m), 0,
+                _p(round_rand))
 
 
 def torch_dtype(dims):

@@ -33,7 +33,7 @@ struct Shape {
 // ---- routing (route.hip) ----
 size_t route_workspace_bytes(int64_t T, int E);
 hipError_t launch_route(const float* logits, int64_t T, int E, int K, int round_mode, int tile_m,
-                        const PlanPtrs& p, void* ws, hipStream_t st);
+                        const uint32_t* round_rand, const PlanPtrs& p, void* ws, hipStream_t st);
 
 // ---- grouped GEMM tile schedule (gemm.hip) ----
 // mtile_off[E+1] = exclusive scan over experts of ceil(counts[e] / 128).

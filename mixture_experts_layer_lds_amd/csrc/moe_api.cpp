@@ -94,8 +94,10 @@ moe_status check_dims(const moe_dims* dm) {
   if (dm->d % 64 || dm->n % 64)
     return fail(MOE_ENOTSUP, "d=%lld and n=%lld must be multiples of 64", (long long)dm->d, (long long)dm->n);
   if (dm->dtype != MOE_F32 && dm->dtype != MOE_BF16) return fail(MOE_ENOTSUP, "dtype %d not supported", dm->dtype);
-  if (dm->round_mode < MOE_ROUND_NONE || dm->round_mode > MOE_ROUND_DOWN)
+  if (dm->round_mode < MOE_ROUND_NONE || dm->round_mode > MOE_ROUND_STOCHASTIC)
     return fail(MOE_EINVAL, "round_mode %d invalid", dm->round_mode);
+  if (dm->round_mode == MOE_ROUND_STOCHASTIC && !dm->round_rand)
+    return fail(MOE_EINVAL, "MOE_ROUND_STOCHASTIC needs round_rand");
   if (dm->round_mode != MOE_ROUND_NONE && (dm->tile_m < 1 || dm->tile_m > 1024))
     return fail(MOE_EINVAL, "tile_m=%d out of range [1, 1024]", dm->tile_m);
   if (dm->flags != 0) return fail(MOE_EINVAL, "flags must be 0");
@@ -232,7 +234,8 @@ moe_status do_route(const moe_dims* dm, const void* X, const void* W_r, const fl
   const Shape s = shape_of(dm);
   if (X) MOE_STAGE(MOE_STAGE_ROUTER_GEMM, st, launch_router_gemm(s, X, W_r, bias, logits, st), "router GEMM");
   MOE_STAGE(MOE_STAGE_ROUTE, st,
-            launch_route(logits, dm->T, dm->E, dm->K, dm->round_mode, dm->tile_m, plan_ptrs(plan), ws, st),
+            launch_route(logits, dm->T, dm->E, dm->K, dm->round_mode, dm->tile_m, dm->round_rand,
+                         plan_ptrs(plan), ws, st),
             "routing");
   return MOE_OK;
 }

@@ -132,7 +132,9 @@ __global__ __launch_bounds__(256) void k_count(const uint32_t* __restrict__ bits
 }
 
 // ---------------------------------------------------------------------------------------------
-// Token rounding, one 1024-thread block per expert.
+// Token rounding, one 1024-thread block per expert.  Direction: NEAREST adds when 2r >= M, UP
+// always, DOWN never, STOCHASTIC when the expert's caller-drawn word w satisfies w M < r 2^32
+// (probability r / M: the expected count stays c); an addition past T tokens drops instead.
 // Key of token t for expert e, larger = chosen first:
 //   adding  (best non-members): (ord(L[t,e]) << 32) | ~t      -> larger logit, then lower t
 //   dropping (worst members):   (~ord(L[t,e]) << 32) | t      -> smaller logit, then higher t
@@ -154,6 +156,7 @@ __host__ __device__ __forceinline__ size_t tr_lds_bytes(int64_t T, int W) {
 
 __global__ __launch_bounds__(TR_THREADS) void k_token_round(const float* __restrict__ logits, int T,
                                                            int E, int W, int M, int mode,
+                                                           const uint32_t* __restrict__ round_rand,
                                                            uint32_t* __restrict__ bits,
                                                            const int32_t* __restrict__ counts) {
   extern __shared__ uint32_t s_dyn[];  // cached: [T] logit keys, then [W] bitmap words
@@ -170,6 +173,7 @@ __global__ __launch_bounds__(TR_THREADS) void k_token_round(const float* __restr
   bool add;
   if (mode == 1) add = 2 * r >= M;
   else if (mode == 2) add = true;
+  else if (mode == 4) add = (uint64_t)round_rand[e] * (uint64_t)M < ((uint64_t)r << 32);  // P = r / M
   else add = false;
   if (add && (int64_t)c + (M - r) > T) add = false;
   const int amount = add ? (M - r) : r;
@@ -473,7 +477,7 @@ size_t route_workspace_bytes(int64_t T, int E) {
 }
 
 hipError_t launch_route(const float* logits, int64_t T, int E, int K, int round_mode, int tile_m,
-                        const PlanPtrs& p, void* ws, hipStream_t st) {
+                        const uint32_t* round_rand, const PlanPtrs& p, void* ws, hipStream_t st) {
   const int W = (int)cdiv(T, 32);
   uint32_t* bits = static_cast<uint32_t*>(ws);
   int32_t* wprefix = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + align_up((size_t)E * W * 4, 256));
@@ -495,7 +499,8 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int K, int round_
                                               hipFuncAttributeMaxDynamicSharedMemorySize,
                                               (int)tr_lds_bytes(TR_LDS_TOKENS, TR_LDS_TOKENS / 32));
     if (ae != hipSuccess) return ae;
-    k_token_round<<<E, TR_THREADS, tr_lds, st>>>(logits, (int)T, E, W, tile_m, round_mode, bits, p.counts);
+    k_token_round<<<E, TR_THREADS, tr_lds, st>>>(logits, (int)T, E, W, tile_m, round_mode, round_rand, bits,
+                                                 p.counts);
     k_count<<<E, 256, 0, st>>>(bits, W, wprefix, p.counts);
   }
   k_offsets<<<1, 1024, 0, st>>>(p.counts, E, p.expert_off, p.meta);

@@ -25,7 +25,7 @@ import math
 
 import torch
 
-TENSOR_IDS = dict(X=0, W_r=1, W_gate=2, W_up=3, W_down=4, dY=5, bias=6, perm=7)
+TENSOR_IDS = dict(X=0, W_r=1, W_gate=2, W_up=3, W_down=4, dY=5, bias=6, perm=7, round_rand=8)
 
 
 @dataclass(frozen=True)
@@ -39,7 +39,7 @@ class LayerShape:
     dtype: str            # "f32" or "bf16"
     bias: str = "none"    # "none" | "normal" | "zipf"
     backward: bool = False
-    round_mode: int = 0   # 0 none, 1 nearest, 2 up, 3 down
+    round_mode: int = 0   # 0 none, 1 nearest, 2 up, 3 down, 4 stochastic
     tile_m: int = 128
     index: int = 0        # seed namespace
 
@@ -113,7 +113,21 @@ def make_inputs(cfg, device="cpu", with_grad_out=None):
     )
     if with_grad_out if with_grad_out is not None else cfg.backward:
         inp["dY"] = _normal(cfg, "dY", (T, d), 1.0, device, chunk_t)
+    inp["round_rand"] = make_round_rand(cfg, device)
     return inp
+
+
+def make_round_rand(cfg, device="cpu"):
+    """[E] uniform 32-bit random words (stored as int32 bit patterns) for stochastic token
+    rounding; drawn like every other input, from the layer's seed namespace."""
+    g = _gen(cfg, "round_rand", device)
+    w = torch.randint(0, 1 << 32, (cfg.E,), generator=g, device=device, dtype=torch.int64)
+    return (w - (w >= (1 << 31)).to(torch.int64) * (1 << 32)).to(torch.int32)
+
+
+def round_rand_words(t):
+    """The words of a make_round_rand tensor as numpy uint32 (for the CPU side)."""
+    return t.cpu().numpy().view("uint32")
 
 
 def small_shape(T, d, E, K, n, dtype="bf16", bias="none", backward=True, round_mode=0,

@@ -13,7 +13,7 @@ sent to, ``w_{t,e}`` its gate weights.  Rows of the permuted (expert-major) layo
 
 import numpy as np
 
-ROUND_NONE, ROUND_NEAREST, ROUND_UP, ROUND_DOWN = 0, 1, 2, 3
+ROUND_NONE, ROUND_NEAREST, ROUND_UP, ROUND_DOWN, ROUND_STOCHASTIC = 0, 1, 2, 3, 4
 
 
 # ----------------------------------------------------------------------------------------------
@@ -62,8 +62,12 @@ def plain_topk_weights(L, topk_idx):
     return ex / ex.sum(axis=1, keepdims=True)
 
 
-def _round_adds(c, M, mode, T):
-    """Decide, for one expert with c tokens, whether token rounding adds or drops tokens."""
+def _round_adds(c, M, mode, T, word=None):
+    """Decide, for one expert with c tokens, whether token rounding adds or drops tokens.
+
+    ``word`` is the expert's uniform 32-bit random word (stochastic mode only): with u = word / 2^32
+    the expert rounds up iff u < r / M, i.e. with probability r / M, which keeps the expected count
+    at c.  The comparison is done in integers (word * M < r * 2^32), so it is exact."""
     r = c % M
     if r == 0:
         return None, 0
@@ -73,6 +77,8 @@ def _round_adds(c, M, mode, T):
         add = True
     elif mode == ROUND_DOWN:
         add = False
+    elif mode == ROUND_STOCHASTIC:
+        add = int(word) * M < r * (1 << 32)
     else:
         raise ValueError("unknown rounding mode %r" % (mode,))
     if add and c + (M - r) > T:   # cannot add more tokens than exist: round down instead
@@ -80,7 +86,7 @@ def _round_adds(c, M, mode, T):
     return add, (M - r) if add else r
 
 
-def token_rounding(L, sel, M, mode):
+def token_rounding(L, sel, M, mode, round_rand=None):
     """Token rounding of per-expert token counts to multiples of the tile M.
 
     SonicMoE summary page, optimization 3 ("Token Rounding 路由算法"): each expert's token count
@@ -93,6 +99,9 @@ def token_rounding(L, sel, M, mode):
     * c = tokens the expert received from plain top-K, r = c mod M;
     * NEAREST: drop r tokens if r < M/2, otherwise add M - r (so half a tile rounds up);
       UP always adds M - r; DOWN always drops r; nothing changes when r = 0;
+    * STOCHASTIC (the one reading under which the expected total is literally kept): add M - r
+      with probability r / M, else drop r, decided by the caller's uniform 32-bit word
+      ``round_rand[e]`` (see ``_round_adds``);
     * an addition that would need more than T tokens drops instead;
     * an expert ranks all T tokens by (L[t, e] descending, t ascending); it drops its r
       lowest-ranked members and adds its M - r highest-ranked non-members.
@@ -105,7 +114,8 @@ def token_rounding(L, sel, M, mode):
     t_ids = np.arange(T)
     for e in range(E):
         member = out[:, e].copy()
-        add, amount = _round_adds(int(member.sum()), M, mode, T)
+        word = None if round_rand is None else int(np.uint32(round_rand[e]))
+        add, amount = _round_adds(int(member.sum()), M, mode, T, word)
         if add is None:
             continue
         # Expert e's preference over tokens: larger logit first, then lower token id.
@@ -140,7 +150,7 @@ def gate_weights(L, sel):
     return W
 
 
-def build_plan(L, K, round_mode=ROUND_NONE, tile_m=128):
+def build_plan(L, K, round_mode=ROUND_NONE, tile_m=128, round_rand=None):
     """Routing plan: selection, optional token rounding, counts, offsets and permutation.
 
     Per-expert counts and their exclusive prefix sum give each expert one contiguous segment of
@@ -164,7 +174,7 @@ def build_plan(L, K, round_mode=ROUND_NONE, tile_m=128):
     sel = np.zeros((T, E), dtype=bool)
     np.put_along_axis(sel, topk_idx, True, axis=1)
     if round_mode != ROUND_NONE:
-        sel = token_rounding(L, sel, tile_m, round_mode)
+        sel = token_rounding(L, sel, tile_m, round_mode, round_rand)
     weights = gate_weights(L, sel)
 
     counts = sel.sum(axis=0).astype(np.int64)

@@ -46,8 +46,8 @@ class LazyExperts:
         return self.t.shape[0]
 
 
-def dims_of(cfg):
-    return B.make_dims(cfg.T, cfg.d, cfg.n, cfg.E, cfg.K, cfg.dtype, cfg.round_mode, cfg.tile_m)
+def dims_of(cfg, round_rand=None):
+    return B.make_dims(cfg.T, cfg.d, cfg.n, cfg.E, cfg.K, cfg.dtype, cfg.round_mode, cfg.tile_m, round_rand)
 
 
 def run_gpu(cfg, inputs=None, backward=None, cache_h=True, with_router_grad=True):
@@ -55,7 +55,7 @@ def run_gpu(cfg, inputs=None, backward=None, cache_h=True, with_router_grad=True
     dev = "cuda"
     inp = inputs if inputs is not None else wl.make_inputs(cfg, device=dev)
     backward = cfg.backward if backward is None else backward
-    dims = dims_of(cfg)
+    dims = dims_of(cfg, inp["round_rand"])
     dt = B.torch_dtype(dims)
     plan = B.Plan(dims, dev)
     R_max = plan.R_max
@@ -82,11 +82,15 @@ def run_gpu(cfg, inputs=None, backward=None, cache_h=True, with_router_grad=True
     return res
 
 
-def check_routing(cfg, res, L=None):
-    """Routing outputs bit-exact against the oracle run on the GPU's fp32 logits."""
+def check_routing(cfg, res, L=None, round_rand=None):
+    """Routing outputs bit-exact against the oracle run on the GPU's fp32 logits (and, for
+    stochastic token rounding, the same random words)."""
     if L is None:
         L = f64(res["logits"])
-    ref = oracle.build_plan(L, cfg.K, round_mode=cfg.round_mode, tile_m=cfg.tile_m)
+    if round_rand is None and "inputs" in res:
+        round_rand = res["inputs"]["round_rand"]
+    words = wl.round_rand_words(round_rand) if round_rand is not None else None
+    ref = oracle.build_plan(L, cfg.K, round_mode=cfg.round_mode, tile_m=cfg.tile_m, round_rand=words)
     got = res["plan"].to_host()
     T, K = cfg.T, cfg.K
     assert np.array_equal(got["topk_idx"].reshape(T, K), ref["topk_idx"]), "topk_idx"

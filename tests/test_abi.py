@@ -67,7 +67,7 @@ def test_workspace_sizes():
     (dict(K=9), -1), (dict(K=0), -1), (dict(E=0, K=1), -1), (dict(E=2000), -1),
     (dict(E=32, K=17), -2), (dict(d=96), -2), (dict(n=100), -2), (dict(d=32), -1), (dict(T=0), -1),
     (dict(dtype="f32", round_mode=7), -1), (dict(round_mode=1, tile_m=0), -1),
-    (dict(round_mode=1, tile_m=4096), -1),
+    (dict(round_mode=1, tile_m=4096), -1), (dict(round_mode=4), -1),
 ])
 def test_invalid_dims_rejected(lib, kw, status):
     d = dims(**kw)
@@ -76,6 +76,15 @@ def test_invalid_dims_rejected(lib, kw, status):
     assert r == status, lib.moe_last_error()
     assert lib.moe_last_error()
     assert B.lib().moe_max_rows(ctypes.byref(d)) == 0
+
+
+def test_stochastic_rounding_needs_words():
+    """MOE_ROUND_STOCHASTIC is valid once round_rand points at the caller's words (it may add up
+    to tile_m - 1 rows per expert, like NEAREST and UP)."""
+    d = dims(round_mode=4)
+    assert B.lib().moe_max_rows(ctypes.byref(d)) == 0
+    d.round_rand = FAKE
+    assert B.lib().moe_max_rows(ctypes.byref(d)) == B.lib().moe_max_rows(ctypes.byref(dims(round_mode=2)))
 
 
 def test_null_and_misaligned_pointers_rejected(lib):

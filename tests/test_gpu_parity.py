@@ -58,6 +58,7 @@ def test_ragged_multi_tile(shape):
 
 @pytest.mark.parametrize("mode,tile_m,dtype", [
     (1, 128, "f32"), (1, 32, "bf16"), (2, 16, "bf16"), (3, 64, "f32"), (2, 128, "f32"), (3, 8, "bf16"),
+    (4, 128, "bf16"), (4, 16, "f32"),
 ])
 def test_token_rounding_layer(mode, tile_m, dtype):
     cfg = wl.small_shape(T=900, d=128, E=6, K=2, n=128, dtype=dtype, bias="zipf", round_mode=mode,
@@ -100,7 +101,7 @@ def test_recompute_equals_cached_and_determinism():
     assert torch.equal(a["dS"][:R], b["dS"][:R])
 
 
-@pytest.mark.parametrize("mode", [0, 1, 2, 3])
+@pytest.mark.parametrize("mode", [0, 1, 2, 3, 4])
 def test_route_from_given_logits_with_ties(mode):
     """Caller-supplied logits with many exact ties (and -0.0): selection and indices bit-exact."""
     T, E, K = 777, 40, 5
@@ -109,13 +110,14 @@ def test_route_from_given_logits_with_ties(mode):
     L[::7] = 0.0
     L[3::11, ::2] = -0.0
     cfg = wl.small_shape(T=T, d=64, E=E, K=K, n=64, dtype="f32", round_mode=mode, tile_m=16)
-    dims = B.make_dims(T, 64, 64, E, K, "f32", mode, 16)
+    rr = wl.make_round_rand(cfg, "cuda")
+    dims = B.make_dims(T, 64, 64, E, K, "f32", mode, 16, rr)
     plan = B.Plan(dims)
     logits = L.cuda()
     ws, nb = B.workspace(dims, B.OP_ROUTE)
     B.moe_route(dims, None, None, None, logits, plan, ws, nb)
     torch.cuda.synchronize()
-    check_routing(cfg, dict(plan=plan), L=L.double().numpy())
+    check_routing(cfg, dict(plan=plan), L=L.double().numpy(), round_rand=rr)
 
 
 def test_permute_packed_ffn_and_combine():

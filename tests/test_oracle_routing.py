@@ -123,8 +123,11 @@ def pref_rank(col):
                      for t in range(T)])
 
 
-def brute_round_expert(col, member, M, mode, T):
-    """Exhaustive token rounding for one expert: target count, then best subset by enumeration."""
+def brute_round_expert(col, member, M, mode, T, word=None):
+    """Exhaustive token rounding for one expert: target count, then best subset by enumeration.
+    Stochastic mode: round up iff the word, read as the exact fraction word / 2^32, is below
+    (c mod M) / M."""
+    from fractions import Fraction
     c = int(member.sum())
     lower, upper = (c // M) * M, (c // M) * M + M
     if c % M == 0:
@@ -133,6 +136,8 @@ def brute_round_expert(col, member, M, mode, T):
         target = upper if 2 * (c - lower) >= M else lower
     elif mode == 2:
         target = upper
+    elif mode == 4:
+        target = upper if Fraction(int(word), 2 ** 32) < Fraction(c - lower, M) else lower
     else:
         target = lower
     if target > T:
@@ -150,7 +155,7 @@ def brute_round_expert(col, member, M, mode, T):
     return new, target
 
 
-@pytest.mark.parametrize("mode", [1, 2, 3])
+@pytest.mark.parametrize("mode", [1, 2, 3, 4])
 @pytest.mark.parametrize("M", [2, 3, 4])
 @pytest.mark.parametrize("seed", range(4))
 def test_token_rounding_matches_enumeration(mode, M, seed):
@@ -159,9 +164,10 @@ def test_token_rounding_matches_enumeration(mode, M, seed):
     L = rng.integers(-2, 3, size=(T, E)).astype(np.float64)    # ties on purpose
     sel = np.zeros((T, E), bool)
     np.put_along_axis(sel, oracle.topk_select(L, K), True, axis=1)
-    got = oracle.token_rounding(L, sel, M, mode)
+    words = rng.integers(0, 2 ** 32, size=E, dtype=np.uint64).astype(np.uint32)
+    got = oracle.token_rounding(L, sel, M, mode, words if mode == 4 else None)
     for e in range(E):
-        exp_col, target = brute_round_expert(L[:, e], sel[:, e], M, mode, T)
+        exp_col, target = brute_round_expert(L[:, e], sel[:, e], M, mode, T, words[e])
         assert np.array_equal(got[:, e], exp_col), (e, L[:, e], sel[:, e], got[:, e], exp_col)
         c, c2 = int(sel[:, e].sum()), int(got[:, e].sum())
         assert c2 == target
@@ -211,3 +217,45 @@ def test_kimi_scale_rounding_statistics():
                 assert m_plain[changed].all()
                 kept_after = np.nonzero(m_tr)[0]
                 assert len(kept_after) == 0 or kept_after.max() < changed.min()
+
+
+def test_stochastic_rounding_limits_and_threshold():
+    """Word 0 rounds every partial expert up (as UP), the largest word rounds every one down (as
+    DOWN); the switch sits exactly at word = ceil(r * 2^32 / M)."""
+    rng = np.random.default_rng(21)
+    T, E, K, M = 200, 12, 3, 16
+    L = rng.normal(size=(T, E))
+    up = oracle.build_plan(L, K, round_mode=2, tile_m=M)
+    down = oracle.build_plan(L, K, round_mode=3, tile_m=M)
+    zero = oracle.build_plan(L, K, round_mode=4, tile_m=M, round_rand=np.zeros(E, np.uint32))
+    full = oracle.build_plan(L, K, round_mode=4, tile_m=M, round_rand=np.full(E, 2 ** 32 - 1, np.uint32))
+    assert np.array_equal(zero["sel"], up["sel"]) and np.array_equal(full["sel"], down["sel"])
+    plain = oracle.build_plan(L, K)
+    for e in range(E):
+        r = int(plain["counts"][e]) % M
+        if r == 0:
+            continue
+        edge = -(-(r << 32) // M)          # smallest word that no longer rounds up
+        words = np.zeros(E, np.uint32)
+        for w, expect_up in ((edge - 1, True), (edge, False)):
+            words[e] = w
+            got = oracle.build_plan(L, K, round_mode=4, tile_m=M, round_rand=words)["counts"][e]
+            assert got == (plain["counts"][e] - r + (M if expect_up else 0)), (e, r, w)
+
+
+def test_stochastic_rounding_keeps_expected_counts():
+    """Over independent words, each expert's mean rounded count matches its plain count (the
+    SonicMoE page's claim that the expected total is kept): within 4 standard errors."""
+    rng = np.random.default_rng(22)
+    T, E, K, M = 300, 10, 2, 32
+    L = rng.normal(size=(T, E))
+    plain = oracle.build_plan(L, K)["counts"].astype(np.float64)
+    n = 600
+    acc = np.zeros(E)
+    for _ in range(n):
+        words = rng.integers(0, 2 ** 32, size=E, dtype=np.uint64).astype(np.uint32)
+        acc += oracle.build_plan(L, K, round_mode=4, tile_m=M, round_rand=words)["counts"]
+    mean = acc / n
+    r = plain % M
+    se = M * np.sqrt((r / M) * (1 - r / M) / n) + 1e-9
+    assert np.all(np.abs(mean - plain) <= 4 * se + 1e-9), (mean, plain)
