@@ -239,9 +239,17 @@ def main():
     torch.cuda.synchronize()
     total_ms = ev0.elapsed_time(ev1)
     stages = {s: B.moe_timing_read(s) for s in B.STAGES}
-    B.moe_timing_enable(False)
     ms_step = total_ms / args.steps
     log("timed %d steps: %.3f ms/step" % (args.steps, ms_step))
+    # the packed-mode permute is not part of the step (the step gathers inside the GEMM); it is
+    # timed on its own afterwards, with the same plan, as the materialised-dispatch reference
+    X_perm = torch.empty(R_max, cfg.d, dtype=dt, device="cuda")
+    for i in range(args.steps):
+        B.moe_permute(dims, plan, inp["X"], X_perm)
+    torch.cuda.synchronize()
+    stages["permute"] = B.moe_timing_read("permute")
+    B.moe_timing_enable(False)
+    del X_perm
 
     T, d, n, E = cfg.T, cfg.d, cfg.n, cfg.E
     es = 2 if cfg.dtype == "bf16" else 4
@@ -271,7 +279,10 @@ def main():
             ent["pct_hbm"] = round(100 * b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 1)
         breakdown[s] = ent
     gemm_stages = [s for s in breakdown if stage_flops(s, R, T, d, n, E)]
-    modelled = [s for s in breakdown if stage_flops(s, R, T, d, n, E) or stage_bytes(s, R, T, d, n, E, es, cfg.K)]
+    if "permute" in breakdown:
+        breakdown["permute"]["in_step"] = False
+    modelled = [s for s in breakdown if s != "permute" and
+                (stage_flops(s, R, T, d, n, E) or stage_bytes(s, R, T, d, n, E, es, cfg.K))]
     dom = max(modelled, key=lambda s: breakdown[s]["ms_per_step"])
     if stage_flops(dom, R, T, d, n, E):
         avg = breakdown[dom]["avg_ms"]

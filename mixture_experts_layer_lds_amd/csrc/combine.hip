@@ -36,8 +36,10 @@ hipError_t launch_permute(const Shape& s, const PlanPtrs& p, const void* X, void
   return hipGetLastError();
 }
 
-// out[t] = sum_{r in rows(t)} w_r Y[r].  Lanes own 16-byte column chunks; up to 4 rows are
-// loaded before they are accumulated so that several loads are in flight per lane.
+// out[t] = sum_{r in rows(t)} w_r Y[r].  Lanes own 16-byte column chunks; up to RB rows (a
+// token's K = 8 rows at once in the common case) are loaded before they are accumulated so that
+// several loads are in flight per lane.
+constexpr int RB = 8;
 template <typename T, bool WEIGHTED>
 __global__ __launch_bounds__(256) void k_combine(const int32_t* __restrict__ tok_off,
                                                  const int32_t* __restrict__ tok_row,
@@ -55,17 +57,17 @@ __global__ __launch_bounds__(256) void k_combine(const int32_t* __restrict__ tok
 #pragma unroll
     for (int k = 0; k < VEC; ++k) acc[k] = 0.0f;
     int i = 0;
-    for (; i + 4 <= cnt; i += 4) {
-      u32x4 v[4];
-      float w[4];
+    for (; i + RB <= cnt; i += RB) {
+      u32x4 v[RB];
+      float w[RB];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < RB; ++q) {
         const int r = clamp_idx(tok_row[base + i + q], rmax);
         v[q] = ld16_nt(Y + (int64_t)r * d + c * VEC);
         w[q] = WEIGHTED ? row_w[r] : 1.0f;
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < RB; ++q) {
         float f[VEC];
         unpack16<T>(v[q], f);
 #pragma unroll
