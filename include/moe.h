@@ -127,7 +127,8 @@ enum {
   MOE_OP_FFN = 2,
   MOE_OP_COMBINE = 3,
   MOE_OP_FORWARD = 4,
-  MOE_OP_BACKWARD = 5
+  MOE_OP_BACKWARD = 5,
+  MOE_OP_DECODE = 6
 };
 
 /* Host: upper bound on R for these dims (T*K without rounding; rounding can add at most
@@ -207,6 +208,25 @@ moe_status moe_backward(const moe_dims* dims, const void* dY, const void* X, con
                         void* dW_up, void* dW_down, float* dS, float* dLogits, void* dW_r,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* moe_decode — the whole forward layer in one kernel launch, for small token counts (decode /
+ * inference): router logits, top-K with softmax, the selected experts' SwiGLU FFNs and the
+ * weighted combine.  apxml.com "自定义核与核融合" (the five steps fused into one kernel) and
+ * "条件参数加载" (only the selected experts' weights are read).  Plain top-K only
+ * (round_mode must be MOE_ROUND_NONE, else MOE_ENOTSUP); T <= 1024.  The launch is cooperative:
+ * every workgroup of the grid is resident at once and the phases are separated by grid-wide
+ * barriers, so the call fails with MOE_EHIP rather than run if the device cannot host the grid.
+ * Results equal moe_forward's up to rounding: the SwiGLU activation stays in fp32 between the
+ * two projections (moe_forward rounds it to dtype), and the per-row dot products accumulate in
+ * another order.
+ *  X [T,d], W_r [E,d], bias [E] fp32 or NULL, W_gate/W_up [E,n,d], W_down [E,d,n] dtype.
+ *  Outputs (overwritten): logits [T,E] fp32, topk_idx [T,K] int32, topk_w [T,K] fp32 (as in the
+ *  plan of moe_route), out [T,d] dtype.
+ *  ws: moe_workspace_bytes(dims, MOE_OP_DECODE) bytes (token lists and fp32 intermediates). */
+moe_status moe_decode(const moe_dims* dims, const void* X, const void* W_r, const float* bias,
+                      const void* W_gate, const void* W_up, const void* W_down, float* logits,
+                      int32_t* topk_idx, float* topk_w, void* out, void* ws, size_t ws_bytes,
+                      void* stream);
+
 /* Stages of the layer, for the timing facility below.  Each stage is one kernel, except ROUTE
  * (top-K, counts, token rounding, offsets, placement) and DWR_GEMM (GEMM + slice reduction). */
 typedef enum {
@@ -223,7 +243,8 @@ typedef enum {
   MOE_STAGE_DX_GEMM = 10,
   MOE_STAGE_ROUTER_BWD = 11, /* dS, dLogits and the dX gather-sum */
   MOE_STAGE_DWR_GEMM = 12,
-  MOE_STAGE_COUNT = 13
+  MOE_STAGE_DECODE = 13,     /* the single-launch forward of moe_decode */
+  MOE_STAGE_COUNT = 14
 } moe_stage;
 
 /* Host: stage timing for measurement tools (not thread-safe; for a single host thread).

@@ -16,14 +16,14 @@ LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 
 MOE_F32, MOE_BF16 = 0, 1
 ROUND_NONE, ROUND_NEAREST, ROUND_UP, ROUND_DOWN, ROUND_STOCHASTIC = 0, 1, 2, 3, 4
-OP_ROUTE, OP_PERMUTE, OP_FFN, OP_COMBINE, OP_FORWARD, OP_BACKWARD = range(6)
+OP_ROUTE, OP_PERMUTE, OP_FFN, OP_COMBINE, OP_FORWARD, OP_BACKWARD, OP_DECODE = range(7)
 STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ENOTSUP", -3: "MOE_EWORKSPACE", -4: "MOE_EHIP"}
 
 EXPORTS = ["moe_max_rows", "moe_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_ffn",
-           "moe_combine", "moe_forward", "moe_backward", "moe_status_string", "moe_last_error",
+           "moe_combine", "moe_forward", "moe_backward", "moe_decode", "moe_status_string", "moe_last_error",
            "moe_version", "moe_timing_enable", "moe_timing_read"]
 STAGES = ["router_gemm", "route", "tiles", "up_gemm", "down_gemm", "permute", "combine", "dact_gemm",
-          "dw_down_gemm", "dw_gu_gemm", "dx_gemm", "router_bwd", "dwr_gemm"]
+          "dw_down_gemm", "dw_gu_gemm", "dx_gemm", "router_bwd", "dwr_gemm", "decode"]
 
 
 class MoEError(RuntimeError):
@@ -70,8 +70,9 @@ def lib():
         L.moe_forward.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, pp, vp, vp, vp, sz, vp]
         L.moe_backward.argtypes = [pd, vp, vp, vp, vp, vp, vp, pp, vp, vp, vp, vp, vp, vp, vp, vp,
                                    vp, sz, vp]
+        L.moe_decode.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         for f in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward",
-                  "moe_backward"):
+                  "moe_backward", "moe_decode"):
             getattr(L, f).restype = st
         L.moe_status_string.argtypes, L.moe_status_string.restype = [ctypes.c_int], ctypes.c_char_p
         L.moe_last_error.argtypes, L.moe_last_error.restype = [], ctypes.c_char_p
@@ -187,6 +188,13 @@ def moe_forward(dims, X, W_r, bias, W_gate, W_up, W_down, logits, plan, H_cache,
     _check(lib().moe_forward(ctypes.byref(dims), _p(X), _p(W_r), _p(bias), _p(W_gate), _p(W_up),
                              _p(W_down), _p(logits), plan.ref(), _p(H_cache), _p(out), _p(ws), ws_bytes,
                              _stream(stream)))
+
+
+def moe_decode(dims, X, W_r, bias, W_gate, W_up, W_down, logits, topk_idx, topk_w, out, ws, ws_bytes,
+               stream=None):
+    _check(lib().moe_decode(ctypes.byref(dims), _p(X), _p(W_r), _p(bias), _p(W_gate), _p(W_up),
+                            _p(W_down), _p(logits), _p(topk_idx), _p(topk_w), _p(out), _p(ws), ws_bytes,
+                            _stream(stream)))
 
 
 def moe_backward(dims, dY, X, W_r, W_gate, W_up, W_down, plan, H_cache, dX, dW_gate, dW_up, dW_down,

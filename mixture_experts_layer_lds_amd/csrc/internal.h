@@ -86,4 +86,10 @@ size_t dwr_workspace_bytes(const Shape& s);
 hipError_t launch_dwr_gemm(const Shape& s, const void* dLop, int E_pad, const void* X, void* dW_r,
                            void* ws, hipStream_t st);
 
+// single-launch forward for small T (decode.hip)
+size_t decode_workspace_bytes(int64_t T, int64_t d, int64_t n, int E, int K);
+hipError_t launch_decode(const Shape& s, const void* X, const void* W_r, const float* bias,
+                         const void* W_gate, const void* W_up, const void* W_down, float* logits,
+                         int32_t* topk_idx, float* topk_w, void* out, void* ws, hipStream_t st);
+
 }  // namespace moe

@@ -189,6 +189,7 @@ size_t ws_bytes_for(const moe_dims* dm, int op) {
       return c.off > r ? c.off : r;
     }
     case MOE_OP_BACKWARD: carve_bwd(c, dm); return c.off;
+    case MOE_OP_DECODE: return decode_workspace_bytes(dm->T, dm->d, dm->n, dm->E, dm->K);
     default: return 0;
   }
 }
@@ -263,7 +264,7 @@ int64_t moe_max_rows(const moe_dims* dims) {
 
 size_t moe_workspace_bytes(const moe_dims* dims, int op) {
   if (check_dims(dims) != MOE_OK) return 0;
-  if (op < MOE_OP_ROUTE || op > MOE_OP_BACKWARD) {
+  if (op < MOE_OP_ROUTE || op > MOE_OP_DECODE) {
     fail(MOE_EINVAL, "unknown op %d", op);
     return 0;
   }
@@ -323,6 +324,33 @@ moe_status moe_combine(const moe_dims* dims, const moe_plan* plan, const void* Y
   hipStream_t st = static_cast<hipStream_t>(stream);
   MOE_STAGE(MOE_STAGE_COMBINE, st, launch_combine(shape_of(dims), plan_ptrs(plan), Y_perm, weighted != 0, out, st),
             "combine");
+  return MOE_OK;
+}
+
+moe_status moe_decode(const moe_dims* dims, const void* X, const void* W_r, const float* bias,
+                      const void* W_gate, const void* W_up, const void* W_down, float* logits,
+                      int32_t* topk_idx, float* topk_w, void* out, void* ws, size_t ws_bytes,
+                      void* stream) {
+  MOE_TRY(check_dims(dims));
+  if (dims->round_mode != MOE_ROUND_NONE)
+    return fail(MOE_ENOTSUP, "moe_decode routes with plain top-K (round_mode must be NONE)");
+  if (dims->T > 1024) return fail(MOE_ENOTSUP, "moe_decode handles T <= 1024 (got %lld)", (long long)dims->T);
+  MOE_TRY(need_ptr(X, "X"));
+  MOE_TRY(need_ptr(W_r, "W_r"));
+  MOE_TRY(opt_ptr(bias, "bias"));
+  MOE_TRY(need_ptr(W_gate, "W_gate"));
+  MOE_TRY(need_ptr(W_up, "W_up"));
+  MOE_TRY(need_ptr(W_down, "W_down"));
+  MOE_TRY(need_ptr(logits, "logits"));
+  MOE_TRY(need_ptr(topk_idx, "topk_idx"));
+  MOE_TRY(need_ptr(topk_w, "topk_w"));
+  MOE_TRY(need_ptr(out, "out"));
+  MOE_TRY(check_ws(dims, MOE_OP_DECODE, ws, ws_bytes));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  MOE_STAGE(MOE_STAGE_DECODE, st,
+            launch_decode(shape_of(dims), X, W_r, bias, W_gate, W_up, W_down, logits, topk_idx,
+                          topk_w, out, ws, st),
+            "decode");
   return MOE_OK;
 }
 

@@ -87,6 +87,20 @@ def test_stochastic_rounding_needs_words():
     assert B.lib().moe_max_rows(ctypes.byref(d)) == B.lib().moe_max_rows(ctypes.byref(dims(round_mode=2)))
 
 
+def test_decode_argument_checks(lib):
+    """moe_decode: plain top-K only, T <= 1024, its own workspace size, required pointers."""
+    call = lambda d, ws=1 << 40, out=FAKE: lib.moe_decode(
+        ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, out, FAKE, ws, None)
+    assert call(dims(round_mode=1)) == -2
+    assert call(dims(T=2000)) == -2
+    d = dims(T=8)
+    need = B.moe_workspace_bytes(d, B.OP_DECODE)
+    assert need >= 8 * 2 * (2 * 256 + 128) * 4     # fp32 h and y rows of the 16 (token, expert) pairs
+    assert call(d, ws=need - 1) == -3
+    assert call(d, out=None) == -1
+    assert lib.moe_last_error()
+
+
 def test_null_and_misaligned_pointers_rejected(lib):
     d = dims()
     plan = B.PlanStruct(*([FAKE] * 9))
