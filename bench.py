@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU baseline time budget")
     ap.add_argument("--forward-only", action="store_true")
+    ap.add_argument("--decode", type=int, default=0, metavar="T",
+                    help="instead of the layer step, time moe_decode (single-launch forward) on T "
+                         "tokens of --config, next to moe_forward on the same tokens")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after warmup, run a plain 256 MiB copy kernel (torch neg on fp32) three times, "
                          "outside the timed region: the byte counters of a profiler run are scaled by it")
@@ -171,6 +174,74 @@ def cpu_baseline(cfg, inp, logits, budget_s):
                       % (len(used), cfg.E, rows, "forward+backward" if dY is not None else "forward", t_total)}
 
 
+def decode_bench(args):
+    """moe_decode on T tokens of a layer shape: per-call latency, the HBM bytes it must move (the
+    routed experts' weights once each, router weights, tokens in and out), and moe_forward on the
+    same tokens for comparison."""
+    import torch
+    from mixture_experts_layer_lds_amd import binding as B
+    from mixture_experts_layer_lds_amd import workloads as wl
+
+    cfg = wl.BY_NAME[args.config].with_(T=args.decode, backward=False, round_mode=0)
+    inp = wl.make_inputs(cfg, device="cuda", with_grad_out=False)
+    dims = B.make_dims(cfg.T, cfg.d, cfg.n, cfg.E, cfg.K, cfg.dtype)
+    dt = B.torch_dtype(dims)
+    es = 2 if cfg.dtype == "bf16" else 4
+    logits = torch.empty(cfg.T, cfg.E, dtype=torch.float32, device="cuda")
+    topk_idx = torch.empty(cfg.T, cfg.K, dtype=torch.int32, device="cuda")
+    topk_w = torch.empty(cfg.T, cfg.K, dtype=torch.float32, device="cuda")
+    out = torch.empty(cfg.T, cfg.d, dtype=dt, device="cuda")
+    ws, nb = B.workspace(dims, B.OP_DECODE)
+    plan = B.Plan(dims)
+    of = torch.empty_like(out)
+    wsf, nbf = B.workspace(dims, B.OP_FORWARD)
+
+    def dec():
+        B.moe_decode(dims, inp["X"], inp["W_r"], inp["bias"], inp["W_gate"], inp["W_up"], inp["W_down"],
+                     logits, topk_idx, topk_w, out, ws, nb)
+
+    def fwd():
+        B.moe_forward(dims, inp["X"], inp["W_r"], inp["bias"], inp["W_gate"], inp["W_up"], inp["W_down"],
+                      logits, plan, None, of, wsf, nbf)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_fwd = timed(fwd)
+    B.moe_timing_enable(True)
+    ms = timed(dec)
+    kern = B.moe_timing_read("decode")
+    B.moe_timing_enable(False)
+    kern_ms = float(np.mean(kern[args.warmup:] if len(kern) > args.warmup else kern))
+    used = np.unique(topk_idx.cpu().numpy())
+    nbytes = (len(used) * 3 * cfg.n * cfg.d * es + cfg.E * cfg.d * es + 2 * cfg.T * cfg.d * es
+              + cfg.T * cfg.E * 4 + cfg.T * cfg.K * 8)
+    gbs = nbytes / (kern_ms * 1e-3) / 1e9
+    res = {
+        "metric": "MoE decode layer forward, single launch (%s, T=%d)" % (cfg.name, cfg.T),
+        "value": round(cfg.T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic (seeded normal inputs and random-init weights)",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "n": cfg.n, "E": cfg.E, "K": cfg.K,
+                   "experts_used": int(len(used)), "parallelism": "single GPU"},
+        "roofline": {"kernel": "decode", "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "avg_ms": round(kern_ms, 4), "algorithmic_bytes": int(nbytes)},
+        "moe_forward_ms": round(ms_fwd, 4),
+        "speedup_vs_moe_forward": round(ms_fwd / ms, 2),
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -178,6 +249,8 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(requested --gpus %d, WORLD_SIZE=%d)" % (args.gpus, world), file=sys.stderr)
         sys.exit(2)
+    if args.decode:
+        return decode_bench(args)
     import torch
     from mixture_experts_layer_lds_amd import binding as B
     from mixture_experts_layer_lds_amd import workloads as wl

@@ -4,32 +4,44 @@
 // parameters, the experts' matmuls and the weighted combine fused into one kernel to avoid global
 // round trips) and "条件参数加载" (only the selected experts' weights are read).
 //
-// At small T the layer is bound by reading the routed experts' weights, and launch count matters,
-// so the whole forward is one cooperative kernel whose workgroups pass five phases separated by
-// grid-wide barriers (every workgroup walks every phase with grid-stride loops, so each reaches
-// every barrier):
-//   A. router logits (+ bias) and top-K with softmax, one token per workgroup;
-//   B. per-expert token lists, in ascending (token, k) order;
-//   C. gate/up: each unit is 32 rows of [W_gate; W_up][e] for one expert with tokens; every
-//      weight row is streamed once (8 lanes x 16 bytes per 128-byte line) and dotted with all of
-//      the expert's tokens (x staged in LDS) -> h[pair][2n] in fp32;
-//   D. SwiGLU + down: each unit is 32 rows (output columns) of W_down[e]; act = silu(G) U is
-//      built from h into LDS, dotted with every row -> y[pair][d] in fp32;
+// At small T every routed expert sees only a handful of tokens, so each projection is a skinny
+// product [rows x k] x [k x tokens] bound by reading the expert's weights once.  Each such
+// product runs on MFMA (16x16 tiles: 16 weight rows by 16 tokens), with the weight rows streamed
+// straight from HBM into the A operand, several 16-byte loads in flight per lane, and the token
+// vectors loaded into the B operand from L2.
+//
+// A tile is taken by a group of W waves of one workgroup (W = 1, 2, 4, 8 or 16, chosen per phase
+// so that the grid has about two tiles per group): the members split the reduction, and member 0
+// adds their partial tiles from LDS in member order and runs the epilogue.  Members hand over
+// through LDS counters (two buffers per group, so members run at most one tile ahead), never
+// through a workgroup barrier; with W = 1 the wave does the whole tile alone.  Every result is
+// deterministic.
+//
+// One cooperative kernel, one workgroup of 16 waves per CU, phases separated by grid-wide
+// barriers (every workgroup walks every phase with grid-stride loops, so each reaches every
+// barrier).  The barrier is a release fence, one relaxed arrival on a 64-bit counter, relaxed
+// polling and an acquire fence: cache maintenance happens once per workgroup and barrier, not
+// once per poll.  Phases:
+//   A. router logits (+ bias): tiles of 16 experts x 16 tokens; also clears the per-expert
+//      counters;
+//   B. per token (one wave): top-K with softmax, and the token's (t, k) pairs appended to the
+//      chosen experts' lists (the order inside a list does not affect any value: each token is
+//      its own MFMA column);
+//   C. gate/up: a tile holds 8 gate rows and the 8 matching up rows of one routed expert, so
+//      the epilogue has G and U of the same column in lanes l and l + 32 and writes
+//      act = silu(G) U in the element type (as the grouped forward does);
+//   D. down: 16 rows of W_down[e] (output columns) against act -> y[pair][d] in fp32;
 //   E. combine: out[t] = sum over the token's experts, in ascending expert order, of w y.
-// Routing is plain top-K (no token rounding); results match moe_forward up to rounding (the
-// activation is kept in fp32 here instead of being rounded to the element type).
+// Routing is plain top-K (no token rounding); results match moe_forward up to the order of the
+// fp32 accumulations.
 #include "internal.h"
-
-#include <hip/hip_cooperative_groups.h>
 
 namespace moe {
 
-namespace cg = cooperative_groups;
-
-constexpr int DEC_THREADS = 256;
-constexpr int DEC_ROWS = 32;     // weight rows per unit (8 lanes per row)
-constexpr int DEC_TOK = 16;      // tokens per pass over a unit's rows
-constexpr int DEC_DBLK = 512;    // reduction elements staged in LDS per block
+constexpr int DEC_THREADS = 1024;  // 16 waves per workgroup, one workgroup per CU
+constexpr int DEC_WAVES = DEC_THREADS / 64;
+constexpr int DEC_U = 4;           // reduction steps per batch with one token group (two batches in flight)
+constexpr int DEC_NG = 2;          // token groups of 16 per pass over a tile's weight rows
 
 struct DecodeArgs {
   const void* X;
@@ -44,112 +56,333 @@ struct DecodeArgs {
   void* out;
   int32_t* cnt;   // [E]
   int32_t* list;  // [E][T] pair ids t * K + k
-  float* h;       // [T * K][2n]
+  void* act;      // [T * K][n] element type
   float* y;       // [T * K][d]
   int T, d, n, E, K;
 };
+
+// One reduction step of a 16x16 tile: every lane holds 16 bytes of its weight row (A, row
+// lane % 16) and 16 bytes of its token's vector (B, column lane % 16), both at the same k offset
+// (lane / 16) * V inside the step, so the products pair the same k on both sides.
+template <typename T> struct DecMma;
+template <> struct DecMma<bf16> {
+  static constexpr int S = 32;  // k elements per step
+  static constexpr int V = 8;   // k elements per lane per step
+  __device__ static f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+template <> struct DecMma<float> {
+  static constexpr int S = 16;
+  static constexpr int V = 4;
+  __device__ static f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
+    // four k = 4 products; product i takes element i of every lane's 4-element chunk
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[i]), __uint_as_float(b[i]), c, 0, 0, 0);
+    return c;
+  }
+};
+
+// Steps per batch: the register budget holds two batches of (1 + NG) 16-byte operands.
+template <int NG> struct DecBatch { static constexpr int U = DEC_U / NG; };
+
+template <typename T, int NG>
+struct DecStream {
+  static constexpr int U = DecBatch<NG>::U;
+  const T* w;       // lane's weight row at its k offset
+  const T* x[NG];   // lane's token vectors at its k offset
+
+  // steps st .. st + U - 1, constant offsets from one base per operand
+  __device__ __forceinline__ void load(u32x4 (&wv)[U], u32x4 (&xv)[NG][U], int st) const {
+    constexpr int S = DecMma<T>::S;
+    const T* wp = w + st * S;
+    const T* xp[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) xp[g] = x[g] + st * S;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {  // in the order the MFMAs consume them
+      wv[u] = ld16(wp + u * S);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) xv[g][u] = ld16(xp[g] + u * S);
+    }
+  }
+};
+
+template <typename T, int NG, int U>
+__device__ __forceinline__ void dec_mma(const u32x4 (&wv)[U], const u32x4 (&xv)[NG][U], f32x4 (&acc)[NG]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) acc[g] = DecMma<T>::mma(wv[u], xv[g][u], acc[g]);
+  }
+}
+
+// Steps [a, b) of one wave (a, b wave-uniform): whole batches with two register sets, the next
+// batch's loads issued before the MFMAs of the current one, then the last (b - a) mod U steps
+// as one short batch.
+template <typename T, int NG>
+__device__ __forceinline__ void dec_stream(const DecStream<T, NG>& ds, int a, int b, f32x4* acc) {
+  constexpr int U = DecBatch<NG>::U;
+  constexpr int S = DecMma<T>::S;
+  f32x4 (&ac)[NG] = *reinterpret_cast<f32x4(*)[NG]>(acc);
+  const int nfull = (b - a) / U;
+  if (nfull > 0) {
+    u32x4 w0[U], x0[NG][U], w1[U], x1[NG][U];
+    ds.load(w0, x0, a);
+    int i = 0;
+    for (; i + 2 < nfull; i += 2) {  // steady state: loads unconditional, so the waits stay partial
+      ds.load(w1, x1, a + (i + 1) * U);
+      dec_mma<T, NG, U>(w0, x0, ac);
+      ds.load(w0, x0, a + (i + 2) * U);
+      dec_mma<T, NG, U>(w1, x1, ac);
+    }
+    if (i + 1 < nfull) {
+      ds.load(w1, x1, a + (i + 1) * U);
+      dec_mma<T, NG, U>(w0, x0, ac);
+      dec_mma<T, NG, U>(w1, x1, ac);
+    } else {
+      dec_mma<T, NG, U>(w0, x0, ac);
+    }
+  }
+  const int st = a + nfull * U, r = b - st;
+  if (r > 0) {  // one more batch, all of its loads in flight together; steps past b repeat b - 1
+    u32x4 wt[U], xt[NG][U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int su = st + min(u, r - 1);
+      wt[u] = ld16(ds.w + su * S);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) xt[g][u] = ld16(ds.x[g] + su * S);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (u < r) {
+#pragma unroll
+        for (int g = 0; g < NG; ++g) ac[g] = DecMma<T>::mma(wt[u], xt[g][u], ac[g]);
+      }
+    }
+  }
+}
+
+// Per-workgroup LDS: partial tiles [wave][buffer][token group][lane] and, per group, the
+// arrival and consumption counters of its two buffers.
+struct DecLds {
+  f32x4 part[DEC_WAVES * 2 * DEC_NG * 64];
+  int arrive[DEC_WAVES][2];
+  int consumed[DEC_WAVES][2];
+  int active[1024];  // routed experts in ascending order
+  int nactive;
+};
+
+__device__ __forceinline__ void dec_lds_wait_ge(int* p, int target) {
+  // members of a group are waves of one resident workgroup: every wait ends
+  while (__hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < target)
+    __builtin_amdgcn_s_sleep(1);
+}
+
+// One wave's view of the tile groups of a phase: W waves per group, this wave is member m of
+// group grp (grid-wide index gid among ngroups groups), seq counts the group's tiles so far.
+struct DecGroup {
+  int W, m, grp, gid, ngroups, seq;
+  __device__ __forceinline__ void setup(int w) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    W = w;
+    m = wave % w;
+    grp = wave / w;
+    gid = blockIdx.x * (DEC_WAVES / w) + grp;
+    ngroups = gridDim.x * (DEC_WAVES / w);
+    seq = 0;
+  }
+};
+
+// Wave count per tile for a phase with `items` tiles of `ns` reduction steps: the smallest W
+// giving about two tiles per group over the grid, with at least two steps per member.
+__device__ __forceinline__ int dec_pick_w(int items, int ns) {
+  const int want = 2 * (int)gridDim.x * DEC_WAVES;
+  int w = 1;
+  while (w < DEC_WAVES && items * w < want) w *= 2;
+  while (w > 1 && ns < 2 * w) w /= 2;
+  return w;
+}
+
+// The group's tile: member m streams its share of steps [s0, s1) for ng token groups; the
+// epilogue epi(v) runs on member 0 with the tile summed over members (v[g], rows 4 (lane / 16)
+// + i, column lane % 16 of token group g).
+template <typename T, class Epi>
+__device__ __forceinline__ void dec_group_tile(DecGroup& G, DecLds& L, const T* wrow, const T* const* xrow,
+                                               int ng, int s0, int s1, Epi epi) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ko = (lane >> 4) * DecMma<T>::V;
+  const int ns = s1 - s0;
+  const int a = s0 + ns * G.m / G.W, b = s0 + ns * (G.m + 1) / G.W;
+  f32x4 acc[DEC_NG];
+#pragma unroll
+  for (int g = 0; g < DEC_NG; ++g) acc[g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  if (ng == 2) {
+    DecStream<T, 2> ds;
+    ds.w = wrow + ko;
+    ds.x[0] = xrow[0] + ko;
+    ds.x[1] = xrow[1] + ko;
+    dec_stream<T, 2>(ds, a, b, acc);
+  } else {
+    DecStream<T, 1> ds;
+    ds.w = wrow + ko;
+    ds.x[0] = xrow[0] + ko;
+    dec_stream<T, 1>(ds, a, b, acc);
+  }
+  if (G.W == 1) {
+    epi(acc);
+    return;
+  }
+  const int buf = G.seq & 1, use = G.seq >> 1;
+  ++G.seq;
+  dec_lds_wait_ge(&L.consumed[G.grp][buf], use);  // the buffer's previous tile has been read
+  for (int g = 0; g < ng; ++g) L.part[((wave * 2 + buf) * DEC_NG + g) * 64 + lane] = acc[g];
+  if (lane == 0) __hip_atomic_fetch_add(&L.arrive[G.grp][buf], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  if (G.m == 0) {
+    dec_lds_wait_ge(&L.arrive[G.grp][buf], (use + 1) * G.W);
+    f32x4 v[DEC_NG];
+    for (int g = 0; g < ng; ++g) {
+      v[g] = L.part[((wave * 2 + buf) * DEC_NG + g) * 64 + lane];
+      for (int mm = 1; mm < G.W; ++mm) v[g] += L.part[(((wave + mm) * 2 + buf) * DEC_NG + g) * 64 + lane];
+    }
+    if (lane == 0) __hip_atomic_store(&L.consumed[G.grp][buf], use + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    epi(v);
+  }
+}
 
 __device__ __forceinline__ uint32_t dec_order_key(float x) {
   if (x != x) return 0u;
   const uint32_t u = __float_as_uint(x == 0.0f ? 0.0f : x);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-
-template <typename T>
-__device__ __forceinline__ float dot8(u32x4 w, const float* x) {
-  float f[8];
-  if constexpr (sizeof(T) == 2) {
-    unpack16<bf16>(w, f);
-  } else {
-    unpack16<float>(w, f);  // 4 elements; the caller passes 4-element chunks for fp32
-  }
-  float s = 0.0f;
-#pragma unroll
-  for (int i = 0; i < (int)(16 / sizeof(T)); ++i) s += f[i] * x[i];
-  return s;
+__device__ __forceinline__ float dec_key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// One unit of phase C or D: rows row0 .. row0 + 31 of a weight matrix whose row r starts at
-// wrow(r) (K_len elements), dotted with the vectors of up to DEC_TOK tokens held in LDS as fp32
-// (xs[tok][DEC_DBLK], refilled block by block by fill(tok, k0, k1)).  Returns through emit(tok,
-// row, value) on the lane that owns the row's sum (sub-lane 0 of each 8-lane group).
-template <typename T, class WRow, class Fill, class Emit>
-__device__ void dec_unit(int nrows, int row0, int K_len, int ntok, WRow wrow, Fill fill, Emit emit,
-                         float* xs) {
-  constexpr int VEC = 16 / sizeof(T);
-  const int tid = threadIdx.x;
-  const int r = tid >> 3, part = tid & 7;  // row within the unit, lane within the row's group
-  const int row = row0 + r;
-  const bool live = row < nrows;
-  const T* wr = live ? reinterpret_cast<const T*>(wrow(row)) : nullptr;
-  float acc[DEC_TOK];
-#pragma unroll
-  for (int i = 0; i < DEC_TOK; ++i) acc[i] = 0.0f;
-  for (int k0 = 0; k0 < K_len; k0 += DEC_DBLK) {
-    const int k1 = min(K_len, k0 + DEC_DBLK);
-    __syncthreads();
-    fill(ntok, k0, k1);
-    __syncthreads();
-    if (live) {
-      for (int k = k0 + part * VEC; k < k1; k += 8 * VEC) {
-        const u32x4 w = ld16(wr + k);
-#pragma unroll
-        for (int i = 0; i < DEC_TOK; ++i)
-          if (i < ntok) acc[i] += dot8<T>(w, xs + i * DEC_DBLK + (k - k0));
-      }
+template <typename T>
+__device__ __forceinline__ void dec_store4(T* p, f32x4 v) {
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, from_f32<bf16>(v[0])) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<bf16>(v[1])) << 16);
+    const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, from_f32<bf16>(v[2])) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<bf16>(v[3])) << 16);
+    *reinterpret_cast<u32x2*>(p) = u32x2{lo, hi};
+  } else {
+    *reinterpret_cast<f32x4*>(p) = v;
+  }
+}
+
+// Experts with at least one routed token, in ascending order, built by wave 0 of every
+// workgroup into its LDS (list[i] = the i-th active expert); returns their number.
+__device__ __forceinline__ int dec_active_experts(const int32_t* cnt, int E, int* list, int* count) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid < 64) {
+    int base = 0;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+      const int e = e0 + lane;
+      const bool on = e < E && cnt[e] > 0;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(on);
+      if (on) list[base + (int)__builtin_popcountll(m & ((1ull << lane) - 1ull))] = e;
+      base += (int)__builtin_popcountll(m);
     }
+    if (lane == 0) *count = base;
   }
-#pragma unroll
-  for (int i = 0; i < DEC_TOK; ++i) {
-    float v = acc[i];
-    v += __shfl_xor(v, 1, 64);
-    v += __shfl_xor(v, 2, 64);
-    v += __shfl_xor(v, 4, 64);
-    if (live && part == 0 && i < ntok) emit(i, row, v);
+  __syncthreads();
+  return *count;
+}
+
+// Arrivals at the grid barrier, one counter per kernel instantiation (per device: each device
+// holds its own copy).  The counter only grows: with nb workgroups, arrival number v (counted
+// from the first launch) belongs to the barrier that completes when the counter reaches
+// (v / nb + 1) nb.  Every launch of one instantiation has the same grid, so each launch starts
+// at a multiple of nb; cooperative launches on one device do not overlap.
+static __device__ unsigned long long g_dec_arrivals[2][32];
+
+// Grid-wide barrier; also clears the workgroup's tile-group counters for the next phase.
+__device__ __forceinline__ void dec_grid_barrier(unsigned long long* ctr, DecLds& L) {
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's loads and stores have completed
+  __syncthreads();
+  if (threadIdx.x < DEC_WAVES * 2) {
+    (&L.arrive[0][0])[threadIdx.x] = 0;
+    (&L.consumed[0][0])[threadIdx.x] = 0;
   }
+  if (threadIdx.x == 0) {
+    const unsigned long long nb = gridDim.x;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const unsigned long long v = __hip_atomic_fetch_add(ctr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long target = (v / nb + 1) * nb;
+    // bounded wait (about a second): a grid that is not fully resident cannot happen under a
+    // cooperative launch; if it ever did, the kernel would finish with wrong results, not hang
+    for (int spin = 0; spin < (1 << 20); ++spin) {
+      if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
 }
 
 template <typename T>
 __global__ __launch_bounds__(DEC_THREADS) void k_decode(DecodeArgs a) {
-  cg::grid_group grid = cg::this_grid();
-  extern __shared__ float dsm[];  // [DEC_TOK][DEC_DBLK] fp32 staging, reused by every phase
-  __shared__ float s_log[1024];
-  constexpr int VEC = 16 / sizeof(T);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  unsigned long long* bar = g_dec_arrivals[sizeof(T) == 2 ? 0 : 1];
+  __shared__ DecLds L;
+  constexpr int S = DecMma<T>::S;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, q = lane >> 4;
   const T* X = reinterpret_cast<const T*>(a.X);
   const int T_ = a.T, d = a.d, n = a.n, E = a.E, K = a.K;
+  if (tid < DEC_WAVES * 2) {
+    (&L.arrive[0][0])[tid] = 0;
+    (&L.consumed[0][0])[tid] = 0;
+  }
+  __syncthreads();
+  DecGroup G;
 
-  // ---- A: router + top-K, one token per workgroup ----
-  for (int t = blockIdx.x; t < T_; t += gridDim.x) {
-    const T* xt = X + (int64_t)t * d;
+  // ---- A: router logits; clear the per-expert counters ----
+  for (int i = blockIdx.x * DEC_THREADS + tid; i < E; i += gridDim.x * DEC_THREADS) a.cnt[i] = 0;
+  {
     const T* Wr = reinterpret_cast<const T*>(a.W_r);
-    for (int e = wave; e < E; e += DEC_THREADS / 64) {
-      float s = 0.0f;
-      for (int c = lane * VEC; c < d; c += 64 * VEC) {
-        float xf[8], wf[8];
-        unpack16<T>(ld16(xt + c), xf);
-        unpack16<T>(ld16(Wr + (int64_t)e * d + c), wf);
+    const int tiles = (E + 15) / 16, groups = (T_ + 15) / 16, passes = (groups + DEC_NG - 1) / DEC_NG;
+    const int items = tiles * passes;
+    G.setup(dec_pick_w(items, d / S));
+    for (int u = G.gid; u < items; u += G.ngroups) {
+      const int pass = u % passes, tile = u / passes;
+      const T* wrow = Wr + (int64_t)min(tile * 16 + r16, E - 1) * d;
+      const int g0 = pass * DEC_NG, ng = min(DEC_NG, groups - g0);
+      const T* xr[DEC_NG];
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) s += xf[i] * wf[i];
-      }
-      s = wave_sum(s);
-      if (lane == 0) {
-        const float L = s + (a.bias ? a.bias[e] : 0.0f);
-        s_log[e] = L;
-        a.logits[(int64_t)t * E + e] = L;
-      }
+      for (int g = 0; g < DEC_NG; ++g) xr[g] = X + (int64_t)min((g0 + g) * 16 + r16, T_ - 1) * d;
+      dec_group_tile<T>(G, L, wrow, xr, ng, 0, d / S, [&](const f32x4* v) {
+        for (int g = 0; g < ng; ++g) {
+          const int t = (g0 + g) * 16 + r16;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = tile * 16 + 4 * q + i;
+            if (t < T_ && e < E) a.logits[(int64_t)t * E + e] = v[g][i] + (a.bias ? a.bias[e] : 0.0f);
+          }
+        }
+      });
     }
-    __syncthreads();
-    if (wave == 0) {
+  }
+  dec_grid_barrier(bar, L);
+
+  // ---- B: top-K + softmax, per-expert lists; one token per wave ----
+  {
+    const int nw = gridDim.x * DEC_WAVES;
+    for (int t = blockIdx.x * DEC_WAVES + wave; t < T_; t += nw) {
       // composite keys (order_key(L) << 32) | ~e: one unsigned maximum orders by logit
       // descending, then expert id ascending; lane i holds experts i + 64 j (E <= 1024)
       uint64_t ck[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int e = lane + 64 * j;
-        ck[j] = e < E ? (((uint64_t)dec_order_key(s_log[e]) << 32) | (uint32_t)~(uint32_t)e) : 0ull;
+        ck[j] = e < E ? (((uint64_t)dec_order_key(a.logits[(int64_t)t * E + e]) << 32) | (uint32_t)~(uint32_t)e)
+                      : 0ull;
       }
       int my_e = 0;
+      float my_v = 0.0f;
       for (int k = 0; k < K; ++k) {
         uint64_t b = 0ull;
 #pragma unroll
@@ -162,134 +395,143 @@ __global__ __launch_bounds__(DEC_THREADS) void k_decode(DecodeArgs a) {
 #pragma unroll
         for (int j = 0; j < 16; ++j)
           if (ck[j] == b) ck[j] = 0ull;
-        const int win = (int)~(uint32_t)b;
-        if (lane == 0) a.topk_idx[(int64_t)t * K + k] = win;
-        if (lane == k) my_e = win;
+        if (lane == k) {
+          my_e = (int)~(uint32_t)b;
+          my_v = dec_key_value((uint32_t)(b >> 32));
+        }
       }
-      const float my_v = lane < K ? s_log[my_e] : 0.0f;
       const float vmax = __shfl(my_v, 0, 64);
       const float ex = lane < K ? __expf(my_v - vmax) : 0.0f;
       const float sum = wave_sum(ex);
-      if (lane < K) a.topk_w[(int64_t)t * K + lane] = ex / sum;
-    }
-    __syncthreads();
-  }
-  grid.sync();
-
-  // ---- B: per-expert token lists in ascending (t, k) order ----
-  {
-    __shared__ int s_wcnt[DEC_THREADS / 64];
-    const int P = T_ * K;
-    for (int e = blockIdx.x; e < E; e += gridDim.x) {
-      int base = 0;
-      for (int p0 = 0; p0 < P; p0 += DEC_THREADS) {
-        const int p = p0 + tid;
-        const bool hit = p < P && a.topk_idx[p] == e;
-        const uint64_t m = __builtin_amdgcn_ballot_w64(hit);
-        if (lane == 0) s_wcnt[wave] = (int)__builtin_popcountll(m);
-        __syncthreads();
-        int off = base;
-        for (int w = 0; w < wave; ++w) off += s_wcnt[w];
-        if (hit) a.list[(int64_t)e * T_ + off + (int)__builtin_popcountll(m & ((1ull << lane) - 1ull))] = p;
-        int tot = 0;
-        for (int w = 0; w < DEC_THREADS / 64; ++w) tot += s_wcnt[w];
-        base += tot;
-        __syncthreads();
+      if (lane < K) {
+        a.topk_idx[(int64_t)t * K + lane] = my_e;
+        a.topk_w[(int64_t)t * K + lane] = ex / sum;
+        const int pos = atomicAdd(&a.cnt[my_e], 1);  // < T: a token picks an expert at most once
+        a.list[(int64_t)my_e * T_ + pos] = t * K + lane;
       }
-      if (tid == 0) a.cnt[e] = base;
     }
   }
-  grid.sync();
+  dec_grid_barrier(bar, L);
 
-  // ---- C: gate/up rows dotted with each routed token's x ----
+  const int nact = dec_active_experts(a.cnt, E, L.active, &L.nactive);
+
+  // ---- C: gate/up tiles (8 gate + 8 up rows) -> act = silu(G) U ----
   {
-    const int nb = (2 * n + DEC_ROWS - 1) / DEC_ROWS;
     const T* Wg = reinterpret_cast<const T*>(a.W_gate);
     const T* Wu = reinterpret_cast<const T*>(a.W_up);
-    for (int u = blockIdx.x; u < E * nb; u += gridDim.x) {
-      const int e = u / nb, rb = u % nb;
-      const int c = a.cnt[e];
-      for (int g0 = 0; g0 < c; g0 += DEC_TOK) {
-        const int ntok = min(DEC_TOK, c - g0);
-        const int32_t* lst = a.list + (int64_t)e * T_ + g0;
-        auto wrow = [&](int j) -> const void* {
-          return j < n ? Wg + ((int64_t)e * n + j) * d : Wu + ((int64_t)e * n + (j - n)) * d;
-        };
-        auto fill = [&](int nt, int k0, int k1) {
-          for (int i = tid; i < nt * DEC_DBLK; i += DEC_THREADS) {
-            const int tk = i / DEC_DBLK, k = k0 + i % DEC_DBLK;
-            const int t = lst[tk] / K;
-            dsm[i] = k < k1 ? to_f32(X[(int64_t)t * d + k]) : 0.0f;
-          }
-        };
-        auto emit = [&](int tk, int j, float v) { a.h[(int64_t)lst[tk] * 2 * n + j] = v; };
-        dec_unit<T>(2 * n, rb * DEC_ROWS, d, ntok, wrow, fill, emit, dsm);
-      }
-    }
-  }
-  grid.sync();
-
-  // ---- D: act = silu(G) U, dotted with W_down rows ----
-  {
-    const int nb = (d + DEC_ROWS - 1) / DEC_ROWS;
-    const T* Wd = reinterpret_cast<const T*>(a.W_down);
-    for (int u = blockIdx.x; u < E * nb; u += gridDim.x) {
-      const int e = u / nb, cb = u % nb;
-      const int c = a.cnt[e];
-      for (int g0 = 0; g0 < c; g0 += DEC_TOK) {
-        const int ntok = min(DEC_TOK, c - g0);
-        const int32_t* lst = a.list + (int64_t)e * T_ + g0;
-        auto wrow = [&](int col) -> const void* { return Wd + ((int64_t)e * d + col) * n; };
-        auto fill = [&](int nt, int k0, int k1) {
-          for (int i = tid; i < nt * DEC_DBLK; i += DEC_THREADS) {
-            const int tk = i / DEC_DBLK, j = k0 + i % DEC_DBLK;
-            float v = 0.0f;
-            if (j < k1) {
-              const float* hp = a.h + (int64_t)lst[tk] * 2 * n;
-              const float G = hp[j], U = hp[n + j];
-              v = G * sigmoid_f32(G) * U;
+    T* act = reinterpret_cast<T*>(a.act);
+    const int tiles = n / 8;
+    const int items = nact * tiles;
+    G.setup(dec_pick_w(items, d / S));
+    for (int u = G.gid; u < items; u += G.ngroups) {
+      const int e = L.active[u / tiles], j0 = (u % tiles) * 8;
+      const int c = __builtin_amdgcn_readfirstlane(a.cnt[e]);
+      const int32_t* lst = a.list + (int64_t)e * T_;
+      const T* wrow = r16 < 8 ? Wg + ((int64_t)e * n + j0 + r16) * d : Wu + ((int64_t)e * n + j0 + r16 - 8) * d;
+      const int groups = (c + 15) / 16;
+      for (int g0 = 0; g0 < groups; g0 += DEC_NG) {
+        const int ng = min(DEC_NG, groups - g0);
+        const T* xr[DEC_NG];
+#pragma unroll
+        for (int g = 0; g < DEC_NG; ++g) xr[g] = X + (int64_t)(lst[min((g0 + g) * 16 + r16, c - 1)] / K) * d;
+        dec_group_tile<T>(G, L, wrow, xr, ng, 0, d / S, [&](const f32x4* v) {
+          for (int g = 0; g < ng; ++g) {
+            f32x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = __shfl_xor(v[g][i], 32, 64);
+            const int slot = (g0 + g) * 16 + r16;
+            if (lane < 32 && slot < c) {  // lanes < 32: gate rows 4q + i, their up rows in lane + 32
+              f32x4 h;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) h[i] = v[g][i] * sigmoid_f32(v[g][i]) * o[i];
+              dec_store4<T>(act + (int64_t)lst[slot] * n + j0 + 4 * q, h);
             }
-            dsm[i] = v;
           }
-        };
-        auto emit = [&](int tk, int col, float v) { a.y[(int64_t)lst[tk] * d + col] = v; };
-        dec_unit<T>(d, cb * DEC_ROWS, n, ntok, wrow, fill, emit, dsm);
+        });
       }
     }
   }
-  grid.sync();
+  dec_grid_barrier(bar, L);
 
-  // ---- E: combine in ascending expert order ----
-  for (int t = blockIdx.x; t < T_; t += gridDim.x) {
-    int ord[16];
-    for (int k = 0; k < K; ++k) ord[k] = k;
-    for (int k = 1; k < K; ++k) {  // insertion sort of the token's k by expert id (K <= 16)
-      const int x = ord[k];
-      int j = k - 1;
-      while (j >= 0 && a.topk_idx[(int64_t)t * K + ord[j]] > a.topk_idx[(int64_t)t * K + x]) {
-        ord[j + 1] = ord[j];
-        --j;
+  // ---- D: down tiles (16 output columns) -> y[pair] ----
+  {
+    const T* Wd = reinterpret_cast<const T*>(a.W_down);
+    const T* act = reinterpret_cast<const T*>(a.act);
+    const int tiles = d / 16;
+    const int items = nact * tiles;
+    G.setup(dec_pick_w(items, n / S));
+    for (int u = G.gid; u < items; u += G.ngroups) {
+      const int e = L.active[u / tiles], col0 = (u % tiles) * 16;
+      const int c = __builtin_amdgcn_readfirstlane(a.cnt[e]);
+      const int32_t* lst = a.list + (int64_t)e * T_;
+      const T* wrow = Wd + ((int64_t)e * d + col0 + r16) * n;
+      const int groups = (c + 15) / 16;
+      for (int g0 = 0; g0 < groups; g0 += DEC_NG) {
+        const int ng = min(DEC_NG, groups - g0);
+        const T* xr[DEC_NG];
+#pragma unroll
+        for (int g = 0; g < DEC_NG; ++g) xr[g] = act + (int64_t)lst[min((g0 + g) * 16 + r16, c - 1)] * n;
+        dec_group_tile<T>(G, L, wrow, xr, ng, 0, n / S, [&](const f32x4* v) {
+          for (int g = 0; g < ng; ++g) {
+            const int slot = (g0 + g) * 16 + r16;
+            if (slot < c) *reinterpret_cast<f32x4*>(a.y + (int64_t)lst[slot] * d + col0 + 4 * q) = v[g];
+          }
+        });
       }
-      ord[j + 1] = x;
     }
-    T* out = reinterpret_cast<T*>(a.out) + (int64_t)t * d;
-    for (int col = tid; col < d; col += DEC_THREADS) {
-      float s = 0.0f;
-      for (int q = 0; q < K; ++q) {
-        const int k = ord[q];
-        s += a.topk_w[(int64_t)t * K + k] * a.y[((int64_t)t * K + k) * d + col];
+  }
+  dec_grid_barrier(bar, L);
+
+  // ---- E: combine in ascending expert order, 4 columns per thread ----
+  {
+    const int chunks = (d + 4 * DEC_THREADS - 1) / (4 * DEC_THREADS);
+    for (int u = blockIdx.x; u < T_ * chunks; u += gridDim.x) {
+      const int t = u / chunks, c0 = (u % chunks) * 4 * DEC_THREADS + 4 * tid;
+      // the token's experts (distinct, uniform over the workgroup) ranked by id: kb[r] is the k
+      // of the r-th smallest
+      int ids[16], kb[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        ids[k] = k < K ? __builtin_amdgcn_readfirstlane(a.topk_idx[(int64_t)t * K + k]) : 0x7fffffff;
+      int prev = -1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        int best = 0x7fffffff, b = 0;
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          if (ids[k] > prev && ids[k] < best) {
+            best = ids[k];
+            b = k;
+          }
+        kb[r] = b;
+        prev = best;
       }
-      out[col] = from_f32<T>(s);
+      if (c0 < d) {
+        f32x4 yv[16];
+        float wv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (r < K) {
+            const int64_t p = (int64_t)t * K + kb[r];
+            wv[r] = a.topk_w[p];
+            yv[r] = *reinterpret_cast<const f32x4*>(a.y + p * d + c0);
+          }
+        }
+        f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (r < K) s += wv[r] * yv[r];
+        dec_store4<T>(reinterpret_cast<T*>(a.out) + (int64_t)t * d + c0, s);
+      }
     }
   }
 }
 
+static size_t dec_align(size_t b) { return (b + 255) / 256 * 256; }
+
 size_t decode_workspace_bytes(int64_t T, int64_t d, int64_t n, int E, int K) {
-  const size_t a = ((size_t)E * 4 + 255) / 256 * 256;
-  const size_t b = ((size_t)E * T * 4 + 255) / 256 * 256;
-  const size_t c = ((size_t)T * K * 2 * n * 4 + 255) / 256 * 256;
-  const size_t y = ((size_t)T * K * d * 4 + 255) / 256 * 256;
-  return a + b + c + y;
+  return dec_align((size_t)E * 4) + dec_align((size_t)E * T * 4) + dec_align((size_t)T * K * n * 4) +
+         dec_align((size_t)T * K * d * 4);
 }
 
 hipError_t launch_decode(const Shape& s, const void* X, const void* W_r, const float* bias,
@@ -300,29 +542,28 @@ hipError_t launch_decode(const Shape& s, const void* X, const void* W_r, const f
   a.logits = logits; a.topk_idx = topk_idx; a.topk_w = topk_w; a.out = out;
   char* w = static_cast<char*>(ws);
   a.cnt = reinterpret_cast<int32_t*>(w);
-  w += ((size_t)s.E * 4 + 255) / 256 * 256;
+  w += dec_align((size_t)s.E * 4);
   a.list = reinterpret_cast<int32_t*>(w);
-  w += ((size_t)s.E * s.T * 4 + 255) / 256 * 256;
-  a.h = reinterpret_cast<float*>(w);
-  w += ((size_t)s.T * s.K * 2 * s.n * 4 + 255) / 256 * 256;
+  w += dec_align((size_t)s.E * s.T * 4);
+  a.act = w;  // element type; sized for fp32
+  w += dec_align((size_t)s.T * s.K * s.n * 4);
   a.y = reinterpret_cast<float*>(w);
   a.T = (int)s.T; a.d = (int)s.d; a.n = (int)s.n; a.E = s.E; a.K = s.K;
   const void* fn = s.bf16 ? reinterpret_cast<const void*>(&k_decode<bf16>)
                           : reinterpret_cast<const void*>(&k_decode<float>);
-  const size_t lds = (size_t)DEC_TOK * DEC_DBLK * sizeof(float);
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, DEC_THREADS, lds);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, DEC_THREADS, 0);
   if (e != hipSuccess) return e;
   if (per_cu < 1) return hipErrorInvalidConfiguration;
   // every workgroup must be resident at once for the grid barriers: the cooperative launch
   // refuses a larger grid
   const int grid = cus * per_cu;
   void* params[] = {&a};
-  return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(DEC_THREADS), params, (unsigned)lds, st);
+  return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(DEC_THREADS), params, 0u, st);
 }
 
 }  // namespace moe

@@ -95,7 +95,7 @@ def test_decode_argument_checks(lib):
     assert call(dims(T=2000)) == -2
     d = dims(T=8)
     need = B.moe_workspace_bytes(d, B.OP_DECODE)
-    assert need >= 8 * 2 * (2 * 256 + 128) * 4     # fp32 h and y rows of the 16 (token, expert) pairs
+    assert need >= 8 * 2 * (256 + 128) * 4     # activation and fp32 y rows of the 16 (token, expert) pairs
     assert call(d, ws=need - 1) == -3
     assert call(d, out=None) == -1
     assert lib.moe_last_error()
