@@ -11,11 +11,11 @@
 // vectors loaded into the B operand from L2.
 //
 // A tile is taken by a group of W waves of one workgroup (W = 1, 2, 4, 8 or 16, chosen per phase
-// so that the grid has about two tiles per group): the members split the reduction, and member 0
-// adds their partial tiles from LDS in member order and runs the epilogue.  Members hand over
-// through LDS counters (two buffers per group, so members run at most one tile ahead), never
-// through a workgroup barrier; with W = 1 the wave does the whole tile alone.  Every result is
-// deterministic.
+// from the tile count and the reduction length to balance the grid): the members split the
+// reduction, and member 0 adds their partial tiles from LDS in member order and runs the
+// epilogue.  Members hand over through LDS counters (two buffers per group, so members run at
+// most one tile ahead), never through a workgroup barrier; with W = 1 the wave does the whole
+// tile alone.  Every result is deterministic.
 //
 // One cooperative kernel, one workgroup of 16 waves per CU, phases separated by grid-wide
 // barriers (every workgroup walks every phase with grid-stride loops, so each reaches every
@@ -41,7 +41,7 @@ namespace moe {
 constexpr int DEC_THREADS = 1024;  // 16 waves per workgroup, one workgroup per CU
 constexpr int DEC_WAVES = DEC_THREADS / 64;
 constexpr int DEC_U = 4;           // reduction steps per batch with one token group (two batches in flight)
-constexpr int DEC_NG = 2;          // token groups of 16 per pass over a tile's weight rows
+constexpr int DEC_NG = 3;          // token groups of 16 per pass over a tile's weight rows
 
 struct DecodeArgs {
   const void* X;
@@ -86,7 +86,7 @@ template <> struct DecMma<float> {
 };
 
 // Steps per batch: the register budget holds two batches of (1 + NG) 16-byte operands.
-template <int NG> struct DecBatch { static constexpr int U = DEC_U / NG; };
+template <int NG> struct DecBatch { static constexpr int U = NG <= 2 ? DEC_U : DEC_U / 2; };
 
 template <typename T, int NG>
 struct DecStream {
@@ -197,14 +197,23 @@ struct DecGroup {
   }
 };
 
-// Wave count per tile for a phase with `items` tiles of `ns` reduction steps: the smallest W
-// giving about two tiles per group over the grid, with at least two steps per member.
+// Wave count per tile for a phase with `items` tiles of `ns` reduction steps: the W in
+// {1, 2, 4, 8, 16} that minimises rounds x (steps per member + a fixed cost per tile, about
+// eight steps' worth for the first load's latency and the hand-over), where rounds =
+// ceil(items W / waves in the grid); ties go to the smaller W.
 __device__ __forceinline__ int dec_pick_w(int items, int ns) {
-  const int want = 2 * (int)gridDim.x * DEC_WAVES;
-  int w = 1;
-  while (w < DEC_WAVES && items * w < want) w *= 2;
-  while (w > 1 && ns < 2 * w) w /= 2;
-  return w;
+  const int waves = (int)gridDim.x * DEC_WAVES;
+  int best_w = 1, best = 0x7fffffff;
+  for (int w = 1; w <= DEC_WAVES; w *= 2) {
+    if (w > 1 && ns < w) break;
+    const int rounds = (items * w + waves - 1) / waves;
+    const int cost = rounds * ((ns + w - 1) / w + 8);
+    if (cost < best) {
+      best = cost;
+      best_w = w;
+    }
+  }
+  return best_w;
 }
 
 // The group's tile: member m streams its share of steps [s0, s1) for ng token groups; the
@@ -220,7 +229,13 @@ __device__ __forceinline__ void dec_group_tile(DecGroup& G, DecLds& L, const T* 
   f32x4 acc[DEC_NG];
 #pragma unroll
   for (int g = 0; g < DEC_NG; ++g) acc[g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  if (ng == 2) {
+  if (ng == 3) {
+    DecStream<T, 3> ds;
+    ds.w = wrow + ko;
+#pragma unroll
+    for (int g = 0; g < 3; ++g) ds.x[g] = xrow[g] + ko;
+    dec_stream<T, 3>(ds, a, b, acc);
+  } else if (ng == 2) {
     DecStream<T, 2> ds;
     ds.w = wrow + ko;
     ds.x[0] = xrow[0] + ko;

@@ -68,8 +68,11 @@ def check_decode(cfg, inp, logits, topk_idx, topk_w, out):
     return assert_close("out", f64(out), want, tol)
 
 
-@pytest.mark.parametrize("T,dtype", [(1, "bf16"), (3, "f32"), (17, "bf16"), (64, "bf16"), (40, "f32")])
+@pytest.mark.parametrize("T,dtype", [(1, "bf16"), (3, "f32"), (17, "bf16"), (64, "bf16"), (40, "f32"),
+                                     (200, "bf16"), (130, "f32")])
 def test_decode_small_shapes(T, dtype):
+    """T = 200 and 130 give experts with 33 to 64 tokens: passes of three token groups and a
+    partial last pass."""
     cfg = wl.small_shape(T=T, d=256, E=16, K=4, n=192, dtype=dtype, bias="normal", backward=False,
                          seed=60 + T)
     inp = wl.make_inputs(cfg, device="cuda")
