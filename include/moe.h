@@ -26,7 +26,8 @@
  *    sizes (rows per expert, the total row count R) stay on the device.
  *  - The caller owns all memory: inputs, outputs, the routing plan and the workspace.  The
  *    library never allocates or frees device memory and keeps no state between calls, apart from
- *    a thread-local error message and, when enabled, the stage-timing records (moe_timing_*).
+ *    a thread-local error message, when enabled the stage-timing records (moe_timing_*), and for
+ *    moe_decode a per-device arrival counter (static device memory) and ordering event.
  *    Outputs are fully overwritten, never accumulated into.
  *  - Arguments are validated on the host before anything is enqueued.  An invalid call returns
  *    MOE_EINVAL / MOE_ENOTSUP / MOE_EWORKSPACE and enqueues nothing; a failed launch returns
@@ -211,17 +212,21 @@ moe_status moe_backward(const moe_dims* dims, const void* dY, const void* X, con
 /* moe_decode — the whole forward layer in one kernel launch, for small token counts (decode /
  * inference): router logits, top-K with softmax, the selected experts' SwiGLU FFNs and the
  * weighted combine.  apxml.com "自定义核与核融合" (the five steps fused into one kernel) and
- * "条件参数加载" (only the selected experts' weights are read).  Plain top-K only
- * (round_mode must be MOE_ROUND_NONE, else MOE_ENOTSUP); T <= 1024.  The launch is cooperative:
- * every workgroup of the grid is resident at once and the phases are separated by grid-wide
- * barriers, so the call fails with MOE_EHIP rather than run if the device cannot host the grid.
- * Results equal moe_forward's up to rounding: the SwiGLU activation stays in fp32 between the
- * two projections (moe_forward rounds it to dtype), and the per-row dot products accumulate in
- * another order.
+ * "条件参数加载" (only the selected experts' weights are read, each once per 48 routed tokens).
+ * Plain top-K only (round_mode must be MOE_ROUND_NONE, else MOE_ENOTSUP); T <= 1024.  The
+ * launch is cooperative (one workgroup per CU, all resident, phases separated by grid-wide
+ * barriers), so the call fails with MOE_EHIP rather than run if the device cannot host the
+ * grid.  Decode kernels on one device never overlap: a call on another stream than the
+ * previous moe_decode call on that device first waits (hipStreamWaitEvent) for that call; the
+ * library keeps one event per device for this, created on first use.  Results
+ * equal moe_forward's with plain top-K up to the order of the fp32 accumulations (the SwiGLU
+ * activation is rounded to dtype between the projections, as in moe_forward); routing is the
+ * same function of the logits, ties to the lower expert id.
  *  X [T,d], W_r [E,d], bias [E] fp32 or NULL, W_gate/W_up [E,n,d], W_down [E,d,n] dtype.
  *  Outputs (overwritten): logits [T,E] fp32, topk_idx [T,K] int32, topk_w [T,K] fp32 (as in the
  *  plan of moe_route), out [T,d] dtype.
- *  ws: moe_workspace_bytes(dims, MOE_OP_DECODE) bytes (token lists and fp32 intermediates). */
+ *  ws: moe_workspace_bytes(dims, MOE_OP_DECODE) bytes (per-expert token lists, the activation
+ *  and the fp32 expert outputs of the T*K (token, expert) pairs); contents on entry unused. */
 moe_status moe_decode(const moe_dims* dims, const void* X, const void* W_r, const float* bias,
                       const void* W_gate, const void* W_up, const void* W_down, float* logits,
                       int32_t* topk_idx, float* topk_w, void* out, void* ws, size_t ws_bytes,

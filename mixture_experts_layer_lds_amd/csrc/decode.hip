@@ -36,6 +36,8 @@
 // fp32 accumulations.
 #include "internal.h"
 
+#include <mutex>
+
 namespace moe {
 
 constexpr int DEC_THREADS = 1024;  // 16 waves per workgroup, one workgroup per CU
@@ -544,6 +546,16 @@ __global__ __launch_bounds__(DEC_THREADS) void k_decode(DecodeArgs a) {
 
 static size_t dec_align(size_t b) { return (b + 255) / 256 * 256; }
 
+// Per device: the stream of the last decode launch and an event recorded after it (created on
+// first use, kept until the process ends).
+constexpr int kDecMaxDevices = 64;
+struct DecOrder {
+  hipEvent_t done = nullptr;
+  hipStream_t stream = nullptr;
+};
+static DecOrder g_dec_order[kDecMaxDevices];
+static std::mutex g_dec_order_mu;
+
 size_t decode_workspace_bytes(int64_t T, int64_t d, int64_t n, int E, int K) {
   return dec_align((size_t)E * 4) + dec_align((size_t)E * T * 4) + dec_align((size_t)T * K * n * 4) +
          dec_align((size_t)T * K * d * 4);
@@ -577,8 +589,25 @@ hipError_t launch_decode(const Shape& s, const void* X, const void* W_r, const f
   // every workgroup must be resident at once for the grid barriers: the cooperative launch
   // refuses a larger grid
   const int grid = cus * per_cu;
+  if (dev < 0 || dev >= kDecMaxDevices) return hipErrorInvalidDevice;
+  // The barrier counter is per device, so two of these kernels must never run at once: a call
+  // on another stream than the previous call on this device waits for that call first.
+  std::lock_guard<std::mutex> lock(g_dec_order_mu);
+  DecOrder& o = g_dec_order[dev];
+  if (!o.done) {
+    e = hipEventCreateWithFlags(&o.done, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+  } else if (o.stream != st) {
+    e = hipStreamWaitEvent(st, o.done, 0);
+    if (e != hipSuccess) return e;
+  }
   void* params[] = {&a};
-  return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(DEC_THREADS), params, 0u, st);
+  e = hipLaunchCooperativeKernel(fn, dim3(grid), dim3(DEC_THREADS), params, 0u, st);
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(o.done, st);
+  if (e != hipSuccess) return e;
+  o.stream = st;
+  return hipSuccess;
 }
 
 }  // namespace moe

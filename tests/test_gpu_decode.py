@@ -110,3 +110,31 @@ def test_decode_full_layer_shapes(name, T):
     cfg = base.with_(T=T, backward=False, round_mode=0)
     inp = wl.make_inputs(cfg, device="cuda")
     print(check_decode(cfg, inp, *run_decode(cfg, inp)))
+
+
+def test_decode_calls_on_two_streams_do_not_overlap():
+    """Decode calls on different streams (each with its own workspace) give the same bits as the
+    same calls on one stream: the library orders them, so their grid barriers never mix."""
+    cfgs = [wl.small_shape(T=24, d=512, E=32, K=4, n=256, dtype="bf16", backward=False, seed=s)
+            for s in (91, 92)]
+    inps = [wl.make_inputs(c, device="cuda") for c in cfgs]
+    refs = [run_decode(c, i) for c, i in zip(cfgs, inps)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for rep in range(3):
+        for j in (0, 1):
+            cfg, inp = cfgs[j], inps[j]
+            dims = B.make_dims(cfg.T, cfg.d, cfg.n, cfg.E, cfg.K, cfg.dtype)
+            with torch.cuda.stream(streams[j]):
+                o = [torch.empty(cfg.T, cfg.E, dtype=torch.float32, device="cuda"),
+                     torch.empty(cfg.T, cfg.K, dtype=torch.int32, device="cuda"),
+                     torch.empty(cfg.T, cfg.K, dtype=torch.float32, device="cuda"),
+                     torch.empty(cfg.T, cfg.d, dtype=torch.bfloat16, device="cuda")]
+                ws, nb = B.workspace(dims, B.OP_DECODE)
+                B.moe_decode(dims, inp["X"], inp["W_r"], inp["bias"], inp["W_gate"], inp["W_up"],
+                             inp["W_down"], *o, ws, nb, stream=streams[j])
+                outs.append((j, o, ws))
+    torch.cuda.synchronize()
+    for j, o, _ in outs:
+        for got, want in zip(o, refs[j]):
+            assert torch.equal(got, want)
