@@ -38,7 +38,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dact(
   if (!find_group_tile(lin, NT, mtile_off, expert_off, E, g)) return;
   const int nt = g.nt;
   const int n0 = nt * BN;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t rowb = (int64_t)d * sizeof(T);
   auto la = k_rows<T>([&](int i) -> const char* {
@@ -91,9 +91,11 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dact(
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          *reinterpret_cast<float*>(frow(acc_row(wm, i, v)) + (wn * 64 + jj * 32 + (lane & 31)) * 4) =
-              acc.c[i][2 * half + jj][v];
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v4 = {acc.c[i][2 * half + jj][4 * q], acc.c[i][2 * half + jj][4 * q + 1],
+                            acc.c[i][2 * half + jj][4 * q + 2], acc.c[i][2 * half + jj][4 * q + 3]};
+          *reinterpret_cast<f32x4*>(frow(acc_m(wm, i)) + (wn * 64 + jj * 32 + acc_n(4 * q)) * 4) = v4;
+        }
     u32x4 gv[UNR], uv[UNR];
     load_batch(half, 0, gv, uv);
     __syncthreads();
@@ -172,7 +174,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dx(
   if (!find_group_tile(lin, NT, mtile_off, expert_off, E, g)) return;
   const int nt = g.nt;
   const int n0 = nt * BN;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t rowb = (int64_t)2 * n * sizeof(T);
   auto la = k_rows<T>([&](int i) -> const char* {
@@ -187,23 +189,12 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dx(
   gemm_mainloop<T>(la, lb, 2 * n / Mma<T>::BK, acc, L, wm, [&](int j) { return bsub_plain(wn, j); });
   const int valid = min(BN, d - n0);
   if constexpr (sizeof(T) == 2) {
-    epi_stage_bf16(L, wm, [&](int j) { return bsub_plain(wn, j) + (lane & 31); },
+    epi_stage_bf16(L, wm, [&](int j) { return bsub_plain(wn, j); },
                    [&](int i, int j, int v) { return acc.c[i][j][v]; });
     __syncthreads();
     epi_store_bf16(L, 0, reinterpret_cast<bf16*>(dXp) + (int64_t)g.m0 * d + n0, d, g.mrows, BN, valid);
   } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = bsub_plain(wn, j) + (lane & 31);
-      if (c >= valid) continue;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = acc_row(wm, i, v);
-          if (m < g.mrows) dXp[(int64_t)(g.m0 + m) * d + n0 + c] = from_f32<T>(acc.c[i][j][v]);
-        }
-    }
+    epi_store_direct(wm, wn, acc, valid, g.mrows, [&](int m) { return dXp + (int64_t)(g.m0 + m) * d + n0; });
   }
 }
 
@@ -244,7 +235,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dw_down(
   int mt, nt;
   raster_tile(lin % per, MT, NT, mt, nt);
   const int m0 = mt * BM, n0 = nt * BN;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int off = expert_off[e];
   const int cnt = expert_off[e + 1] - off;
@@ -258,23 +249,12 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dw_down(
   T* out = dWd + (int64_t)e * d * n;
   const int mrows = min(BM, d - m0), valid = min(BN, n - n0);
   if constexpr (sizeof(T) == 2) {
-    epi_stage_bf16(L, wm, [&](int j) { return bsub_plain(wn, j) + (lane & 31); },
+    epi_stage_bf16(L, wm, [&](int j) { return bsub_plain(wn, j); },
                    [&](int i, int j, int v) { return acc.c[i][j][v]; });
     __syncthreads();
     epi_store_bf16(L, 0, reinterpret_cast<bf16*>(out) + (int64_t)m0 * n + n0, n, mrows, BN, valid);
   } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = bsub_plain(wn, j) + (lane & 31);
-      if (c >= valid) continue;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = acc_row(wm, i, v);
-          if (m < mrows) out[(int64_t)(m0 + m) * n + n0 + c] = from_f32<T>(acc.c[i][j][v]);
-        }
-    }
+    epi_store_direct(wm, wn, acc, valid, mrows, [&](int m) { return out + (int64_t)(m0 + m) * n + n0; });
   }
 }
 
@@ -306,7 +286,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dw_gu(
   int mt, nt;
   raster_tile(lin % per, MT, NT, mt, nt);
   const int m0 = mt * BM, n0 = nt * BN;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int off = expert_off[e];
   const int cnt = expert_off[e + 1] - off;
@@ -323,23 +303,12 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dw_gu(
     return (m < n ? dWg + ((int64_t)e * n + m) * d : dWu + ((int64_t)e * n + (m - n)) * d) + n0;
   };
   if constexpr (sizeof(T) == 2) {
-    epi_stage_bf16(L, wm, [&](int j) { return bsub_plain(wn, j) + (lane & 31); },
+    epi_stage_bf16(L, wm, [&](int j) { return bsub_plain(wn, j); },
                    [&](int i, int j, int v) { return acc.c[i][j][v]; });
     __syncthreads();
     epi_store_rows(L, 0, [&](int r) { return reinterpret_cast<bf16*>(row_ptr(r)); }, mrows, BN, valid);
   } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = bsub_plain(wn, j) + (lane & 31);
-      if (c >= valid) continue;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = acc_row(wm, i, v);
-          if (m < mrows) row_ptr(m)[c] = from_f32<T>(acc.c[i][j][v]);
-        }
-    }
+    epi_store_direct(wm, wn, acc, valid, mrows, row_ptr);
   }
 }
 
@@ -512,7 +481,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dwr(
   int mt, nt;
   raster_tile(lin % per, MT, NT, mt, nt);
   const int m0 = mt * BM, n0 = nt * BN;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int t0 = sl * TS;
   const int klen = min(TS, T_ - t0);
@@ -523,19 +492,19 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dwr(
   WaveAcc acc;
   gemm_mainloop<T>(la, lb, (int)cdiv(klen, Mma<T>::BK), acc, L, wm, [&](int j) { return bsub_plain(wn, j); });
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = n0 + bsub_plain(wn, j) + (lane & 31);
-    if (c >= d) continue;
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int v = 0; v < 16; ++v) {
+      const int c = n0 + bsub_plain(wn, j) + acc_n(v);
+      if (c >= d) continue;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = m0 + acc_row(wm, i, v);
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + acc_m(wm, i);
         if (m >= E) continue;
         if (S == 1) dWr[(int64_t)m * d + c] = from_f32<T>(acc.c[i][j][v]);
         else part[((int64_t)sl * E + m) * d + c] = acc.c[i][j][v];
       }
-  }
+    }
 }
 
 template <typename T>

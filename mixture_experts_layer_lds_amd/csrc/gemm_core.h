@@ -40,6 +40,8 @@
 //   row (v / 4) * 8 + (l / 32) * 4 + (v % 4), column l % 32.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -248,11 +250,13 @@ __device__ __forceinline__ void load_frags(const char* slot, int ks, int wm, BSu
 
 // MFMA blocks p = FROM .. TO-1 of one k-step, block p = (i, j) = (p / 4, p % 4).  Block 0 goes
 // first on its own: the compiler waits for all outstanding LDS reads before an MFMA that needs
-// fragments, so reads issued after it never delay the current k-step.
+// fragments, so reads issued after it never delay the current k-step.  The B fragment is the
+// MFMA's first operand, so each block accumulates the transposed product: a lane holds one tile
+// row and runs of four consecutive columns (acc_m / acc_n below).
 template <int FROM, int TO>
 __device__ __forceinline__ void mma_range(const FragSet& F, WaveAcc& acc) {
 #pragma unroll
-  for (int p = FROM; p < TO; ++p) acc.c[p >> 2][p & 3] = Mma<bf16>::mma(F.a[p >> 2], F.b[p & 3], acc.c[p >> 2][p & 3]);
+  for (int p = FROM; p < TO; ++p) acc.c[p >> 2][p & 3] = Mma<bf16>::mma(F.b[p & 3], F.a[p >> 2], acc.c[p >> 2][p & 3]);
 }
 
 // Workgroup barrier without a memory fence (the DMA waits are explicit); the empty asm keeps the
@@ -408,15 +412,10 @@ __device__ __forceinline__ void dma_step_burst(AL& la, BL& lb, int s, int nkt, c
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// The bf16 main loop over nkt stages.  SPLIT selects dma_step_split (each refill in two halves,
-// one DMA per four MFMAs: for K-major operands with good cache locality) or dma_step_burst.
-template <bool SPLIT, class AL, class BL, class BSub>
-__device__ __forceinline__ void gemm_mainloop_dma(AL& la, BL& lb, int nkt, WaveAcc& acc,
-                                                  LdsBufs L, int wm, BSub bsub) {
-  zero_acc(acc);
-  if (nkt <= 0) return;
-  // SPLIT: stages 0 and 1 whole and the first half of stage 2 (its second half goes out in
-  // step 0); burst: stages 0, 1 and 2 whole
+// Issues stages 0, 1 and 2 of a tile into ring slots 0, 1 and 2 (SPLIT: the first half of stage
+// 2; step 0 issues the rest).  The slots must be free.  Requires nkt >= 1.
+template <bool SPLIT, class AL, class BL>
+__device__ __forceinline__ void gemm_prologue_dma(AL& la, BL& lb, int nkt, LdsBufs L) {
 #pragma unroll
   for (int i = 0; i < 3; ++i) {
     const int r = min(i, nkt - 1);
@@ -433,14 +432,24 @@ __device__ __forceinline__ void gemm_mainloop_dma(AL& la, BL& lb, int nkt, WaveA
       lb.issue_q(q, L.b[i] + DMA_B_OFF);
     }
   }
-  FragSet F0, F1;
   if constexpr (SPLIT) {
     la.fetch(min(3, nkt - 1));  // ids of the stage step 0 prepares
     lb.fetch(min(3, nkt - 1));
-    wait_vmcnt<12>();  // stage 0 has landed: stage 1 (8) and half of stage 2 (4) came after it
-  } else {
-    wait_vmcnt<16>();  // stage 0 has landed: stages 1 and 2 (16) came after it
   }
+}
+
+// The k-steps of a tile whose prologue has been issued: waits for stage 0 and runs all nkt
+// steps, accumulating from zero.  Memory operations issued between the prologue and this call
+// (a previous tile's epilogue stores) only make the waits longer: loads complete in order among
+// themselves, so "at most N operations outstanding" still implies that every load older than
+// the newest N has landed.  Ends with the LDS free.
+template <bool SPLIT, class AL, class BL, class BSub>
+__device__ __forceinline__ void gemm_body_dma(AL& la, BL& lb, int nkt, WaveAcc& acc, LdsBufs L, int wm,
+                                              BSub bsub) {
+  zero_acc(acc);
+  FragSet F0, F1;
+  if constexpr (SPLIT) wait_vmcnt<12>();  // stage 0 has landed: stage 1 (8) and half of stage 2 (4) came after it
+  else wait_vmcnt<16>();                  // stage 0 has landed: stages 1 and 2 (16) came after it
   ring_barrier();
   load_frags<AL, BL>(L.b[0], 0, wm, bsub, F0);
   auto step = [&](int st, char* b0, char* b1, char* b2, char* b3) {
@@ -459,6 +468,19 @@ __device__ __forceinline__ void gemm_mainloop_dma(AL& la, BL& lb, int nkt, WaveA
   if (s + 1 < nkt) step(s + 1, L.b[1], L.b[2], L.b[3], L.b[0]);
   if (s + 2 < nkt) step(s + 2, L.b[2], L.b[3], L.b[0], L.b[1]);
   __syncthreads();  // drains the trailing loads; the LDS is free for the epilogue
+}
+
+// The bf16 main loop over nkt stages.  SPLIT selects dma_step_split (each refill in two halves,
+// one DMA per four MFMAs: for K-major operands with good cache locality) or dma_step_burst.
+template <bool SPLIT, class AL, class BL, class BSub>
+__device__ __forceinline__ void gemm_mainloop_dma(AL& la, BL& lb, int nkt, WaveAcc& acc,
+                                                  LdsBufs L, int wm, BSub bsub) {
+  if (nkt <= 0) {
+    zero_acc(acc);
+    return;
+  }
+  gemm_prologue_dma<SPLIT>(la, lb, nkt, L);
+  gemm_body_dma<SPLIT>(la, lb, nkt, acc, L, wm, bsub);
 }
 
 // ===============================================================================================
@@ -560,7 +582,7 @@ __device__ __forceinline__ void gemm_mainloop_reg(LA& la, LB& lb, int nkt, WaveA
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc.c[i][j] = Mma<float>::mma(a[i], b[j], acc.c[i][j]);
+        for (int j = 0; j < 4; ++j) acc.c[i][j] = Mma<float>::mma(b[j], a[i], acc.c[i][j]);
     }
     if (more) {
       la.store((kt & 1) ? L.b[0] : L.b[2]);
@@ -620,25 +642,27 @@ __device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nkt, WaveAcc& 
 // K stages for a K extent of `k` elements.
 template <typename T> __host__ __device__ constexpr int stage_k() { return Mma<T>::BK; }
 
-// Column (within the 256-wide tile) of N block j of wave column wn, for lane l:
-//   plain:  wn * 128 + j * 32 + l % 32
-//   halved: (j / 2) * 128 + wn * 64 + (j % 2) * 32 + l % 32   (each 128-column half of the tile
-//           holds two of the wave's blocks: used where the tile's halves are gate and up, or where
-//           the epilogue works one half at a time)
+// First tile column (within the 256-wide tile) of N block j of wave column wn; the block covers
+// 32 columns from there (lane l's B fragment is column + l % 32):
+//   plain:  wn * 128 + j * 32
+//   halved: (j / 2) * 128 + wn * 64 + (j % 2) * 32   (each 128-column half of the tile holds two
+//           of the wave's blocks: used where the tile's halves are gate and up, or where the
+//           epilogue works one half at a time)
 __device__ __forceinline__ int bsub_plain(int wn, int j) { return wn * 128 + j * 32; }
 __device__ __forceinline__ int bsub_halved(int wn, int j) { return (j >> 1) * 128 + wn * 64 + (j & 1) * 32; }
 
-// Tile row of accumulator register v for M block i of wave row wm.
-__device__ __forceinline__ int acc_row(int wm, int i, int v) {
-  const int lane = threadIdx.x & 63;
-  return wm * 128 + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-}
+// Accumulator placement (the MFMAs compute the transposed block): register v of block (i, j)
+// of wave (wm, wn) holds tile row acc_m(wm, i) and column bsub(wn, j) + acc_n(v); registers
+// 4q .. 4q + 3 are four consecutive columns of the same row.
+__device__ __forceinline__ int acc_m(int wm, int i) { return wm * 128 + i * 32 + (threadIdx.x & 31); }
+__device__ __forceinline__ int acc_n(int v) { return (v >> 2) * 8 + ((threadIdx.x >> 5) & 1) * 4 + (v & 3); }
 
 // ---------------------------------------------------------------------------------------------
 // Epilogue through LDS for 2-byte outputs.  Tile row r lives in buffer r / 64 at row r % 64 of a
-// [64][256 bf16 + 16 B] staging array.  epi_stage_bf16 writes val(i, j, v) at (acc_row, col(j))
-// (col < 0 skips), epi_store_bf16 stores rows < mrows and columns < ncols_valid with 16-byte
-// writes through row_ptr(r) (null skips).  Requires the LDS to be free.
+// [64][256 bf16 + 16 B] staging array.  epi_stage_bf16 writes val(i, j, v) at (acc_m, col(j) +
+// acc_n(v)), four consecutive columns per 8-byte LDS write (col(j) < 0 skips block j);
+// epi_store_bf16 stores rows < mrows and columns < ncols_valid with 16-byte writes through
+// row_ptr(r) (null skips).  Requires the LDS to be free.
 // ---------------------------------------------------------------------------------------------
 constexpr int EPI_ROW = 256 * 2 + 16;
 static_assert(64 * EPI_ROW <= LDS_BUF, "staging rows per buffer");
@@ -648,6 +672,10 @@ __device__ __forceinline__ char* epi_buf(LdsBufs L, int r) {
 }
 __device__ __forceinline__ char* epi_row(LdsBufs L, int r) { return epi_buf(L, r) + (r & 63) * EPI_ROW; }
 
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)hi) << 16);
+}
+
 template <class Col, class Val>
 __device__ __forceinline__ void epi_stage_bf16(LdsBufs L, int wm, Col col, Val val) {
 #pragma unroll
@@ -655,10 +683,15 @@ __device__ __forceinline__ void epi_stage_bf16(LdsBufs L, int wm, Col col, Val v
     const int c = col(j);
     if (c < 0) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      char* row = epi_row(L, acc_m(wm, i));
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        *reinterpret_cast<bf16*>(epi_row(L, acc_row(wm, i, v)) + c * 2) = (bf16)val(i, j, v);
+      for (int q = 0; q < 4; ++q) {
+        const u32x2 pk = {pack_bf16x2(val(i, j, 4 * q), val(i, j, 4 * q + 1)),
+                          pack_bf16x2(val(i, j, 4 * q + 2), val(i, j, 4 * q + 3))};
+        *reinterpret_cast<u32x2*>(row + (c + acc_n(4 * q)) * 2) = pk;
+      }
+    }
   }
 }
 
@@ -694,6 +727,28 @@ __device__ __forceinline__ void epi_store_rows(LdsBufs L, int col0, RowPtr row_p
 __device__ __forceinline__ void epi_store_bf16(LdsBufs L, int col0, bf16* out, int64_t ld, int mrows,
                                                int ncols, int ncols_valid) {
   epi_store_rows(L, col0, [&](int r) { return out + (int64_t)r * ld; }, mrows, ncols, ncols_valid);
+}
+
+// Direct element stores of a wave's accumulators (the fp32 layers' epilogue): row_ptr(m) is tile
+// row m's output at the tile's first column (plain block layout); rows >= mrows and columns >=
+// valid are skipped.
+template <class RowPtr>
+__device__ __forceinline__ void epi_store_direct(int wm, int wn, const WaveAcc& acc, int valid, int mrows,
+                                                 RowPtr row_ptr) {
+  using T = typename std::remove_pointer<decltype(row_ptr(0))>::type;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = acc_m(wm, i);
+    if (m >= mrows) continue;
+    T* out = row_ptr(m);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int c = bsub_plain(wn, j) + acc_n(v);
+        if (c < valid) out[c] = from_f32<T>(acc.c[i][j][v]);
+      }
+  }
 }
 
 // Grouped tiles.  The experts' ceil(rows / BM) m-tiles are concatenated (mtile_off is their

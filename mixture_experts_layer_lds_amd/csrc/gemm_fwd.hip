@@ -57,7 +57,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_router(const T* __restrict_
   const int mt = lin / NT, nt = lin % NT;
   const int m0 = mt * BM, n0 = nt * BN;
   if (m0 >= T_) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t rowb = (int64_t)d * sizeof(T);
   auto la = k_rows<T>([&](int i) -> const char* {
@@ -69,18 +69,18 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_router(const T* __restrict_
   WaveAcc acc;
   gemm_mainloop<T, true>(la, lb, d / Mma<T>::BK, acc, L, wm, [&](int j) { return bsub_plain(wn, j); });
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = n0 + bsub_plain(wn, j) + (lane & 31);
-    if (n >= E) continue;
-    const float b = bias ? bias[n] : 0.0f;
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int v = 0; v < 16; ++v) {
+      const int n = n0 + bsub_plain(wn, j) + acc_n(v);
+      if (n >= E) continue;
+      const float b = bias ? bias[n] : 0.0f;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = m0 + acc_row(wm, i, v);
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + acc_m(wm, i);
         if (m < T_) logits[(int64_t)m * E + n] = acc.c[i][j][v] + b;
       }
-  }
+    }
 }
 
 hipError_t launch_router_gemm(const Shape& s, const void* X, const void* W_r, const float* bias,
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_up(
   if (!find_group_tile(lin, NT, mtile_off, expert_off, E, g)) return;
   const int nt = g.nt;
   const int j0 = nt * 128;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t rowb = (int64_t)d * sizeof(T);
   auto la = k_rows<T>([&](int i) -> const char* {
@@ -139,14 +139,14 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_up(
       const float gv = acc.c[i][j & 1][v], uv = acc.c[i][(j & 1) + 2][v];
       return gv * sigmoid_f32(gv) * uv;
     };
-    auto colf = [&](int j) { return j < 2 ? bsub_halved(wn, j) + (lane & 31) : -1; };
+    auto colf = [&](int j) { return j < 2 ? bsub_halved(wn, j) : -1; };
     epi_stage_bf16(L, wm, colf, silu_u);
     __syncthreads();
     epi_store_bf16(L, 0, reinterpret_cast<bf16*>(act) + (int64_t)g.m0 * n + j0, n, g.mrows, 128, valid);
     if (H) {
       // G and U halves side by side in one staging tile: columns [0,128) G, [128,256) U
       __syncthreads();
-      auto both = [&](int j) { return bsub_halved(wn, j) + (lane & 31); };
+      auto both = [&](int j) { return bsub_halved(wn, j); };
       epi_stage_bf16(L, wm, both, [&](int i, int j, int v) { return acc.c[i][j][v]; });
       __syncthreads();
       bf16* hb = reinterpret_cast<bf16*>(H) + (int64_t)g.m0 * 2 * n;
@@ -155,15 +155,15 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_up(
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int ccol = bsub_halved(wn, j) + (lane & 31);  // act column within the tile
-      if (ccol >= valid) continue;
-      const int col = j0 + ccol;
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int v = 0; v < 16; ++v) {
+        const int ccol = bsub_halved(wn, j) + acc_n(v);  // act column within the tile
+        if (ccol >= valid) continue;
+        const int col = j0 + ccol;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = acc_row(wm, i, v);
+        for (int i = 0; i < 4; ++i) {
+          const int m = acc_m(wm, i);
           if (m >= g.mrows) continue;
           const int64_t r = g.m0 + m;
           const float gv = acc.c[i][j][v], uv = acc.c[i][j + 2][v];
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_up(
             H[r * 2 * n + n + col] = from_f32<T>(uv);
           }
         }
-    }
+      }
   }
 }
 
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_down(
   if (!find_group_tile(lin, NT, mtile_off, expert_off, E, g)) return;
   const int nt = g.nt;
   const int n0 = nt * BN;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t rowb = (int64_t)n * sizeof(T);
   auto la = k_rows<T>([&](int i) -> const char* {
@@ -219,23 +219,12 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_down(
   gemm_mainloop<T, true>(la, lb, n / Mma<T>::BK, acc, L, wm, [&](int j) { return bsub_plain(wn, j); });
   const int valid = min(BN, d - n0);
   if constexpr (sizeof(T) == 2) {
-    epi_stage_bf16(L, wm, [&](int j) { return bsub_plain(wn, j) + (lane & 31); },
+    epi_stage_bf16(L, wm, [&](int j) { return bsub_plain(wn, j); },
                    [&](int i, int j, int v) { return acc.c[i][j][v]; });
     __syncthreads();
     epi_store_bf16(L, 0, reinterpret_cast<bf16*>(Y) + (int64_t)g.m0 * d + n0, d, g.mrows, BN, valid);
   } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = bsub_plain(wn, j) + (lane & 31);
-      if (c >= valid) continue;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = acc_row(wm, i, v);
-          if (m < g.mrows) Y[(int64_t)(g.m0 + m) * d + n0 + c] = from_f32<T>(acc.c[i][j][v]);
-        }
-    }
+    epi_store_direct(wm, wn, acc, valid, g.mrows, [&](int m) { return Y + (int64_t)(g.m0 + m) * d + n0; });
   }
 }
 
