@@ -129,7 +129,8 @@ enum {
   MOE_OP_COMBINE = 3,
   MOE_OP_FORWARD = 4,
   MOE_OP_BACKWARD = 5,
-  MOE_OP_DECODE = 6
+  MOE_OP_DECODE = 6,
+  MOE_OP_FFN_FP8 = 7
 };
 
 /* Host: upper bound on R for these dims (T*K without rounding; rounding can add at most
@@ -232,6 +233,34 @@ moe_status moe_decode(const moe_dims* dims, const void* X, const void* W_r, cons
                       int32_t* topk_idx, float* topk_w, void* out, void* ws, size_t ws_bytes,
                       void* stream);
 
+/* moe_quantize_fp8 — per-row FP8 quantisation (apxml.com "硬件加速的考量", section "利用稀疏性和
+ * 量化": FP8 weights and activations).  Format: OCP FP8 E4M3 codes (bias 7, largest finite 448,
+ * no infinities), one fp32 scale per row: the smallest power of two s with max|row| / s <= 448
+ * (s = 1 for a row of zeros); code = the nearest E4M3 value to x / s, ties to even.  Value of an
+ * element = decode(code) * s.
+ *  src [rows, K] dtype (MOE_BF16 or MOE_F32), rows >= 0, K a positive multiple of 8; finite
+ *  values (results for NaN / infinity are unspecified).  codes [rows, K] uint8 and scales [rows]
+ *  fp32, overwritten.  Weights are quantised once with this call (W_gate / W_up as [E*n, d],
+ *  W_down as [E*d, n]); moe_grouped_ffn_fp8 quantises its activation itself. */
+moe_status moe_quantize_fp8(int64_t rows, int64_t K, int dtype, const void* src, uint8_t* codes,
+                            float* scales, void* stream);
+
+/* moe_grouped_ffn_fp8 — the experts' SwiGLU FFN with FP8 (E4M3, per-row scales, see
+ * moe_quantize_fp8) operands on gathered token rows: MFMA on the codes with fp32 accumulation,
+ * scales applied to the sums.  dims.dtype must be MOE_BF16 (the activation and Y_perm are bf16).
+ *  Xq [T,d] uint8 + sx [T] fp32: the tokens, quantised per row;
+ *  Wg_q, Wu_q [E,n,d] uint8 + sg, su [E,n] fp32;  Wd_q [E,d,n] uint8 + sd [E,d] fp32.
+ *  Outputs (rows r < R of the plan; rows past R untouched):
+ *    act   [R_max,n] bf16: silu(G_r) U_r with G = s_x s_g (xq wg_q^T), U likewise;
+ *    act_q [R_max,n] uint8 + sact [R_max] fp32: act quantised per row;
+ *    Y_perm [R_max,d] bf16: Y_r = s_a s_d (act_q wd_q^T).
+ *  ws: moe_workspace_bytes(dims, MOE_OP_FFN_FP8) bytes. */
+moe_status moe_grouped_ffn_fp8(const moe_dims* dims, const moe_plan* plan, const uint8_t* Xq,
+                               const float* sx, const uint8_t* Wg_q, const float* sg,
+                               const uint8_t* Wu_q, const float* su, const uint8_t* Wd_q,
+                               const float* sd, void* act, uint8_t* act_q, float* sact,
+                               void* Y_perm, void* ws, size_t ws_bytes, void* stream);
+
 /* Stages of the layer, for the timing facility below.  Each stage is one kernel, except ROUTE
  * (top-K, counts, token rounding, offsets, placement) and DWR_GEMM (GEMM + slice reduction). */
 typedef enum {
@@ -249,7 +278,10 @@ typedef enum {
   MOE_STAGE_ROUTER_BWD = 11, /* dS, dLogits and the dX gather-sum */
   MOE_STAGE_DWR_GEMM = 12,
   MOE_STAGE_DECODE = 13,     /* the single-launch forward of moe_decode */
-  MOE_STAGE_COUNT = 14
+  MOE_STAGE_FP8_QUANT = 14,  /* FP8 row quantisation (moe_quantize_fp8 and the activation's) */
+  MOE_STAGE_FP8_UP = 15,     /* FP8 gate/up GEMM + SwiGLU */
+  MOE_STAGE_FP8_DOWN = 16,   /* FP8 down GEMM */
+  MOE_STAGE_COUNT = 17
 } moe_stage;
 
 /* Host: stage timing for measurement tools (not thread-safe; for a single host thread).

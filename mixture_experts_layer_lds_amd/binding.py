@@ -4,7 +4,8 @@ Argument marshalling only: torch tensors become device pointers, the current tor
 becomes the hipStream_t, and non-zero status codes become ``MoEError``.  Every computation runs
 in the library's HIP kernels; if the library is missing, the first call raises.
 The functions keep the C names: ``moe_route``, ``moe_permute``, ``moe_grouped_ffn``,
-``moe_combine``, ``moe_forward``, ``moe_backward`` (plus sizing helpers).
+``moe_combine``, ``moe_forward``, ``moe_backward``, ``moe_decode``, ``moe_quantize_fp8``,
+``moe_grouped_ffn_fp8`` (plus sizing helpers).
 """
 import ctypes
 import os
@@ -16,14 +17,16 @@ LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 
 MOE_F32, MOE_BF16 = 0, 1
 ROUND_NONE, ROUND_NEAREST, ROUND_UP, ROUND_DOWN, ROUND_STOCHASTIC = 0, 1, 2, 3, 4
-OP_ROUTE, OP_PERMUTE, OP_FFN, OP_COMBINE, OP_FORWARD, OP_BACKWARD, OP_DECODE = range(7)
+OP_ROUTE, OP_PERMUTE, OP_FFN, OP_COMBINE, OP_FORWARD, OP_BACKWARD, OP_DECODE, OP_FFN_FP8 = range(8)
 STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ENOTSUP", -3: "MOE_EWORKSPACE", -4: "MOE_EHIP"}
 
 EXPORTS = ["moe_max_rows", "moe_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_ffn",
-           "moe_combine", "moe_forward", "moe_backward", "moe_decode", "moe_status_string", "moe_last_error",
+           "moe_combine", "moe_forward", "moe_backward", "moe_decode", "moe_quantize_fp8",
+           "moe_grouped_ffn_fp8", "moe_status_string", "moe_last_error",
            "moe_version", "moe_timing_enable", "moe_timing_read"]
 STAGES = ["router_gemm", "route", "tiles", "up_gemm", "down_gemm", "permute", "combine", "dact_gemm",
-          "dw_down_gemm", "dw_gu_gemm", "dx_gemm", "router_bwd", "dwr_gemm", "decode"]
+          "dw_down_gemm", "dw_gu_gemm", "dx_gemm", "router_bwd", "dwr_gemm", "decode", "fp8_quant",
+          "fp8_up_gemm", "fp8_down_gemm"]
 
 
 class MoEError(RuntimeError):
@@ -71,8 +74,10 @@ def lib():
         L.moe_backward.argtypes = [pd, vp, vp, vp, vp, vp, vp, pp, vp, vp, vp, vp, vp, vp, vp, vp,
                                    vp, sz, vp]
         L.moe_decode.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_quantize_fp8.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, vp, vp, vp, vp]
+        L.moe_grouped_ffn_fp8.argtypes = [pd, pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         for f in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward",
-                  "moe_backward", "moe_decode"):
+                  "moe_backward", "moe_decode", "moe_quantize_fp8", "moe_grouped_ffn_fp8"):
             getattr(L, f).restype = st
         L.moe_status_string.argtypes, L.moe_status_string.restype = [ctypes.c_int], ctypes.c_char_p
         L.moe_last_error.argtypes, L.moe_last_error.restype = [], ctypes.c_char_p
@@ -195,6 +200,20 @@ def moe_decode(dims, X, W_r, bias, W_gate, W_up, W_down, logits, topk_idx, topk_
     _check(lib().moe_decode(ctypes.byref(dims), _p(X), _p(W_r), _p(bias), _p(W_gate), _p(W_up),
                             _p(W_down), _p(logits), _p(topk_idx), _p(topk_w), _p(out), _p(ws), ws_bytes,
                             _stream(stream)))
+
+
+def moe_quantize_fp8(src, codes, scales, stream=None):
+    """Per-row E4M3 codes and power-of-two scales of a 2-D bf16 / fp32 tensor (rows x K)."""
+    rows, K = src.shape[0], src.shape[-1]
+    dtype = MOE_BF16 if src.dtype == torch.bfloat16 else MOE_F32
+    _check(lib().moe_quantize_fp8(rows, K, dtype, _p(src), _p(codes), _p(scales), _stream(stream)))
+
+
+def moe_grouped_ffn_fp8(dims, plan, Xq, sx, Wg_q, sg, Wu_q, su, Wd_q, sd, act, act_q, sact, Y_perm, ws,
+                        ws_bytes, stream=None):
+    _check(lib().moe_grouped_ffn_fp8(ctypes.byref(dims), plan.ref(), _p(Xq), _p(sx), _p(Wg_q), _p(sg),
+                                     _p(Wu_q), _p(su), _p(Wd_q), _p(sd), _p(act), _p(act_q), _p(sact),
+                                     _p(Y_perm), _p(ws), ws_bytes, _stream(stream)))
 
 
 def moe_backward(dims, dY, X, W_r, W_gate, W_up, W_down, plan, H_cache, dX, dW_gate, dW_up, dW_down,

@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_mi355x.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["route.hip", "gemm_fwd.hip", "backward.hip", "combine.hip", "decode.hip", "moe_api.cpp"]
+SOURCES = ["route.hip", "gemm_fwd.hip", "backward.hip", "combine.hip", "decode.hip", "fp8.hip", "moe_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -1,0 +1,223 @@
+// FP8 expert FFN: per-row E4M3 quantisation and the grouped gate/up and down GEMMs on codes.
+//
+// Pages: apxml.com "硬件加速的考量", section "利用稀疏性和量化" / "量化" (weights and activations
+// in low precision such as FP8: smaller experts, fewer bytes moved when the active experts are
+// loaded, faster low-precision matrix units).  The pages fix no format or scaling; this path
+// uses OCP FP8 E4M3 codes with one power-of-two scale per row of every operand (token rows of
+// activations, output channels of weights): the smallest power of two s with max|row| / s <= 448.
+// A power of two makes x / s exact, so the encoding (nearest code, ties to even) is decided the
+// same way in any precision.
+//
+//   k_quant_fp8:  rows x K elements -> codes [rows][K] (uint8) and scales [rows] (fp32);
+//   k_up_fp8:     act = silu(G) U with G, U = (Xq[rows] [Wg_q; Wu_q]^T) * s_x * s_w, gathered token
+//                 rows as in the bf16 gate/up GEMM; act stored in bf16;
+//   k_down_fp8:   Y = (act_q Wd_q^T) * s_a * s_d, stored in bf16.
+// The GEMMs run the bf16 path's DMA ring and tile schedule with 64 one-byte elements per stage
+// on v_mfma_scale_f32_32x32x64_f8f6f4 (fp32 accumulation of exact products); the scales are
+// applied in the epilogue.
+#include "gemm_core.h"
+#include "internal.h"
+
+namespace moe {
+
+// Nearest E4M3 code of a finite fp32 value with |q| <= 448, ties to even.  As an integer a
+// non-negative code is monotone in its value: subnormals m 2^-9 have code m (m = 8 is the
+// smallest normal 2^-6), a normal value (1 + f) 2^e has code 8 (e + 7) + round(8 f).
+__device__ __forceinline__ uint32_t e4m3_code(float q) {
+  const uint32_t b = __float_as_uint(q);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const float a = fabsf(q);
+  uint32_t code;
+  if (a < 0.015625f) {
+    code = (uint32_t)rintf(a * 512.0f);  // exact product; rintf rounds half to even
+  } else {
+    const uint32_t ab = b & 0x7fffffffu;
+    const int e = (int)(ab >> 23) - 127;
+    const uint32_t m = ab & 0x7fffffu, r = m >> 20, rem = m & 0xfffffu;
+    const uint32_t up = (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ? 1u : 0u;
+    code = (uint32_t)((e + 7) << 3) + r + up;
+  }
+  return code | sign;
+}
+
+// One wave per row (four per workgroup).  rows_dev (optional) bounds the rows on the device.
+template <typename T>
+__global__ __launch_bounds__(256) void k_quant_fp8(const T* __restrict__ src, int64_t rows, int K,
+                                                   const int32_t* __restrict__ rows_dev, uint8_t* __restrict__ codes,
+                                                   float* __restrict__ scales) {
+  constexpr int VEC = 16 / sizeof(T);
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t nrows = rows_dev ? (int64_t)rows_dev[0] : rows;
+  if (row >= rows || row >= nrows) return;
+  const T* s = src + row * K;
+  float amax = 0.0f;
+  for (int c = lane * VEC; c < K; c += 64 * VEC) {
+    float f[8];
+    unpack16<T>(ld16(s + c), f);
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  }
+  amax = wave_max(amax);
+  int sexp = 0;
+  if (amax > 0.0f) {
+    int ex;
+    const float fr = frexpf(amax, &ex);  // amax = fr 2^ex, fr in [0.5, 1)
+    sexp = ex - 9 + (fr > 0.875f ? 1 : 0);
+  }
+  if (lane == 0) scales[row] = ldexpf(1.0f, sexp);
+  uint8_t* o = codes + row * K;
+  for (int c = lane * VEC; c < K; c += 64 * VEC) {
+    float f[8];
+    unpack16<T>(ld16(s + c), f);
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) w[i >> 2] |= e4m3_code(ldexpf(f[i], -sexp)) << (8 * (i & 3));
+    if constexpr (VEC == 8) *reinterpret_cast<u32x2*>(o + c) = u32x2{w[0], w[1]};
+    else *reinterpret_cast<uint32_t*>(o + c) = w[0];
+  }
+}
+
+hipError_t launch_quant_fp8(const void* src, bool is_bf16, int64_t rows, int64_t K, const int32_t* rows_dev,
+                            uint8_t* codes, float* scales, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)((rows + 3) / 4);
+  if (is_bf16)
+    k_quant_fp8<bf16><<<grid, 256, 0, st>>>(static_cast<const bf16*>(src), rows, (int)K, rows_dev, codes, scales);
+  else
+    k_quant_fp8<float><<<grid, 256, 0, st>>>(static_cast<const float*>(src), rows, (int)K, rows_dev, codes, scales);
+  return hipGetLastError();
+}
+
+// Four consecutive fp32 scales at p (16-byte aligned), or zeros past `valid` columns.
+__device__ __forceinline__ f32x4 scales4(const float* p, bool ok) {
+  return ok ? *reinterpret_cast<const f32x4*>(p) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+// ---------------------------------------------------------------------------------------------
+// Gate/up: tile = 256 rows of one expert x 128 act columns j0 .. j0 + 127; the B tile stacks
+// W_gate[e] rows j0 .. j0 + 127 over W_up[e] rows j0 .. j0 + 127 (halved block layout, so G and
+// U of a (row, column) sit in accumulator blocks j and j + 2 of the same lane).
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(GEMM_THREADS, 1) void k_up_fp8(
+    const int32_t* __restrict__ mtile_off, const int32_t* __restrict__ expert_off,
+    const int32_t* __restrict__ row_token, const uint8_t* __restrict__ Xq, const float* __restrict__ sx,
+    const uint8_t* __restrict__ Wgq, const float* __restrict__ sg, const uint8_t* __restrict__ Wuq,
+    const float* __restrict__ su, bf16* __restrict__ act, int d, int n, int E, int NT, int T_) {
+  MOE_GEMM_LDS(L);
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  GroupTile g;
+  if (!find_group_tile(lin, NT, mtile_off, expert_off, E, g)) return;
+  const int j0 = g.nt * 128;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t rowb = d;  // one byte per element
+  KDma la, lb;
+  la.init([&](int i) -> const char* {
+    if (i >= g.mrows) return nullptr;
+    return reinterpret_cast<const char*>(Xq) + (int64_t)clamp_idx(row_token[g.m0 + i], T_) * rowb;
+  });
+  const char* wg = reinterpret_cast<const char*>(Wgq) + (int64_t)g.e * n * rowb;
+  const char* wu = reinterpret_cast<const char*>(Wuq) + (int64_t)g.e * n * rowb;
+  lb.init([&](int i) -> const char* {
+    const int j = j0 + (i & 127);
+    if (j >= n) return nullptr;
+    return (i < 128 ? wg : wu) + (int64_t)j * rowb;
+  });
+  WaveAcc acc;
+  auto bsub = [&](int j) { return bsub_halved(wn, j); };
+  gemm_mainloop_f8(la, lb, d / 64, acc, L, wm, bsub);
+  const int valid = min(128, n - j0);
+  // row scales of the wave's four row blocks (token rows) and column scales of its gate/up columns
+  float srow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = acc_m(wm, i);
+    srow[i] = r < g.mrows ? sx[clamp_idx(row_token[g.m0 + r], T_)] : 0.0f;
+  }
+  f32x4 cg[2][4], cu[2][4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = bsub(j) + acc_n(4 * q);
+      const int64_t w = (int64_t)g.e * n + j0 + c;
+      cg[j][q] = scales4(sg + w, c < valid);
+      cu[j][q] = scales4(su + w, c < valid);
+    }
+  auto silu_u = [&](int i, int j, int v) {
+    const float gv = acc.c[i][j & 1][v] * srow[i] * cg[j & 1][v >> 2][v & 3];
+    const float uv = acc.c[i][(j & 1) + 2][v] * srow[i] * cu[j & 1][v >> 2][v & 3];
+    return gv * sigmoid_f32(gv) * uv;
+  };
+  epi_stage_bf16(L, wm, [&](int j) { return j < 2 ? bsub(j) : -1; }, silu_u);
+  __syncthreads();
+  epi_store_bf16(L, 0, act + (int64_t)g.m0 * n + j0, n, g.mrows, 128, valid);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Down: Y[r][c] = (sum_j act_q[r][j] Wd_q[e][c][j]) s_a[r] s_d[e][c]; tile 256 rows x 256
+// columns of d.
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(GEMM_THREADS, 1) void k_down_fp8(
+    const int32_t* __restrict__ mtile_off, const int32_t* __restrict__ expert_off,
+    const uint8_t* __restrict__ Aq, const float* __restrict__ sa, const uint8_t* __restrict__ Wdq,
+    const float* __restrict__ sd, bf16* __restrict__ Y, int d, int n, int E, int NT) {
+  MOE_GEMM_LDS(L);
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  GroupTile g;
+  if (!find_group_tile(lin, NT, mtile_off, expert_off, E, g)) return;
+  const int n0 = g.nt * BN;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t rowb = n;
+  KDma la, lb;
+  la.init([&](int i) -> const char* {
+    return i < g.mrows ? reinterpret_cast<const char*>(Aq) + (int64_t)(g.m0 + i) * rowb : nullptr;
+  });
+  const char* wd = reinterpret_cast<const char*>(Wdq) + (int64_t)g.e * d * rowb;
+  lb.init([&](int i) -> const char* { return n0 + i < d ? wd + (int64_t)(n0 + i) * rowb : nullptr; });
+  WaveAcc acc;
+  auto bsub = [&](int j) { return bsub_plain(wn, j); };
+  gemm_mainloop_f8(la, lb, n / 64, acc, L, wm, bsub);
+  const int valid = min(BN, d - n0);
+  float srow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = acc_m(wm, i);
+    srow[i] = r < g.mrows ? sa[g.m0 + r] : 0.0f;
+  }
+  f32x4 cs[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = bsub(j) + acc_n(4 * q);
+      cs[j][q] = scales4(sd + (int64_t)g.e * d + n0 + c, c < valid);
+    }
+  epi_stage_bf16(L, wm, bsub, [&](int i, int j, int v) { return acc.c[i][j][v] * srow[i] * cs[j][v >> 2][v & 3]; });
+  __syncthreads();
+  epi_store_bf16(L, 0, Y + (int64_t)g.m0 * d + n0, d, g.mrows, BN, valid);
+}
+
+static inline int grid8f(int64_t n) { return (int)((n + 7) / 8 * 8); }
+
+hipError_t launch_up_fp8(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off, const uint8_t* Xq,
+                         const float* sx, const uint8_t* Wgq, const float* sg, const uint8_t* Wuq,
+                         const float* su, void* act, hipStream_t st) {
+  const int NT = (int)cdiv(s.n, 128);
+  k_up_fp8<<<grid8f(max_mtiles(s.R_max, s.E) * NT), GEMM_THREADS, 0, st>>>(
+      mtile_off, p.expert_off, p.row_token, Xq, sx, Wgq, sg, Wuq, su, static_cast<bf16*>(act), (int)s.d,
+      (int)s.n, s.E, NT, (int)s.T);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_fp8(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off, const uint8_t* Aq,
+                           const float* sa, const uint8_t* Wdq, const float* sd, void* Y, hipStream_t st) {
+  const int NT = (int)cdiv(s.d, BN);
+  k_down_fp8<<<grid8f(max_mtiles(s.R_max, s.E) * NT), GEMM_THREADS, 0, st>>>(
+      mtile_off, p.expert_off, Aq, sa, Wdq, sd, static_cast<bf16*>(Y), (int)s.d, (int)s.n, s.E, NT);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -484,6 +484,104 @@ __device__ __forceinline__ void gemm_mainloop_dma(AL& la, BL& lb, int nkt, WaveA
 }
 
 // ===============================================================================================
+// FP8 (OCP E4M3) operands: 1-byte elements through the same DMA ring.  A stage's 64 bytes per
+// row are 64 elements, so K-major loading (KDma) is unchanged and a stage is one k-step of 16
+// v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales; per-row scales are applied by the
+// epilogue).  A lane's fragment is 32 consecutive k of its row (lane half h: k 32 h .. 32 h + 31);
+// A and B use the same placement, which is all the product needs.
+// ===============================================================================================
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+struct FragSet8 {
+  i32x8 a[4], b[4];
+};
+
+__device__ __forceinline__ i32x8 frag8(const char* t, int row0) {
+  const int lane = threadIdx.x & 63;
+  const int r = row0 + (lane & 31), h = lane >> 5, sw = (r >> 2) & 3;
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(t + r * 64 + ((2 * h) ^ sw) * 16);
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(t + r * 64 + ((2 * h + 1) ^ sw) * 16);
+  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+template <class BSub>
+__device__ __forceinline__ void load_frags8(const char* slot, int wm, BSub bsub, FragSet8& F) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) F.b[j] = frag8(slot + DMA_B_OFF, bsub(j));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) F.a[i] = frag8(slot, wm * 128 + i * 32);
+}
+
+// Blocks p = FROM .. TO-1, block p = (i, j) = (p / 4, p % 4); B first (transposed block, as in
+// the bf16 path).  Scale operands 127 = 2^0 in E8M0.
+template <int FROM, int TO>
+__device__ __forceinline__ void mma8_range(const FragSet8& F, WaveAcc& acc) {
+#pragma unroll
+  for (int p = FROM; p < TO; ++p)
+    acc.c[p >> 2][p & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.b[p & 3], F.a[p >> 2], acc.c[p >> 2][p & 3],
+                                                                           0, 0, 0, 127, 0, 127);
+}
+
+// One ring step for stage s (FP8): F0 holds stage s's fragments.  Its first eight blocks go
+// first; then the wait for stage s + 1 and the barrier (every wave is done with stage s - 1,
+// whose slot takes stage s + 3 -- past the end, the last stage again, so the DMA count per step
+// is fixed); then stage s + 1's fragments are read into F1 and the refill goes out, one
+// instruction per operand between pairs of the last eight blocks.
+template <class AL, class BL, class BSub>
+__device__ __forceinline__ void dma_step_f8(AL& la, BL& lb, int s, int nkt, const char* next, char* refill,
+                                            FragSet8& F0, FragSet8& F1, WaveAcc& acc, int wm, BSub bsub) {
+  const int r = min(s + 3, nkt - 1);
+  mma8_range<0, 1>(F0, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  la.fetch(r);
+  lb.fetch(r);
+  mma8_range<1, 8>(F0, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<8>();
+  ring_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  load_frags8(next, wm, bsub, F1);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    la.prepare_q(r, q);
+    lb.prepare_q(r, q);
+    la.issue_q(q, refill);
+    lb.issue_q(q, refill + DMA_B_OFF);
+    __builtin_amdgcn_sched_barrier(0);
+    if (q == 0) mma8_range<8, 10>(F0, acc);
+    if (q == 1) mma8_range<10, 12>(F0, acc);
+    if (q == 2) mma8_range<12, 14>(F0, acc);
+    if (q == 3) mma8_range<14, 16>(F0, acc);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// The FP8 main loop over nkt stages of 64 elements (prologue as in the bf16 burst schedule).
+template <class AL, class BL, class BSub>
+__device__ __forceinline__ void gemm_mainloop_f8(AL& la, BL& lb, int nkt, WaveAcc& acc, LdsBufs L, int wm,
+                                                 BSub bsub) {
+  zero_acc(acc);
+  if (nkt <= 0) return;
+  gemm_prologue_dma<false>(la, lb, nkt, L);
+  FragSet8 F0, F1;
+  wait_vmcnt<16>();  // stage 0 has landed: stages 1 and 2 (16) came after it
+  ring_barrier();
+  load_frags8(L.b[0], wm, bsub, F0);
+  int s = 0;
+  for (; s + 4 <= nkt; s += 4) {
+    dma_step_f8(la, lb, s, nkt, L.b[1], L.b[3], F0, F1, acc, wm, bsub);
+    dma_step_f8(la, lb, s + 1, nkt, L.b[2], L.b[0], F1, F0, acc, wm, bsub);
+    dma_step_f8(la, lb, s + 2, nkt, L.b[3], L.b[1], F0, F1, acc, wm, bsub);
+    dma_step_f8(la, lb, s + 3, nkt, L.b[0], L.b[2], F1, F0, acc, wm, bsub);
+  }
+  if (s < nkt) dma_step_f8(la, lb, s, nkt, L.b[1], L.b[3], F0, F1, acc, wm, bsub);
+  if (s + 1 < nkt) dma_step_f8(la, lb, s + 1, nkt, L.b[2], L.b[0], F1, F0, acc, wm, bsub);
+  if (s + 2 < nkt) dma_step_f8(la, lb, s + 2, nkt, L.b[3], L.b[1], F0, F1, acc, wm, bsub);
+  __syncthreads();  // drains the trailing loads; the LDS is free for the epilogue
+}
+
+// ===============================================================================================
 // fp32: register-staged double buffer
 // ===============================================================================================
 constexpr int KROW = 128 + 16;              // padded K-major row pitch (bytes)

@@ -35,8 +35,8 @@ size_t route_workspace_bytes(int64_t T, int E);
 hipError_t launch_route(const float* logits, int64_t T, int E, int K, int round_mode, int tile_m,
                         const uint32_t* round_rand, const PlanPtrs& p, void* ws, hipStream_t st);
 
-// ---- grouped GEMM tile schedule (gemm.hip) ----
-// mtile_off[E+1] = exclusive scan over experts of ceil(counts[e] / 128).
+// ---- grouped GEMM tile schedule (gemm_fwd.hip) ----
+// mtile_off[E+1] = exclusive scan over experts of ceil(counts[e] / 256).
 hipError_t launch_tile_offsets(const int32_t* counts, int E, int32_t* mtile_off, hipStream_t st);
 int64_t max_mtiles(int64_t R_max, int E);
 
@@ -51,6 +51,16 @@ hipError_t launch_up_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mtil
 // Y[R,d] = Act[R,n] W_down[e]^T
 hipError_t launch_down_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off,
                             const void* act, const void* W_down, void* Y, hipStream_t st);
+
+// ---- FP8 expert FFN (fp8.hip) ----
+// codes/scales of rows x K elements (rows_dev: optional device row bound, e.g. the plan's R)
+hipError_t launch_quant_fp8(const void* src, bool is_bf16, int64_t rows, int64_t K, const int32_t* rows_dev,
+                            uint8_t* codes, float* scales, hipStream_t st);
+hipError_t launch_up_fp8(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off, const uint8_t* Xq,
+                         const float* sx, const uint8_t* Wgq, const float* sg, const uint8_t* Wuq,
+                         const float* su, void* act, hipStream_t st);
+hipError_t launch_down_fp8(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off, const uint8_t* Aq,
+                           const float* sa, const uint8_t* Wdq, const float* sd, void* Y, hipStream_t st);
 
 // ---- permute / combine (combine.hip) ----
 hipError_t launch_permute(const Shape& s, const PlanPtrs& p, const void* X, void* X_perm, hipStream_t st);

@@ -190,6 +190,7 @@ size_t ws_bytes_for(const moe_dims* dm, int op) {
     }
     case MOE_OP_BACKWARD: carve_bwd(c, dm); return c.off;
     case MOE_OP_DECODE: return decode_workspace_bytes(dm->T, dm->d, dm->n, dm->E, dm->K);
+    case MOE_OP_FFN_FP8: c.take((size_t)(dm->E + 1) * 4); return c.off;
     default: return 0;
   }
 }
@@ -264,7 +265,7 @@ int64_t moe_max_rows(const moe_dims* dims) {
 
 size_t moe_workspace_bytes(const moe_dims* dims, int op) {
   if (check_dims(dims) != MOE_OK) return 0;
-  if (op < MOE_OP_ROUTE || op > MOE_OP_DECODE) {
+  if (op < MOE_OP_ROUTE || op > MOE_OP_FFN_FP8) {
     fail(MOE_EINVAL, "unknown op %d", op);
     return 0;
   }
@@ -324,6 +325,56 @@ moe_status moe_combine(const moe_dims* dims, const moe_plan* plan, const void* Y
   hipStream_t st = static_cast<hipStream_t>(stream);
   MOE_STAGE(MOE_STAGE_COMBINE, st, launch_combine(shape_of(dims), plan_ptrs(plan), Y_perm, weighted != 0, out, st),
             "combine");
+  return MOE_OK;
+}
+
+moe_status moe_quantize_fp8(int64_t rows, int64_t K, int dtype, const void* src, uint8_t* codes,
+                            float* scales, void* stream) {
+  if (rows < 0 || rows > ((int64_t)1 << 31)) return fail(MOE_EINVAL, "rows=%lld out of range", (long long)rows);
+  if (K < 8 || K > 65536 || K % 8) return fail(MOE_EINVAL, "K=%lld must be a multiple of 8 in [8, 65536]", (long long)K);
+  if (dtype != MOE_BF16 && dtype != MOE_F32) return fail(MOE_ENOTSUP, "dtype %d not supported", dtype);
+  if (rows == 0) return MOE_OK;
+  MOE_TRY(need_ptr(src, "src"));
+  MOE_TRY(need_ptr(codes, "codes"));
+  MOE_TRY(need_ptr(scales, "scales"));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  MOE_STAGE(MOE_STAGE_FP8_QUANT, st, launch_quant_fp8(src, dtype == MOE_BF16, rows, K, nullptr, codes, scales, st),
+            "fp8 quantisation");
+  return MOE_OK;
+}
+
+moe_status moe_grouped_ffn_fp8(const moe_dims* dims, const moe_plan* plan, const uint8_t* Xq,
+                               const float* sx, const uint8_t* Wg_q, const float* sg,
+                               const uint8_t* Wu_q, const float* su, const uint8_t* Wd_q,
+                               const float* sd, void* act, uint8_t* act_q, float* sact,
+                               void* Y_perm, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_dims(dims));
+  if (dims->dtype != MOE_BF16) return fail(MOE_ENOTSUP, "moe_grouped_ffn_fp8 needs dtype MOE_BF16");
+  MOE_TRY(check_plan(plan));
+  MOE_TRY(need_ptr(Xq, "Xq"));
+  MOE_TRY(need_ptr(sx, "sx"));
+  MOE_TRY(need_ptr(Wg_q, "Wg_q"));
+  MOE_TRY(need_ptr(sg, "sg"));
+  MOE_TRY(need_ptr(Wu_q, "Wu_q"));
+  MOE_TRY(need_ptr(su, "su"));
+  MOE_TRY(need_ptr(Wd_q, "Wd_q"));
+  MOE_TRY(need_ptr(sd, "sd"));
+  MOE_TRY(need_ptr(act, "act"));
+  MOE_TRY(need_ptr(act_q, "act_q"));
+  MOE_TRY(need_ptr(sact, "sact"));
+  MOE_TRY(need_ptr(Y_perm, "Y_perm"));
+  MOE_TRY(check_ws(dims, MOE_OP_FFN_FP8, ws, ws_bytes));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const Shape s = shape_of(dims);
+  const PlanPtrs p = plan_ptrs(plan);
+  int32_t* mtile_off = static_cast<int32_t*>(ws);
+  MOE_STAGE(MOE_STAGE_TILES, st, launch_tile_offsets(p.counts, dims->E, mtile_off, st), "tile offsets");
+  MOE_STAGE(MOE_STAGE_FP8_UP, st, launch_up_fp8(s, p, mtile_off, Xq, sx, Wg_q, sg, Wu_q, su, act, st),
+            "fp8 gate/up GEMM");
+  MOE_STAGE(MOE_STAGE_FP8_QUANT, st, launch_quant_fp8(act, true, s.R_max, dims->n, p.meta, act_q, sact, st),
+            "fp8 activation quantisation");
+  MOE_STAGE(MOE_STAGE_FP8_DOWN, st, launch_down_fp8(s, p, mtile_off, act_q, sact, Wd_q, sd, Y_perm, st),
+            "fp8 down GEMM");
   return MOE_OK;
 }
 

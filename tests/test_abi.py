@@ -17,7 +17,7 @@ def header_functions():
     with open(os.path.join(ROOT, "include", "moe.h")) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -139,3 +139,22 @@ def test_binding_raises_moe_error():
     with pytest.raises(B.MoEError) as ei:
         B.moe_max_rows(dims(K=99))
     assert ei.value.status == -1
+
+
+def test_fp8_argument_checks(lib):
+    """moe_quantize_fp8: K a multiple of 8, bf16 / fp32 sources, required pointers, nothing to do
+    for rows = 0.  moe_grouped_ffn_fp8: bf16 layers only, required pointers, its workspace."""
+    q = lambda rows, K, dt=1, src=FAKE: lib.moe_quantize_fp8(rows, K, dt, src, FAKE, FAKE, None)
+    assert q(4, 12) == -1 and q(4, 0) == -1 and q(-1, 8) == -1
+    assert q(4, 16, dt=7) == -2
+    assert q(4, 16, src=None) == -1
+    assert q(0, 16, src=None) == 0
+    plan = B.PlanStruct(*([FAKE] * 9))
+    ffn = lambda d, ws=1 << 40, act=FAKE: lib.moe_grouped_ffn_fp8(
+        ctypes.byref(d), ctypes.byref(plan), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, act, FAKE,
+        FAKE, FAKE, FAKE, ws, None)
+    assert ffn(dims(dtype="f32")) == -2
+    assert ffn(dims(), act=None) == -1
+    need = B.moe_workspace_bytes(dims(), B.OP_FFN_FP8)
+    assert need >= (8 + 1) * 4
+    assert ffn(dims(), ws=need - 1) == -3
