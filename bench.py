@@ -24,6 +24,7 @@ import numpy as np
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
 PEAK_FP32_TFLOPS = 157.3      # MI355X dense fp32 MFMA (published)
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA (published)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
 METRIC = "MoE layer fwd+bwd useful TFLOPS and % bf16 MFMA peak, T=32768 fine-grained"
 
@@ -47,6 +48,9 @@ def parse():
     ap.add_argument("--decode", type=int, default=0, metavar="T",
                     help="instead of the layer step, time moe_decode (single-launch forward) on T "
                          "tokens of --config, next to moe_forward on the same tokens")
+    ap.add_argument("--fp8", action="store_true",
+                    help="instead of the layer step, time the forward with FP8 expert GEMMs (moe_route, "
+                         "moe_quantize_fp8 of X, moe_grouped_ffn_fp8, moe_combine) next to the bf16 moe_forward")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after warmup, run a plain 256 MiB copy kernel (torch neg on fp32) three times, "
                          "outside the timed region: the byte counters of a profiler run are scaled by it")
@@ -242,6 +246,108 @@ def decode_bench(args):
     print(json.dumps(res), flush=True)
 
 
+def fp8_bench(args):
+    """Forward layer with FP8 expert GEMMs on --config: routing as in bf16, X quantised per row
+    each step, the experts' weights quantised once before timing (they are the stored model),
+    activation quantised inside moe_grouped_ffn_fp8.  Useful FLOPs as for the bf16 forward."""
+    import torch
+    from mixture_experts_layer_lds_amd import binding as B
+    from mixture_experts_layer_lds_amd import workloads as wl
+
+    cfg = wl.BY_NAME[args.config].with_(backward=False, round_mode=0)
+    inp = wl.make_inputs(cfg, device="cuda", with_grad_out=False)
+    dims = B.make_dims(cfg.T, cfg.d, cfg.n, cfg.E, cfg.K, "bf16", cfg.round_mode, cfg.tile_m,
+                       inp["round_rand"])
+    T, d, n, E = cfg.T, cfg.d, cfg.n, cfg.E
+    plan = B.Plan(dims)
+    R_max = plan.R_max
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+
+    def quant(t, rows, K):
+        c, s_ = torch.empty(rows, K, **u8), torch.empty(rows, **f32)
+        B.moe_quantize_fp8(t.reshape(rows, K), c, s_)
+        return c, s_
+
+    Wgq, sg = quant(inp["W_gate"], E * n, d)
+    Wuq, su = quant(inp["W_up"], E * n, d)
+    Wdq, sd = quant(inp["W_down"], E * d, n)
+    Xq, sx = torch.empty(T, d, **u8), torch.empty(T, **f32)
+    logits = torch.empty(T, E, **f32)
+    act = torch.empty(R_max, n, dtype=torch.bfloat16, device="cuda")
+    act_q, sact = torch.empty(R_max, n, **u8), torch.empty(R_max, **f32)
+    Y = torch.empty(R_max, d, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(T, d, dtype=torch.bfloat16, device="cuda")
+    ws_r, nb_r = B.workspace(dims, B.OP_ROUTE)
+    ws_q, nb_q = B.workspace(dims, B.OP_FFN_FP8)
+    ws_f, nb_f = B.workspace(dims, B.OP_FORWARD)
+    out_bf = torch.empty_like(out)
+
+    def step():
+        B.moe_route(dims, inp["X"], inp["W_r"], inp["bias"], logits, plan, ws_r, nb_r)
+        B.moe_quantize_fp8(inp["X"], Xq, sx)
+        B.moe_grouped_ffn_fp8(dims, plan, Xq, sx, Wgq, sg, Wuq, su, Wdq, sd, act, act_q, sact, Y, ws_q, nb_q)
+        B.moe_combine(dims, plan, Y, 1, out)
+
+    def bf16_step():
+        B.moe_forward(dims, inp["X"], inp["W_r"], inp["bias"], inp["W_gate"], inp["W_up"], inp["W_down"],
+                      logits, plan, None, out_bf, ws_f, nb_f)
+
+    def timed(fn, with_stages):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        if with_stages:
+            B.moe_timing_enable(True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        st = {s: B.moe_timing_read(s) for s in B.STAGES} if with_stages else None
+        if with_stages:
+            B.moe_timing_enable(False)
+        return e0.elapsed_time(e1) / args.steps, st
+
+    ms_bf, _ = timed(bf16_step, False)
+    ms, stages = timed(step, True)
+    R = int(plan.meta[0].item())
+    rel = float((out.float() - out_bf.float()).abs().max() / out_bf.float().abs().max())
+    flops = 6 * R * d * n + 2 * T * d * E
+    value = flops / (ms * 1e-3) / 1e12
+    stage_fl = {"router_gemm": 2 * T * d * E, "fp8_up_gemm": 4 * R * d * n, "fp8_down_gemm": 2 * R * d * n}
+    breakdown = {}
+    for s_, v in stages.items():
+        if not v:
+            continue
+        avg = float(np.mean(v))
+        ent = {"launches_per_step": round(len(v) / args.steps, 3), "avg_ms": round(avg, 4),
+               "ms_per_step": round(float(np.sum(v)) / args.steps, 4)}
+        if s_ in stage_fl:
+            ent["tflops"] = round(stage_fl[s_] / (avg * 1e-3) / 1e12, 1)
+        breakdown[s_] = ent
+    dom = max(("fp8_up_gemm", "fp8_down_gemm"), key=lambda s_: breakdown[s_]["ms_per_step"])
+    avg = breakdown[dom]["avg_ms"]
+    ach = stage_fl[dom] / (avg * 1e-3) / 1e12
+    res = {
+        "metric": "MoE layer fwd useful TFLOPS, FP8 (E4M3, per-row scales) expert GEMMs, %s" % cfg.name,
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3 (bf16 activations between the GEMMs)",
+        "data": "synthetic (seeded normal inputs and random-init weights)",
+        "config": {"workload": cfg.name, "T": T, "d": d, "n": n, "E": E, "K": cfg.K, "pass": "fwd", "rows": R,
+                   "parallelism": "single GPU"},
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": None, "avg_ms": avg},
+        "bf16_forward_ms": round(ms_bf, 4),
+        "speedup_vs_bf16_forward": round(ms_bf / ms, 3),
+        "max_rel_diff_vs_bf16_forward": round(rel, 4),
+        "stages": breakdown,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -251,6 +357,8 @@ def main():
         sys.exit(2)
     if args.decode:
         return decode_bench(args)
+    if args.fp8:
+        return fp8_bench(args)
     import torch
     from mixture_experts_layer_lds_amd import binding as B
     from mixture_experts_layer_lds_amd import workloads as wl
