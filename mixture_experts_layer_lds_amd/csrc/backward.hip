@@ -60,12 +60,15 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dact(
   float* red = reinterpret_cast<float*>(L.b[0] + 64 * FROW);  // [256] dS partials of this tile
   auto frow = [&](int r) { return epi_buf(L, r) + (r & 63) * FROW; };
   const int valid = min(BN, n - n0);
-  // The block walks chunk c = row * CPR + ch in batches of UNR chunks per thread; a batch's G and
-  // U loads are all issued before any of them is used (the first batch of a half before the
-  // barrier that follows the accumulator dump), so their latency overlaps.
+  // The block walks chunk c = row * CPR + ch in batches of UNR chunks per thread.  The G, U and
+  // row-weight loads of PF batches go out together -- for bf16 a whole half, issued before the
+  // accumulator dump and its barrier -- so the half costs one memory round trip, not one per
+  // batch.
   constexpr int UNR = 4;
   constexpr int NB = 256 * CPR / (UNR * GEMM_THREADS);  // batches per half
   static_assert(NB * UNR * GEMM_THREADS == 256 * CPR, "whole batches");
+  constexpr int PF = sizeof(T) == 2 ? 2 : 1;             // batches in flight together
+  static_assert(NB % PF == 0, "whole groups");
   auto chunk_at = [&](int half, int b, int u, int& row, int& ch, int& col) {
     const int c = (b * UNR + u) * GEMM_THREADS + threadIdx.x;
     row = c / CPR;
@@ -73,19 +76,25 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dact(
     col = half * 128 + ch * VEC;
     return row < g.mrows && col < valid;
   };
-  auto load_batch = [&](int half, int b, u32x4* gv, u32x4* uv) {
+  u32x4 gv[PF][UNR], uv[PF][UNR];
+  float wv[PF][UNR];
+  auto load_group = [&](int half, int b0) {
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      int row, ch, col;
-      if (chunk_at(half, b, u, row, ch, col)) {
-        const int64_t r = g.m0 + row;
-        gv[u] = ld16(H + r * 2 * n + n0 + col);
-        uv[u] = ld16(H + r * 2 * n + n + n0 + col);
+    for (int pb = 0; pb < PF; ++pb)
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        int row, ch, col;
+        if (chunk_at(half, b0 + pb, u, row, ch, col)) {
+          const int64_t r = g.m0 + row;
+          gv[pb][u] = ld16(H + r * 2 * n + n0 + col);
+          uv[pb][u] = ld16(H + r * 2 * n + n + n0 + col);
+          wv[pb][u] = row_w[r];
+        }
       }
-    }
   };
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
+    load_group(half, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -96,42 +105,43 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dact(
                             acc.c[i][2 * half + jj][4 * q + 2], acc.c[i][2 * half + jj][4 * q + 3]};
           *reinterpret_cast<f32x4*>(frow(acc_m(wm, i)) + (wn * 64 + jj * 32 + acc_n(4 * q)) * 4) = v4;
         }
-    u32x4 gv[UNR], uv[UNR];
-    load_batch(half, 0, gv, uv);
     __syncthreads();
-    for (int b = 0; b < NB; ++b) {
-      if (b > 0) load_batch(half, b, gv, uv);
+#pragma unroll 1
+    for (int b0 = 0; b0 < NB; b0 += PF) {
+      if (b0 > 0) load_group(half, b0);
 #pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        int row, ch, col;
-        float p = 0.0f;
-        if (chunk_at(half, b, u, row, ch, col)) {
-          const int64_t r = g.m0 + row;
-          const float w = row_w[r];
-          float dAp[VEC], G[VEC], U[VEC], oG[VEC], oU[VEC], oA[VEC];
+      for (int pb = 0; pb < PF; ++pb)
 #pragma unroll
-          for (int k = 0; k < VEC; ++k) dAp[k] = *reinterpret_cast<const float*>(frow(row) + (ch * VEC + k) * 4);
-          unpack16<T>(gv[u], G);
-          unpack16<T>(uv[u], U);
+        for (int u = 0; u < UNR; ++u) {
+          int row, ch, col;
+          float p = 0.0f;
+          if (chunk_at(half, b0 + pb, u, row, ch, col)) {
+            const int64_t r = g.m0 + row;
+            const float w = wv[pb][u];
+            float dAp[VEC], G[VEC], U[VEC], oG[VEC], oU[VEC], oA[VEC];
 #pragma unroll
-          for (int k = 0; k < VEC; ++k) {
-            const float sg = sigmoid_f32(G[k]);
-            const float silu = G[k] * sg;
-            const float A = silu * U[k];
-            p += dAp[k] * A;
-            const float dA = w * dAp[k];
-            oG[k] = dA * U[k] * sg * (1.0f + G[k] * (1.0f - sg));
-            oU[k] = dA * silu;
-            oA[k] = w * A;
+            for (int k = 0; k < VEC; ++k) dAp[k] = *reinterpret_cast<const float*>(frow(row) + (ch * VEC + k) * 4);
+            unpack16<T>(gv[pb][u], G);
+            unpack16<T>(uv[pb][u], U);
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+              const float sg = sigmoid_f32(G[k]);
+              const float silu = G[k] * sg;
+              const float A = silu * U[k];
+              p += dAp[k] * A;
+              const float dA = w * dAp[k];
+              oG[k] = dA * U[k] * sg * (1.0f + G[k] * (1.0f - sg));
+              oU[k] = dA * silu;
+              oA[k] = w * A;
+            }
+            st16(dH + r * 2 * n + n0 + col, pack16<T>(oG));
+            st16(dH + r * 2 * n + n + n0 + col, pack16<T>(oU));
+            st16(wA + r * n + n0 + col, pack16<T>(oA));
           }
-          st16(dH + r * 2 * n + n0 + col, pack16<T>(oG));
-          st16(dH + r * 2 * n + n + n0 + col, pack16<T>(oU));
-          st16(wA + r * n + n0 + col, pack16<T>(oA));
-        }
 #pragma unroll
-        for (int o = 1; o < CPR; o <<= 1) p += __shfl_xor(p, o, 64);
-        if (ch == 0) red[row] = half == 0 ? p : red[row] + p;
-      }
+          for (int o = 1; o < CPR; o <<= 1) p += __shfl_xor(p, o, 64);
+          if (ch == 0) red[row] = half == 0 ? p : red[row] + p;
+        }
     }
     __syncthreads();
   }

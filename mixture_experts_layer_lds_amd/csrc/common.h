@@ -22,9 +22,11 @@ template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 
-// silu(g) = g * sigmoid(g); sigmoid via the hardware exp2.  For g -> -inf, exp(-g) -> inf and the
-// quotient goes to -0, which is the limit.
-__device__ __forceinline__ float sigmoid_f32(float g) { return 1.0f / (1.0f + __expf(-g)); }
+// silu(g) = g * sigmoid(g); sigmoid via the hardware exp2 and the hardware reciprocal
+// (v_rcp_f32, about 1 ulp: the correctly rounded quotient costs a ten-instruction sequence per
+// element, which dominated the SwiGLU epilogues).  For g -> -inf, exp(-g) -> inf and the
+// reciprocal goes to 0, which is the limit.
+__device__ __forceinline__ float sigmoid_f32(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 // Wave-wide reductions (64 lanes) through cross-lane shuffles.
 __device__ __forceinline__ float wave_sum(float v) {
