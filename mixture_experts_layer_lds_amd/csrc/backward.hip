@@ -452,8 +452,9 @@ hipError_t launch_router_bwd(const Shape& s, const PlanPtrs& p, const float* dS_
 
 // ---------------------------------------------------------------------------------------------
 // Router weight gradient dW_r[e][c] = sum_t dL[t][e] X[t][c]  (M = E, N = d, K = T).  The token
-// range is split into S contiguous slices so that the few output tiles still fill the chip;
-// each slice writes fp32 partials and a second kernel sums the slices in a fixed order.
+// range is split into S contiguous slices so that the few output tiles still fill the chip in one
+// round (S * tiles <= 256 workgroups, one per CU); each slice writes fp32 partials, four
+// consecutive columns per 16-byte store, and a second kernel sums the slices in a fixed order.
 // ---------------------------------------------------------------------------------------------
 struct DwrPlan {
   int MT, NT, S, TS;  // tiles, slices, tokens per slice (multiple of the stage depth)
@@ -464,7 +465,7 @@ static DwrPlan dwr_plan(const Shape& s) {
   q.NT = (int)cdiv(s.d, BN);
   const int bk = s.bf16 ? Mma<bf16>::BK : Mma<float>::BK;
   const int tiles = q.MT * q.NT;
-  int S = (int)cdiv(512, tiles);
+  int S = 256 / tiles;
   const int max_s = (int)cdiv(s.T, bk);
   if (S > max_s) S = max_s;
   if (S > 64) S = 64;
@@ -501,18 +502,35 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dwr(
   auto lb = mn_rows<T>([=](int k) { return xb + (int64_t)(t0 + k) * d * sizeof(T); }, klen, n0, d);
   WaveAcc acc;
   gemm_mainloop<T>(la, lb, (int)cdiv(klen, Mma<T>::BK), acc, L, wm, [&](int j) { return bsub_plain(wn, j); });
+  if (S == 1) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int c = n0 + bsub_plain(wn, j) + acc_n(v);
+        if (c >= d) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = m0 + acc_m(wm, i);
+          if (m < E) dWr[(int64_t)m * d + c] = from_f32<T>(acc.c[i][j][v]);
+        }
+      }
+    return;
+  }
+  // partials: a lane's four accumulators v = 4q .. 4q + 3 are consecutive columns (d is a
+  // multiple of 64, so c < d implies c + 3 < d)
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int c = n0 + bsub_plain(wn, j) + acc_n(v);
+    for (int q = 0; q < 4; ++q) {
+      const int c = n0 + bsub_plain(wn, j) + acc_n(4 * q);
       if (c >= d) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = m0 + acc_m(wm, i);
         if (m >= E) continue;
-        if (S == 1) dWr[(int64_t)m * d + c] = from_f32<T>(acc.c[i][j][v]);
-        else part[((int64_t)sl * E + m) * d + c] = acc.c[i][j][v];
+        const f32x4 v4 = {acc.c[i][j][4 * q], acc.c[i][j][4 * q + 1], acc.c[i][j][4 * q + 2], acc.c[i][j][4 * q + 3]};
+        *reinterpret_cast<f32x4*>(part + ((int64_t)sl * E + m) * d + c) = v4;
       }
     }
 }
