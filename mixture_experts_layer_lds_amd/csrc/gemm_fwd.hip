@@ -68,17 +68,33 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_router(const T* __restrict_
   });
   WaveAcc acc;
   gemm_mainloop<T, true>(la, lb, d / Mma<T>::BK, acc, L, wm, [&](int j) { return bsub_plain(wn, j); });
+  // a lane's accumulators v = 4q .. 4q + 3 are four consecutive experts of one token: one 16-byte
+  // store when the logits rows keep them aligned (E % 4 == 0), else four 4-byte stores
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int n = n0 + bsub_plain(wn, j) + acc_n(v);
+    for (int q = 0; q < 4; ++q) {
+      const int n = n0 + bsub_plain(wn, j) + acc_n(4 * q);
       if (n >= E) continue;
-      const float b = bias ? bias[n] : 0.0f;
+      f32x4 b = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (bias) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) b[u] = n + u < E ? bias[n + u] : 0.0f;
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = m0 + acc_m(wm, i);
-        if (m < T_) logits[(int64_t)m * E + n] = acc.c[i][j][v] + b;
+        if (m >= T_) continue;
+        float* o = logits + (int64_t)m * E + n;
+        const f32x4 v4 = {acc.c[i][j][4 * q] + b[0], acc.c[i][j][4 * q + 1] + b[1], acc.c[i][j][4 * q + 2] + b[2],
+                          acc.c[i][j][4 * q + 3] + b[3]};
+        if ((E & 3) == 0) {
+          *reinterpret_cast<f32x4*>(o) = v4;
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (n + u < E) o[u] = v4[u];
+        }
       }
     }
 }
