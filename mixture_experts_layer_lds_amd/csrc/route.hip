@@ -12,11 +12,13 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------------------------
-// top-K: one wave per token, 16 waves per block of 64 tokens.  Lane i holds logits e = i + 64 j
-// as composite keys (order_key(L) << 32) | ~e, so that one unsigned maximum orders by logit
-// descending and then by expert id ascending; K rounds of a wave maximum pick the winners, whose
-// logits are re-read for the softmax over the K of them.  The winners set their bit in the
-// block's LDS bitmap (bitwise OR is order independent).
+// top-K: one wave per token, 16 waves per block of 64 tokens.  Lane i holds the order keys of
+// logits e = i + 64 j.  Each of K rounds picks the largest key among the candidates still in
+// play (a wave maximum through DPP row shifts and row broadcasts, no LDS traffic) and, among the
+// candidates holding it, the lowest expert id (ballots scanned in ascending e) -- the order of
+// logit descending, then expert id ascending.  The winners' logits are re-read for the softmax
+// over the K of them, and the winners set their bit in the block's LDS bitmap (bitwise OR is
+// order independent).
 // ---------------------------------------------------------------------------------------------
 constexpr int TOPK_TOKENS_PER_BLOCK = 64;  // two 32-bit bitmap words per expert per block
 constexpr int TOPK_THREADS = 1024;
@@ -30,6 +32,27 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   if (x != x) return 0u;
   const uint32_t u = __float_as_uint(x == 0.0f ? 0.0f : x);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Maximum of v over the 64 lanes, returned in every lane.  Within each row of 16 lanes, row
+// shifts by 1, 2, 3, 4 (lanes 4-15) and 8 (lanes 8-15) leave the row's maximum in its lane 15;
+// row broadcasts of lane 15 (into rows 1 and 3) and of lane 31 (into rows 2 and 3) then leave the
+// wave's maximum in lane 63.  Lanes whose DPP source is off the row or masked keep their own
+// value, which a maximum ignores.
+__device__ __forceinline__ uint32_t dpp_max_step(uint32_t v, uint32_t x) { return v > x ? v : x; }
+template <int CTRL, int ROWS, int BANKS>
+__device__ __forceinline__ uint32_t dpp_src(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWS, BANKS, false);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_max_step(v, dpp_src<0x111, 0xf, 0xf>(v));  // row_shr:1
+  v = dpp_max_step(v, dpp_src<0x112, 0xf, 0xf>(v));  // row_shr:2
+  v = dpp_max_step(v, dpp_src<0x113, 0xf, 0xf>(v));  // row_shr:3
+  v = dpp_max_step(v, dpp_src<0x114, 0xf, 0xe>(v));  // row_shr:4, lanes 4-15 of each row
+  v = dpp_max_step(v, dpp_src<0x118, 0xf, 0xc>(v));  // row_shr:8, lanes 8-15 of each row
+  v = dpp_max_step(v, dpp_src<0x142, 0xa, 0xf>(v));  // row_bcast:15 into rows 1 and 3
+  v = dpp_max_step(v, dpp_src<0x143, 0xc, 0xf>(v));  // row_bcast:31 into rows 2 and 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 template <int EPL>
@@ -46,26 +69,30 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const float* __restrict__
     const int t = t0 + tt;
     if (t >= T) break;
     const float* row = logits + (int64_t)t * E;
-    uint64_t ck[EPL];  // 0 = no candidate (a live composite is never 0: ~e != 0)
+    uint32_t key[EPL];
+    uint32_t alive = 0;  // bit j: candidate e = lane + 64 j still in play
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
       const int e = lane + 64 * j;
-      ck[j] = e < E ? (((uint64_t)order_key(row[e]) << 32) | (uint32_t)~(uint32_t)e) : 0ull;
+      key[j] = e < E ? order_key(row[e]) : 0u;
+      alive |= e < E ? (1u << j) : 0u;
     }
     int my_e = 0;
     for (int k = 0; k < K; ++k) {
-      uint64_t b = ck[0];
-#pragma unroll
-      for (int j = 1; j < EPL; ++j) b = ck[j] > b ? ck[j] : b;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint64_t x = __shfl_xor(b, o, 64);
-        b = x > b ? x : b;
-      }
+      uint32_t lm = 0;  // NaN keys are 0 too; ties at 0 are settled below among live candidates
 #pragma unroll
       for (int j = 0; j < EPL; ++j)
-        if (ck[j] == b) ck[j] = 0ull;
-      if (lane == k) my_e = (int)~(uint32_t)b;
+        if ((alive >> j) & 1u) lm = key[j] > lm ? key[j] : lm;
+      const uint32_t kmax = wave_max_u32(lm);
+      int win = -1;  // lowest expert id holding kmax (uniform)
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const uint64_t m = __builtin_amdgcn_ballot_w64(((alive >> j) & 1u) && key[j] == kmax);
+        if (win < 0 && m != 0ull) win = 64 * j + (int)__builtin_ctzll(m);
+      }
+      win = __builtin_amdgcn_readfirstlane(win);
+      if (lane == (win & 63)) alive &= ~(1u << (win >> 6));
+      if (lane == k) my_e = win;
     }
     const float my_v = lane < K ? row[my_e] : 0.0f;
     const float vmax = __shfl(my_v, 0, 64);
