@@ -430,8 +430,28 @@ __global__ __launch_bounds__(1024) void k_tok_scan(int T, int32_t* __restrict__ 
 // Placement: one thread per token.  The token's final experts in ascending id (plain top-K: its
 // K ids sorted; token rounding: the set bits of its bitmap column); gate weights = softmax of
 // its final logits; row of (t, e) = expert_off[e] + (members of e before t), a popcount.
+// Plain top-K sorts the ids with a bitonic network over KM >= K registers (padded with INT_MAX),
+// every index fixed at compile time so that nothing goes to scratch memory.
 // ---------------------------------------------------------------------------------------------
-template <bool ROUNDED>
+template <int N>
+__device__ __forceinline__ void bitonic_sort_i32(int (&a)[N]) {
+#pragma unroll
+  for (int k = 2; k <= N; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1)
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int l = i ^ j;
+        if (l > i) {
+          const int x = a[i], y = a[l];
+          const bool sw = ((i & k) == 0) ? (x > y) : (x < y);
+          a[i] = sw ? y : x;
+          a[l] = sw ? x : y;
+        }
+      }
+}
+
+template <bool ROUNDED, int KM>
 __global__ __launch_bounds__(256) void k_place(const float* __restrict__ logits, int T, int E,
                                                int K, int W, const int32_t* __restrict__ topk_idx,
                                                const uint32_t* __restrict__ bits,
@@ -452,24 +472,29 @@ __global__ __launch_bounds__(256) void k_place(const float* __restrict__ logits,
   const uint32_t me = 1u << (t & 31);
   const int base = tok_off[t];
   if (!ROUNDED) {
-    int ids[16];
-    for (int k = 0; k < K; ++k) ids[k] = topk_idx[(int64_t)t * K + k];
-    for (int k = 1; k < K; ++k) {  // insertion sort, K <= 16
-      const int x = ids[k];
-      int j = k - 1;
-      while (j >= 0 && ids[j] > x) { ids[j + 1] = ids[j]; --j; }
-      ids[j + 1] = x;
-    }
-    float m = L[ids[0]];
-    for (int k = 1; k < K; ++k) m = fmaxf(m, L[ids[k]]);
+    int ids[KM];
+    float lv[KM];
+#pragma unroll
+    for (int k = 0; k < KM; ++k) ids[k] = k < K ? topk_idx[(int64_t)t * K + k] : INT_MAX;
+    bitonic_sort_i32(ids);
+#pragma unroll
+    for (int k = 0; k < KM; ++k) lv[k] = k < K ? L[ids[k]] : -INFINITY;
+    float m = lv[0];
+#pragma unroll
+    for (int k = 1; k < KM; ++k)
+      if (k < K) m = fmaxf(m, lv[k]);
     float s = 0.0f;
-    for (int k = 0; k < K; ++k) s += __expf(L[ids[k]] - m);
+#pragma unroll
+    for (int k = 0; k < KM; ++k)
+      if (k < K) s += __expf(lv[k] - m);
     const float inv = 1.0f / s;
-    for (int k = 0; k < K; ++k) {
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+      if (k >= K) break;
       const int e = ids[k];
       const int row = expert_off[e] + wprefix[(int64_t)e * W + w] + __popc(bits[(int64_t)e * W + w] & below);
       row_token[row] = t;
-      row_w[row] = __expf(L[e] - m) * inv;
+      row_w[row] = __expf(lv[k] - m) * inv;
       tok_row[base + k] = row;
     }
   } else {
@@ -534,12 +559,18 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int K, int round_
   if (rounded) {
     k_tok_count<<<(int)cdiv(T, 256), 256, (size_t)E * 32, st>>>(bits, (int)T, E, W, p.tok_off);
     k_tok_scan<<<1, 1024, 0, st>>>((int)T, p.tok_off);
-    k_place<true><<<(int)cdiv(T, 256), 256, (size_t)E * 32, st>>>(logits, (int)T, E, K, W, p.topk_idx, bits, wprefix,
-                                                     p.expert_off, p.tok_off, p.row_token, p.row_w, p.tok_row);
+    k_place<true, 1><<<(int)cdiv(T, 256), 256, (size_t)E * 32, st>>>(logits, (int)T, E, K, W, p.topk_idx, bits,
+                                                                     wprefix, p.expert_off, p.tok_off, p.row_token,
+                                                                     p.row_w, p.tok_row);
   } else {
     k_tok_fill<<<(int)cdiv(T + 1, 256), 256, 0, st>>>((int)T, K, p.tok_off);
-    k_place<false><<<(int)cdiv(T, 256), 256, 0, st>>>(logits, (int)T, E, K, W, p.topk_idx, bits, wprefix,
-                                                      p.expert_off, p.tok_off, p.row_token, p.row_w, p.tok_row);
+#define MOE_PLACE(KM) k_place<false, KM><<<(int)cdiv(T, 256), 256, 0, st>>>(logits, (int)T, E, K, W, p.topk_idx, \
+      bits, wprefix, p.expert_off, p.tok_off, p.row_token, p.row_w, p.tok_row)
+    if (K <= 2) MOE_PLACE(2);
+    else if (K <= 4) MOE_PLACE(4);
+    else if (K <= 8) MOE_PLACE(8);
+    else MOE_PLACE(16);
+#undef MOE_PLACE
   }
   return hipGetLastError();
 }
