@@ -360,19 +360,23 @@ __device__ __forceinline__ void stage_block_bits(const uint32_t* __restrict__ bi
   __syncthreads();
 }
 
-// Tokens' final expert counts after token rounding -> tok_off[t+1] (scanned afterwards).
-// 256 threads per block, one token each; dynamic LDS E * 8 words.
+// Token rounding: the number of final rows of each block of 256 tokens -> blk[b + 1] (scanned
+// afterwards by k_tok_scan over the blocks).  256 threads per block, one token each; dynamic LDS
+// E * 8 words.
 __global__ __launch_bounds__(256) void k_tok_count(const uint32_t* __restrict__ bits, int T, int E,
-                                                   int W, int32_t* __restrict__ tok_off) {
+                                                   int W, int32_t* __restrict__ blk) {
   extern __shared__ uint32_t sb[];
+  __shared__ int sh[4];
   stage_block_bits(bits, E, W, sb);
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= T) return;
   const int wl = threadIdx.x >> 5;
-  const uint32_t m = 1u << (t & 31);
+  const uint32_t sh_t = t & 31;
   int c = 0;
-  for (int e = 0; e < E; ++e) c += (sb[e * 8 + wl] & m) ? 1 : 0;
-  tok_off[t + 1] = c;
+  if (t < T)
+    for (int e = 0; e < E; ++e) c += (sb[e * 8 + wl] >> sh_t) & 1u;
+  int tot;
+  block_exscan_256(c, &tot, sh);
+  if (threadIdx.x == 0) blk[blockIdx.x + 1] = tot;
 }
 
 // Plain top-K: every token has K rows.
@@ -433,6 +437,16 @@ __global__ __launch_bounds__(1024) void k_tok_scan(int T, int32_t* __restrict__ 
 // Plain top-K sorts the ids with a bitonic network over KM >= K registers (padded with INT_MAX),
 // every index fixed at compile time so that nothing goes to scratch memory.
 // ---------------------------------------------------------------------------------------------
+// Bit b of the result: token bit `tb` of the block bitmap word of expert e0 + b (experts >= E
+// read as 0).
+__device__ __forceinline__ uint32_t member_word(const uint32_t* sb, int E, int e0, int wl, int tb) {
+  uint32_t w32 = 0;
+#pragma unroll
+  for (int b = 0; b < 32; ++b)
+    if (e0 + b < E) w32 |= ((sb[(e0 + b) * 8 + wl] >> tb) & 1u) << b;
+  return w32;
+}
+
 template <int N>
 __device__ __forceinline__ void bitonic_sort_i32(int (&a)[N]) {
 #pragma unroll
@@ -457,20 +471,34 @@ __global__ __launch_bounds__(256) void k_place(const float* __restrict__ logits,
                                                const uint32_t* __restrict__ bits,
                                                const int32_t* __restrict__ wprefix,
                                                const int32_t* __restrict__ expert_off,
-                                               const int32_t* __restrict__ tok_off,
+                                               int32_t* __restrict__ tok_off,
+                                               const int32_t* __restrict__ blk,
                                                int32_t* __restrict__ row_token,
                                                float* __restrict__ row_w,
                                                int32_t* __restrict__ tok_row) {
   extern __shared__ uint32_t sb[];  // ROUNDED: the block's bitmap words, E * 8
-  if (ROUNDED) stage_block_bits(bits, E, W, sb);
+  __shared__ int sh[4];
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  const int wl = threadIdx.x >> 5;
+  int base;
+  if (ROUNDED) {
+    // the token's row count from the bitmap; its first row = the block's prefix (blk, scanned
+    // over blocks) + the exclusive scan of the counts inside the block
+    stage_block_bits(bits, E, W, sb);
+    int c = 0;
+    if (t < T)
+      for (int e = 0; e < E; ++e) c += (sb[e * 8 + wl] >> (t & 31)) & 1u;
+    int tot;
+    base = blk[blockIdx.x] + block_exscan_256(c, &tot, sh);
+    if (t < T) tok_off[t] = base;
+    if (t == T - 1) tok_off[T] = base + c;
+  } else {
+    base = t < T ? tok_off[t] : 0;
+  }
   if (t >= T) return;
   const float* L = logits + (int64_t)t * E;
   const int w = t >> 5;
-  const int wl = threadIdx.x >> 5;
   const uint32_t below = (1u << (t & 31)) - 1u;
-  const uint32_t me = 1u << (t & 31);
-  const int base = tok_off[t];
   if (!ROUNDED) {
     int ids[KM];
     float lv[KM];
@@ -498,24 +526,49 @@ __global__ __launch_bounds__(256) void k_place(const float* __restrict__ logits,
       tok_row[base + k] = row;
     }
   } else {
-    const int cnt = tok_off[t + 1] - base;
-    if (cnt == 0) return;
+    // The token's members, 32 experts at a time: a member word from the LDS bitmap, then the
+    // members' logits loaded together (independent loads), in ascending expert id throughout.
+    const int nck = (E + 31) / 32;
     float m = -INFINITY;
-    for (int e = 0; e < E; ++e)
-      if (sb[e * 8 + wl] & me) m = fmaxf(m, L[e]);
+    for (int ck = 0; ck < nck; ++ck) {
+      const uint32_t w32 = member_word(sb, E, ck * 32, wl, t & 31);
+      if (!w32) continue;
+      float v[32];
+#pragma unroll
+      for (int b = 0; b < 32; ++b) v[b] = ((w32 >> b) & 1u) ? L[ck * 32 + b] : -INFINITY;
+#pragma unroll
+      for (int b = 0; b < 32; ++b)
+        if ((w32 >> b) & 1u) m = fmaxf(m, v[b]);
+    }
     float s = 0.0f;
-    for (int e = 0; e < E; ++e)
-      if (sb[e * 8 + wl] & me) s += __expf(L[e] - m);
+    for (int ck = 0; ck < nck; ++ck) {
+      const uint32_t w32 = member_word(sb, E, ck * 32, wl, t & 31);
+      if (!w32) continue;
+      float v[32];
+#pragma unroll
+      for (int b = 0; b < 32; ++b) v[b] = ((w32 >> b) & 1u) ? L[ck * 32 + b] : 0.0f;
+#pragma unroll
+      for (int b = 0; b < 32; ++b)
+        if ((w32 >> b) & 1u) s += __expf(v[b] - m);
+    }
     const float inv = 1.0f / s;
     int i = 0;
-    for (int e = 0; e < E; ++e) {
-      const uint32_t word = sb[e * 8 + wl];
-      if (!(word & me)) continue;
-      const int row = expert_off[e] + wprefix[(int64_t)e * W + w] + __popc(word & below);
-      row_token[row] = t;
-      row_w[row] = __expf(L[e] - m) * inv;
-      tok_row[base + i] = row;
-      ++i;
+    for (int ck = 0; ck < nck; ++ck) {
+      const uint32_t w32 = member_word(sb, E, ck * 32, wl, t & 31);
+      if (!w32) continue;
+      float v[32];
+#pragma unroll
+      for (int b = 0; b < 32; ++b) v[b] = ((w32 >> b) & 1u) ? L[ck * 32 + b] : 0.0f;
+#pragma unroll
+      for (int b = 0; b < 32; ++b) {
+        if (!((w32 >> b) & 1u)) continue;
+        const int e = ck * 32 + b;
+        const int row = expert_off[e] + wprefix[(int64_t)e * W + w] + __popc(sb[e * 8 + wl] & below);
+        row_token[row] = t;
+        row_w[row] = __expf(v[b] - m) * inv;
+        tok_row[base + i] = row;
+        ++i;
+      }
     }
   }
 }
@@ -525,7 +578,7 @@ __global__ __launch_bounds__(256) void k_place(const float* __restrict__ logits,
 // ---------------------------------------------------------------------------------------------
 size_t route_workspace_bytes(int64_t T, int E) {
   const int64_t W = cdiv(T, 32);
-  return align_up((size_t)E * W * 4, 256) * 2;
+  return align_up((size_t)E * W * 4, 256) * 2 + align_up((size_t)(cdiv(T, 256) + 1) * 4, 256);
 }
 
 hipError_t launch_route(const float* logits, int64_t T, int E, int K, int round_mode, int tile_m,
@@ -533,6 +586,7 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int K, int round_
   const int W = (int)cdiv(T, 32);
   uint32_t* bits = static_cast<uint32_t*>(ws);
   int32_t* wprefix = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + align_up((size_t)E * W * 4, 256));
+  int32_t* blk = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + 2 * align_up((size_t)E * W * 4, 256));
   const int nblk = (int)cdiv(T, TOPK_TOKENS_PER_BLOCK);
   const size_t lds = (size_t)E * 2 * sizeof(uint32_t);
 #define MOE_TOPK(EPL) k_topk<EPL><<<nblk, TOPK_THREADS, lds, st>>>(logits, (int)T, E, K, W, p.topk_idx, p.topk_w, bits)
@@ -557,15 +611,16 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int K, int round_
   }
   k_offsets<<<1, 1024, 0, st>>>(p.counts, E, p.expert_off, p.meta);
   if (rounded) {
-    k_tok_count<<<(int)cdiv(T, 256), 256, (size_t)E * 32, st>>>(bits, (int)T, E, W, p.tok_off);
-    k_tok_scan<<<1, 1024, 0, st>>>((int)T, p.tok_off);
-    k_place<true, 1><<<(int)cdiv(T, 256), 256, (size_t)E * 32, st>>>(logits, (int)T, E, K, W, p.topk_idx, bits,
-                                                                     wprefix, p.expert_off, p.tok_off, p.row_token,
-                                                                     p.row_w, p.tok_row);
+    const int nb = (int)cdiv(T, 256);
+    k_tok_count<<<nb, 256, (size_t)E * 32, st>>>(bits, (int)T, E, W, blk);
+    k_tok_scan<<<1, 1024, 0, st>>>(nb, blk);
+    k_place<true, 1><<<nb, 256, (size_t)E * 32, st>>>(logits, (int)T, E, K, W, p.topk_idx, bits, wprefix,
+                                                      p.expert_off, p.tok_off, blk, p.row_token, p.row_w,
+                                                      p.tok_row);
   } else {
     k_tok_fill<<<(int)cdiv(T + 1, 256), 256, 0, st>>>((int)T, K, p.tok_off);
 #define MOE_PLACE(KM) k_place<false, KM><<<(int)cdiv(T, 256), 256, 0, st>>>(logits, (int)T, E, K, W, p.topk_idx, \
-      bits, wprefix, p.expert_off, p.tok_off, p.row_token, p.row_w, p.tok_row)
+      bits, wprefix, p.expert_off, p.tok_off, nullptr, p.row_token, p.row_w, p.tok_row)
     if (K <= 2) MOE_PLACE(2);
     else if (K <= 4) MOE_PLACE(4);
     else if (K <= 8) MOE_PLACE(8);
