@@ -41,6 +41,7 @@ def parse():
     ap.add_argument("--config", default="fine_grained_7b")
     ap.add_argument("--round-mode", type=int, default=None,
                     help="override token rounding: 0 none, 1 nearest, 2 up, 3 down, 4 stochastic")
+    ap.add_argument("--tile-m", type=int, default=None, help="override the token-rounding tile (with --round-mode)")
     ap.add_argument("--no-h-cache", action="store_true", help="backward recomputes [G|U] from X")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU baseline time budget")
@@ -366,6 +367,8 @@ def main():
     cfg = wl.BY_NAME[args.config]
     if args.round_mode is not None:
         cfg = cfg.with_(round_mode=args.round_mode)
+    if args.tile_m is not None:
+        cfg = cfg.with_(tile_m=args.tile_m)
     backward = cfg.backward and not args.forward_only
     log("config", cfg)
     inp = wl.make_inputs(cfg, device="cuda", with_grad_out=backward)
@@ -441,8 +444,9 @@ def main():
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
 
     # the counter record is per exact workload: shape, pass, token rounding and H cache
-    workload_key = "%s:%s:round%d:%s" % (cfg.name, "fwd+bwd" if backward else "fwd", cfg.round_mode,
-                                         ("h_cache" if not args.no_h_cache else "recompute") if backward else "-")
+    workload_key = "%s:%s:round%d%s:%s" % (cfg.name, "fwd+bwd" if backward else "fwd", cfg.round_mode,
+                                           (":tile%d" % cfg.tile_m) if cfg.round_mode else "",
+                                           ("h_cache" if not args.no_h_cache else "recompute") if backward else "-")
     breakdown = {}
     for s, v in stages.items():
         if not v:

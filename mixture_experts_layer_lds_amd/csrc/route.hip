@@ -360,23 +360,21 @@ __device__ __forceinline__ void stage_block_bits(const uint32_t* __restrict__ bi
   __syncthreads();
 }
 
-// Token rounding: the number of final rows of each block of 256 tokens -> blk[b + 1] (scanned
-// afterwards by k_tok_scan over the blocks).  256 threads per block, one token each; dynamic LDS
-// E * 8 words.
+// Token rounding: the number of final rows of each group of 32 tokens (one bitmap word) ->
+// grp[g + 1], scanned afterwards by k_tok_scan over the groups.  256 threads per block, one token
+// each; dynamic LDS E * 8 words.
 __global__ __launch_bounds__(256) void k_tok_count(const uint32_t* __restrict__ bits, int T, int E,
-                                                   int W, int32_t* __restrict__ blk) {
+                                                   int W, int32_t* __restrict__ grp) {
   extern __shared__ uint32_t sb[];
-  __shared__ int sh[4];
   stage_block_bits(bits, E, W, sb);
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   const int wl = threadIdx.x >> 5;
-  const uint32_t sh_t = t & 31;
   int c = 0;
   if (t < T)
-    for (int e = 0; e < E; ++e) c += (sb[e * 8 + wl] >> sh_t) & 1u;
-  int tot;
-  block_exscan_256(c, &tot, sh);
-  if (threadIdx.x == 0) blk[blockIdx.x + 1] = tot;
+    for (int e = 0; e < E; ++e) c += (sb[e * 8 + wl] >> (t & 31)) & 1u;
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) c += __shfl_xor(c, o, 32);
+  if ((threadIdx.x & 31) == 0 && t < T) grp[(t >> 5) + 1] = c;
 }
 
 // Plain top-K: every token has K rows.
@@ -431,22 +429,11 @@ __global__ __launch_bounds__(1024) void k_tok_scan(int T, int32_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------------------------
-// Placement: one thread per token.  The token's final experts in ascending id (plain top-K: its
-// K ids sorted; token rounding: the set bits of its bitmap column); gate weights = softmax of
-// its final logits; row of (t, e) = expert_off[e] + (members of e before t), a popcount.
-// Plain top-K sorts the ids with a bitonic network over KM >= K registers (padded with INT_MAX),
-// every index fixed at compile time so that nothing goes to scratch memory.
+// Placement of plain top-K: one thread per token.  The token's K ids in ascending order (a bitonic
+// network over KM >= K registers, padded with INT_MAX, every index fixed at compile time so that
+// nothing goes to scratch memory); gate weights = softmax of its K logits; row of (t, e) =
+// expert_off[e] + (members of e before t), a popcount.
 // ---------------------------------------------------------------------------------------------
-// Bit b of the result: token bit `tb` of the block bitmap word of expert e0 + b (experts >= E
-// read as 0).
-__device__ __forceinline__ uint32_t member_word(const uint32_t* sb, int E, int e0, int wl, int tb) {
-  uint32_t w32 = 0;
-#pragma unroll
-  for (int b = 0; b < 32; ++b)
-    if (e0 + b < E) w32 |= ((sb[(e0 + b) * 8 + wl] >> tb) & 1u) << b;
-  return w32;
-}
-
 template <int N>
 __device__ __forceinline__ void bitonic_sort_i32(int (&a)[N]) {
 #pragma unroll
@@ -465,110 +452,149 @@ __device__ __forceinline__ void bitonic_sort_i32(int (&a)[N]) {
       }
 }
 
-template <bool ROUNDED, int KM>
+template <int KM>
 __global__ __launch_bounds__(256) void k_place(const float* __restrict__ logits, int T, int E,
                                                int K, int W, const int32_t* __restrict__ topk_idx,
                                                const uint32_t* __restrict__ bits,
                                                const int32_t* __restrict__ wprefix,
                                                const int32_t* __restrict__ expert_off,
-                                               int32_t* __restrict__ tok_off,
-                                               const int32_t* __restrict__ blk,
+                                               const int32_t* __restrict__ tok_off,
                                                int32_t* __restrict__ row_token,
                                                float* __restrict__ row_w,
                                                int32_t* __restrict__ tok_row) {
-  extern __shared__ uint32_t sb[];  // ROUNDED: the block's bitmap words, E * 8
-  __shared__ int sh[4];
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  const int wl = threadIdx.x >> 5;
-  int base;
-  if (ROUNDED) {
-    // the token's row count from the bitmap; its first row = the block's prefix (blk, scanned
-    // over blocks) + the exclusive scan of the counts inside the block
-    stage_block_bits(bits, E, W, sb);
-    int c = 0;
-    if (t < T)
-      for (int e = 0; e < E; ++e) c += (sb[e * 8 + wl] >> (t & 31)) & 1u;
-    int tot;
-    base = blk[blockIdx.x] + block_exscan_256(c, &tot, sh);
-    if (t < T) tok_off[t] = base;
-    if (t == T - 1) tok_off[T] = base + c;
-  } else {
-    base = t < T ? tok_off[t] : 0;
-  }
   if (t >= T) return;
+  const int base = tok_off[t];
   const float* L = logits + (int64_t)t * E;
   const int w = t >> 5;
   const uint32_t below = (1u << (t & 31)) - 1u;
-  if (!ROUNDED) {
-    int ids[KM];
-    float lv[KM];
+  int ids[KM];
+  float lv[KM];
 #pragma unroll
-    for (int k = 0; k < KM; ++k) ids[k] = k < K ? topk_idx[(int64_t)t * K + k] : INT_MAX;
-    bitonic_sort_i32(ids);
+  for (int k = 0; k < KM; ++k) ids[k] = k < K ? topk_idx[(int64_t)t * K + k] : INT_MAX;
+  bitonic_sort_i32(ids);
 #pragma unroll
-    for (int k = 0; k < KM; ++k) lv[k] = k < K ? L[ids[k]] : -INFINITY;
-    float m = lv[0];
+  for (int k = 0; k < KM; ++k) lv[k] = k < K ? L[ids[k]] : -INFINITY;
+  float m = lv[0];
 #pragma unroll
-    for (int k = 1; k < KM; ++k)
-      if (k < K) m = fmaxf(m, lv[k]);
-    float s = 0.0f;
+  for (int k = 1; k < KM; ++k)
+    if (k < K) m = fmaxf(m, lv[k]);
+  float s = 0.0f;
 #pragma unroll
-    for (int k = 0; k < KM; ++k)
-      if (k < K) s += __expf(lv[k] - m);
-    const float inv = 1.0f / s;
+  for (int k = 0; k < KM; ++k)
+    if (k < K) s += __expf(lv[k] - m);
+  const float inv = 1.0f / s;
 #pragma unroll
-    for (int k = 0; k < KM; ++k) {
-      if (k >= K) break;
-      const int e = ids[k];
-      const int row = expert_off[e] + wprefix[(int64_t)e * W + w] + __popc(bits[(int64_t)e * W + w] & below);
+  for (int k = 0; k < KM; ++k) {
+    if (k >= K) break;
+    const int e = ids[k];
+    const int row = expert_off[e] + wprefix[(int64_t)e * W + w] + __popc(bits[(int64_t)e * W + w] & below);
+    row_token[row] = t;
+    row_w[row] = __expf(lv[k] - m) * inv;
+    tok_row[base + k] = row;
+  }
+}
+
+// Placement after token rounding: a token's final experts are the set bits of its bitmap column
+// (any number of them).  Eight lanes per token, 32 tokens (one bitmap word per expert) per block of
+// 256 threads: lane j of a token takes experts j * EP .. j * EP + EP - 1 (EP = ceil(E / 8)), so the
+// lanes' member lists, concatenated in lane order, are in ascending expert id.  The token's
+// logit maximum and softmax sum are combined over its eight lanes; each member's place among the
+// token's rows is the lane's exclusive prefix of member counts plus its rank in the lane.  The
+// token's first row is the group prefix (grp, scanned over groups of 32 tokens) plus the
+// exclusive scan of the counts of the group's earlier tokens.
+constexpr int PR_CHUNK = 16;  // experts per unrolled chunk of a lane's range
+__global__ __launch_bounds__(256) void k_place_rounded(const float* __restrict__ logits, int T, int E, int W,
+                                                       const uint32_t* __restrict__ bits,
+                                                       const int32_t* __restrict__ wprefix,
+                                                       const int32_t* __restrict__ expert_off,
+                                                       const int32_t* __restrict__ grp,
+                                                       int32_t* __restrict__ tok_off,
+                                                       int32_t* __restrict__ row_token,
+                                                       float* __restrict__ row_w,
+                                                       int32_t* __restrict__ tok_row) {
+  extern __shared__ uint32_t sw[];  // [E]: this group's bitmap word of each expert
+  __shared__ int scnt[32];
+  const int g = blockIdx.x;          // group of 32 tokens = bitmap word g
+  for (int e = threadIdx.x; e < E; e += 256) sw[e] = bits[(int64_t)e * W + g];
+  __syncthreads();
+  const int tt = threadIdx.x >> 3, sub = threadIdx.x & 7;
+  const int t = g * 32 + tt;
+  const bool live = t < T;
+  const int EP = (E + 7) / 8;
+  const int e_lo = sub * EP, e_hi = min(E, e_lo + EP);
+  const uint32_t below = (1u << tt) - 1u;
+  const float* L = logits + (int64_t)(live ? t : 0) * E;
+  // members of this lane and the lane's logit maximum
+  int c = 0;
+  float m = -INFINITY;
+  for (int e0 = e_lo; e0 < e_hi; e0 += PR_CHUNK) {
+    uint32_t mw = 0;
+#pragma unroll
+    for (int b = 0; b < PR_CHUNK; ++b)
+      if (live && e0 + b < e_hi) mw |= ((sw[e0 + b] >> tt) & 1u) << b;
+    c += __popc(mw);
+    float v[PR_CHUNK];
+#pragma unroll
+    for (int b = 0; b < PR_CHUNK; ++b) v[b] = ((mw >> b) & 1u) ? L[e0 + b] : -INFINITY;
+#pragma unroll
+    for (int b = 0; b < PR_CHUNK; ++b)
+      if ((mw >> b) & 1u) m = fmaxf(m, v[b]);
+  }
+  // combine over the token's eight lanes (xor partners stay inside the aligned group of 8)
+  int cnt = c, pre = c;
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) {
+    m = fmaxf(m, __shfl_xor(m, o, 64));
+    cnt += __shfl_xor(cnt, o, 64);
+    const int up = __shfl_up(pre, o, 8);
+    if (sub >= o) pre += up;
+  }
+  pre -= c;  // exclusive prefix of member counts over the token's lanes
+  // token offsets: group prefix + exclusive scan over the group's tokens
+  if (sub == 0) scnt[tt] = live ? cnt : 0;
+  __syncthreads();
+  int before = 0;
+  for (int j = 0; j < tt; ++j) before += scnt[j];
+  const int base = grp[g] + before;
+  if (live && sub == 0) {
+    tok_off[t] = base;
+    if (t == T - 1) tok_off[T] = base + cnt;
+  }
+  if (!live || cnt == 0) return;
+  float s = 0.0f;
+  for (int e0 = e_lo; e0 < e_hi; e0 += PR_CHUNK) {
+    uint32_t mw = 0;
+#pragma unroll
+    for (int b = 0; b < PR_CHUNK; ++b)
+      if (e0 + b < e_hi) mw |= ((sw[e0 + b] >> tt) & 1u) << b;
+    float v[PR_CHUNK];
+#pragma unroll
+    for (int b = 0; b < PR_CHUNK; ++b) v[b] = ((mw >> b) & 1u) ? L[e0 + b] : 0.0f;
+#pragma unroll
+    for (int b = 0; b < PR_CHUNK; ++b)
+      if ((mw >> b) & 1u) s += __expf(v[b] - m);
+  }
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) s += __shfl_xor(s, o, 64);
+  const float inv = 1.0f / s;
+  int i = base + pre;
+  for (int e0 = e_lo; e0 < e_hi; e0 += PR_CHUNK) {
+    uint32_t mw = 0;
+#pragma unroll
+    for (int b = 0; b < PR_CHUNK; ++b)
+      if (e0 + b < e_hi) mw |= ((sw[e0 + b] >> tt) & 1u) << b;
+    float v[PR_CHUNK];
+#pragma unroll
+    for (int b = 0; b < PR_CHUNK; ++b) v[b] = ((mw >> b) & 1u) ? L[e0 + b] : 0.0f;
+#pragma unroll
+    for (int b = 0; b < PR_CHUNK; ++b) {
+      if (!((mw >> b) & 1u)) continue;
+      const int e = e0 + b;
+      const int row = expert_off[e] + wprefix[(int64_t)e * W + g] + __popc(sw[e] & below);
       row_token[row] = t;
-      row_w[row] = __expf(lv[k] - m) * inv;
-      tok_row[base + k] = row;
-    }
-  } else {
-    // The token's members, 32 experts at a time: a member word from the LDS bitmap, then the
-    // members' logits loaded together (independent loads), in ascending expert id throughout.
-    const int nck = (E + 31) / 32;
-    float m = -INFINITY;
-    for (int ck = 0; ck < nck; ++ck) {
-      const uint32_t w32 = member_word(sb, E, ck * 32, wl, t & 31);
-      if (!w32) continue;
-      float v[32];
-#pragma unroll
-      for (int b = 0; b < 32; ++b) v[b] = ((w32 >> b) & 1u) ? L[ck * 32 + b] : -INFINITY;
-#pragma unroll
-      for (int b = 0; b < 32; ++b)
-        if ((w32 >> b) & 1u) m = fmaxf(m, v[b]);
-    }
-    float s = 0.0f;
-    for (int ck = 0; ck < nck; ++ck) {
-      const uint32_t w32 = member_word(sb, E, ck * 32, wl, t & 31);
-      if (!w32) continue;
-      float v[32];
-#pragma unroll
-      for (int b = 0; b < 32; ++b) v[b] = ((w32 >> b) & 1u) ? L[ck * 32 + b] : 0.0f;
-#pragma unroll
-      for (int b = 0; b < 32; ++b)
-        if ((w32 >> b) & 1u) s += __expf(v[b] - m);
-    }
-    const float inv = 1.0f / s;
-    int i = 0;
-    for (int ck = 0; ck < nck; ++ck) {
-      const uint32_t w32 = member_word(sb, E, ck * 32, wl, t & 31);
-      if (!w32) continue;
-      float v[32];
-#pragma unroll
-      for (int b = 0; b < 32; ++b) v[b] = ((w32 >> b) & 1u) ? L[ck * 32 + b] : 0.0f;
-#pragma unroll
-      for (int b = 0; b < 32; ++b) {
-        if (!((w32 >> b) & 1u)) continue;
-        const int e = ck * 32 + b;
-        const int row = expert_off[e] + wprefix[(int64_t)e * W + w] + __popc(sb[e * 8 + wl] & below);
-        row_token[row] = t;
-        row_w[row] = __expf(v[b] - m) * inv;
-        tok_row[base + i] = row;
-        ++i;
-      }
+      row_w[row] = __expf(v[b] - m) * inv;
+      tok_row[i++] = row;
     }
   }
 }
@@ -578,7 +604,7 @@ __global__ __launch_bounds__(256) void k_place(const float* __restrict__ logits,
 // ---------------------------------------------------------------------------------------------
 size_t route_workspace_bytes(int64_t T, int E) {
   const int64_t W = cdiv(T, 32);
-  return align_up((size_t)E * W * 4, 256) * 2 + align_up((size_t)(cdiv(T, 256) + 1) * 4, 256);
+  return align_up((size_t)E * W * 4, 256) * 2 + align_up((size_t)(W + 1) * 4, 256);
 }
 
 hipError_t launch_route(const float* logits, int64_t T, int E, int K, int round_mode, int tile_m,
@@ -586,7 +612,7 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int K, int round_
   const int W = (int)cdiv(T, 32);
   uint32_t* bits = static_cast<uint32_t*>(ws);
   int32_t* wprefix = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + align_up((size_t)E * W * 4, 256));
-  int32_t* blk = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + 2 * align_up((size_t)E * W * 4, 256));
+  int32_t* grp = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + 2 * align_up((size_t)E * W * 4, 256));
   const int nblk = (int)cdiv(T, TOPK_TOKENS_PER_BLOCK);
   const size_t lds = (size_t)E * 2 * sizeof(uint32_t);
 #define MOE_TOPK(EPL) k_topk<EPL><<<nblk, TOPK_THREADS, lds, st>>>(logits, (int)T, E, K, W, p.topk_idx, p.topk_w, bits)
@@ -611,16 +637,14 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int K, int round_
   }
   k_offsets<<<1, 1024, 0, st>>>(p.counts, E, p.expert_off, p.meta);
   if (rounded) {
-    const int nb = (int)cdiv(T, 256);
-    k_tok_count<<<nb, 256, (size_t)E * 32, st>>>(bits, (int)T, E, W, blk);
-    k_tok_scan<<<1, 1024, 0, st>>>(nb, blk);
-    k_place<true, 1><<<nb, 256, (size_t)E * 32, st>>>(logits, (int)T, E, K, W, p.topk_idx, bits, wprefix,
-                                                      p.expert_off, p.tok_off, blk, p.row_token, p.row_w,
-                                                      p.tok_row);
+    k_tok_count<<<(int)cdiv(T, 256), 256, (size_t)E * 32, st>>>(bits, (int)T, E, W, grp);
+    k_tok_scan<<<1, 1024, 0, st>>>(W, grp);
+    k_place_rounded<<<W, 256, (size_t)E * 4, st>>>(logits, (int)T, E, W, bits, wprefix, p.expert_off, grp,
+                                                   p.tok_off, p.row_token, p.row_w, p.tok_row);
   } else {
     k_tok_fill<<<(int)cdiv(T + 1, 256), 256, 0, st>>>((int)T, K, p.tok_off);
-#define MOE_PLACE(KM) k_place<false, KM><<<(int)cdiv(T, 256), 256, 0, st>>>(logits, (int)T, E, K, W, p.topk_idx, \
-      bits, wprefix, p.expert_off, p.tok_off, nullptr, p.row_token, p.row_w, p.tok_row)
+#define MOE_PLACE(KM) k_place<KM><<<(int)cdiv(T, 256), 256, 0, st>>>(logits, (int)T, E, K, W, p.topk_idx, bits, \
+      wprefix, p.expert_off, p.tok_off, p.row_token, p.row_w, p.tok_row)
     if (K <= 2) MOE_PLACE(2);
     else if (K <= 4) MOE_PLACE(4);
     else if (K <= 8) MOE_PLACE(8);
