@@ -31,7 +31,7 @@ struct Shape {
 };
 
 // ---- routing (route.hip) ----
-size_t route_workspace_bytes(int64_t T, int E);
+size_t route_workspace_bytes(int64_t T, int E, bool rounded);
 hipError_t launch_route(const float* logits, int64_t T, int E, int K, int round_mode, int tile_m,
                         const uint32_t* round_rand, const PlanPtrs& p, void* ws, hipStream_t st);
 

@@ -178,14 +178,14 @@ BwdWs carve_bwd(Carve& c, const moe_dims* dm) {
 size_t ws_bytes_for(const moe_dims* dm, int op) {
   Carve c(nullptr);
   switch (op) {
-    case MOE_OP_ROUTE: return route_workspace_bytes(dm->T, dm->E);
+    case MOE_OP_ROUTE: return route_workspace_bytes(dm->T, dm->E, dm->round_mode != 0);
     case MOE_OP_PERMUTE: return 0;
     case MOE_OP_COMBINE: return 0;
     case MOE_OP_FFN: carve_ffn(c, dm); return c.off;
     case MOE_OP_FORWARD: {
       carve_ffn(c, dm);
       c.take((size_t)max_rows(dm) * dm->d * esize(dm));  // Y_perm
-      const size_t r = route_workspace_bytes(dm->T, dm->E);
+      const size_t r = route_workspace_bytes(dm->T, dm->E, dm->round_mode != 0);
       return c.off > r ? c.off : r;
     }
     case MOE_OP_BACKWARD: carve_bwd(c, dm); return c.off;

@@ -55,12 +55,19 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
+// keysT (token rounding only, else null): the order keys transposed, keysT[e][t], for the rounding
+// kernel's per-expert scans.  With E <= TOPK_STAGE_E the block's keys are staged in LDS
+// ([e][65], conflict-free) and written out as 64-token rows; otherwise each lane stores its own.
+constexpr int TOPK_STAGE_E = 192;  // E * (2 + 65) words stay within the default 64 KiB of dynamic LDS
 template <int EPL>
 __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const float* __restrict__ logits, int T, int E,
                                                        int K, int W, int32_t* __restrict__ topk_idx,
                                                        float* __restrict__ topk_w,
-                                                       uint32_t* __restrict__ bits) {
-  extern __shared__ uint32_t sbits[];  // [E][2]
+                                                       uint32_t* __restrict__ bits,
+                                                       uint32_t* __restrict__ keysT) {
+  extern __shared__ uint32_t sbits[];  // [E][2], then (keysT staged) [E][65] keys
+  uint32_t* skeys = sbits + 2 * E;
+  const bool stage = keysT && E <= TOPK_STAGE_E;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t0 = blockIdx.x * TOPK_TOKENS_PER_BLOCK;
   for (int i = threadIdx.x; i < 2 * E; i += blockDim.x) sbits[i] = 0u;
@@ -76,6 +83,10 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const float* __restrict__
       const int e = lane + 64 * j;
       key[j] = e < E ? order_key(row[e]) : 0u;
       alive |= e < E ? (1u << j) : 0u;
+      if (keysT && e < E) {
+        if (stage) skeys[e * 65 + tt] = key[j];
+        else keysT[(int64_t)e * T + t] = key[j];
+      }
     }
     int my_e = 0;
     for (int k = 0; k < K; ++k) {
@@ -110,6 +121,11 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const float* __restrict__
     const int e = i >> 1, w = w0 + (i & 1);
     if (w < W) bits[(int64_t)e * W + w] = sbits[i];
   }
+  if (stage)
+    for (int i = threadIdx.x; i < E * 64; i += blockDim.x) {
+      const int e = i >> 6, c = i & 63;
+      if (t0 + c < T) keysT[(int64_t)e * T + t0 + c] = skeys[e * 65 + c];
+    }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -185,7 +201,8 @@ __global__ __launch_bounds__(TR_THREADS) void k_token_round(const float* __restr
                                                            int E, int W, int M, int mode,
                                                            const uint32_t* __restrict__ round_rand,
                                                            uint32_t* __restrict__ bits,
-                                                           const int32_t* __restrict__ counts) {
+                                                           const int32_t* __restrict__ counts,
+                                                           const uint32_t* __restrict__ keysT) {
   extern __shared__ uint32_t s_dyn[];  // cached: [T] logit keys, then [W] bitmap words
   __shared__ int hist[256];
   __shared__ uint64_t s_prefix;
@@ -210,7 +227,8 @@ __global__ __launch_bounds__(TR_THREADS) void k_token_round(const float* __restr
   uint32_t* s_bits = s_dyn + T;
   if (cached) {
 #pragma unroll 8
-    for (int t = threadIdx.x; t < T; t += TR_THREADS) s_ord[t] = order_key(logits[(int64_t)t * E + e]);
+    for (int t = threadIdx.x; t < T; t += TR_THREADS)
+      s_ord[t] = keysT ? keysT[(int64_t)e * T + t] : order_key(logits[(int64_t)t * E + e]);
     for (int w = threadIdx.x; w < W; w += TR_THREADS) s_bits[w] = brow[w];
     __syncthreads();
   }
@@ -218,7 +236,7 @@ __global__ __launch_bounds__(TR_THREADS) void k_token_round(const float* __restr
     const uint32_t word = cached ? s_bits[t >> 5] : brow[t >> 5];
     const bool mem = (word >> (t & 31)) & 1u;
     cand = add ? !mem : mem;
-    const uint32_t o = cached ? s_ord[t] : order_key(logits[(int64_t)t * E + e]);
+    const uint32_t o = cached ? s_ord[t] : keysT ? keysT[(int64_t)e * T + t] : order_key(logits[(int64_t)t * E + e]);
     return add ? (((uint64_t)o << 32) | (uint32_t)(~(uint32_t)t))
                : (((uint64_t)(~o) << 32) | (uint32_t)t);
   };
@@ -311,7 +329,7 @@ __global__ __launch_bounds__(TR_THREADS) void k_token_round(const float* __restr
       if (t >= T) break;
       const bool mem = (orig >> b) & 1u;
       const bool cand = add ? !mem : mem;
-      const uint32_t o = cached ? s_ord[t] : order_key(logits[(int64_t)t * E + e]);
+      const uint32_t o = cached ? s_ord[t] : keysT ? keysT[(int64_t)e * T + t] : order_key(logits[(int64_t)t * E + e]);
       const uint64_t k = add ? (((uint64_t)o << 32) | (uint32_t)(~(uint32_t)t))
                              : (((uint64_t)(~o) << 32) | (uint32_t)t);
       if (cand && k >= thr) word ^= (1u << b);
@@ -602,9 +620,11 @@ __global__ __launch_bounds__(256) void k_place_rounded(const float* __restrict__
 // ---------------------------------------------------------------------------------------------
 // Host launcher for the whole routing plan from fp32 logits.
 // ---------------------------------------------------------------------------------------------
-size_t route_workspace_bytes(int64_t T, int E) {
+// bits [E][W] | wprefix [E][W] | grp [W + 1] | (token rounding) keysT [E][T]
+size_t route_workspace_bytes(int64_t T, int E, bool rounded) {
   const int64_t W = cdiv(T, 32);
-  return align_up((size_t)E * W * 4, 256) * 2 + align_up((size_t)(W + 1) * 4, 256);
+  return align_up((size_t)E * W * 4, 256) * 2 + align_up((size_t)(W + 1) * 4, 256) +
+         (rounded ? align_up((size_t)E * T * 4, 256) : 0);
 }
 
 hipError_t launch_route(const float* logits, int64_t T, int E, int K, int round_mode, int tile_m,
@@ -613,9 +633,12 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int K, int round_
   uint32_t* bits = static_cast<uint32_t*>(ws);
   int32_t* wprefix = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + align_up((size_t)E * W * 4, 256));
   int32_t* grp = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + 2 * align_up((size_t)E * W * 4, 256));
+  const bool rounded = round_mode != 0;
+  uint32_t* keysT = rounded ? reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(grp) + align_up((size_t)(W + 1) * 4, 256))
+                            : nullptr;
   const int nblk = (int)cdiv(T, TOPK_TOKENS_PER_BLOCK);
-  const size_t lds = (size_t)E * 2 * sizeof(uint32_t);
-#define MOE_TOPK(EPL) k_topk<EPL><<<nblk, TOPK_THREADS, lds, st>>>(logits, (int)T, E, K, W, p.topk_idx, p.topk_w, bits)
+  const size_t lds = (size_t)E * 2 * sizeof(uint32_t) + (rounded && E <= TOPK_STAGE_E ? (size_t)E * 65 * 4 : 0);
+#define MOE_TOPK(EPL) k_topk<EPL><<<nblk, TOPK_THREADS, lds, st>>>(logits, (int)T, E, K, W, p.topk_idx, p.topk_w, bits, keysT)
   if (E <= 64) MOE_TOPK(1);
   else if (E <= 128) MOE_TOPK(2);
   else if (E <= 256) MOE_TOPK(4);
@@ -623,7 +646,6 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int K, int round_
   else MOE_TOPK(16);
 #undef MOE_TOPK
   k_count<<<E, 256, 0, st>>>(bits, W, wprefix, p.counts);
-  const bool rounded = round_mode != 0;
   if (rounded) {
     const size_t tr_lds = tr_lds_bytes(T, W);
     // dynamic LDS above 64 KiB must be opted into (per device; a cheap host call)
@@ -632,7 +654,7 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int K, int round_
                                               (int)tr_lds_bytes(TR_LDS_TOKENS, TR_LDS_TOKENS / 32));
     if (ae != hipSuccess) return ae;
     k_token_round<<<E, TR_THREADS, tr_lds, st>>>(logits, (int)T, E, W, tile_m, round_mode, round_rand, bits,
-                                                 p.counts);
+                                                 p.counts, keysT);
     k_count<<<E, 256, 0, st>>>(bits, W, wprefix, p.counts);
   }
   k_offsets<<<1, 1024, 0, st>>>(p.counts, E, p.expert_off, p.meta);
