@@ -20,27 +20,10 @@
 
 namespace moe {
 
-// Nearest E4M3 code of a finite fp32 value with |q| <= 448, ties to even.  As an integer a
-// non-negative code is monotone in its value: subnormals m 2^-9 have code m (m = 8 is the
-// smallest normal 2^-6), a normal value (1 + f) 2^e has code 8 (e + 7) + round(8 f).
-__device__ __forceinline__ uint32_t e4m3_code(float q) {
-  const uint32_t b = __float_as_uint(q);
-  const uint32_t sign = (b >> 24) & 0x80u;
-  const float a = fabsf(q);
-  uint32_t code;
-  if (a < 0.015625f) {
-    code = (uint32_t)rintf(a * 512.0f);  // exact product; rintf rounds half to even
-  } else {
-    const uint32_t ab = b & 0x7fffffffu;
-    const int e = (int)(ab >> 23) - 127;
-    const uint32_t m = ab & 0x7fffffu, r = m >> 20, rem = m & 0xfffffu;
-    const uint32_t up = (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ? 1u : 0u;
-    code = (uint32_t)((e + 7) << 3) + r + up;
-  }
-  return code | sign;
-}
-
 // One wave per row (four per workgroup).  rows_dev (optional) bounds the rows on the device.
+// The codes come from the hardware conversion v_cvt_pk_fp8_f32 (two values per instruction;
+// OCP E4M3, nearest with ties to the even code, subnormals kept), applied to x / s, which is
+// exact because s is a power of two.
 template <typename T>
 __global__ __launch_bounds__(256) void k_quant_fp8(const T* __restrict__ src, int64_t rows, int K,
                                                    const int32_t* __restrict__ rows_dev, uint8_t* __restrict__ codes,
@@ -72,7 +55,10 @@ __global__ __launch_bounds__(256) void k_quant_fp8(const T* __restrict__ src, in
     unpack16<T>(ld16(s + c), f);
     uint32_t w[2] = {0u, 0u};
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) w[i >> 2] |= e4m3_code(ldexpf(f[i], -sexp)) << (8 * (i & 3));
+    for (int i = 0; i < VEC; i += 4) {
+      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(f[i], -sexp), ldexpf(f[i + 1], -sexp), 0, false);
+      w[i >> 2] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(f[i + 2], -sexp), ldexpf(f[i + 3], -sexp), lo, true);
+    }
     if constexpr (VEC == 8) *reinterpret_cast<u32x2*>(o + c) = u32x2{w[0], w[1]};
     else *reinterpret_cast<uint32_t*>(o + c) = w[0];
   }

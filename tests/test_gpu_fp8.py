@@ -55,6 +55,31 @@ def test_quantize_matches_oracle(dtype):
     assert np.array_equal(scales.cpu().numpy().astype(np.float64), ref_s)
 
 
+def test_quantize_ties_and_subnormals():
+    """Rows whose elements sit exactly halfway between adjacent E4M3 values (normal and subnormal,
+    both signs), just beside those midpoints, and on the codes themselves: the kernel's codes
+    must be the oracle's (nearest, ties to the even code).  Each row's maximum is 448 times a
+    power of two, so its scale is that power and every scaled value is exact."""
+    grid = F.e4m3_decode(np.arange(0, 0x7F))
+    mids = (grid[1:] + grid[:-1]) / 2
+    m32 = mids.astype(np.float32)  # every midpoint is exact in fp32
+    vals = np.concatenate([m32, grid.astype(np.float32), np.nextafter(m32, np.float32(0)),
+                           np.nextafter(m32, np.float32(1e9))]).astype(np.float64)
+    rows = []
+    for sgn in (1.0, -1.0):
+        for p2 in (0, -20, 7):
+            r = np.concatenate([[448.0], sgn * vals]) * 2.0 ** p2
+            rows.append(np.resize(r, 512))
+    X = torch.tensor(np.array(rows), dtype=torch.float32).cuda()
+    codes, scales = quantize(X)
+    torch.cuda.synchronize()
+    ref_c, ref_s = F.quantize_rows(f64(X))
+    assert np.array_equal(scales.cpu().numpy().astype(np.float64), ref_s)
+    got = codes.cpu().numpy()
+    bad = np.argwhere(got != ref_c)
+    assert bad.size == 0, [(int(i), int(j), float(f64(X)[i, j]), int(got[i, j]), int(ref_c[i, j])) for i, j in bad[:8]]
+
+
 def run_ffn_fp8(cfg, inp):
     dims = B.make_dims(cfg.T, cfg.d, cfg.n, cfg.E, cfg.K, "bf16")
     logits = torch.empty(cfg.T, cfg.E, dtype=torch.float32, device="cuda")
