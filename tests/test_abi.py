@@ -87,6 +87,18 @@ def test_stochastic_rounding_needs_words():
     assert B.lib().moe_max_rows(ctypes.byref(d)) == B.lib().moe_max_rows(ctypes.byref(dims(round_mode=2)))
 
 
+def test_route_workspace_grows_with_token_rounding():
+    """Token rounding keeps the routing keys transposed ([E][T] words) in the routing workspace,
+    on top of the plain plan's bitmap, per-word prefixes and group offsets."""
+    T, E = 4096, 64
+    plain = B.moe_workspace_bytes(dims(T=T, E=E), B.OP_ROUTE)
+    rounded = B.moe_workspace_bytes(dims(T=T, E=E, round_mode=1), B.OP_ROUTE)
+    W = T // 32
+    assert plain >= 2 * E * W * 4 + (W + 1) * 4
+    assert rounded >= plain + E * T * 4
+    assert B.moe_workspace_bytes(dims(T=T, E=E, round_mode=1), B.OP_FORWARD) >= rounded
+
+
 def test_decode_argument_checks(lib):
     """moe_decode: plain top-K only, T <= 1024, its own workspace size, required pointers."""
     call = lambda d, ws=1 << 40, out=FAKE: lib.moe_decode(
