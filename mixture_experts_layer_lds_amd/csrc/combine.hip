@@ -6,33 +6,52 @@
 // kernel-comparison table (no separate scatter kernel: each token gathers its own rows, so no
 // two workgroups ever write the same output row and no atomics are needed).
 //
-// Both kernels stream whole rows with 16-byte accesses, one 64-lane wave per row (permute) or
-// per token (combine); the combine accumulates in fp32 over the token's rows in ascending expert
-// order and rounds once.
+// Both kernels stream whole rows with 16-byte accesses, one 64-lane wave per token: the permute
+// reads the token's row once and writes it to each of its expert-major rows (tok_row, the
+// token-major inverse index; every destination row has exactly one source, so no atomics), the
+// combine gathers the token's rows and accumulates them in fp32 in ascending expert order,
+// rounding once.
 #include "internal.h"
 
 namespace moe {
 
-template <typename T>
-__global__ __launch_bounds__(256) void k_permute(const int32_t* __restrict__ meta,
-                                                 const int32_t* __restrict__ row_token,
+// Lanes own 16-byte column chunks, PC per pass (a whole row of up to 64 * PC chunks is loaded
+// once, then stored to every destination row).
+template <typename T, int PC>
+__global__ __launch_bounds__(256) void k_permute(const int32_t* __restrict__ tok_off,
+                                                 const int32_t* __restrict__ tok_row,
                                                  const T* __restrict__ X, T* __restrict__ Xp, int d,
-                                                 int T_) {
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+                                                 int T_, int rmax) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (r >= meta[0]) return;
-  const int64_t src = clamp_idx(row_token[r], T_);
+  if (t >= T_) return;
+  const int base = tok_off[t], cnt = tok_off[t + 1] - base;
   constexpr int VEC = 16 / sizeof(T);
   const int nch = d / VEC;
-  const T* s = X + src * d;
-  T* o = Xp + (int64_t)r * d;
-  for (int c = lane; c < nch; c += 64) st16_nt(o + c * VEC, ld16(s + c * VEC));
+  const T* s = X + (int64_t)t * d;
+  for (int c0 = lane; c0 < nch; c0 += 64 * PC) {
+    u32x4 v[PC];
+#pragma unroll
+    for (int q = 0; q < PC; ++q)
+      if (c0 + 64 * q < nch) v[q] = ld16(s + (c0 + 64 * q) * VEC);
+    for (int i = 0; i < cnt; ++i) {
+      T* o = Xp + (int64_t)clamp_idx(tok_row[base + i], rmax) * d;
+#pragma unroll
+      for (int q = 0; q < PC; ++q)
+        if (c0 + 64 * q < nch) st16_nt(o + (c0 + 64 * q) * VEC, v[q]);
+    }
+  }
 }
 
 hipError_t launch_permute(const Shape& s, const PlanPtrs& p, const void* X, void* X_perm, hipStream_t st) {
-  const int grid = (int)cdiv(s.R_max, 4);
-  if (s.bf16) k_permute<bf16><<<grid, 256, 0, st>>>(p.meta, p.row_token, (const bf16*)X, (bf16*)X_perm, (int)s.d, (int)s.T);
-  else k_permute<float><<<grid, 256, 0, st>>>(p.meta, p.row_token, (const float*)X, (float*)X_perm, (int)s.d, (int)s.T);
+  const int grid = (int)cdiv(s.T, 4);
+  const int rmax = (int)s.R_max;
+  if (s.bf16)
+    k_permute<bf16, 4><<<grid, 256, 0, st>>>(p.tok_off, p.tok_row, (const bf16*)X, (bf16*)X_perm, (int)s.d,
+                                             (int)s.T, rmax);
+  else
+    k_permute<float, 4><<<grid, 256, 0, st>>>(p.tok_off, p.tok_row, (const float*)X, (float*)X_perm, (int)s.d,
+                                              (int)s.T, rmax);
   return hipGetLastError();
 }
 
