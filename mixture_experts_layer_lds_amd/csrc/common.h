@@ -39,6 +39,27 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
   return v;
 }
+// Maximum of v over the 64 lanes, returned in every lane.  Within each row of 16 lanes, row
+// shifts by 1, 2, 3, 4 (lanes 4-15) and 8 (lanes 8-15) leave the row's maximum in its lane 15;
+// row broadcasts of lane 15 (into rows 1 and 3) and of lane 31 (into rows 2 and 3) then leave the
+// wave's maximum in lane 63.  Lanes whose DPP source is off the row or masked keep their own
+// value, which a maximum ignores.
+__device__ __forceinline__ uint32_t dpp_max_step(uint32_t v, uint32_t x) { return v > x ? v : x; }
+template <int CTRL, int ROWS, int BANKS>
+__device__ __forceinline__ uint32_t dpp_src(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWS, BANKS, false);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_max_step(v, dpp_src<0x111, 0xf, 0xf>(v));  // row_shr:1
+  v = dpp_max_step(v, dpp_src<0x112, 0xf, 0xf>(v));  // row_shr:2
+  v = dpp_max_step(v, dpp_src<0x113, 0xf, 0xf>(v));  // row_shr:3
+  v = dpp_max_step(v, dpp_src<0x114, 0xf, 0xe>(v));  // row_shr:4, lanes 4-15 of each row
+  v = dpp_max_step(v, dpp_src<0x118, 0xf, 0xc>(v));  // row_shr:8, lanes 8-15 of each row
+  v = dpp_max_step(v, dpp_src<0x142, 0xa, 0xf>(v));  // row_bcast:15 into rows 1 and 3
+  v = dpp_max_step(v, dpp_src<0x143, 0xc, 0xf>(v));  // row_bcast:31 into rows 2 and 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 __device__ __forceinline__ int wave_sum_i(int v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);

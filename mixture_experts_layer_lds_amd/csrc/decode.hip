@@ -389,32 +389,38 @@ __global__ __launch_bounds__(DEC_THREADS) void k_decode(DecodeArgs a) {
   {
     const int nw = gridDim.x * DEC_WAVES;
     for (int t = blockIdx.x * DEC_WAVES + wave; t < T_; t += nw) {
-      // composite keys (order_key(L) << 32) | ~e: one unsigned maximum orders by logit
-      // descending, then expert id ascending; lane i holds experts i + 64 j (E <= 1024)
-      uint64_t ck[16];
+      // lane i holds the order keys of experts i + 64 j (E <= 1024); each round takes the largest
+      // key still in play (a DPP wave maximum) and, among the experts holding it, the lowest id
+      // (ballots in ascending e): logit descending, then expert id ascending
+      const int ej = (E + 63) >> 6;
+      uint32_t key[16];
+      uint32_t alive = 0;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int e = lane + 64 * j;
-        ck[j] = e < E ? (((uint64_t)dec_order_key(a.logits[(int64_t)t * E + e]) << 32) | (uint32_t)~(uint32_t)e)
-                      : 0ull;
+        key[j] = e < E ? dec_order_key(a.logits[(int64_t)t * E + e]) : 0u;
+        alive |= e < E ? (1u << j) : 0u;
       }
       int my_e = 0;
       float my_v = 0.0f;
       for (int k = 0; k < K; ++k) {
-        uint64_t b = 0ull;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) b = ck[j] > b ? ck[j] : b;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint64_t x = __shfl_xor(b, o, 64);
-          b = x > b ? x : b;
-        }
+        uint32_t lm = 0;  // NaN keys are 0 too; ties at 0 are settled among live candidates
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-          if (ck[j] == b) ck[j] = 0ull;
+          if (j < ej && ((alive >> j) & 1u)) lm = key[j] > lm ? key[j] : lm;
+        const uint32_t kmax = wave_max_u32(lm);
+        int win = -1;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          if (j >= ej) break;
+          const uint64_t m = __builtin_amdgcn_ballot_w64(((alive >> j) & 1u) && key[j] == kmax);
+          if (win < 0 && m != 0ull) win = 64 * j + (int)__builtin_ctzll(m);
+        }
+        win = __builtin_amdgcn_readfirstlane(win);
+        if (lane == (win & 63)) alive &= ~(1u << (win >> 6));
         if (lane == k) {
-          my_e = (int)~(uint32_t)b;
-          my_v = dec_key_value((uint32_t)(b >> 32));
+          my_e = win;
+          my_v = dec_key_value(kmax);
         }
       }
       const float vmax = __shfl(my_v, 0, 64);

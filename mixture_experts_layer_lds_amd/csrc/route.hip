@@ -34,27 +34,6 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Maximum of v over the 64 lanes, returned in every lane.  Within each row of 16 lanes, row
-// shifts by 1, 2, 3, 4 (lanes 4-15) and 8 (lanes 8-15) leave the row's maximum in its lane 15;
-// row broadcasts of lane 15 (into rows 1 and 3) and of lane 31 (into rows 2 and 3) then leave the
-// wave's maximum in lane 63.  Lanes whose DPP source is off the row or masked keep their own
-// value, which a maximum ignores.
-__device__ __forceinline__ uint32_t dpp_max_step(uint32_t v, uint32_t x) { return v > x ? v : x; }
-template <int CTRL, int ROWS, int BANKS>
-__device__ __forceinline__ uint32_t dpp_src(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWS, BANKS, false);
-}
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = dpp_max_step(v, dpp_src<0x111, 0xf, 0xf>(v));  // row_shr:1
-  v = dpp_max_step(v, dpp_src<0x112, 0xf, 0xf>(v));  // row_shr:2
-  v = dpp_max_step(v, dpp_src<0x113, 0xf, 0xf>(v));  // row_shr:3
-  v = dpp_max_step(v, dpp_src<0x114, 0xf, 0xe>(v));  // row_shr:4, lanes 4-15 of each row
-  v = dpp_max_step(v, dpp_src<0x118, 0xf, 0xc>(v));  // row_shr:8, lanes 8-15 of each row
-  v = dpp_max_step(v, dpp_src<0x142, 0xa, 0xf>(v));  // row_bcast:15 into rows 1 and 3
-  v = dpp_max_step(v, dpp_src<0x143, 0xc, 0xf>(v));  // row_bcast:31 into rows 2 and 3
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-
 // keysT (token rounding only, else null): the order keys transposed, keysT[e][t], for the rounding
 // kernel's per-expert scans.  With E <= TOPK_STAGE_E the block's keys are staged in LDS
 // ([e][65], conflict-free) and written out as 64-token rows; otherwise each lane stores its own.
