@@ -120,6 +120,29 @@ def test_route_from_given_logits_with_ties(mode):
     check_routing(cfg, dict(plan=plan), L=L.double().numpy(), round_rand=rr)
 
 
+@pytest.mark.parametrize("round_mode", [2, 3])
+def test_permute_after_token_rounding(round_mode):
+    """Packed permute with token rounding: tokens with more than K rows (UP) or none (DOWN);
+    every row r < R is a bit-exact copy of X[row_token[r]] and rows >= R are left untouched."""
+    cfg = wl.small_shape(T=777, d=256, E=7, K=2, n=128, dtype="bf16", seed=29, round_mode=round_mode, tile_m=64)
+    inp = wl.make_inputs(cfg, device="cuda")
+    dims = B.make_dims(cfg.T, cfg.d, cfg.n, cfg.E, cfg.K, "bf16", cfg.round_mode, cfg.tile_m)
+    plan = B.Plan(dims)
+    logits = torch.empty(cfg.T, cfg.E, device="cuda")
+    ws, nb = B.workspace(dims, B.OP_ROUTE)
+    B.moe_route(dims, inp["X"], inp["W_r"], None, logits, plan, ws, nb)
+    Xp = torch.full((plan.R_max, cfg.d), 7.0, dtype=torch.bfloat16, device="cuda")
+    B.moe_permute(dims, plan, inp["X"], Xp)
+    torch.cuda.synchronize()
+    hp = plan.to_host()
+    R = hp["R"]
+    cnt = np.diff(hp["tok_off"])
+    assert (cnt.max() > cfg.K) if round_mode == 2 else (cnt.min() == 0)
+    want = inp["X"][torch.as_tensor(hp["row_token"], device="cuda").long()]
+    assert torch.equal(Xp[:R].view(torch.int16), want.view(torch.int16))
+    assert bool((Xp[R:] == 7.0).all())
+
+
 def test_permute_packed_ffn_and_combine():
     cfg = wl.small_shape(T=600, d=192, E=6, K=3, n=128, dtype="bf16", seed=11)
     inp = wl.make_inputs(cfg, device="cuda")
