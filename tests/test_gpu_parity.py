@@ -38,7 +38,7 @@ def full_check(cfg, **kw):
 
 
 def test_tiny_fp32_layer_forward_backward():
-    cfg = wl.CONFIGS[0].with_(backward=True)
+    cfg = wl.BY_NAME["tiny_fp32"].with_(backward=True)
     _, ref, errs = full_check(cfg)
     assert int(ref["counts"].sum()) == cfg.T * cfg.K
     print(errs)
