@@ -208,15 +208,46 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dx(
   }
 }
 
+// bf16 dX on the eight-wave engine (same tiles, operands and bits as k_dx).
+__global__ __launch_bounds__(GEMM8_THREADS, 1) void k_dx_w8(
+    const int32_t* __restrict__ mtile_off, const int32_t* __restrict__ expert_off,
+    const bf16* __restrict__ dH, const bf16* __restrict__ Wg, const bf16* __restrict__ Wu,
+    bf16* __restrict__ dXp, int d, int n, int E, int NT) {
+  MOE_GEMM_LDS(L);
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  GroupTile g;
+  if (!find_group_tile(lin, NT, mtile_off, expert_off, E, g)) return;
+  const int n0 = g.nt * BN;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int64_t rowb = (int64_t)2 * n * sizeof(bf16);
+  KDmaW8 la;
+  la.init([&](int i) -> const char* {
+    return i < g.mrows ? reinterpret_cast<const char*>(dH) + (int64_t)(g.m0 + i) * rowb : nullptr;
+  });
+  const int64_t wrow = (int64_t)d * sizeof(bf16);
+  const char* wg = reinterpret_cast<const char*>(Wg) + (int64_t)g.e * n * wrow + n0 * sizeof(bf16);
+  const char* wu = reinterpret_cast<const char*>(Wu) + (int64_t)g.e * n * wrow + n0 * sizeof(bf16);
+  auto lb = mn_rows_w8([=](int k) { return k < n ? wg + (int64_t)k * wrow : wu + (int64_t)(k - n) * wrow; },
+                       2 * n, n0, d);
+  auto bsub = [&](int j) { return bsub_w8(wn, j); };
+  AccW8 acc;
+  gemm_mainloop_w8(la, lb, 2 * n / Mma<bf16>::BK, acc, L, wm, bsub);
+  const int valid = min(BN, d - n0);
+  epi_stage_w8(L, wm, bsub, [&](int i, int j, int v) { return acc.c[i][j][v]; });
+  __syncthreads();
+  bf16* out = dXp + (int64_t)g.m0 * d + n0;
+  epi_store_rows<GEMM8_THREADS>(L, 0, [&](int r) { return out + (int64_t)r * d; }, g.mrows, BN, valid);
+}
+
 hipError_t launch_dx_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off,
                           const void* dH, const void* W_gate, const void* W_up, void* dX_perm,
                           hipStream_t st) {
   const int NT = (int)cdiv(s.d, BN);
   const int grid = grid8(max_mtiles(s.R_max, s.E) * NT);
   if (s.bf16)
-    k_dx<bf16><<<grid, GEMM_THREADS, 0, st>>>(mtile_off, p.expert_off, (const bf16*)dH,
-                                              (const bf16*)W_gate, (const bf16*)W_up, (bf16*)dX_perm,
-                                              (int)s.d, (int)s.n, s.E, NT);
+    k_dx_w8<<<grid, GEMM8_THREADS, 0, st>>>(mtile_off, p.expert_off, (const bf16*)dH, (const bf16*)W_gate,
+                                            (const bf16*)W_up, (bf16*)dX_perm, (int)s.d, (int)s.n, s.E, NT);
   else
     k_dx<float><<<grid, GEMM_THREADS, 0, st>>>(mtile_off, p.expert_off, (const float*)dH,
                                                (const float*)W_gate, (const float*)W_up, (float*)dX_perm,
@@ -268,14 +299,45 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dw_down(
   }
 }
 
+// bf16 dW_down on the eight-wave engine (same tiles, operands and bits as k_dw_down).
+__global__ __launch_bounds__(GEMM8_THREADS, 1) void k_dw_down_w8(
+    const int32_t* __restrict__ expert_off, const int32_t* __restrict__ row_token,
+    const bf16* __restrict__ dY, const bf16* __restrict__ wA, bf16* __restrict__ dWd, int d, int n,
+    int E, int MT, int NT, int T_) {
+  MOE_GEMM_LDS(L);
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int per = MT * NT;
+  const int e = lin / per;
+  if (e >= E) return;
+  int mt, nt;
+  raster_tile(lin % per, MT, NT, mt, nt);
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int off = expert_off[e];
+  const int cnt = expert_off[e + 1] - off;
+  const char* dyb = reinterpret_cast<const char*>(dY) + m0 * sizeof(bf16);
+  const char* wab = reinterpret_cast<const char*>(wA) + n0 * sizeof(bf16);
+  auto la = mn_rows_idx_w8([=](int k) { return clamp_idx(sload_i32(row_token + off, k), T_); },
+                           [=](int t) { return dyb + (int64_t)t * d * sizeof(bf16); }, cnt, m0, d);
+  auto lb = mn_rows_w8([=](int k) { return wab + (int64_t)(off + k) * n * sizeof(bf16); }, cnt, n0, n);
+  auto bsub = [&](int j) { return bsub_w8(wn, j); };
+  AccW8 acc;
+  gemm_mainloop_w8(la, lb, (int)cdiv(cnt, Mma<bf16>::BK), acc, L, wm, bsub);
+  bf16* out = dWd + (int64_t)e * d * n + (int64_t)m0 * n + n0;
+  const int mrows = min(BM, d - m0), valid = min(BN, n - n0);
+  epi_stage_w8(L, wm, bsub, [&](int i, int j, int v) { return acc.c[i][j][v]; });
+  __syncthreads();
+  epi_store_rows<GEMM8_THREADS>(L, 0, [&](int r) { return out + (int64_t)r * n; }, mrows, BN, valid);
+}
+
 hipError_t launch_dw_down_gemm(const Shape& s, const PlanPtrs& p, const void* dY, const void* wA,
                                void* dW_down, hipStream_t st) {
   const int MT = (int)cdiv(s.d, BM), NT = (int)cdiv(s.n, BN);
   const int grid = grid8((int64_t)s.E * MT * NT);
   if (s.bf16)
-    k_dw_down<bf16><<<grid, GEMM_THREADS, 0, st>>>(p.expert_off, p.row_token, (const bf16*)dY,
-                                                   (const bf16*)wA, (bf16*)dW_down, (int)s.d,
-                                                   (int)s.n, s.E, MT, NT, (int)s.T);
+    k_dw_down_w8<<<grid, GEMM8_THREADS, 0, st>>>(p.expert_off, p.row_token, (const bf16*)dY, (const bf16*)wA,
+                                                 (bf16*)dW_down, (int)s.d, (int)s.n, s.E, MT, NT, (int)s.T);
   else
     k_dw_down<float><<<grid, GEMM_THREADS, 0, st>>>(p.expert_off, p.row_token, (const float*)dY,
                                                     (const float*)wA, (float*)dW_down, (int)s.d,
@@ -322,14 +384,48 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dw_gu(
   }
 }
 
+// bf16 dW_gate | dW_up on the eight-wave engine (same tiles, operands and bits as k_dw_gu).
+__global__ __launch_bounds__(GEMM8_THREADS, 1) void k_dw_gu_w8(
+    const int32_t* __restrict__ expert_off, const int32_t* __restrict__ row_token,
+    const bf16* __restrict__ dH, const bf16* __restrict__ X, bf16* __restrict__ dWg, bf16* __restrict__ dWu,
+    int d, int n, int E, int MT, int NT, int T_) {
+  MOE_GEMM_LDS(L);
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int per = MT * NT;
+  const int e = lin / per;
+  if (e >= E) return;
+  int mt, nt;
+  raster_tile(lin % per, MT, NT, mt, nt);
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int off = expert_off[e];
+  const int cnt = expert_off[e + 1] - off;
+  const char* dhb = reinterpret_cast<const char*>(dH) + m0 * sizeof(bf16);
+  const char* xb = reinterpret_cast<const char*>(X) + n0 * sizeof(bf16);
+  auto la = mn_rows_w8([=](int k) { return dhb + (int64_t)(off + k) * 2 * n * sizeof(bf16); }, cnt, m0, 2 * n);
+  auto lb = mn_rows_idx_w8([=](int k) { return clamp_idx(sload_i32(row_token + off, k), T_); },
+                           [=](int t) { return xb + (int64_t)t * d * sizeof(bf16); }, cnt, n0, d);
+  auto bsub = [&](int j) { return bsub_w8(wn, j); };
+  AccW8 acc;
+  gemm_mainloop_w8(la, lb, (int)cdiv(cnt, Mma<bf16>::BK), acc, L, wm, bsub);
+  const int mrows = min(BM, 2 * n - m0), valid = min(BN, d - n0);
+  epi_stage_w8(L, wm, bsub, [&](int i, int j, int v) { return acc.c[i][j][v]; });
+  __syncthreads();
+  epi_store_rows<GEMM8_THREADS>(L, 0, [&](int r) -> bf16* {
+    const int m = m0 + r;
+    return (m < n ? dWg + ((int64_t)e * n + m) * d : dWu + ((int64_t)e * n + (m - n)) * d) + n0;
+  }, mrows, BN, valid);
+}
+
 hipError_t launch_dw_gu_gemm(const Shape& s, const PlanPtrs& p, const void* dH, const void* X,
                              void* dW_gate, void* dW_up, hipStream_t st) {
   const int MT = (int)cdiv(2 * s.n, BM), NT = (int)cdiv(s.d, BN);
   const int grid = grid8((int64_t)s.E * MT * NT);
   if (s.bf16)
-    k_dw_gu<bf16><<<grid, GEMM_THREADS, 0, st>>>(p.expert_off, p.row_token, (const bf16*)dH,
-                                                 (const bf16*)X, (bf16*)dW_gate, (bf16*)dW_up,
-                                                 (int)s.d, (int)s.n, s.E, MT, NT, (int)s.T);
+    k_dw_gu_w8<<<grid, GEMM8_THREADS, 0, st>>>(p.expert_off, p.row_token, (const bf16*)dH, (const bf16*)X,
+                                               (bf16*)dW_gate, (bf16*)dW_up, (int)s.d, (int)s.n, s.E, MT, NT,
+                                               (int)s.T);
   else
     k_dw_gu<float><<<grid, GEMM_THREADS, 0, st>>>(p.expert_off, p.row_token, (const float*)dH,
                                                   (const float*)X, (float*)dW_gate, (float*)dW_up,
