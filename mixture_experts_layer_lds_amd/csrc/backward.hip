@@ -25,34 +25,18 @@ static inline int grid8(int64_t n) { return (int)((n + 7) / 8 * 8); }
 // dS partials are reduced over the tile's columns in registers, lanes and LDS, and written per
 // column tile: dS_part[nt][r].
 // ---------------------------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(GEMM_THREADS, 1) void k_dact(
-    const int32_t* __restrict__ mtile_off, const int32_t* __restrict__ expert_off,
-    const int32_t* __restrict__ row_token, const float* __restrict__ row_w,
-    const T* __restrict__ dY, const T* __restrict__ Wd, const T* __restrict__ H,
-    T* __restrict__ dH, T* __restrict__ wA, float* __restrict__ dS_part, int64_t R_max, int d,
-    int n, int E, int NT, int T_) {
-  MOE_GEMM_LDS(L);
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  GroupTile g;
-  if (!find_group_tile(lin, NT, mtile_off, expert_off, E, g)) return;
-  const int nt = g.nt;
-  const int n0 = nt * BN;
-  const int wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t rowb = (int64_t)d * sizeof(T);
-  auto la = k_rows<T>([&](int i) -> const char* {
-    return i < g.mrows ? reinterpret_cast<const char*>(dY) + (int64_t)clamp_idx(row_token[g.m0 + i], T_) * rowb
-                       : nullptr;
-  });
-  const char* wd = reinterpret_cast<const char*>(Wd) + ((int64_t)g.e * d * n + n0) * sizeof(T);
-  auto lb = mn_rows<T>([=](int k) { return wd + (int64_t)k * n * sizeof(T); }, d, n0, n);
-  WaveAcc acc;
-  gemm_mainloop<T>(la, lb, d / Mma<T>::BK, acc, L, wm, [&](int j) { return bsub_halved(wn, j); });
-  // Epilogue, one 128-column half of the tile at a time: the wave dumps its fp32 accumulators
-  // into an LDS tile [256][128], then the block walks the half row by row in 16-byte chunks
-  // (coalesced loads of G, U and coalesced stores of dG, dU, w A), and the 16 or 32 lanes that
-  // share a row reduce its dS partial.
+// The dAct epilogue of one tile, one 128-column half at a time: dump(half, frow) writes the
+// waves' fp32 accumulators of that half into an LDS tile [256][128] (row r at frow(r)), then the
+// block walks the half row by row in 16-byte chunks (coalesced loads of G, U and coalesced
+// stores of dG, dU, w A), and the 16 or 32 lanes that share a row reduce its dS partial.  The
+// block walks chunk c = row * CPR + ch in batches of UNR chunks per thread; the G, U and
+// row-weight loads of PF batches go out together -- the first group before the accumulator dump
+// and its barrier -- so a group costs one memory round trip, not one per batch.
+template <typename T, int NTHR, int PF, class Dump>
+__device__ __forceinline__ void dact_epilogue(LdsBufs L, const GroupTile& g, int n0, int n, int nt, int64_t R_max,
+                                              const float* __restrict__ row_w, const T* __restrict__ H,
+                                              T* __restrict__ dH, T* __restrict__ wA, float* __restrict__ dS_part,
+                                              Dump dump) {
   constexpr int VEC = 16 / sizeof(T);
   constexpr int CPR = 128 / VEC;                 // chunks per half-row
   constexpr int FROW = 128 * 4 + 16;             // fp32 staging pitch
@@ -60,17 +44,12 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dact(
   float* red = reinterpret_cast<float*>(L.b[0] + 64 * FROW);  // [256] dS partials of this tile
   auto frow = [&](int r) { return epi_buf(L, r) + (r & 63) * FROW; };
   const int valid = min(BN, n - n0);
-  // The block walks chunk c = row * CPR + ch in batches of UNR chunks per thread.  The G, U and
-  // row-weight loads of PF batches go out together -- for bf16 a whole half, issued before the
-  // accumulator dump and its barrier -- so the half costs one memory round trip, not one per
-  // batch.
   constexpr int UNR = 4;
-  constexpr int NB = 256 * CPR / (UNR * GEMM_THREADS);  // batches per half
-  static_assert(NB * UNR * GEMM_THREADS == 256 * CPR, "whole batches");
-  constexpr int PF = sizeof(T) == 2 ? 2 : 1;             // batches in flight together
+  constexpr int NB = 256 * CPR / (UNR * NTHR);  // batches per half
+  static_assert(NB * UNR * NTHR == 256 * CPR, "whole batches");
   static_assert(NB % PF == 0, "whole groups");
   auto chunk_at = [&](int half, int b, int u, int& row, int& ch, int& col) {
-    const int c = (b * UNR + u) * GEMM_THREADS + threadIdx.x;
+    const int c = (b * UNR + u) * NTHR + threadIdx.x;
     row = c / CPR;
     ch = c % CPR;
     col = half * 128 + ch * VEC;
@@ -95,16 +74,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dact(
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     load_group(half, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 v4 = {acc.c[i][2 * half + jj][4 * q], acc.c[i][2 * half + jj][4 * q + 1],
-                            acc.c[i][2 * half + jj][4 * q + 2], acc.c[i][2 * half + jj][4 * q + 3]};
-          *reinterpret_cast<f32x4*>(frow(acc_m(wm, i)) + (wn * 64 + jj * 32 + acc_n(4 * q)) * 4) = v4;
-        }
+    dump(half, frow);
     __syncthreads();
 #pragma unroll 1
     for (int b0 = 0; b0 < NB; b0 += PF) {
@@ -149,6 +119,85 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dact(
     dS_part[(int64_t)nt * R_max + g.m0 + threadIdx.x] = red[threadIdx.x];
 }
 
+template <typename T>
+__global__ __launch_bounds__(GEMM_THREADS, 1) void k_dact(
+    const int32_t* __restrict__ mtile_off, const int32_t* __restrict__ expert_off,
+    const int32_t* __restrict__ row_token, const float* __restrict__ row_w,
+    const T* __restrict__ dY, const T* __restrict__ Wd, const T* __restrict__ H,
+    T* __restrict__ dH, T* __restrict__ wA, float* __restrict__ dS_part, int64_t R_max, int d,
+    int n, int E, int NT, int T_) {
+  MOE_GEMM_LDS(L);
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  GroupTile g;
+  if (!find_group_tile(lin, NT, mtile_off, expert_off, E, g)) return;
+  const int nt = g.nt;
+  const int n0 = nt * BN;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t rowb = (int64_t)d * sizeof(T);
+  auto la = k_rows<T>([&](int i) -> const char* {
+    return i < g.mrows ? reinterpret_cast<const char*>(dY) + (int64_t)clamp_idx(row_token[g.m0 + i], T_) * rowb
+                       : nullptr;
+  });
+  const char* wd = reinterpret_cast<const char*>(Wd) + ((int64_t)g.e * d * n + n0) * sizeof(T);
+  auto lb = mn_rows<T>([=](int k) { return wd + (int64_t)k * n * sizeof(T); }, d, n0, n);
+  WaveAcc acc;
+  gemm_mainloop<T>(la, lb, d / Mma<T>::BK, acc, L, wm, [&](int j) { return bsub_halved(wn, j); });
+  // half h holds the wave's blocks j = 2 h and 2 h + 1 (halved layout)
+  dact_epilogue<T, GEMM_THREADS, sizeof(T) == 2 ? 2 : 1>(L, g, n0, n, nt, R_max, row_w, H, dH, wA, dS_part,
+                                                         [&](int half, auto frow) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v4 = {acc.c[i][2 * half + jj][4 * q], acc.c[i][2 * half + jj][4 * q + 1],
+                            acc.c[i][2 * half + jj][4 * q + 2], acc.c[i][2 * half + jj][4 * q + 3]};
+          *reinterpret_cast<f32x4*>(frow(acc_m(wm, i)) + (wn * 64 + jj * 32 + acc_n(4 * q)) * 4) = v4;
+        }
+  });
+}
+
+// bf16 dAct on the eight-wave engine (same tiles, operands and bits as k_dact).  Block j of wave
+// column wn covers columns j * 128 + wn * 32 .. + 31, so half h of the tile holds each wave's
+// block h.
+__global__ __launch_bounds__(GEMM8_THREADS, 1) void k_dact_w8(
+    const int32_t* __restrict__ mtile_off, const int32_t* __restrict__ expert_off,
+    const int32_t* __restrict__ row_token, const float* __restrict__ row_w,
+    const bf16* __restrict__ dY, const bf16* __restrict__ Wd, const bf16* __restrict__ H,
+    bf16* __restrict__ dH, bf16* __restrict__ wA, float* __restrict__ dS_part, int64_t R_max, int d,
+    int n, int E, int NT, int T_) {
+  MOE_GEMM_LDS(L);
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  GroupTile g;
+  if (!find_group_tile(lin, NT, mtile_off, expert_off, E, g)) return;
+  const int nt = g.nt;
+  const int n0 = nt * BN;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int64_t rowb = (int64_t)d * sizeof(bf16);
+  KDmaW8 la;
+  la.init([&](int i) -> const char* {
+    return i < g.mrows ? reinterpret_cast<const char*>(dY) + (int64_t)clamp_idx(row_token[g.m0 + i], T_) * rowb
+                       : nullptr;
+  });
+  const char* wd = reinterpret_cast<const char*>(Wd) + ((int64_t)g.e * d * n + n0) * sizeof(bf16);
+  auto lb = mn_rows_w8([=](int k) { return wd + (int64_t)k * n * sizeof(bf16); }, d, n0, n);
+  AccW8 acc;
+  gemm_mainloop_w8(la, lb, d / Mma<bf16>::BK, acc, L, wm, [&](int j) { return j * 128 + wn * 32; });
+  dact_epilogue<bf16, GEMM8_THREADS, 2>(L, g, n0, n, nt, R_max, row_w, H, dH, wA, dS_part, [&](int half, auto frow) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v4 = {acc.c[i][half][4 * q], acc.c[i][half][4 * q + 1], acc.c[i][half][4 * q + 2],
+                          acc.c[i][half][4 * q + 3]};
+        *reinterpret_cast<f32x4*>(frow(acc_m(wm, i)) + (wn * 32 + acc_n(4 * q)) * 4) = v4;
+      }
+  });
+}
+
 int dact_ntiles(int64_t n) { return (int)cdiv(n, BN); }
 
 hipError_t launch_dact_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off,
@@ -157,10 +206,9 @@ hipError_t launch_dact_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mt
   const int NT = dact_ntiles(s.n);
   const int grid = grid8(max_mtiles(s.R_max, s.E) * NT);
   if (s.bf16)
-    k_dact<bf16><<<grid, GEMM_THREADS, 0, st>>>(mtile_off, p.expert_off, p.row_token, p.row_w,
-                                                (const bf16*)dY, (const bf16*)W_down, (const bf16*)H,
-                                                (bf16*)dH, (bf16*)wA, dS_part, s.R_max, (int)s.d,
-                                                (int)s.n, s.E, NT, (int)s.T);
+    k_dact_w8<<<grid, GEMM8_THREADS, 0, st>>>(mtile_off, p.expert_off, p.row_token, p.row_w, (const bf16*)dY,
+                                              (const bf16*)W_down, (const bf16*)H, (bf16*)dH, (bf16*)wA, dS_part,
+                                              s.R_max, (int)s.d, (int)s.n, s.E, NT, (int)s.T);
   else
     k_dact<float><<<grid, GEMM_THREADS, 0, st>>>(mtile_off, p.expert_off, p.row_token, p.row_w,
                                                  (const float*)dY, (const float*)W_down, (const float*)H,
