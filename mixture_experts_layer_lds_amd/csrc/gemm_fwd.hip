@@ -193,17 +193,72 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_up(
   }
 }
 
+// bf16 gate/up on the eight-wave engine (same tiles, operands and bits as k_up; 4% faster on the
+// fine-grained layer, where the down GEMM, K = n = 256, was 4% slower on it and stays on four
+// waves): wave column wn
+// takes gate block j = 0 at columns wn * 32 and up block j = 1 at 128 + wn * 32 of the stacked B
+// tile, so G and U of one (row, column) again sit in the same lane.
+__global__ __launch_bounds__(GEMM8_THREADS, 1) void k_up_w8(
+    const int32_t* __restrict__ mtile_off, const int32_t* __restrict__ expert_off,
+    const int32_t* __restrict__ row_token, const bf16* __restrict__ A_in, int gathered,
+    const bf16* __restrict__ Wg, const bf16* __restrict__ Wu, bf16* __restrict__ act, bf16* __restrict__ H,
+    int d, int n, int E, int NT, int T_) {
+  MOE_GEMM_LDS(L);
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  GroupTile g;
+  if (!find_group_tile(lin, NT, mtile_off, expert_off, E, g)) return;
+  const int j0 = g.nt * 128;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int64_t rowb = (int64_t)d * sizeof(bf16);
+  KDmaW8 la, lb;
+  la.init([&](int i) -> const char* {
+    if (i >= g.mrows) return nullptr;
+    const int64_t src = gathered ? clamp_idx(row_token[g.m0 + i], T_) : (int64_t)(g.m0 + i);
+    return reinterpret_cast<const char*>(A_in) + src * rowb;
+  });
+  const char* wg = reinterpret_cast<const char*>(Wg) + (int64_t)g.e * n * rowb;
+  const char* wu = reinterpret_cast<const char*>(Wu) + (int64_t)g.e * n * rowb;
+  lb.init([&](int i) -> const char* {
+    const int j = j0 + (i & 127);
+    if (j >= n) return nullptr;
+    return (i < 128 ? wg : wu) + (int64_t)j * rowb;
+  });
+  auto bsub = [&](int j) { return j * 128 + wn * 32; };
+  AccW8 acc;
+  gemm_mainloop_w8(la, lb, d / Mma<bf16>::BK, acc, L, wm, bsub);
+  const int valid = min(128, n - j0);
+  epi_stage_w8(L, wm, [&](int j) { return j == 0 ? wn * 32 : -1; }, [&](int i, int, int v) {
+    const float gv = acc.c[i][0][v], uv = acc.c[i][1][v];
+    return gv * sigmoid_f32(gv) * uv;
+  });
+  __syncthreads();
+  bf16* ab = act + (int64_t)g.m0 * n + j0;
+  epi_store_rows<GEMM8_THREADS>(L, 0, [&](int r) { return ab + (int64_t)r * n; }, g.mrows, 128, valid);
+  if (H) {
+    // G and U side by side in one staging tile: columns [0,128) G, [128,256) U
+    __syncthreads();
+    epi_stage_w8(L, wm, bsub, [&](int i, int j, int v) { return acc.c[i][j][v]; });
+    __syncthreads();
+    bf16* hb = H + (int64_t)g.m0 * 2 * n;
+    epi_store_rows<GEMM8_THREADS>(L, 0, [&](int r) { return hb + (int64_t)r * 2 * n + j0; }, g.mrows, 128, valid);
+    epi_store_rows<GEMM8_THREADS>(L, 128, [&](int r) { return hb + (int64_t)r * 2 * n + n + j0; }, g.mrows, 128,
+                                  valid);
+  }
+}
+
 hipError_t launch_up_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off,
                           const void* A_in, bool gathered, const void* W_gate, const void* W_up,
                           void* act, void* H, hipStream_t st) {
   const int NT = (int)cdiv(s.n, 128);
   const int grid = grid8(max_mtiles(s.R_max, s.E) * NT);
-  if (s.bf16)
-    k_up<bf16><<<grid, GEMM_THREADS, 0, st>>>(mtile_off, p.expert_off, p.row_token, (const bf16*)A_in,
-                                                     gathered, (const bf16*)W_gate, (const bf16*)W_up,
-                                                     (bf16*)act, (bf16*)H, (int)s.d, (int)s.n, s.E, NT, (int)s.T);
-  else
-    k_up<float><<<grid, GEMM_THREADS, 0, st>>>(mtile_off, p.expert_off, p.row_token, (const float*)A_in,
+  if (s.bf16) {
+    k_up_w8<<<grid, GEMM8_THREADS, 0, st>>>(mtile_off, p.expert_off, p.row_token, (const bf16*)A_in, gathered,
+                                            (const bf16*)W_gate, (const bf16*)W_up, (bf16*)act, (bf16*)H, (int)s.d,
+                                            (int)s.n, s.E, NT, (int)s.T);
+    return hipGetLastError();
+  }
+  k_up<float><<<grid, GEMM_THREADS, 0, st>>>(mtile_off, p.expert_off, p.row_token, (const float*)A_in,
                                                       gathered, (const float*)W_gate, (const float*)W_up,
                                                       (float*)act, (float*)H, (int)s.d, (int)s.n, s.E, NT, (int)s.T);
   return hipGetLastError();
