@@ -32,6 +32,10 @@
 //   conflict with the DMAs still in flight into the others.  Fragment reads are double-buffered
 //   in registers so that LDS latency hides behind the previous k-step's MFMAs.
 //
+// Two further layouts of the same bf16 ring share the wave code: the eight-wave engine (512
+// threads, 128 x 64 per wave, two waves per SIMD) and the half-width engine (256 x 128 tiles of
+// four such waves, a three-slot ring, two workgroups per CU); see their sections below.
+//
 // fp32 path (small fp32 layers only) — register-staged double buffer: stage j uses buffers
 // 2j (A) and 2j+1 (B) as [256][128 B + 16 B pad]; MN-major fp32 operands are transposed in
 // registers while staged.
@@ -1102,6 +1106,158 @@ __device__ __forceinline__ void epi_stage_w8(LdsBufs L, int wm, Col col, Val val
   }
 }
 
+// ===============================================================================================
+// Half-width engine: 256 x 128 output tiles, four waves of 128 x 64 (the eight-wave wave tile)
+// and a three-slot ring of 24 KB stages, so that two workgroups fit on a CU (72 KB of LDS and at
+// most 256 registers per wave each) and one's prologue and epilogue run beside the other's
+// main loop.  For the GEMMs with short K, whose tiles spend much of their time filling the ring
+// and draining the output.
+// ===============================================================================================
+constexpr int HBN = 128;                  // output columns per tile
+constexpr int H_SLOT = 24576;             // A 16 KB (256 rows x 64 B) + B 8 KB (128 rows x 64 B)
+constexpr int H_EPI_ROW = HBN * 2 + 16;   // staging row pitch of the epilogue
+constexpr int H_EPI_ROWS = H_SLOT / H_EPI_ROW;  // staging rows per slot (90; three slots hold 256)
+static_assert(3 * H_EPI_ROWS >= BM, "epilogue staging fits the ring");
+
+// K-major operand of the half-width engine (layout as KDma): wave w instruction q fills tile rows
+// (4 q + w) * 16 .. + 15; NQ = 4 for the 256 A rows, 2 for the 128 B rows.
+template <int NQ>
+struct KDmaH {
+  const char* g[NQ];
+  int step[NQ];
+  template <class RowPtr>
+  __device__ void init(RowPtr row_ptr) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int chunk = (lane & 3) ^ (lane >> 4);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const char* p = row_ptr((4 * q + w) * 16 + (lane >> 2));
+      g[q] = p ? p + chunk * 16 : g_zero_page + chunk * 16;
+      step[q] = p ? 64 : 0;
+    }
+  }
+  __device__ void issue(int q, int s, char* dst) const {
+    const int w = threadIdx.x >> 6;
+    dma16(g[q] + (int64_t)s * step[q], dst + (4 * q + w) * 1024);
+  }
+  __device__ static bf16x8 frag(const char* t, int row0, int s) { return KDma::frag(t, row0, s); }
+};
+
+// One ring step: wait for stage s (stage s + 1, six instructions, may still be in flight),
+// barrier (every wave is done with the slot stage s - 1 used), refill that slot with stage s + 2
+// (stages past the end repeat the last one, so every wait counts the same), and the 16 MFMAs of
+// stage s with the six DMA instructions spread between them.
+template <class BL, class BSub>
+__device__ __forceinline__ void step_h(const KDmaH<4>& la, const BL& lb, int s, int nkt, const char* cur,
+                                       char* refill, AccW8& acc, int wm, BSub bsub) {
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<6>();
+  ring_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  const int r = min(s + 2, nkt - 1);
+  FragW8 F0, F1;
+  load_frags_w8<KDmaH<4>, BL>(cur, 0, wm, bsub, F0);
+  load_frags_w8<KDmaH<4>, BL>(cur, 1, wm, bsub, F1);
+  __builtin_amdgcn_sched_barrier(0);
+  la.issue(0, r, refill);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_range_w8<0, 3>(F0, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  la.issue(1, r, refill);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_range_w8<3, 6>(F0, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  la.issue(2, r, refill);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_range_w8<6, 8>(F0, acc);
+  mma_range_w8<0, 1>(F1, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  la.issue(3, r, refill);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_range_w8<1, 4>(F1, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  lb.issue(0, r, refill + DMA_B_OFF);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_range_w8<4, 6>(F1, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  lb.issue(1, r, refill + DMA_B_OFF);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_range_w8<6, 8>(F1, acc);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// The half-width main loop over nkt stages (accumulating from zero; ends with the LDS free).
+template <class BL, class BSub>
+__device__ __forceinline__ void gemm_mainloop_h(const KDmaH<4>& la, const BL& lb, int nkt, AccW8& acc,
+                                                char* b0, char* b1, char* b2, int wm, BSub bsub) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc.c[i][j][v] = 0.0f;
+  if (nkt <= 0) return;
+  const int r1 = min(1, nkt - 1);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) la.issue(q, 0, b0);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) lb.issue(q, 0, b0 + DMA_B_OFF);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) la.issue(q, r1, b1);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) lb.issue(q, r1, b1 + DMA_B_OFF);
+  int s = 0;
+  for (; s + 3 <= nkt; s += 3) {
+    step_h(la, lb, s, nkt, b0, b2, acc, wm, bsub);
+    step_h(la, lb, s + 1, nkt, b1, b0, acc, wm, bsub);
+    step_h(la, lb, s + 2, nkt, b2, b1, acc, wm, bsub);
+  }
+  if (s < nkt) {  // nested, so that the compiler sees that the second tail step follows the first
+    step_h(la, lb, s, nkt, b0, b2, acc, wm, bsub);
+    if (s + 1 < nkt) step_h(la, lb, s + 1, nkt, b1, b0, acc, wm, bsub);
+  }
+  __syncthreads();  // drains the trailing loads; the LDS is free for the epilogue
+}
+
+// Epilogue of a half-width tile: rows staged H_EPI_ROWS to a slot, then stored as 16-byte chunks
+// (rows < mrows, columns < valid) through row_ptr(r).
+__device__ __forceinline__ char* epi_row_h(char* b0, char* b1, char* b2, int r) {
+  return r < H_EPI_ROWS ? b0 + r * H_EPI_ROW
+                        : (r < 2 * H_EPI_ROWS ? b1 + (r - H_EPI_ROWS) * H_EPI_ROW : b2 + (r - 2 * H_EPI_ROWS) * H_EPI_ROW);
+}
+template <class BSub, class RowPtr>
+__device__ __forceinline__ void epi_h(const AccW8& acc, char* b0, char* b1, char* b2, int wm, BSub bsub,
+                                      RowPtr row_ptr, int mrows, int valid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    char* row = epi_row_h(b0, b1, b2, acc_m(wm, i));
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x2 pk = {pack_bf16x2(acc.c[i][j][4 * q], acc.c[i][j][4 * q + 1]),
+                          pack_bf16x2(acc.c[i][j][4 * q + 2], acc.c[i][j][4 * q + 3])};
+        *reinterpret_cast<u32x2*>(row + (bsub(j) + acc_n(4 * q)) * 2) = pk;
+      }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int b0_ = 0; b0_ < 16; b0_ += 8) {
+    u32x4 v[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const int c = threadIdx.x + (b0_ + b) * GEMM_THREADS;
+      v[b] = *reinterpret_cast<const u32x4*>(epi_row_h(b0, b1, b2, c >> 4) + (c & 15) * 16);
+    }
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const int c = threadIdx.x + (b0_ + b) * GEMM_THREADS;
+      const int r = c >> 4, ch = c & 15;
+      if (r < mrows && ch * 8 < valid) st16_nt(row_ptr(r) + ch * 8, v[b]);
+    }
+  }
+}
+
 // Grouped tiles.  The experts' ceil(rows / BM) m-tiles are concatenated (mtile_off is their
 // exclusive scan), and each m-tile has NT n-tiles.  Tile `lin` is found expert by expert; inside
 // an expert the tiles run in groups of RASTER_M m-tiles, n-tile outer and m-tile inner, so that
@@ -1147,5 +1303,10 @@ __device__ __forceinline__ bool find_group_tile(int lin, int NT, const int32_t* 
   __shared__ __attribute__((aligned(1024))) char L##_2[LDS_BUF];     \
   __shared__ __attribute__((aligned(1024))) char L##_3[LDS_BUF];     \
   const LdsBufs L{{L##_0, L##_1, L##_2, L##_3}}
+
+#define MOE_GEMM_LDS_H(L)                                            \
+  __shared__ __attribute__((aligned(1024))) char L##_0[H_SLOT];      \
+  __shared__ __attribute__((aligned(1024))) char L##_1[H_SLOT];      \
+  __shared__ __attribute__((aligned(1024))) char L##_2[H_SLOT]
 
 }  // namespace moe

@@ -265,19 +265,20 @@ hipError_t launch_up_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mtil
 }
 
 // ---------------------------------------------------------------------------------------------
-// Down projection: Y[r][c] = sum_j Act[r][j] W_down[e][c][j];  tile 256 rows x 256 columns of d.
+// Down projection: Y[r][c] = sum_j Act[r][j] W_down[e][c][j].  fp32 layers: tile 256 rows x 256
+// columns of d on the four-wave engine.  bf16: k_down_h below.
 // ---------------------------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void k_down(
     const int32_t* __restrict__ mtile_off, const int32_t* __restrict__ expert_off,
     const T* __restrict__ act, const T* __restrict__ Wd, T* __restrict__ Y, int d, int n, int E,
     int NT) {
+  static_assert(sizeof(T) == 4, "bf16 layers use k_down_h");
   MOE_GEMM_LDS(L);
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   GroupTile g;
   if (!find_group_tile(lin, NT, mtile_off, expert_off, E, g)) return;
-  const int nt = g.nt;
-  const int n0 = nt * BN;
+  const int n0 = g.nt * BN;
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t rowb = (int64_t)n * sizeof(T);
@@ -288,27 +289,49 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_down(
   auto lb = k_rows<T>([&](int i) -> const char* { return n0 + i < d ? wd + (int64_t)(n0 + i) * rowb : nullptr; });
   WaveAcc acc;
   gemm_mainloop<T, true>(la, lb, n / Mma<T>::BK, acc, L, wm, [&](int j) { return bsub_plain(wn, j); });
-  const int valid = min(BN, d - n0);
-  if constexpr (sizeof(T) == 2) {
-    epi_stage_bf16(L, wm, [&](int j) { return bsub_plain(wn, j); },
-                   [&](int i, int j, int v) { return acc.c[i][j][v]; });
-    __syncthreads();
-    epi_store_bf16(L, 0, reinterpret_cast<bf16*>(Y) + (int64_t)g.m0 * d + n0, d, g.mrows, BN, valid);
-  } else {
-    epi_store_direct(wm, wn, acc, valid, g.mrows, [&](int m) { return Y + (int64_t)(g.m0 + m) * d + n0; });
-  }
+  epi_store_direct(wm, wn, acc, min(BN, d - n0), g.mrows, [&](int m) { return Y + (int64_t)(g.m0 + m) * d + n0; });
+}
+
+// bf16 down projection on the half-width engine: tile 256 rows x 128 columns of d, two
+// workgroups per CU (a tile has only n / 32 k-stages, so filling the ring and storing the R x d
+// output are a large share of its time; the second workgroup's main loop runs beside them).
+__global__ __launch_bounds__(GEMM_THREADS, 2) void k_down_h(
+    const int32_t* __restrict__ mtile_off, const int32_t* __restrict__ expert_off,
+    const bf16* __restrict__ act, const bf16* __restrict__ Wd, bf16* __restrict__ Y, int d, int n, int E,
+    int NT) {
+  MOE_GEMM_LDS_H(L);
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  GroupTile g;
+  if (!find_group_tile(lin, NT, mtile_off, expert_off, E, g)) return;
+  const int n0 = g.nt * HBN;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t rowb = (int64_t)n * sizeof(bf16);
+  KDmaH<4> la;
+  la.init([&](int i) -> const char* {
+    return i < g.mrows ? reinterpret_cast<const char*>(act) + (int64_t)(g.m0 + i) * rowb : nullptr;
+  });
+  const char* wd = reinterpret_cast<const char*>(Wd) + (int64_t)g.e * d * rowb;
+  KDmaH<2> lb;
+  lb.init([&](int i) -> const char* { return n0 + i < d ? wd + (int64_t)(n0 + i) * rowb : nullptr; });
+  auto bsub = [&](int j) { return bsub_w8(wn, j); };
+  AccW8 acc;
+  gemm_mainloop_h(la, lb, n / Mma<bf16>::BK, acc, L_0, L_1, L_2, wm, bsub);
+  bf16* out = Y + (int64_t)g.m0 * d + n0;
+  epi_h(acc, L_0, L_1, L_2, wm, bsub, [&](int r) { return out + (int64_t)r * d; }, g.mrows, min(HBN, d - n0));
 }
 
 hipError_t launch_down_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off,
                             const void* act, const void* W_down, void* Y, hipStream_t st) {
-  const int NT = (int)cdiv(s.d, BN);
-  const int grid = grid8(max_mtiles(s.R_max, s.E) * NT);
-  if (s.bf16)
-    k_down<bf16><<<grid, GEMM_THREADS, 0, st>>>(mtile_off, p.expert_off, (const bf16*)act,
-                                                       (const bf16*)W_down, (bf16*)Y, (int)s.d, (int)s.n, s.E, NT);
-  else
-    k_down<float><<<grid, GEMM_THREADS, 0, st>>>(mtile_off, p.expert_off, (const float*)act,
-                                                        (const float*)W_down, (float*)Y, (int)s.d, (int)s.n, s.E, NT);
+  if (s.bf16) {
+    const int NT = (int)cdiv(s.d, HBN);
+    k_down_h<<<grid8(max_mtiles(s.R_max, s.E) * NT), GEMM_THREADS, 0, st>>>(
+        mtile_off, p.expert_off, (const bf16*)act, (const bf16*)W_down, (bf16*)Y, (int)s.d, (int)s.n, s.E, NT);
+  } else {
+    const int NT = (int)cdiv(s.d, BN);
+    k_down<float><<<grid8(max_mtiles(s.R_max, s.E) * NT), GEMM_THREADS, 0, st>>>(
+        mtile_off, p.expert_off, (const float*)act, (const float*)W_down, (float*)Y, (int)s.d, (int)s.n, s.E, NT);
+  }
   return hipGetLastError();
 }
 
