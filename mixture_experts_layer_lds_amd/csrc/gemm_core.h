@@ -1145,9 +1145,21 @@ struct KDmaH {
 
 // One ring step: wait for stage s (stage s + 1, six instructions, may still be in flight),
 // barrier (every wave is done with the slot stage s - 1 used), refill that slot with stage s + 2
-// (stages past the end repeat the last one, so every wait counts the same), and the 16 MFMAs of
-// stage s with the six DMA instructions spread between them.
-template <class BL, class BSub>
+// (stages past the end repeat the last one, so every wait counts the same), and the MFMAs of
+// stage s with the six DMA instructions spread between them: bf16, two k-steps of 8 blocks; FP8
+// (F8), one k-step of 8 v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales.
+struct FragH8 {
+  i32x8 a[4], b[2];
+};
+template <int FROM, int TO>
+__device__ __forceinline__ void mma8_range_h(const FragH8& F, AccW8& acc) {
+#pragma unroll
+  for (int p = FROM; p < TO; ++p)
+    acc.c[p >> 1][p & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.b[p & 1], F.a[p >> 1], acc.c[p >> 1][p & 1],
+                                                                           0, 0, 0, 127, 0, 127);
+}
+
+template <bool F8, class BL, class BSub>
 __device__ __forceinline__ void step_h(const KDmaH<4>& la, const BL& lb, int s, int nkt, const char* cur,
                                        char* refill, AccW8& acc, int wm, BSub bsub) {
   __builtin_amdgcn_sched_barrier(0);
@@ -1155,39 +1167,72 @@ __device__ __forceinline__ void step_h(const KDmaH<4>& la, const BL& lb, int s, 
   ring_barrier();
   __builtin_amdgcn_sched_barrier(0);
   const int r = min(s + 2, nkt - 1);
-  FragW8 F0, F1;
-  load_frags_w8<KDmaH<4>, BL>(cur, 0, wm, bsub, F0);
-  load_frags_w8<KDmaH<4>, BL>(cur, 1, wm, bsub, F1);
-  __builtin_amdgcn_sched_barrier(0);
-  la.issue(0, r, refill);
-  __builtin_amdgcn_sched_barrier(0);
-  mma_range_w8<0, 3>(F0, acc);
-  __builtin_amdgcn_sched_barrier(0);
-  la.issue(1, r, refill);
-  __builtin_amdgcn_sched_barrier(0);
-  mma_range_w8<3, 6>(F0, acc);
-  __builtin_amdgcn_sched_barrier(0);
-  la.issue(2, r, refill);
-  __builtin_amdgcn_sched_barrier(0);
-  mma_range_w8<6, 8>(F0, acc);
-  mma_range_w8<0, 1>(F1, acc);
-  __builtin_amdgcn_sched_barrier(0);
-  la.issue(3, r, refill);
-  __builtin_amdgcn_sched_barrier(0);
-  mma_range_w8<1, 4>(F1, acc);
-  __builtin_amdgcn_sched_barrier(0);
-  lb.issue(0, r, refill + DMA_B_OFF);
-  __builtin_amdgcn_sched_barrier(0);
-  mma_range_w8<4, 6>(F1, acc);
-  __builtin_amdgcn_sched_barrier(0);
-  lb.issue(1, r, refill + DMA_B_OFF);
-  __builtin_amdgcn_sched_barrier(0);
-  mma_range_w8<6, 8>(F1, acc);
+  if constexpr (F8) {
+    FragH8 F;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) F.b[j] = frag8(cur + DMA_B_OFF, bsub(j));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) F.a[i] = frag8(cur, wm * 128 + i * 32);
+    __builtin_amdgcn_sched_barrier(0);
+    la.issue(0, r, refill);
+    __builtin_amdgcn_sched_barrier(0);
+    mma8_range_h<0, 1>(F, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    la.issue(1, r, refill);
+    __builtin_amdgcn_sched_barrier(0);
+    mma8_range_h<1, 3>(F, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    la.issue(2, r, refill);
+    __builtin_amdgcn_sched_barrier(0);
+    mma8_range_h<3, 5>(F, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    la.issue(3, r, refill);
+    __builtin_amdgcn_sched_barrier(0);
+    mma8_range_h<5, 6>(F, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    lb.issue(0, r, refill + DMA_B_OFF);
+    __builtin_amdgcn_sched_barrier(0);
+    mma8_range_h<6, 7>(F, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    lb.issue(1, r, refill + DMA_B_OFF);
+    __builtin_amdgcn_sched_barrier(0);
+    mma8_range_h<7, 8>(F, acc);
+  } else {
+    FragW8 F0, F1;
+    load_frags_w8<KDmaH<4>, BL>(cur, 0, wm, bsub, F0);
+    load_frags_w8<KDmaH<4>, BL>(cur, 1, wm, bsub, F1);
+    __builtin_amdgcn_sched_barrier(0);
+    la.issue(0, r, refill);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_range_w8<0, 3>(F0, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    la.issue(1, r, refill);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_range_w8<3, 6>(F0, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    la.issue(2, r, refill);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_range_w8<6, 8>(F0, acc);
+    mma_range_w8<0, 1>(F1, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    la.issue(3, r, refill);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_range_w8<1, 4>(F1, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    lb.issue(0, r, refill + DMA_B_OFF);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_range_w8<4, 6>(F1, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    lb.issue(1, r, refill + DMA_B_OFF);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_range_w8<6, 8>(F1, acc);
+  }
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// The half-width main loop over nkt stages (accumulating from zero; ends with the LDS free).
-template <class BL, class BSub>
+// The half-width main loop over nkt stages (accumulating from zero; ends with the LDS free); a
+// stage is 32 bf16 or (F8) 64 fp8 k-values.
+template <bool F8, class BL, class BSub>
 __device__ __forceinline__ void gemm_mainloop_h(const KDmaH<4>& la, const BL& lb, int nkt, AccW8& acc,
                                                 char* b0, char* b1, char* b2, int wm, BSub bsub) {
 #pragma unroll
@@ -1208,26 +1253,26 @@ __device__ __forceinline__ void gemm_mainloop_h(const KDmaH<4>& la, const BL& lb
   for (int q = 0; q < 2; ++q) lb.issue(q, r1, b1 + DMA_B_OFF);
   int s = 0;
   for (; s + 3 <= nkt; s += 3) {
-    step_h(la, lb, s, nkt, b0, b2, acc, wm, bsub);
-    step_h(la, lb, s + 1, nkt, b1, b0, acc, wm, bsub);
-    step_h(la, lb, s + 2, nkt, b2, b1, acc, wm, bsub);
+    step_h<F8>(la, lb, s, nkt, b0, b2, acc, wm, bsub);
+    step_h<F8>(la, lb, s + 1, nkt, b1, b0, acc, wm, bsub);
+    step_h<F8>(la, lb, s + 2, nkt, b2, b1, acc, wm, bsub);
   }
   if (s < nkt) {  // nested, so that the compiler sees that the second tail step follows the first
-    step_h(la, lb, s, nkt, b0, b2, acc, wm, bsub);
-    if (s + 1 < nkt) step_h(la, lb, s + 1, nkt, b1, b0, acc, wm, bsub);
+    step_h<F8>(la, lb, s, nkt, b0, b2, acc, wm, bsub);
+    if (s + 1 < nkt) step_h<F8>(la, lb, s + 1, nkt, b1, b0, acc, wm, bsub);
   }
   __syncthreads();  // drains the trailing loads; the LDS is free for the epilogue
 }
 
-// Epilogue of a half-width tile: rows staged H_EPI_ROWS to a slot, then stored as 16-byte chunks
-// (rows < mrows, columns < valid) through row_ptr(r).
+// Epilogue of a half-width tile: val(i, j, v) of every accumulator staged in bf16, H_EPI_ROWS rows
+// to a slot, then stored as 16-byte chunks (rows < mrows, columns < valid) through row_ptr(r).
 __device__ __forceinline__ char* epi_row_h(char* b0, char* b1, char* b2, int r) {
   return r < H_EPI_ROWS ? b0 + r * H_EPI_ROW
                         : (r < 2 * H_EPI_ROWS ? b1 + (r - H_EPI_ROWS) * H_EPI_ROW : b2 + (r - 2 * H_EPI_ROWS) * H_EPI_ROW);
 }
-template <class BSub, class RowPtr>
-__device__ __forceinline__ void epi_h(const AccW8& acc, char* b0, char* b1, char* b2, int wm, BSub bsub,
-                                      RowPtr row_ptr, int mrows, int valid) {
+template <class Val, class BSub, class RowPtr>
+__device__ __forceinline__ void epi_h(Val val, char* b0, char* b1, char* b2, int wm, BSub bsub, RowPtr row_ptr,
+                                      int mrows, int valid) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     char* row = epi_row_h(b0, b1, b2, acc_m(wm, i));
@@ -1235,8 +1280,8 @@ __device__ __forceinline__ void epi_h(const AccW8& acc, char* b0, char* b1, char
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const u32x2 pk = {pack_bf16x2(acc.c[i][j][4 * q], acc.c[i][j][4 * q + 1]),
-                          pack_bf16x2(acc.c[i][j][4 * q + 2], acc.c[i][j][4 * q + 3])};
+        const u32x2 pk = {pack_bf16x2(val(i, j, 4 * q), val(i, j, 4 * q + 1)),
+                          pack_bf16x2(val(i, j, 4 * q + 2), val(i, j, 4 * q + 3))};
         *reinterpret_cast<u32x2*>(row + (bsub(j) + acc_n(4 * q)) * 2) = pk;
       }
   }

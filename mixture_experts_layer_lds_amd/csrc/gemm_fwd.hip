@@ -316,9 +316,10 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_down_h(
   lb.init([&](int i) -> const char* { return n0 + i < d ? wd + (int64_t)(n0 + i) * rowb : nullptr; });
   auto bsub = [&](int j) { return bsub_w8(wn, j); };
   AccW8 acc;
-  gemm_mainloop_h(la, lb, n / Mma<bf16>::BK, acc, L_0, L_1, L_2, wm, bsub);
+  gemm_mainloop_h<false>(la, lb, n / Mma<bf16>::BK, acc, L_0, L_1, L_2, wm, bsub);
   bf16* out = Y + (int64_t)g.m0 * d + n0;
-  epi_h(acc, L_0, L_1, L_2, wm, bsub, [&](int r) { return out + (int64_t)r * d; }, g.mrows, min(HBN, d - n0));
+  epi_h([&](int i, int j, int v) { return acc.c[i][j][v]; }, L_0, L_1, L_2, wm, bsub,
+        [&](int r) { return out + (int64_t)r * d; }, g.mrows, min(HBN, d - n0));
 }
 
 hipError_t launch_down_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off,
