@@ -11,7 +11,7 @@
 //   k_quant_fp8:  rows x K elements -> codes [rows][K] (uint8) and scales [rows] (fp32);
 //   k_up_fp8:     act = silu(G) U with G, U = (Xq[rows] [Wg_q; Wu_q]^T) * s_x * s_w, gathered token
 //                 rows as in the bf16 gate/up GEMM; act stored in bf16;
-//   k_down_fp8_h: Y = (act_q Wd_q^T) * s_a * s_d, stored in bf16.
+//   k_down_fp8 / k_down_fp8_h: Y = (act_q Wd_q^T) * s_a * s_d, stored in bf16.
 // The GEMMs run the bf16 path's DMA ring and tile schedule with 64 one-byte elements per stage
 // on v_mfma_scale_f32_32x32x64_f8f6f4 (fp32 accumulation of exact products); the scales are
 // applied in the epilogue.
@@ -142,10 +142,55 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_up_fp8(
 }
 
 // ---------------------------------------------------------------------------------------------
-// Down: Y[r][c] = (sum_j act_q[r][j] Wd_q[e][c][j]) s_a[r] s_d[e][c] on the half-width engine:
-// tile 256 rows x 128 columns of d, two workgroups per CU (n / 64 k-stages per tile only, so the
-// ring fill and the bf16 output stores of one workgroup run beside the other's MFMAs).
+// Down: Y[r][c] = (sum_j act_q[r][j] Wd_q[e][c][j]) s_a[r] s_d[e][c].
+//   k_down_fp8:   tile 256 rows x 256 columns of d on the four-wave engine;
+//   k_down_fp8_h: tile 256 rows x 128 columns on the half-width engine, two workgroups per CU,
+//                 for short K (n <= DOWN_H_MAX_N_FP8): a tile's ring fill and bf16 output stores
+//                 are then a large share of its time, and the second workgroup's MFMAs run
+//                 beside them.  With long K the four-wave tile's operand reuse wins.
 // ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(GEMM_THREADS, 1) void k_down_fp8(
+    const int32_t* __restrict__ mtile_off, const int32_t* __restrict__ expert_off,
+    const uint8_t* __restrict__ Aq, const float* __restrict__ sa, const uint8_t* __restrict__ Wdq,
+    const float* __restrict__ sd, bf16* __restrict__ Y, int d, int n, int E, int NT) {
+  MOE_GEMM_LDS(L);
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  GroupTile g;
+  if (!find_group_tile(lin, NT, mtile_off, expert_off, E, g)) return;
+  const int n0 = g.nt * BN;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t rowb = n;
+  KDma la, lb;
+  la.init([&](int i) -> const char* {
+    return i < g.mrows ? reinterpret_cast<const char*>(Aq) + (int64_t)(g.m0 + i) * rowb : nullptr;
+  });
+  const char* wd = reinterpret_cast<const char*>(Wdq) + (int64_t)g.e * d * rowb;
+  lb.init([&](int i) -> const char* { return n0 + i < d ? wd + (int64_t)(n0 + i) * rowb : nullptr; });
+  WaveAcc acc;
+  auto bsub = [&](int j) { return bsub_plain(wn, j); };
+  gemm_mainloop_f8(la, lb, n / 64, acc, L, wm, bsub);
+  const int valid = min(BN, d - n0);
+  float srow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = acc_m(wm, i);
+    srow[i] = r < g.mrows ? sa[g.m0 + r] : 0.0f;
+  }
+  f32x4 cs[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = bsub(j) + acc_n(4 * q);
+      cs[j][q] = scales4(sd + (int64_t)g.e * d + n0 + c, c < valid);
+    }
+  epi_stage_bf16(L, wm, bsub, [&](int i, int j, int v) { return acc.c[i][j][v] * srow[i] * cs[j][v >> 2][v & 3]; });
+  __syncthreads();
+  epi_store_bf16(L, 0, Y + (int64_t)g.m0 * d + n0, d, g.mrows, BN, valid);
+}
+
+
 __global__ __launch_bounds__(GEMM_THREADS, 2) void k_down_fp8_h(
     const int32_t* __restrict__ mtile_off, const int32_t* __restrict__ expert_off,
     const uint8_t* __restrict__ Aq, const float* __restrict__ sa, const uint8_t* __restrict__ Wdq,
@@ -202,9 +247,15 @@ hipError_t launch_up_fp8(const Shape& s, const PlanPtrs& p, const int32_t* mtile
 
 hipError_t launch_down_fp8(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off, const uint8_t* Aq,
                            const float* sa, const uint8_t* Wdq, const float* sd, void* Y, hipStream_t st) {
-  const int NT = (int)cdiv(s.d, HBN);
-  k_down_fp8_h<<<grid8f(max_mtiles(s.R_max, s.E) * NT), GEMM_THREADS, 0, st>>>(
-      mtile_off, p.expert_off, Aq, sa, Wdq, sd, static_cast<bf16*>(Y), (int)s.d, (int)s.n, s.E, NT);
+  if (s.n <= DOWN_H_MAX_N_FP8) {
+    const int NT = (int)cdiv(s.d, HBN);
+    k_down_fp8_h<<<grid8f(max_mtiles(s.R_max, s.E) * NT), GEMM_THREADS, 0, st>>>(
+        mtile_off, p.expert_off, Aq, sa, Wdq, sd, static_cast<bf16*>(Y), (int)s.d, (int)s.n, s.E, NT);
+  } else {
+    const int NT = (int)cdiv(s.d, BN);
+    k_down_fp8<<<grid8f(max_mtiles(s.R_max, s.E) * NT), GEMM_THREADS, 0, st>>>(
+        mtile_off, p.expert_off, Aq, sa, Wdq, sd, static_cast<bf16*>(Y), (int)s.d, (int)s.n, s.E, NT);
+  }
   return hipGetLastError();
 }
 

@@ -1114,6 +1114,11 @@ __device__ __forceinline__ void epi_stage_w8(LdsBufs L, int wm, Col col, Val val
 // and draining the output.
 // ===============================================================================================
 constexpr int HBN = 128;                  // output columns per tile
+// The down GEMMs take this engine up to these n (K): 16 bf16 or 32 fp8 stages per tile.  Measured
+// on layers with n = 256 (8 / 4 stages: faster), 2048 (64 bf16 stages: slower; 32 fp8 stages:
+// faster) and 14336 (slower in both).
+constexpr int DOWN_H_MAX_N = 512;
+constexpr int DOWN_H_MAX_N_FP8 = 2048;
 constexpr int H_SLOT = 24576;             // A 16 KB (256 rows x 64 B) + B 8 KB (128 rows x 64 B)
 constexpr int H_EPI_ROW = HBN * 2 + 16;   // staging row pitch of the epilogue
 constexpr int H_EPI_ROWS = H_SLOT / H_EPI_ROW;  // staging rows per slot (90; three slots hold 256)

@@ -265,15 +265,14 @@ hipError_t launch_up_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mtil
 }
 
 // ---------------------------------------------------------------------------------------------
-// Down projection: Y[r][c] = sum_j Act[r][j] W_down[e][c][j].  fp32 layers: tile 256 rows x 256
-// columns of d on the four-wave engine.  bf16: k_down_h below.
+// Down projection: Y[r][c] = sum_j Act[r][j] W_down[e][c][j];  tile 256 rows x 256 columns of d on
+// the four-wave engine (fp32 layers, and bf16 layers with long K; k_down_h below for short K).
 // ---------------------------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void k_down(
     const int32_t* __restrict__ mtile_off, const int32_t* __restrict__ expert_off,
     const T* __restrict__ act, const T* __restrict__ Wd, T* __restrict__ Y, int d, int n, int E,
     int NT) {
-  static_assert(sizeof(T) == 4, "bf16 layers use k_down_h");
   MOE_GEMM_LDS(L);
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   GroupTile g;
@@ -289,12 +288,21 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_down(
   auto lb = k_rows<T>([&](int i) -> const char* { return n0 + i < d ? wd + (int64_t)(n0 + i) * rowb : nullptr; });
   WaveAcc acc;
   gemm_mainloop<T, true>(la, lb, n / Mma<T>::BK, acc, L, wm, [&](int j) { return bsub_plain(wn, j); });
-  epi_store_direct(wm, wn, acc, min(BN, d - n0), g.mrows, [&](int m) { return Y + (int64_t)(g.m0 + m) * d + n0; });
+  const int valid = min(BN, d - n0);
+  if constexpr (sizeof(T) == 2) {
+    epi_stage_bf16(L, wm, [&](int j) { return bsub_plain(wn, j); },
+                   [&](int i, int j, int v) { return acc.c[i][j][v]; });
+    __syncthreads();
+    epi_store_bf16(L, 0, reinterpret_cast<bf16*>(Y) + (int64_t)g.m0 * d + n0, d, g.mrows, BN, valid);
+  } else {
+    epi_store_direct(wm, wn, acc, valid, g.mrows, [&](int m) { return Y + (int64_t)(g.m0 + m) * d + n0; });
+  }
 }
 
-// bf16 down projection on the half-width engine: tile 256 rows x 128 columns of d, two
-// workgroups per CU (a tile has only n / 32 k-stages, so filling the ring and storing the R x d
-// output are a large share of its time; the second workgroup's main loop runs beside them).
+// bf16 down projection on the half-width engine, for n <= DOWN_H_MAX_N: tile 256 rows x 128
+// columns of d, two workgroups per CU (a tile has only n / 32 k-stages, so filling the ring and
+// storing the R x d output are a large share of its time; the second workgroup's main loop runs
+// beside them).  With long K the four-wave tile's operand reuse wins.
 __global__ __launch_bounds__(GEMM_THREADS, 2) void k_down_h(
     const int32_t* __restrict__ mtile_off, const int32_t* __restrict__ expert_off,
     const bf16* __restrict__ act, const bf16* __restrict__ Wd, bf16* __restrict__ Y, int d, int n, int E,
@@ -324,9 +332,13 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_down_h(
 
 hipError_t launch_down_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off,
                             const void* act, const void* W_down, void* Y, hipStream_t st) {
-  if (s.bf16) {
+  if (s.bf16 && s.n <= DOWN_H_MAX_N) {
     const int NT = (int)cdiv(s.d, HBN);
     k_down_h<<<grid8(max_mtiles(s.R_max, s.E) * NT), GEMM_THREADS, 0, st>>>(
+        mtile_off, p.expert_off, (const bf16*)act, (const bf16*)W_down, (bf16*)Y, (int)s.d, (int)s.n, s.E, NT);
+  } else if (s.bf16) {
+    const int NT = (int)cdiv(s.d, BN);
+    k_down<bf16><<<grid8(max_mtiles(s.R_max, s.E) * NT), GEMM_THREADS, 0, st>>>(
         mtile_off, p.expert_off, (const bf16*)act, (const bf16*)W_down, (bf16*)Y, (int)s.d, (int)s.n, s.E, NT);
   } else {
     const int NT = (int)cdiv(s.d, BN);

@@ -49,6 +49,7 @@ def test_tiny_fp32_layer_forward_backward():
     dict(T=700, d=128, E=5, K=3, n=192, dtype="f32"),
     dict(T=333, d=256, E=16, K=4, n=128, dtype="bf16"),
     dict(T=129, d=64, E=3, K=1, n=64, dtype="f32"),
+    dict(T=400, d=192, E=3, K=2, n=576, dtype="bf16"),  # n > 512: the four-wave bf16 down GEMM
 ])
 def test_ragged_multi_tile(shape):
     cfg = wl.small_shape(**shape, seed=31)
