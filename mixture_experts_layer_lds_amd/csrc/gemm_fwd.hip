@@ -44,7 +44,8 @@ int64_t max_mtiles(int64_t R_max, int E) { return R_max / BM + E; }
 static inline int grid8(int64_t n) { return (int)((n + 7) / 8 * 8); }
 
 // ---------------------------------------------------------------------------------------------
-// Router: logits[t][e] = sum_i X[t][i] W_r[e][i] + bias[e]   (fp32 out, direct stores)
+// Router: logits[t][e] = sum_i X[t][i] W_r[e][i] + bias[e]   (fp32 out, direct stores).  fp32
+// layers: k_router (four-wave engine); bf16: k_router_h below.
 // ---------------------------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void k_router(const T* __restrict__ X,
@@ -99,16 +100,72 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_router(const T* __restrict_
     }
 }
 
+// bf16 router GEMM on the half-width engine: tile 256 tokens x 128 experts (the four-wave
+// 256 x 256 tile would leave half its columns empty at E = 128), two workgroups per CU.
+__global__ __launch_bounds__(GEMM_THREADS, 2) void k_router_h(const bf16* __restrict__ X, const bf16* __restrict__ Wr,
+                                                              const float* __restrict__ bias,
+                                                              float* __restrict__ logits, int T_, int d, int E,
+                                                              int NT) {
+  MOE_GEMM_LDS_H(L);
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int mt = lin / NT, nt = lin % NT;
+  const int m0 = mt * BM, n0 = nt * HBN;
+  if (m0 >= T_) return;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t rowb = (int64_t)d * sizeof(bf16);
+  KDmaH<4> la;
+  la.init([&](int i) -> const char* {
+    return m0 + i < T_ ? reinterpret_cast<const char*>(X) + (m0 + i) * rowb : nullptr;
+  });
+  KDmaH<2> lb;
+  lb.init([&](int i) -> const char* {
+    return n0 + i < E ? reinterpret_cast<const char*>(Wr) + (n0 + i) * rowb : nullptr;
+  });
+  auto bsub = [&](int j) { return bsub_w8(wn, j); };
+  AccW8 acc;
+  gemm_mainloop_h<false>(la, lb, d / Mma<bf16>::BK, acc, L_0, L_1, L_2, wm, bsub);
+  // as in k_router: a lane's v = 4q .. 4q + 3 are four consecutive experts of one token
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int n = n0 + bsub(j) + acc_n(4 * q);
+      if (n >= E) continue;
+      f32x4 b = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (bias) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) b[u] = n + u < E ? bias[n + u] : 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + acc_m(wm, i);
+        if (m >= T_) continue;
+        float* o = logits + (int64_t)m * E + n;
+        const f32x4 v4 = {acc.c[i][j][4 * q] + b[0], acc.c[i][j][4 * q + 1] + b[1], acc.c[i][j][4 * q + 2] + b[2],
+                          acc.c[i][j][4 * q + 3] + b[3]};
+        if ((E & 3) == 0) {
+          *reinterpret_cast<f32x4*>(o) = v4;
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (n + u < E) o[u] = v4[u];
+        }
+      }
+    }
+}
+
 hipError_t launch_router_gemm(const Shape& s, const void* X, const void* W_r, const float* bias,
                               float* logits, hipStream_t st) {
-  const int NT = (int)cdiv(s.E, BN);
-  const int n = grid8(cdiv(s.T, BM) * NT);
-  if (s.bf16)
-    k_router<bf16><<<n, GEMM_THREADS, 0, st>>>((const bf16*)X, (const bf16*)W_r, bias, logits,
-                                                      (int)s.T, (int)s.d, s.E, NT);
-  else
-    k_router<float><<<n, GEMM_THREADS, 0, st>>>((const float*)X, (const float*)W_r, bias, logits,
-                                                       (int)s.T, (int)s.d, s.E, NT);
+  if (s.bf16) {
+    const int NT = (int)cdiv(s.E, HBN);
+    k_router_h<<<grid8(cdiv(s.T, BM) * NT), GEMM_THREADS, 0, st>>>((const bf16*)X, (const bf16*)W_r, bias, logits,
+                                                                  (int)s.T, (int)s.d, s.E, NT);
+  } else {
+    const int NT = (int)cdiv(s.E, BN);
+    k_router<float><<<grid8(cdiv(s.T, BM) * NT), GEMM_THREADS, 0, st>>>((const float*)X, (const float*)W_r, bias,
+                                                                       logits, (int)s.T, (int)s.d, s.E, NT);
+  }
   return hipGetLastError();
 }
 
