@@ -223,10 +223,10 @@ moe_status moe_backward(const moe_dims* dims, const void* dY, const void* X, con
  * equal moe_forward's with plain top-K up to the order of the fp32 accumulations (the SwiGLU
  * activation is rounded to dtype between the projections, as in moe_forward); routing is the
  * same function of the logits, ties to the lower expert id.  It pays off while few experts
- * see each a few tokens (on MI355X it beats moe_forward at T = 1 and T = 8 on the layer shapes
- * with large experts, and is on par at T = 1 on the fine-grained one); once most experts are
- * routed with several tokens each (T = 64 on those shapes), moe_forward's grouped GEMMs are as
- * fast or faster.
+ * see each a few tokens and their weights are large (on MI355X it beats moe_forward at T = 1
+ * and T = 8 on the layer shapes with large experts); once most experts are routed with several
+ * tokens each (T = 64 on those shapes), or when the experts are small (the fine-grained shape:
+ * d = 1536, n = 256, at any T tried), moe_forward is as fast or faster.
  *  X [T,d], W_r [E,d], bias [E] fp32 or NULL, W_gate/W_up [E,n,d], W_down [E,d,n] dtype.
  *  Outputs (overwritten): logits [T,E] fp32, topk_idx [T,K] int32, topk_w [T,K] fp32 (as in the
  *  plan of moe_route), out [T,d] dtype.
