@@ -9,7 +9,7 @@
 // same way in any precision.
 //
 //   k_quant_fp8:  rows x K elements -> codes [rows][K] (uint8) and scales [rows] (fp32);
-//   k_up_fp8:     act = silu(G) U with G, U = (Xq[rows] [Wg_q; Wu_q]^T) * s_x * s_w, gathered token
+//   k_up_fp8 / k_up_fp8_h: act = silu(G) U with G, U = (Xq[rows] [Wg_q; Wu_q]^T) * s_x * s_w, gathered token
 //                 rows as in the bf16 gate/up GEMM; act stored in bf16;
 //   k_down_fp8 / k_down_fp8_h: Y = (act_q Wd_q^T) * s_a * s_d, stored in bf16.
 // The GEMMs run the bf16 path's DMA ring and tile schedule with 64 one-byte elements per stage
@@ -141,6 +141,94 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_up_fp8(
   epi_store_bf16(L, 0, act + (int64_t)g.m0 * n + j0, n, g.mrows, 128, valid);
 }
 
+// The same on the half-width engine, for d <= UP_H_MAX_D_FP8 (at most 32 fp8 k-stages per tile,
+// where the second workgroup per CU hides the ring fill and the epilogue; with longer K the
+// four-wave tile's operand reuse wins): tile 256 rows x 64 act columns (B: W_gate rows j0 .. j0 + 63
+// over W_up rows j0 .. j0 + 63; block j of wave column wn at j * 64 + wn * 32, so G and U of a
+// (row, column) sit in accumulator blocks 0 and 1 of one lane), two workgroups per CU.
+constexpr int UP_H_MAX_D_FP8 = 2048;
+constexpr int UP8H_COLS = 64;
+constexpr int UP8H_ROW = UP8H_COLS * 2 + 16;  // bf16 staging pitch
+constexpr int UP8H_ROWS = H_SLOT / UP8H_ROW;   // staging rows per slot (170; two slots hold 256)
+static_assert(2 * UP8H_ROWS >= BM, "act staging fits two slots");
+
+__global__ __launch_bounds__(GEMM_THREADS, 2) void k_up_fp8_h(
+    const int32_t* __restrict__ mtile_off, const int32_t* __restrict__ expert_off,
+    const int32_t* __restrict__ row_token, const uint8_t* __restrict__ Xq, const float* __restrict__ sx,
+    const uint8_t* __restrict__ Wgq, const float* __restrict__ sg, const uint8_t* __restrict__ Wuq,
+    const float* __restrict__ su, bf16* __restrict__ act, int d, int n, int E, int NT, int T_) {
+  MOE_GEMM_LDS_H(L);
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  GroupTile g;
+  if (!find_group_tile(lin, NT, mtile_off, expert_off, E, g)) return;
+  const int j0 = g.nt * UP8H_COLS;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t rowb = d;  // one byte per element
+  KDmaH<4> la;
+  la.init([&](int i) -> const char* {
+    if (i >= g.mrows) return nullptr;
+    return reinterpret_cast<const char*>(Xq) + (int64_t)clamp_idx(row_token[g.m0 + i], T_) * rowb;
+  });
+  const char* wg = reinterpret_cast<const char*>(Wgq) + (int64_t)g.e * n * rowb;
+  const char* wu = reinterpret_cast<const char*>(Wuq) + (int64_t)g.e * n * rowb;
+  KDmaH<2> lb;
+  lb.init([&](int i) -> const char* {
+    const int j = j0 + (i & 63);
+    if (j >= n) return nullptr;
+    return (i < 64 ? wg : wu) + (int64_t)j * rowb;
+  });
+  auto bsub = [&](int j) { return j * 64 + wn * 32; };
+  AccW8 acc;
+  gemm_mainloop_h<true>(la, lb, d / 64, acc, L_0, L_1, L_2, wm, bsub);
+  const int valid = min(UP8H_COLS, n - j0);
+  float srow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = acc_m(wm, i);
+    srow[i] = r < g.mrows ? sx[clamp_idx(row_token[g.m0 + r], T_)] : 0.0f;
+  }
+  f32x4 cg[4], cu[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int c = wn * 32 + acc_n(4 * q);
+    const int64_t w = (int64_t)g.e * n + j0 + c;
+    cg[q] = scales4(sg + w, c < valid);
+    cu[q] = scales4(su + w, c < valid);
+  }
+  auto srow_ptr = [&](int r) { return (r < UP8H_ROWS ? L_0 + r * UP8H_ROW : L_1 + (r - UP8H_ROWS) * UP8H_ROW); };
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    char* row = srow_ptr(acc_m(wm, i));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float a[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float gv = acc.c[i][0][4 * q + u] * srow[i] * cg[q][u];
+        const float uv = acc.c[i][1][4 * q + u] * srow[i] * cu[q][u];
+        a[u] = gv * sigmoid_f32(gv) * uv;
+      }
+      const u32x2 pk = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+      *reinterpret_cast<u32x2*>(row + (wn * 32 + acc_n(4 * q)) * 2) = pk;
+    }
+  }
+  __syncthreads();
+  bf16* out = act + (int64_t)g.m0 * n + j0;
+  u32x4 v[8];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const int c = threadIdx.x + b * GEMM_THREADS;
+    v[b] = *reinterpret_cast<const u32x4*>(srow_ptr(c >> 3) + (c & 7) * 16);
+  }
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const int c = threadIdx.x + b * GEMM_THREADS;
+    const int r = c >> 3, ch = c & 7;
+    if (r < g.mrows && ch * 8 < valid) st16_nt(out + (int64_t)r * n + ch * 8, v[b]);
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Down: Y[r][c] = (sum_j act_q[r][j] Wd_q[e][c][j]) s_a[r] s_d[e][c].
 //   k_down_fp8:   tile 256 rows x 256 columns of d on the four-wave engine;
@@ -238,10 +326,17 @@ static inline int grid8f(int64_t n) { return (int)((n + 7) / 8 * 8); }
 hipError_t launch_up_fp8(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off, const uint8_t* Xq,
                          const float* sx, const uint8_t* Wgq, const float* sg, const uint8_t* Wuq,
                          const float* su, void* act, hipStream_t st) {
-  const int NT = (int)cdiv(s.n, 128);
-  k_up_fp8<<<grid8f(max_mtiles(s.R_max, s.E) * NT), GEMM_THREADS, 0, st>>>(
-      mtile_off, p.expert_off, p.row_token, Xq, sx, Wgq, sg, Wuq, su, static_cast<bf16*>(act), (int)s.d,
-      (int)s.n, s.E, NT, (int)s.T);
+  if (s.d <= UP_H_MAX_D_FP8) {
+    const int NT = (int)cdiv(s.n, UP8H_COLS);
+    k_up_fp8_h<<<grid8f(max_mtiles(s.R_max, s.E) * NT), GEMM_THREADS, 0, st>>>(
+        mtile_off, p.expert_off, p.row_token, Xq, sx, Wgq, sg, Wuq, su, static_cast<bf16*>(act), (int)s.d,
+        (int)s.n, s.E, NT, (int)s.T);
+  } else {
+    const int NT = (int)cdiv(s.n, 128);
+    k_up_fp8<<<grid8f(max_mtiles(s.R_max, s.E) * NT), GEMM_THREADS, 0, st>>>(
+        mtile_off, p.expert_off, p.row_token, Xq, sx, Wgq, sg, Wuq, su, static_cast<bf16*>(act), (int)s.d,
+        (int)s.n, s.E, NT, (int)s.T);
+  }
   return hipGetLastError();
 }
 

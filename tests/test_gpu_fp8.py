@@ -139,9 +139,10 @@ def check_ffn_fp8(cfg, inp, out, experts):
     return worst
 
 
-# n <= 2048 runs the down GEMM on the half-width engine, n = 2112 on the four-wave one
+# d <= 2048 runs the gate/up GEMM and n <= 2048 the down GEMM on the half-width engine; d or n =
+# 2112 takes the four-wave one
 @pytest.mark.parametrize("T,d,n,E,K", [(700, 320, 192, 6, 2), (129, 256, 64, 4, 4), (1000, 512, 320, 8, 2),
-                                       (300, 192, 2112, 4, 2)])
+                                       (300, 192, 2112, 4, 2), (200, 2112, 128, 3, 2)])
 def test_grouped_ffn_fp8_small(T, d, n, E, K):
     cfg = wl.small_shape(T=T, d=d, E=E, K=K, n=n, dtype="bf16", backward=False, seed=T + d)
     inp = wl.make_inputs(cfg, device="cuda")
