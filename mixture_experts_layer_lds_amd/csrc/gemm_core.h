@@ -1111,7 +1111,8 @@ __device__ __forceinline__ void epi_stage_w8(LdsBufs L, int wm, Col col, Val val
 // and a three-slot ring of 24 KB stages, so that two workgroups fit on a CU (72 KB of LDS and at
 // most 256 registers per wave each) and one's prologue and epilogue run beside the other's
 // main loop.  For the GEMMs with short K, whose tiles spend much of their time filling the ring
-// and draining the output.
+// and draining the output (the down GEMMs, the FP8 gate/up GEMM at small d), and for the router
+// GEMM, whose N = E (128 on the fine-grained layer) would leave half of a 256-wide tile empty.
 // ===============================================================================================
 constexpr int HBN = 128;                  // output columns per tile
 // The down GEMMs take this engine up to these n (K): 16 bf16 or 32 fp8 stages per tile.  Measured
