@@ -9,8 +9,11 @@ router backward with the dX gather-sum, router weight gradient).
 
 Prints ONE JSON line.  "Useful" FLOPs count real (token, expert) rows only:
 6 R d n forward + 12 R d n backward for the experts, plus 2 T d E (router forward) and
-4 T d E (router backward).  Per-stage durations come from hipEvent pairs the library records
-around each stage on the stream it launches on, inside the timed region.
+4 T d E (router backward).  The K timed steps run with the library's stage timing off; a second
+pass of K steps records a hipEvent pair around each stage on the stream the library launches it
+on, which gives the per-stage durations and the roofline of the dominant kernel.  Combine and
+permute are also timed on their own with a 1 GiB write between reps that flushes the caches
+(median and min).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu]
 """
@@ -131,6 +134,25 @@ def stage_min_bytes(stage, R, T, d, n, E, es):
         "dx_gemm": R * 2 * n * es + 2 * Wb + R * d * es,
         "dwr_gemm": T * E * 4 + T * d * es + E * d * es,
     }.get(stage)
+
+
+def memory_accounting(cfg, dims, R_max, backward, B):
+    """Bytes the layer keeps from the forward to the backward, and the workspaces: with the H
+    cache (H = [G|U], the plan and the logits) and with full recompute (the plan and the logits),
+    against a layer that also keeps the gathered inputs, the SwiGLU output and the expert outputs
+    (X_perm [R,d], A [R,n], Y [R,d] besides H)."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    T, d, n, E, K = cfg.T, cfg.d, cfg.n, cfg.E, cfg.K
+    plan = T * K * 8 + E * 8 + 4 + R_max * 12 + (T + 1) * 4 + 64
+    logits = T * E * 4
+    H = R_max * 2 * n * es
+    conventional = plan + logits + H + R_max * d * es + R_max * n * es + R_max * d * es
+    m = {"kept_with_h_cache": plan + logits + H, "kept_recompute": plan + logits,
+         "kept_conventional": conventional,
+         "forward_workspace": int(B.moe_workspace_bytes(dims, B.OP_FORWARD))}
+    if backward:
+        m["backward_workspace"] = int(B.moe_workspace_bytes(dims, B.OP_BACKWARD))
+    return m
 
 
 def cpu_baseline(cfg, inp, logits, budget_s):
@@ -412,28 +434,77 @@ def main():
         del src, dst
         log("calibration copy: 3 x (256 MiB read + 256 MiB written)")
 
-    B.moe_timing_enable(True)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    # headline: K steps with the library's stage timing off; one event per step boundary gives the
+    # per-step distribution
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    ev0.record()
+    evs[0].record()
     for i in range(args.steps):
         step()
-    ev1.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
-    total_ms = ev0.elapsed_time(ev1)
-    stages = {s: B.moe_timing_read(s) for s in B.STAGES}
+    total_ms = evs[0].elapsed_time(evs[-1])
+    per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
     ms_step = total_ms / args.steps
-    log("timed %d steps: %.3f ms/step" % (args.steps, ms_step))
-    # the packed-mode permute is not part of the step (the step gathers inside the GEMM); it is
-    # timed on its own afterwards, with the same plan, as the materialised-dispatch reference
-    X_perm = torch.empty(R_max, cfg.d, dtype=dt, device="cuda")
+    log("timed %d steps: %.3f ms/step (median %.3f, min %.3f)"
+        % (args.steps, ms_step, float(np.median(per_step)), min(per_step)))
+
+    # stage pass: the same K steps again with a hipEvent pair around every stage, recorded by the
+    # library on the stream it launches on
+    B.moe_timing_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
     for i in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    stage_pass_ms = e0.elapsed_time(e1) / args.steps
+    stages = {s: B.moe_timing_read(s) for s in B.STAGES}
+    B.moe_timing_enable(False)
+    log("stage pass: %.3f ms/step" % stage_pass_ms)
+
+    # the HBM-bound gather kernels on their own, each rep after a 1 GiB write that flushes the
+    # 256 MB MALL and the L2s (inputs would otherwise stay cached between reps): combine of the
+    # expert outputs, and the packed-mode permute, which the step does not run (its GEMMs gather
+    # rows themselves) but which is the materialised dispatch of the same plan
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    Y_perm = torch.empty(R_max, cfg.d, dtype=dt, device="cuda")
+    H_tmp = torch.empty(R_max, 2 * cfg.n, dtype=dt, device="cuda")
+    ws_ffn, nb_ffn = B.workspace(dims, B.OP_FFN)
+    B.moe_grouped_ffn(dims, plan, inp["X"], 1, inp["W_gate"], inp["W_up"], inp["W_down"], H_tmp, Y_perm,
+                      ws_ffn, nb_ffn)
+    del H_tmp, ws_ffn
+    X_perm = torch.empty(R_max, cfg.d, dtype=dt, device="cuda")
+    out_c = torch.empty_like(out)
+    B.moe_timing_enable(True)
+    for i in range(args.steps):
+        flush.fill_(i & 255)
+        B.moe_combine(dims, plan, Y_perm, 1, out_c)
+        flush.fill_((i + 7) & 255)
         B.moe_permute(dims, plan, inp["X"], X_perm)
     torch.cuda.synchronize()
-    stages["permute"] = B.moe_timing_read("permute")
+    flushed = {"combine": B.moe_timing_read("combine"), "permute": B.moe_timing_read("permute")}
     B.moe_timing_enable(False)
-    del X_perm
+    del flush, Y_perm, X_perm, out_c
+
+    # the backward recomputing [G|U] from X instead of reading the forward's H cache
+    recompute_ms = None
+    if backward and not args.no_h_cache:
+        def step_recompute():
+            B.moe_forward(dims, inp["X"], inp["W_r"], inp["bias"], inp["W_gate"], inp["W_up"], inp["W_down"],
+                          logits, plan, None, out, ws_f, nb_f)
+            B.moe_backward(dims, inp["dY"], inp["X"], inp["W_r"], inp["W_gate"], inp["W_up"], inp["W_down"],
+                           plan, None, g["dX"], g["dW_gate"], g["dW_up"], g["dW_down"], g["dS"],
+                           g["dLogits"], g["dW_r"], ws_b, nb_b)
+        for _ in range(args.warmup):
+            step_recompute()
+        e0.record()
+        for i in range(args.steps):
+            step_recompute()
+        e1.record()
+        torch.cuda.synchronize()
+        recompute_ms = e0.elapsed_time(e1) / args.steps
+        log("recompute step: %.3f ms" % recompute_ms)
 
     T, d, n, E = cfg.T, cfg.d, cfg.n, cfg.E
     es = 2 if cfg.dtype == "bf16" else 4
@@ -453,6 +524,7 @@ def main():
             continue
         avg = float(np.mean(v))
         ent = {"launches_per_step": round(len(v) / args.steps, 3), "avg_ms": round(avg, 4),
+               "median_ms": round(float(np.median(v)), 4), "min_ms": round(float(np.min(v)), 4),
                "ms_per_step": round(float(np.sum(v)) / args.steps, 4)}
         f = stage_flops(s, R, T, d, n, E)
         b = stage_bytes(s, R, T, d, n, E, es, cfg.K)
@@ -464,10 +536,17 @@ def main():
             ent["pct_hbm"] = round(100 * b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 1)
         breakdown[s] = ent
     gemm_stages = [s for s in breakdown if stage_flops(s, R, T, d, n, E)]
-    if "permute" in breakdown:
-        breakdown["permute"]["in_step"] = False
-    modelled = [s for s in breakdown if s != "permute" and
+    modelled = [s for s in breakdown if
                 (stage_flops(s, R, T, d, n, E) or stage_bytes(s, R, T, d, n, E, es, cfg.K))]
+    hbm_flushed = {}
+    for s, v in flushed.items():
+        b = stage_bytes(s, R, T, d, n, E, es, cfg.K)
+        med, mn = float(np.median(v)), float(np.min(v))
+        hbm_flushed[s] = {"reps": len(v), "median_ms": round(med, 4), "min_ms": round(mn, 4),
+                          "bytes": int(b), "gbs_median": round(b / (med * 1e-3) / 1e9, 1),
+                          "gbs_best": round(b / (mn * 1e-3) / 1e9, 1),
+                          "pct_hbm_median": round(100 * b / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 1),
+                          "in_step": s != "permute"}
     dom = max(modelled, key=lambda s: breakdown[s]["ms_per_step"])
     if stage_flops(dom, R, T, d, n, E):
         avg = breakdown[dom]["avg_ms"]
@@ -504,8 +583,16 @@ def main():
         "pct_bf16_peak": round(100 * value / peak, 2),
         "grouped_gemm_pct_peak": round(100 * expert_flops / (gemm_ms * 1e-3) / 1e12 / peak, 2) if gemm_ms else None,
         "roofline": roof,
+        "step_ms_median": round(float(np.median(per_step)), 4),
+        "step_ms_min": round(float(np.min(per_step)), 4),
+        "stage_pass_ms_per_step": round(stage_pass_ms, 4),
         "stages": breakdown,
+        "hbm_kernels_flushed": hbm_flushed,
+        "memory": memory_accounting(cfg, dims, R_max, backward, B),
     }
+    if recompute_ms is not None:
+        res["no_h_cache"] = {"ms_per_step": round(recompute_ms, 4),
+                             "value": round(flops / (recompute_ms * 1e-3) / 1e12, 2)}
     if not args.no_cpu:
         log("CPU oracle baseline ...")
         res["cpu_baseline"] = cpu_baseline(cfg, inp, logits, args.cpu_seconds)

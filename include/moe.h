@@ -27,7 +27,7 @@
  *  - The caller owns all memory: inputs, outputs, the routing plan and the workspace.  The
  *    library never allocates or frees device memory and keeps no state between calls, apart from
  *    a thread-local error message, when enabled the stage-timing records (moe_timing_*), and for
- *    moe_decode a per-device arrival counter (static device memory) and ordering event.
+ *    moe_decode a per-device status word (static device memory, see moe_decode_status).
  *    Outputs are fully overwritten, never accumulated into.
  *  - Arguments are validated on the host before anything is enqueued.  An invalid call returns
  *    MOE_EINVAL / MOE_ENOTSUP / MOE_EWORKSPACE and enqueues nothing; a failed launch returns
@@ -217,9 +217,12 @@ moe_status moe_backward(const moe_dims* dims, const void* dY, const void* X, con
  * Plain top-K only (round_mode must be MOE_ROUND_NONE, else MOE_ENOTSUP); T <= 1024.  The
  * launch is cooperative (one workgroup per CU, all resident, phases separated by grid-wide
  * barriers), so the call fails with MOE_EHIP rather than run if the device cannot host the
- * grid.  Decode kernels on one device never overlap: a call on another stream than the
- * previous moe_decode call on that device first waits (hipStreamWaitEvent) for that call; the
- * library keeps one event per device for this, created on first use.  Results
+ * grid.  The barriers count arrivals in the call's workspace, which a small kernel clears right
+ * before the launch, so calls share no device state: calls that may overlap (other streams) need
+ * only their own workspaces.  A barrier wait is bounded (about a second of polling; see
+ * moe_decode_set_spin_limit); a workgroup that reaches the bound leaves the kernel and sets the
+ * device's decode status word, the other workgroups give up at the next barrier, and the call's
+ * outputs are then invalid: moe_decode_status() reports it.  Results
  * equal moe_forward's with plain top-K up to the order of the fp32 accumulations (the SwiGLU
  * activation is rounded to dtype between the projections, as in moe_forward); routing is the
  * same function of the logits, ties to the lower expert id.  It pays off while few experts
@@ -230,12 +233,25 @@ moe_status moe_backward(const moe_dims* dims, const void* dY, const void* X, con
  *  X [T,d], W_r [E,d], bias [E] fp32 or NULL, W_gate/W_up [E,n,d], W_down [E,d,n] dtype.
  *  Outputs (overwritten): logits [T,E] fp32, topk_idx [T,K] int32, topk_w [T,K] fp32 (as in the
  *  plan of moe_route), out [T,d] dtype.
- *  ws: moe_workspace_bytes(dims, MOE_OP_DECODE) bytes (per-expert token lists, the activation
- *  and the fp32 expert outputs of the T*K (token, expert) pairs); contents on entry unused. */
+ *  ws: moe_workspace_bytes(dims, MOE_OP_DECODE) bytes (barrier counter, per-expert token lists,
+ *  the activation and the fp32 expert outputs of the T*K (token, expert) pairs); contents on
+ *  entry unused. */
 moe_status moe_decode(const moe_dims* dims, const void* X, const void* W_r, const float* bias,
                       const void* W_gate, const void* W_up, const void* W_down, float* logits,
                       int32_t* topk_idx, float* topk_w, void* out, void* ws, size_t ws_bytes,
                       void* stream);
+
+/* moe_decode_status — host: waits for `stream` (hipStreamSynchronize), then reads and clears the
+ * current device's decode status word.  Returns MOE_EHIP (with a message) if a moe_decode kernel
+ * on this device gave up waiting at a grid barrier since the last call, so that its outputs are
+ * invalid; MOE_OK otherwise; MOE_EHIP also if the runtime fails. */
+moe_status moe_decode_status(void* stream);
+
+/* moe_decode_set_spin_limit — host: polls of the counter before a moe_decode grid barrier gives
+ * up, for launches made after this call (default 2^20, about a second; 0 gives up at the first
+ * barrier without waiting, which exercises the failure report).  Returns the previous limit, or
+ * -1 (MOE_EINVAL in moe_last_error) for a negative limit.  Not thread-safe. */
+long long moe_decode_set_spin_limit(long long limit);
 
 /* moe_quantize_fp8 — per-row FP8 quantisation (apxml.com "硬件加速的考量", section "利用稀疏性和
  * 量化": FP8 weights and activations).  Format: OCP FP8 E4M3 codes (bias 7, largest finite 448,

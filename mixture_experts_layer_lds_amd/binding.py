@@ -21,7 +21,8 @@ OP_ROUTE, OP_PERMUTE, OP_FFN, OP_COMBINE, OP_FORWARD, OP_BACKWARD, OP_DECODE, OP
 STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ENOTSUP", -3: "MOE_EWORKSPACE", -4: "MOE_EHIP"}
 
 EXPORTS = ["moe_max_rows", "moe_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_ffn",
-           "moe_combine", "moe_forward", "moe_backward", "moe_decode", "moe_quantize_fp8",
+           "moe_combine", "moe_forward", "moe_backward", "moe_decode", "moe_decode_status",
+           "moe_decode_set_spin_limit", "moe_quantize_fp8",
            "moe_grouped_ffn_fp8", "moe_status_string", "moe_last_error",
            "moe_version", "moe_timing_enable", "moe_timing_read"]
 STAGES = ["router_gemm", "route", "tiles", "up_gemm", "down_gemm", "permute", "combine", "dact_gemm",
@@ -74,6 +75,9 @@ def lib():
         L.moe_backward.argtypes = [pd, vp, vp, vp, vp, vp, vp, pp, vp, vp, vp, vp, vp, vp, vp, vp,
                                    vp, sz, vp]
         L.moe_decode.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_decode_status.argtypes, L.moe_decode_status.restype = [vp], st
+        L.moe_decode_set_spin_limit.argtypes = [ctypes.c_longlong]
+        L.moe_decode_set_spin_limit.restype = ctypes.c_longlong
         L.moe_quantize_fp8.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, vp, vp, vp, vp]
         L.moe_grouped_ffn_fp8.argtypes = [pd, pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         for f in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward",
@@ -200,6 +204,20 @@ def moe_decode(dims, X, W_r, bias, W_gate, W_up, W_down, logits, topk_idx, topk_
     _check(lib().moe_decode(ctypes.byref(dims), _p(X), _p(W_r), _p(bias), _p(W_gate), _p(W_up),
                             _p(W_down), _p(logits), _p(topk_idx), _p(topk_w), _p(out), _p(ws), ws_bytes,
                             _stream(stream)))
+
+
+def moe_decode_status(stream=None):
+    """Raises MoEError(MOE_EHIP) if a moe_decode kernel on the current device gave up at a grid
+    barrier since the last check (waits for the stream first); clears the device's status word."""
+    _check(lib().moe_decode_status(_stream(stream)))
+
+
+def moe_decode_set_spin_limit(limit):
+    """Polls before a moe_decode grid barrier gives up (later launches); returns the previous limit."""
+    prev = lib().moe_decode_set_spin_limit(int(limit))
+    if prev < 0:
+        raise MoEError(-1, lib().moe_last_error().decode())
+    return prev
 
 
 def moe_quantize_fp8(src, codes, scales, stream=None):

@@ -21,9 +21,13 @@
 // barriers (every workgroup walks every phase with grid-stride loops, so each reaches every
 // barrier).  The barrier is a release fence, one relaxed arrival on a 64-bit counter, relaxed
 // polling and an acquire fence: cache maintenance happens once per workgroup and barrier, not
-// once per poll.  Phases:
-//   A. router logits (+ bias): tiles of 16 experts x 16 tokens; also clears the per-expert
-//      counters;
+// once per poll.  The counter lives in the call's workspace and a one-workgroup kernel clears it
+// (with the per-expert counters) right before the launch, so calls share no device state and
+// need no ordering beyond their workspace's stream.  A workgroup that polls longer than the spin
+// limit (about a second) gives up: it raises the device's status word and leaves the kernel, so
+// the workgroups still waiting give up at the next barrier and every one of them exits;
+// moe_decode_status() reports and clears the word.  Phases:
+//   A. router logits (+ bias): tiles of 16 experts x 16 tokens;
 //   B. per token (one wave): top-K with softmax, and the token's (t, k) pairs appended to the
 //      chosen experts' lists (the order inside a list does not affect any value: each token is
 //      its own MFMA column);
@@ -35,8 +39,6 @@
 // Routing is plain top-K (no token rounding); results match moe_forward up to the order of the
 // fp32 accumulations.
 #include "internal.h"
-
-#include <mutex>
 
 namespace moe {
 
@@ -56,11 +58,13 @@ struct DecodeArgs {
   int32_t* topk_idx;
   float* topk_w;
   void* out;
-  int32_t* cnt;   // [E]
-  int32_t* list;  // [E][T] pair ids t * K + k
-  void* act;      // [T * K][n] element type
-  float* y;       // [T * K][d]
+  unsigned long long* bar;  // grid-barrier arrivals (cleared before the launch)
+  int32_t* cnt;             // [E] (cleared before the launch)
+  int32_t* list;            // [E][T] pair ids t * K + k
+  void* act;                // [T * K][n] element type
+  float* y;                 // [T * K][d]
   int T, d, n, E, K;
+  long long spin_limit;     // polls before a grid barrier gives up
 };
 
 // One reduction step of a 16x16 tile: every lane holds 16 bytes of its weight row (A, row
@@ -176,6 +180,7 @@ struct DecLds {
   int consumed[DEC_WAVES][2];
   int active[1024];  // routed experts in ascending order
   int nactive;
+  int proceed;       // set by the barrier: 0 if this workgroup gave up waiting
 };
 
 __device__ __forceinline__ void dec_lds_wait_ge(int* p, int target) {
@@ -311,15 +316,16 @@ __device__ __forceinline__ int dec_active_experts(const int32_t* cnt, int E, int
   return *count;
 }
 
-// Arrivals at the grid barrier, one counter per kernel instantiation (per device: each device
-// holds its own copy).  The counter only grows: with nb workgroups, arrival number v (counted
-// from the first launch) belongs to the barrier that completes when the counter reaches
-// (v / nb + 1) nb.  Every launch of one instantiation has the same grid, so each launch starts
-// at a multiple of nb; cooperative launches on one device do not overlap.
-static __device__ unsigned long long g_dec_arrivals[2][32];
+// Set when a workgroup gave up waiting at a grid barrier; read and cleared by
+// moe_decode_status() (one word per device: each device holds its own copy).
+__device__ int g_dec_status;
 
-// Grid-wide barrier; also clears the workgroup's tile-group counters for the next phase.
-__device__ __forceinline__ void dec_grid_barrier(unsigned long long* ctr, DecLds& L) {
+// Grid-wide barrier on the call's arrival counter, which only grows from zero: with nb
+// workgroups, arrival number v belongs to the barrier that completes when the counter reaches
+// (v / nb + 1) nb.  Also clears the workgroup's tile-group counters for the next phase.
+// Returns false if this workgroup gave up (the status word is then set): the caller leaves the
+// kernel, whose later phases would read results that were never written.
+__device__ __forceinline__ bool dec_grid_barrier(unsigned long long* ctr, long long spin_limit, DecLds& L) {
   __builtin_amdgcn_s_waitcnt(0);  // this wave's loads and stores have completed
   __syncthreads();
   if (threadIdx.x < DEC_WAVES * 2) {
@@ -331,20 +337,34 @@ __device__ __forceinline__ void dec_grid_barrier(unsigned long long* ctr, DecLds
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const unsigned long long v = __hip_atomic_fetch_add(ctr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const unsigned long long target = (v / nb + 1) * nb;
-    // bounded wait (about a second): a grid that is not fully resident cannot happen under a
-    // cooperative launch; if it ever did, the kernel would finish with wrong results, not hang
-    for (int spin = 0; spin < (1 << 20); ++spin) {
-      if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) break;
+    // bounded wait: under a cooperative launch every workgroup is resident and arrives, so the
+    // limit is only reached if that guarantee fails; then the call reports an error instead of
+    // hanging or finishing with wrong results
+    int ok = 0;
+    for (long long spin = 0; spin < spin_limit; ++spin) {
+      if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) {
+        ok = 1;
+        break;
+      }
       __builtin_amdgcn_s_sleep(1);
     }
+    if (!ok) __hip_atomic_store(&g_dec_status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    L.proceed = ok;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
+  return L.proceed != 0;
+}
+
+// Clears a call's barrier counter and per-expert token counters before the decode kernel.
+__global__ __launch_bounds__(256) void k_dec_clear(unsigned long long* bar, int32_t* cnt, int E) {
+  if (threadIdx.x == 0) *bar = 0ull;
+  for (int i = threadIdx.x; i < E; i += 256) cnt[i] = 0;
 }
 
 template <typename T>
 __global__ __launch_bounds__(DEC_THREADS) void k_decode(DecodeArgs a) {
-  unsigned long long* bar = g_dec_arrivals[sizeof(T) == 2 ? 0 : 1];
+  unsigned long long* bar = a.bar;
   __shared__ DecLds L;
   constexpr int S = DecMma<T>::S;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, q = lane >> 4;
@@ -357,8 +377,7 @@ __global__ __launch_bounds__(DEC_THREADS) void k_decode(DecodeArgs a) {
   __syncthreads();
   DecGroup G;
 
-  // ---- A: router logits; clear the per-expert counters ----
-  for (int i = blockIdx.x * DEC_THREADS + tid; i < E; i += gridDim.x * DEC_THREADS) a.cnt[i] = 0;
+  // ---- A: router logits ----
   {
     const T* Wr = reinterpret_cast<const T*>(a.W_r);
     const int tiles = (E + 15) / 16, groups = (T_ + 15) / 16, passes = (groups + DEC_NG - 1) / DEC_NG;
@@ -383,7 +402,7 @@ __global__ __launch_bounds__(DEC_THREADS) void k_decode(DecodeArgs a) {
       });
     }
   }
-  dec_grid_barrier(bar, L);
+  if (!dec_grid_barrier(bar, a.spin_limit, L)) return;
 
   // ---- B: top-K + softmax, per-expert lists; one token per wave ----
   {
@@ -434,7 +453,7 @@ __global__ __launch_bounds__(DEC_THREADS) void k_decode(DecodeArgs a) {
       }
     }
   }
-  dec_grid_barrier(bar, L);
+  if (!dec_grid_barrier(bar, a.spin_limit, L)) return;
 
   const int nact = dec_active_experts(a.cnt, E, L.active, &L.nactive);
 
@@ -474,7 +493,7 @@ __global__ __launch_bounds__(DEC_THREADS) void k_decode(DecodeArgs a) {
       }
     }
   }
-  dec_grid_barrier(bar, L);
+  if (!dec_grid_barrier(bar, a.spin_limit, L)) return;
 
   // ---- D: down tiles (16 output columns) -> y[pair] ----
   {
@@ -503,7 +522,7 @@ __global__ __launch_bounds__(DEC_THREADS) void k_decode(DecodeArgs a) {
       }
     }
   }
-  dec_grid_barrier(bar, L);
+  if (!dec_grid_barrier(bar, a.spin_limit, L)) return;
 
   // ---- E: combine in ascending expert order, 4 columns per thread ----
   {
@@ -552,19 +571,31 @@ __global__ __launch_bounds__(DEC_THREADS) void k_decode(DecodeArgs a) {
 
 static size_t dec_align(size_t b) { return (b + 255) / 256 * 256; }
 
-// Per device: the stream of the last decode launch and an event recorded after it (created on
-// first use, kept until the process ends).
-constexpr int kDecMaxDevices = 64;
-struct DecOrder {
-  hipEvent_t done = nullptr;
-  hipStream_t stream = nullptr;
-};
-static DecOrder g_dec_order[kDecMaxDevices];
-static std::mutex g_dec_order_mu;
-
 size_t decode_workspace_bytes(int64_t T, int64_t d, int64_t n, int E, int K) {
-  return dec_align((size_t)E * 4) + dec_align((size_t)E * T * 4) + dec_align((size_t)T * K * n * 4) +
-         dec_align((size_t)T * K * d * 4);
+  return dec_align(8) + dec_align((size_t)E * 4) + dec_align((size_t)E * T * 4) +
+         dec_align((size_t)T * K * n * 4) + dec_align((size_t)T * K * d * 4);
+}
+
+static long long g_dec_spin_limit = 1ll << 20;  // about a second of polling
+
+long long decode_set_spin_limit(long long limit) {
+  const long long prev = g_dec_spin_limit;
+  g_dec_spin_limit = limit;
+  return prev;
+}
+
+hipError_t decode_read_status(hipStream_t st, int* failed) {
+  hipError_t e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return e;
+  int v = 0;
+  e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_dec_status), sizeof v, 0, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return e;
+  *failed = v;
+  if (v) {
+    const int zero = 0;
+    e = hipMemcpyToSymbol(HIP_SYMBOL(g_dec_status), &zero, sizeof zero, 0, hipMemcpyHostToDevice);
+  }
+  return e;
 }
 
 hipError_t launch_decode(const Shape& s, const void* X, const void* W_r, const float* bias,
@@ -574,6 +605,8 @@ hipError_t launch_decode(const Shape& s, const void* X, const void* W_r, const f
   a.X = X; a.W_r = W_r; a.bias = bias; a.W_gate = W_gate; a.W_up = W_up; a.W_down = W_down;
   a.logits = logits; a.topk_idx = topk_idx; a.topk_w = topk_w; a.out = out;
   char* w = static_cast<char*>(ws);
+  a.bar = reinterpret_cast<unsigned long long*>(w);
+  w += dec_align(8);
   a.cnt = reinterpret_cast<int32_t*>(w);
   w += dec_align((size_t)s.E * 4);
   a.list = reinterpret_cast<int32_t*>(w);
@@ -582,6 +615,7 @@ hipError_t launch_decode(const Shape& s, const void* X, const void* W_r, const f
   w += dec_align((size_t)s.T * s.K * s.n * 4);
   a.y = reinterpret_cast<float*>(w);
   a.T = (int)s.T; a.d = (int)s.d; a.n = (int)s.n; a.E = s.E; a.K = s.K;
+  a.spin_limit = g_dec_spin_limit;
   const void* fn = s.bf16 ? reinterpret_cast<const void*>(&k_decode<bf16>)
                           : reinterpret_cast<const void*>(&k_decode<float>);
   int dev = 0, cus = 0, per_cu = 0;
@@ -595,25 +629,11 @@ hipError_t launch_decode(const Shape& s, const void* X, const void* W_r, const f
   // every workgroup must be resident at once for the grid barriers: the cooperative launch
   // refuses a larger grid
   const int grid = cus * per_cu;
-  if (dev < 0 || dev >= kDecMaxDevices) return hipErrorInvalidDevice;
-  // The barrier counter is per device, so two of these kernels must never run at once: a call
-  // on another stream than the previous call on this device waits for that call first.
-  std::lock_guard<std::mutex> lock(g_dec_order_mu);
-  DecOrder& o = g_dec_order[dev];
-  if (!o.done) {
-    e = hipEventCreateWithFlags(&o.done, hipEventDisableTiming);
-    if (e != hipSuccess) return e;
-  } else if (o.stream != st) {
-    e = hipStreamWaitEvent(st, o.done, 0);
-    if (e != hipSuccess) return e;
-  }
+  k_dec_clear<<<1, 256, 0, st>>>(a.bar, a.cnt, s.E);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   void* params[] = {&a};
-  e = hipLaunchCooperativeKernel(fn, dim3(grid), dim3(DEC_THREADS), params, 0u, st);
-  if (e != hipSuccess) return e;
-  e = hipEventRecord(o.done, st);
-  if (e != hipSuccess) return e;
-  o.stream = st;
-  return hipSuccess;
+  return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(DEC_THREADS), params, 0u, st);
 }
 
 }  // namespace moe

@@ -101,5 +101,10 @@ size_t decode_workspace_bytes(int64_t T, int64_t d, int64_t n, int E, int K);
 hipError_t launch_decode(const Shape& s, const void* X, const void* W_r, const float* bias,
                          const void* W_gate, const void* W_up, const void* W_down, float* logits,
                          int32_t* topk_idx, float* topk_w, void* out, void* ws, hipStream_t st);
+// polls before a decode grid barrier gives up (later launches); returns the previous limit
+long long decode_set_spin_limit(long long limit);
+// synchronises st, then reads and clears the current device's decode status word (1 = a
+// workgroup gave up at a grid barrier since the last read)
+hipError_t decode_read_status(hipStream_t st, int* failed);
 
 }  // namespace moe

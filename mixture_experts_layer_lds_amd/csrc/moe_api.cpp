@@ -50,25 +50,30 @@ struct Timing {
 };
 Timing g_timing;
 
-// Record the start of a stage; returns the slot or -1.
-int stage_begin(int stage, hipStream_t st) {
-  if (!g_timing.on || g_timing.used >= kTimingSlots) return -1;
-  const int i = g_timing.used++;
+// Record the start of a stage: the slot, or -1 when timing is off or the slots are used up.
+hipError_t stage_begin(int stage, hipStream_t st, int* slot) {
+  *slot = -1;
+  if (!g_timing.on || g_timing.used >= kTimingSlots) return hipSuccess;
+  const int i = g_timing.used;
+  const hipError_t e = hipEventRecord(g_timing.ev0[i], st);
+  if (e != hipSuccess) return e;
   g_timing.stage[i] = stage;
-  hipEventRecord(g_timing.ev0[i], st);
-  return i;
+  g_timing.used = i + 1;
+  *slot = i;
+  return hipSuccess;
 }
-void stage_end(int slot, hipStream_t st) {
-  if (slot >= 0) hipEventRecord(g_timing.ev1[slot], st);
+hipError_t stage_end(int slot, hipStream_t st) {
+  return slot >= 0 ? hipEventRecord(g_timing.ev1[slot], st) : hipSuccess;
 }
 
-// Run one stage's launcher between timing events.
-#define MOE_STAGE(stage, st, expr, where)          \
-  do {                                             \
-    const int _slot = stage_begin((stage), (st));  \
-    const hipError_t _e = (expr);                  \
-    stage_end(_slot, (st));                        \
-    MOE_HIP(_e, where);                            \
+// Run one stage's launcher between timing events; a failed launch or event record is MOE_EHIP.
+#define MOE_STAGE(stage, st, expr, where)                      \
+  do {                                                         \
+    int _slot;                                                 \
+    MOE_HIP(stage_begin((stage), (st), &_slot), "timing event"); \
+    const hipError_t _e = (expr);                              \
+    MOE_HIP(_e, where);                                        \
+    MOE_HIP(stage_end(_slot, (st)), "timing event");           \
   } while (0)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -405,6 +410,23 @@ moe_status moe_decode(const moe_dims* dims, const void* X, const void* W_r, cons
   return MOE_OK;
 }
 
+moe_status moe_decode_status(void* stream) {
+  int failed = 0;
+  MOE_HIP(decode_read_status(static_cast<hipStream_t>(stream), &failed), "moe_decode_status");
+  if (failed)
+    return fail(MOE_EHIP, "moe_decode: a workgroup gave up waiting at a grid barrier; the outputs of "
+                          "that call are invalid");
+  return MOE_OK;
+}
+
+long long moe_decode_set_spin_limit(long long limit) {
+  if (limit < 0) {
+    fail(MOE_EINVAL, "spin limit %lld < 0", limit);
+    return -1;
+  }
+  return decode_set_spin_limit(limit);
+}
+
 moe_status moe_forward(const moe_dims* dims, const void* X, const void* W_r, const float* bias,
                        const void* W_gate, const void* W_up, const void* W_down, float* logits,
                        const moe_plan* plan, void* H_cache, void* out, void* ws, size_t ws_bytes,
@@ -496,16 +518,21 @@ int moe_timing_enable(int on) {
     return MOE_OK;
   }
   g_timing.on = false;
+  hipError_t first = hipSuccess;
   if (g_timing.created) {
-    for (int i = 0; i < g_timing.used; ++i) hipEventSynchronize(g_timing.ev1[i]);
+    for (int i = 0; i < g_timing.used; ++i) {
+      const hipError_t e = hipEventSynchronize(g_timing.ev1[i]);
+      if (first == hipSuccess) first = e;
+    }
     for (int i = 0; i < kTimingSlots; ++i) {
-      hipEventDestroy(g_timing.ev0[i]);
-      hipEventDestroy(g_timing.ev1[i]);
+      const hipError_t e0 = hipEventDestroy(g_timing.ev0[i]);
+      const hipError_t e1 = hipEventDestroy(g_timing.ev1[i]);
+      if (first == hipSuccess) first = e0 != hipSuccess ? e0 : e1;
     }
     g_timing.created = false;
   }
   g_timing.used = 0;
-  return MOE_OK;
+  return hip_status(first, "moe_timing_enable(0)");
 }
 
 int moe_timing_read(int stage, float* ms, int max) {

@@ -24,3 +24,15 @@ def announce_case(nodeid):
             f.write("START %s\n" % nodeid)
             f.flush()
             os.fsync(f.fileno())
+
+
+def progress(msg):
+    """A progress line of a long GPU case (same destinations as announce_case)."""
+    sys.stderr.write("  %s\n" % msg)
+    sys.stderr.flush()
+    d = os.environ.get("MOE_TEST_LOG_DIR")
+    if d:
+        os.makedirs(d, exist_ok=True)
+        with open(os.path.join(d, "gpu_test_progress.txt"), "a") as f:
+            f.write("  %s\n" % msg)
+            f.flush()

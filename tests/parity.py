@@ -82,6 +82,21 @@ def run_gpu(cfg, inputs=None, backward=None, cache_h=True, with_router_grad=True
     return res
 
 
+def run_grouped_ffn(cfg, res):
+    """moe_grouped_ffn on gathered rows with the plan of ``res`` (the kernels moe_forward runs):
+    returns (H, Y_perm) as device tensors, so that Y_perm rows, which moe_forward keeps in its
+    workspace, can be compared."""
+    dims, plan, inp = res["dims"], res["plan"], res["inputs"]
+    dt = B.torch_dtype(dims)
+    H = torch.empty(plan.R_max, 2 * cfg.n, dtype=dt, device="cuda")
+    Y = torch.empty(plan.R_max, cfg.d, dtype=dt, device="cuda")
+    ws, nb = B.workspace(dims, B.OP_FFN, "cuda")
+    B.moe_grouped_ffn(dims, plan, inp["X"], 1, inp["W_gate"], inp["W_up"], inp["W_down"], H, Y, ws, nb)
+    torch.cuda.synchronize()
+    del ws
+    return H, Y
+
+
 def check_routing(cfg, res, L=None, round_rand=None):
     """Routing outputs bit-exact against the oracle run on the GPU's fp32 logits (and, for
     stochastic token rounding, the same random words)."""

@@ -170,3 +170,12 @@ def test_fp8_argument_checks(lib):
     need = B.moe_workspace_bytes(dims(), B.OP_FFN_FP8)
     assert need >= (8 + 1) * 4
     assert ffn(dims(), ws=need - 1) == -3
+
+
+def test_decode_spin_limit_is_validated_on_the_host(lib):
+    """A negative spin limit is rejected; a valid one returns the previous limit (host state only)."""
+    prev = B.moe_decode_set_spin_limit(1 << 20)
+    assert prev >= 0
+    with pytest.raises(B.MoEError):
+        B.moe_decode_set_spin_limit(-1)
+    assert B.moe_decode_set_spin_limit(prev) == 1 << 20

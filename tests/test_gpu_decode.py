@@ -114,7 +114,8 @@ def test_decode_full_layer_shapes(name, T):
 
 def test_decode_calls_on_two_streams_do_not_overlap():
     """Decode calls on different streams (each with its own workspace) give the same bits as the
-    same calls on one stream: the library orders them, so their grid barriers never mix."""
+    same calls on one stream: each call's grid barriers count in its own workspace, so calls share
+    no device state, and no call reports a barrier that gave up."""
     cfgs = [wl.small_shape(T=24, d=512, E=32, K=4, n=256, dtype="bf16", backward=False, seed=s)
             for s in (91, 92)]
     inps = [wl.make_inputs(c, device="cuda") for c in cfgs]
@@ -135,6 +136,32 @@ def test_decode_calls_on_two_streams_do_not_overlap():
                              inp["W_down"], *o, ws, nb, stream=streams[j])
                 outs.append((j, o, ws))
     torch.cuda.synchronize()
+    B.moe_decode_status()
     for j, o, _ in outs:
         for got, want in zip(o, refs[j]):
             assert torch.equal(got, want)
+
+
+def test_decode_barrier_give_up_is_reported():
+    """The give-up path of the grid barrier, forced from the host: with a spin limit of 0 every
+    workgroup gives up at the first barrier without polling (it never waits, so every workgroup
+    leaves the kernel normally).  moe_decode_status then raises MOE_EHIP once and clears the status
+    word; the next call with the default limit matches a clean call bit for bit and reports
+    nothing."""
+    cfg = wl.small_shape(T=16, d=256, E=16, K=2, n=128, dtype="bf16", backward=False, seed=93)
+    inp = wl.make_inputs(cfg, device="cuda")
+    ref = run_decode(cfg, inp)
+    B.moe_decode_status()                                  # nothing pending
+    prev = B.moe_decode_set_spin_limit(0)
+    try:
+        run_decode(cfg, inp)
+    finally:
+        assert B.moe_decode_set_spin_limit(prev) == 0
+    with pytest.raises(B.MoEError) as err:
+        B.moe_decode_status()
+    assert err.value.status == -4 and "grid barrier" in str(err.value)
+    B.moe_decode_status()                                  # cleared by the read
+    again = run_decode(cfg, inp)
+    B.moe_decode_status()
+    for got, want in zip(again, ref):
+        assert torch.equal(got, want)

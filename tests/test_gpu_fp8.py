@@ -118,8 +118,11 @@ def check_ffn_fp8(cfg, inp, out, experts):
         r0, r1 = int(off[e]), int(off[e + 1])
         if r1 == r0:
             continue
-        wg_c, wg_s = F.quantize_rows(f64(inp["W_gate"][e]))
-        assert np.array_equal(out["Wgq"][e].cpu().numpy(), wg_c) and np.array_equal(out["sg"][e].cpu().numpy(), wg_s)
+        # every weight operand's codes and scales bit-exact against the oracle's quantisation
+        for w, q, sc in (("W_gate", "Wgq", "sg"), ("W_up", "Wuq", "su"), ("W_down", "Wdq", "sd")):
+            c_ref, s_ref = F.quantize_rows(f64(inp[w][e]))
+            assert np.array_equal(out[q][e].cpu().numpy(), c_ref), "%s codes e%d" % (w, e)
+            assert np.array_equal(out[sc][e].cpu().numpy(), s_ref), "%s scales e%d" % (w, e)
         Wgq = {e: out["Wgq"][e].cpu().numpy()}
         Wuq = {e: out["Wuq"][e].cpu().numpy()}
         sg = {e: out["sg"][e].cpu().numpy().astype(np.float64)}

@@ -172,3 +172,21 @@ def test_backward_matches_finite_differences():
             dn = loss(q)
             fd = (up - dn) / (2 * h)
             assert abs(fd - g[idx]) <= 1e-6 * max(1.0, abs(g[idx])), (name, idx, fd, g[idx])
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_weighted_combine_is_the_dense_mixture(mode):
+    """The weighted branch of ``oracle.combine`` (per token, rows in ascending expert, each scaled
+    by its gate weight) applied to the experts' outputs Y_perm equals the dense brute force (every
+    expert on every token, masked softmax weights), with and without token rounding; and a hand
+    example with distinct weights."""
+    p = rand_layer(40 + mode, T=11, d=6, E=5, n=7)
+    L, plan = oracle_plan(p, K=2, mode=mode, M=4)
+    fw = oracle.layer_forward(p["X"], p["Wg"], p["Wu"], p["Wd"], plan)
+    out = oracle.combine(fw["Y_perm"], plan["tok_off"], plan["tok_row"], plan["row_w"])
+    dense, _, _ = dense_torch(p, plan["sel"])
+    assert np.allclose(out, dense.numpy(), rtol=0, atol=1e-12)
+    # hand example: token 0 owns rows 0 and 2, token 1 row 1, token 2 none
+    Y = np.array([[1.0, 2.0], [3.0, 4.0], [5.0, 6.0]])
+    got = oracle.combine(Y, np.array([0, 2, 3, 3]), np.array([0, 2, 1]), np.array([0.25, 0.5, 0.75]))
+    assert np.array_equal(got, np.array([[4.0, 5.0], [1.5, 2.0], [0.0, 0.0]]))
