@@ -156,6 +156,22 @@ moe_status moe_route(const moe_dims* dims, const void* X, const void* W_r, const
                      float* logits, const moe_plan* plan, void* ws, size_t ws_bytes,
                      void* stream);
 
+/* moe_route_noalloc — moe_route with its workspace in a static device buffer of the library
+ * instead of a caller workspace: for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  Arguments, outputs and
+ * results are those of moe_route; the call itself allocates nothing.
+ *  Limit: moe_workspace_bytes(dims, MOE_OP_ROUTE) must not exceed moe_route_noalloc_max_bytes()
+ *  (64 MiB; e.g. T = 32768 tokens with E = 384 experts and token rounding need 51 MiB), else
+ *  MOE_EWORKSPACE and nothing is enqueued.
+ *  The buffer: one copy per device, held until the process ends; its address is looked up on
+ *  the first call on each device.  No part of it needs to start at zero.  Every call on a device
+ *  shares that device's copy, so calls that may overlap on one device (other streams, other host
+ *  threads) race and corrupt each other's plans: order them on one stream. */
+moe_status moe_route_noalloc(const moe_dims* dims, const void* X, const void* W_r, const float* bias,
+                             float* logits, const moe_plan* plan, void* stream);
+/* Host: size in bytes of moe_route_noalloc's static buffer. */
+size_t moe_route_noalloc_max_bytes(void);
+
 /* moe_permute — materialise the expert-major copy of the tokens ("contiguous packed" input):
  * X_perm[r] = X[row_token[r]] for r < R.  X [T,d] dtype, X_perm [R_max,d] dtype (rows >= R are
  * left untouched).  Bit-exact copies.  Needs a plan from moe_route. */

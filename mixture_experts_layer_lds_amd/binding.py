@@ -22,6 +22,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ENOTSUP", -3: "MOE_EWORKSPACE"
 
 EXPORTS = ["moe_max_rows", "moe_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_ffn",
            "moe_combine", "moe_forward", "moe_backward", "moe_decode", "moe_decode_status",
+           "moe_route_noalloc", "moe_route_noalloc_max_bytes",
            "moe_decode_set_spin_limit", "moe_quantize_fp8",
            "moe_grouped_ffn_fp8", "moe_status_string", "moe_last_error",
            "moe_version", "moe_timing_enable", "moe_timing_read"]
@@ -68,6 +69,8 @@ def lib():
         L.moe_max_rows.argtypes, L.moe_max_rows.restype = [pd], ctypes.c_int64
         L.moe_workspace_bytes.argtypes, L.moe_workspace_bytes.restype = [pd, ctypes.c_int], sz
         L.moe_route.argtypes = [pd, vp, vp, vp, vp, pp, vp, sz, vp]
+        L.moe_route_noalloc.argtypes = [pd, vp, vp, vp, vp, pp, vp]
+        L.moe_route_noalloc_max_bytes.argtypes, L.moe_route_noalloc_max_bytes.restype = [], sz
         L.moe_permute.argtypes = [pd, pp, vp, vp, vp]
         L.moe_grouped_ffn.argtypes = [pd, pp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_combine.argtypes = [pd, pp, vp, ctypes.c_int, vp, vp]
@@ -80,7 +83,7 @@ def lib():
         L.moe_decode_set_spin_limit.restype = ctypes.c_longlong
         L.moe_quantize_fp8.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, vp, vp, vp, vp]
         L.moe_grouped_ffn_fp8.argtypes = [pd, pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-        for f in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward",
+        for f in ("moe_route", "moe_route_noalloc", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward",
                   "moe_backward", "moe_decode", "moe_quantize_fp8", "moe_grouped_ffn_fp8"):
             getattr(L, f).restype = st
         L.moe_status_string.argtypes, L.moe_status_string.restype = [ctypes.c_int], ctypes.c_char_p
@@ -174,6 +177,16 @@ def workspace(dims, op, device="cuda"):
 def moe_route(dims, X, W_r, bias, logits, plan, ws, ws_bytes, stream=None):
     _check(lib().moe_route(ctypes.byref(dims), _p(X), _p(W_r), _p(bias), _p(logits), plan.ref(),
                            _p(ws), ws_bytes, _stream(stream)))
+
+
+def moe_route_noalloc(dims, X, W_r, bias, logits, plan, stream=None):
+    """moe_route with the library's static routing buffer as workspace (no allocation)."""
+    _check(lib().moe_route_noalloc(ctypes.byref(dims), _p(X), _p(W_r), _p(bias), _p(logits), plan.ref(),
+                                   _stream(stream)))
+
+
+def moe_route_noalloc_max_bytes():
+    return lib().moe_route_noalloc_max_bytes()
 
 
 def moe_permute(dims, plan, X, X_perm, stream=None):

@@ -5,6 +5,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/moe.h"
@@ -259,6 +260,32 @@ moe_status do_ffn(const moe_dims* dm, const moe_plan* plan, const void* A_in, bo
   return MOE_OK;
 }
 
+// ---- allocation-free routing (moe_route_noalloc) ----
+// The routing workspace of moe_route_noalloc: one copy per device, held until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory; kernels get the device
+// address from hipGetSymbolAddress, resolved once per device.
+constexpr size_t kRouteScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) char scratch[kRouteScratchBytes];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+moe_status route_scratch(void** out) {
+  int dev = 0;
+  MOE_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_EHIP, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    MOE_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(MOE_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -288,6 +315,27 @@ moe_status moe_route(const moe_dims* dims, const void* X, const void* W_r, const
     MOE_TRY(opt_ptr(bias, "bias"));
   }
   MOE_TRY(check_ws(dims, MOE_OP_ROUTE, ws, ws_bytes));
+  return do_route(dims, X, W_r, bias, logits, plan, ws, static_cast<hipStream_t>(stream));
+}
+
+size_t moe_route_noalloc_max_bytes(void) { return kRouteScratchBytes; }
+
+moe_status moe_route_noalloc(const moe_dims* dims, const void* X, const void* W_r, const float* bias,
+                             float* logits, const moe_plan* plan, void* stream) {
+  MOE_TRY(check_dims(dims));
+  MOE_TRY(check_plan(plan));
+  MOE_TRY(need_ptr(logits, "logits"));
+  if (X) {
+    MOE_TRY(need_ptr(X, "X"));
+    MOE_TRY(need_ptr(W_r, "W_r"));
+    MOE_TRY(opt_ptr(bias, "bias"));
+  }
+  const size_t need = ws_bytes_for(dims, MOE_OP_ROUTE);
+  if (need > kRouteScratchBytes)
+    return fail(MOE_EWORKSPACE, "routing needs %zu bytes of workspace, more than the %zu of the static buffer",
+                need, kRouteScratchBytes);
+  void* ws = nullptr;
+  MOE_TRY(route_scratch(&ws));
   return do_route(dims, X, W_r, bias, logits, plan, ws, static_cast<hipStream_t>(stream));
 }
 

@@ -179,3 +179,14 @@ def test_decode_spin_limit_is_validated_on_the_host(lib):
     with pytest.raises(B.MoEError):
         B.moe_decode_set_spin_limit(-1)
     assert B.moe_decode_set_spin_limit(prev) == 1 << 20
+
+
+def test_route_noalloc_rejects_layers_beyond_its_buffer(lib):
+    """moe_route_noalloc checks the routing workspace the dims need against its static buffer on
+    the host, before it touches the device: too large is MOE_EWORKSPACE, nothing enqueued."""
+    assert B.moe_route_noalloc_max_bytes() == 64 << 20
+    big = dims(T=1 << 20, E=1024, K=8, round_mode=B.ROUND_NEAREST, tile_m=128)
+    assert B.moe_workspace_bytes(big, B.OP_ROUTE) > B.moe_route_noalloc_max_bytes()
+    plan = B.PlanStruct(*([FAKE] * 9))
+    st = lib.moe_route_noalloc(ctypes.byref(big), None, None, None, FAKE, ctypes.byref(plan), None)
+    assert st == -3 and b"static buffer" in lib.moe_last_error()
