@@ -181,3 +181,30 @@ def subset_plan(plan, tokens):
     sub["tok_off"] = tok_off
     sub["tok_row"] = np.concatenate(tok_rows) if tok_rows else np.zeros(0, np.int64)
     return sub, rows
+
+
+class ExpertSubset:
+    """W[j] = W[experts[j]]: the weights of a plan compacted to the experts it uses."""
+
+    def __init__(self, W, experts):
+        self.W = W
+        self.experts = experts
+
+    def __getitem__(self, j):
+        return self.W[int(self.experts[j])]
+
+    def __len__(self):
+        return len(self.experts)
+
+
+def compact_plan(plan):
+    """The plan renumbered to the experts that own rows (ascending id), so that the oracle's loops
+    over experts visit only those.  Returns (compacted plan, the experts' original ids)."""
+    used = np.unique(plan["row_expert"])
+    new_of = {int(e): j for j, e in enumerate(used)}
+    row_expert = np.array([new_of[int(e)] for e in plan["row_expert"]], np.int64)
+    off = np.zeros(len(used) + 1, np.int64)
+    off[1:] = np.cumsum(np.bincount(row_expert, minlength=len(used)))
+    out = dict(plan)
+    out.update(expert_off=off, row_expert=row_expert)
+    return out, used

@@ -25,8 +25,8 @@ import torch
 import oracle
 from mixture_experts_layer_lds_amd import workloads as wl
 from conftest import announce_case, progress
-from parity import (TOL, assert_close, check_backward, check_forward, check_routing, f64, run_gpu,
-                    run_grouped_ffn, subset_plan)
+from parity import (TOL, ExpertSubset, assert_close, check_backward, check_forward, check_routing,
+                    compact_plan, run_gpu, run_grouped_ffn, subset_plan)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -98,25 +98,32 @@ def run_sampled(cfg, n_tokens):
     Wg, Wu, Wd = GpuExperts(inp["W_gate"]), GpuExperts(inp["W_up"]), GpuExperts(inp["W_down"])
     errs = {}
 
-    # sampled tokens: logits, out, the tokens' H rows and, with the backward, dX, dS, dLogits
+    # sampled tokens: logits, out, the tokens' H rows and, with the backward, dX, dS, dLogits.  The
+    # plan restricted to the tokens is renumbered to the experts they use, so the oracle touches
+    # only those experts' weights.
     toks = sample_tokens(cfg.T, n_tokens, cfg.index)
     sub, rows = subset_plan(ref, toks)
+    subc, used = compact_plan(sub)
+    Wgs, Wus, Wds = ExpertSubset(Wg, used), ExpertSubset(Wu, used), ExpertSubset(Wd, used)
     tt = torch.from_numpy(toks).cuda()
     bias = None if inp["bias"] is None else gpu_f64(inp["bias"])
-    L_ref = oracle.router_logits(X[toks], gpu_f64(inp["W_r"]), bias)
+    W_r = gpu_f64(inp["W_r"])
+    L_ref = oracle.router_logits(X[toks], W_r, bias)
     errs["logits"] = assert_close("logits", gpu_f64(res["logits"][tt]), L_ref, tol)
-    progress("tokens %s: oracle forward" % list(toks))
-    fw = oracle.layer_forward(X, Wg, Wu, Wd, sub)
+    progress("tokens %s on %d experts: oracle forward" % ([int(t) for t in toks], len(used)))
+    fw = oracle.layer_forward(X, Wgs, Wus, Wds, subc)
     errs["out"] = assert_close("out", gpu_f64(res["out"][tt]), fw["out"][toks], tol)
     rows_t = torch.from_numpy(rows).cuda()
     errs["H(tokens)"] = assert_close("H", gpu_f64(res["H"][rows_t]), fw["H"], tol)
     if cfg.backward:
         progress("tokens: oracle backward")
         dY = gpu_f64(inp["dY"])
-        bw = oracle.layer_backward(dY, X, Wg, Wu, Wd, sub, W_r=gpu_f64(inp["W_r"]))
+        bw = oracle.layer_backward(dY, X, Wgs, Wus, Wds, subc, W_r=W_r[used])
+        dL = np.zeros((cfg.T, cfg.E))
+        dL[:, used] = bw["dLogits"]
         errs["dX"] = assert_close("dX", gpu_f64(res["dX"][tt]), bw["dX"][toks], tol)
         errs["dS(tokens)"] = assert_close("dS", gpu_f64(res["dS"][rows_t]), bw["dS"], tol)
-        errs["dLogits"] = assert_close("dLogits", gpu_f64(res["dLogits"][tt]), bw["dLogits"][toks], tol)
+        errs["dLogits"] = assert_close("dLogits", gpu_f64(res["dLogits"][tt]), dL[toks], tol)
 
     # whole experts: every row of H and Y_perm, their dS rows and their weight gradients
     picks = pick_experts(ref["counts"])
