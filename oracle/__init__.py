@@ -15,8 +15,10 @@ Everything here is plain float64 numpy, written from the pages' description of t
   "反向传播优化" (which operands each backward GEMM gathers) and the kernel-comparison table
   (SwiGLU fusion, dS computation, no separate scatter kernel).
 
-``oracle/fp8.py`` adds the FP8 (OCP E4M3) row quantisation and the quantised expert FFN, from the
-apxml.com page's section "利用稀疏性和量化" (quantisation of weights and activations).
+``oracle/fp8.py`` adds the FP8 (OCP E4M3) row quantisation and the quantised expert FFN, and
+``oracle/mx.py`` the block-scaled variant (E4M3 or E5M2 elements, one power-of-two scale per 32
+elements along K), both from the apxml.com page's section "利用稀疏性和量化" (quantisation of
+weights and activations).
 
 Where the pages leave a step open, the reading taken is stated at the function that takes it.
 Every function's result is pinned by tests under ``tests/`` (brute force, closed forms,
