@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--fp8", action="store_true",
                     help="instead of the layer step, time the forward with FP8 expert GEMMs (moe_route, "
                          "moe_quantize_fp8 of X, moe_grouped_ffn_fp8, moe_combine) next to the bf16 moe_forward")
+    ap.add_argument("--mx", choices=["e4m3", "e5m2"], default=None,
+                    help="instead of the layer step, time the forward with block-scaled FP8 expert GEMMs (moe_route, "
+                         "moe_quantize_mx of X, moe_grouped_ffn_mx, moe_combine) next to the bf16 moe_forward")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after warmup, run a plain 256 MiB copy kernel (torch neg on fp32) three times, "
                          "outside the timed region: the byte counters of a profiler run are scaled by it")
@@ -270,9 +273,11 @@ def decode_bench(args):
 
 
 def fp8_bench(args):
-    """Forward layer with FP8 expert GEMMs on --config: routing as in bf16, X quantised per row
-    each step, the experts' weights quantised once before timing (they are the stored model),
-    activation quantised inside moe_grouped_ffn_fp8.  Useful FLOPs as for the bf16 forward."""
+    """Forward layer with FP8 expert GEMMs on --config: routing as in bf16, X quantised each step,
+    the experts' weights quantised once before timing (they are the stored model).  --fp8: per-row
+    power-of-two scales, the activation quantised by a separate pass inside
+    moe_grouped_ffn_fp8; --mx FMT: 32-element block scales applied by the MFMA, the activation
+    quantised in the gate/up GEMM's epilogue.  Useful FLOPs as for the bf16 forward."""
     import torch
     from mixture_experts_layer_lds_amd import binding as B
     from mixture_experts_layer_lds_amd import workloads as wl
@@ -286,30 +291,42 @@ def fp8_bench(args):
     R_max = plan.R_max
     u8 = dict(dtype=torch.uint8, device="cuda")
     f32 = dict(dtype=torch.float32, device="cuda")
+    mx = args.mx is not None
+    fmt = {"e4m3": B.FP8_E4M3, "e5m2": B.FP8_E5M2}.get(args.mx)
 
     def quant(t, rows, K):
-        c, s_ = torch.empty(rows, K, **u8), torch.empty(rows, **f32)
-        B.moe_quantize_fp8(t.reshape(rows, K), c, s_)
+        c = torch.empty(rows, K, **u8)
+        if mx:
+            s_ = torch.empty(B.moe_mx_scale_bytes(rows, K), **u8)
+            B.moe_quantize_mx(t.reshape(rows, K), fmt, c, s_)
+        else:
+            s_ = torch.empty(rows, **f32)
+            B.moe_quantize_fp8(t.reshape(rows, K), c, s_)
         return c, s_
 
     Wgq, sg = quant(inp["W_gate"], E * n, d)
     Wuq, su = quant(inp["W_up"], E * n, d)
     Wdq, sd = quant(inp["W_down"], E * d, n)
-    Xq, sx = torch.empty(T, d, **u8), torch.empty(T, **f32)
+    Xq, sx = quant(inp["X"], T, d)
     logits = torch.empty(T, E, **f32)
-    act = torch.empty(R_max, n, dtype=torch.bfloat16, device="cuda")
-    act_q, sact = torch.empty(R_max, n, **u8), torch.empty(R_max, **f32)
+    act = None if mx else torch.empty(R_max, n, dtype=torch.bfloat16, device="cuda")
+    act_q = torch.empty(R_max, n, **u8)
+    sact = torch.empty(B.moe_mx_scale_bytes(R_max, n), **u8) if mx else torch.empty(R_max, **f32)
     Y = torch.empty(R_max, d, dtype=torch.bfloat16, device="cuda")
     out = torch.empty(T, d, dtype=torch.bfloat16, device="cuda")
     ws_r, nb_r = B.workspace(dims, B.OP_ROUTE)
-    ws_q, nb_q = B.workspace(dims, B.OP_FFN_FP8)
+    ws_q, nb_q = B.workspace(dims, B.OP_FFN_MX if mx else B.OP_FFN_FP8)
     ws_f, nb_f = B.workspace(dims, B.OP_FORWARD)
     out_bf = torch.empty_like(out)
 
     def step():
         B.moe_route(dims, inp["X"], inp["W_r"], inp["bias"], logits, plan, ws_r, nb_r)
-        B.moe_quantize_fp8(inp["X"], Xq, sx)
-        B.moe_grouped_ffn_fp8(dims, plan, Xq, sx, Wgq, sg, Wuq, su, Wdq, sd, act, act_q, sact, Y, ws_q, nb_q)
+        if mx:
+            B.moe_quantize_mx(inp["X"], fmt, Xq, sx)
+            B.moe_grouped_ffn_mx(dims, plan, fmt, Xq, sx, Wgq, sg, Wuq, su, Wdq, sd, None, act_q, sact, Y, ws_q, nb_q)
+        else:
+            B.moe_quantize_fp8(inp["X"], Xq, sx)
+            B.moe_grouped_ffn_fp8(dims, plan, Xq, sx, Wgq, sg, Wuq, su, Wdq, sd, act, act_q, sact, Y, ws_q, nb_q)
         B.moe_combine(dims, plan, Y, 1, out)
 
     def bf16_step():
@@ -353,11 +370,12 @@ def fp8_bench(args):
     dom = max(("fp8_up_gemm", "fp8_down_gemm"), key=lambda s_: breakdown[s_]["ms_per_step"])
     avg = breakdown[dom]["avg_ms"]
     ach = stage_fl[dom] / (avg * 1e-3) / 1e12
+    scaling = ("%s, 32-element E8M0 block scales" % args.mx.upper()) if mx else "E4M3, per-row scales"
     res = {
-        "metric": "MoE layer fwd useful TFLOPS, FP8 (E4M3, per-row scales) expert GEMMs, %s" % cfg.name,
+        "metric": "MoE layer fwd useful TFLOPS, FP8 (%s) expert GEMMs, %s" % (scaling, cfg.name),
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8_e4m3 (bf16 activations between the GEMMs)",
+        "dtype": ("fp8_%s (block scales)" % args.mx) if mx else "fp8_e4m3 (bf16 activations between the GEMMs)",
         "data": "synthetic (seeded normal inputs and random-init weights)",
         "config": {"workload": cfg.name, "T": T, "d": d, "n": n, "E": E, "K": cfg.K, "pass": "fwd", "rows": R,
                    "parallelism": "single GPU"},
@@ -380,7 +398,7 @@ def main():
         sys.exit(2)
     if args.decode:
         return decode_bench(args)
-    if args.fp8:
+    if args.fp8 or args.mx:
         return fp8_bench(args)
     import torch
     from mixture_experts_layer_lds_amd import binding as B
@@ -485,7 +503,20 @@ def main():
     torch.cuda.synchronize()
     flushed = {"combine": B.moe_timing_read("combine"), "permute": B.moe_timing_read("permute")}
     B.moe_timing_enable(False)
-    del flush, Y_perm, X_perm, out_c
+    # the practical ceiling of the same protocol: torch's device copy of the combine's byte count
+    # (half read, half written), each rep after the same flush
+    nb_copy = stage_bytes("combine", R, cfg.T, cfg.d, cfg.n, cfg.E, 2 if cfg.dtype == "bf16" else 4, cfg.K) // 2
+    csrc = torch.ones(nb_copy // 16, 4, dtype=torch.float32, device="cuda")
+    cdst = torch.empty_like(csrc)
+    copy_ms = []
+    for i in range(args.steps):
+        flush.fill_(i & 255)
+        e0.record()
+        cdst.copy_(csrc)
+        e1.record()
+        torch.cuda.synchronize()
+        copy_ms.append(e0.elapsed_time(e1))
+    del flush, Y_perm, X_perm, out_c, csrc, cdst
 
     # the backward recomputing [G|U] from X instead of reading the forward's H cache
     recompute_ms = None
@@ -547,6 +578,13 @@ def main():
                           "gbs_best": round(b / (mn * 1e-3) / 1e9, 1),
                           "pct_hbm_median": round(100 * b / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 1),
                           "in_step": s != "permute"}
+    cb = 2 * (stage_bytes("combine", R, T, d, n, E, es, cfg.K) // 2 // 16) * 16
+    hbm_flushed["copy_reference"] = {"reps": len(copy_ms), "median_ms": round(float(np.median(copy_ms)), 4),
+                                     "bytes": int(cb),
+                                     "gbs_median": round(cb / (float(np.median(copy_ms)) * 1e-3) / 1e9, 1),
+                                     "pct_hbm_median": round(100 * cb / (float(np.median(copy_ms)) * 1e-3) / 1e9
+                                                             / PEAK_HBM_GBS, 1),
+                                     "what": "torch device copy of the combine's byte count, half read and half written"}
     dom = max(modelled, key=lambda s: breakdown[s]["ms_per_step"])
     if stage_flops(dom, R, T, d, n, E):
         avg = breakdown[dom]["avg_ms"]

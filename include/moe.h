@@ -130,7 +130,8 @@ enum {
   MOE_OP_FORWARD = 4,
   MOE_OP_BACKWARD = 5,
   MOE_OP_DECODE = 6,
-  MOE_OP_FFN_FP8 = 7
+  MOE_OP_FFN_FP8 = 7,
+  MOE_OP_FFN_MX = 8
 };
 
 /* Host: upper bound on R for these dims (T*K without rounding; rounding can add at most
@@ -296,6 +297,48 @@ moe_status moe_grouped_ffn_fp8(const moe_dims* dims, const moe_plan* plan, const
                                const uint8_t* Wu_q, const float* su, const uint8_t* Wd_q,
                                const float* sd, void* act, uint8_t* act_q, float* sact,
                                void* Y_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* Block-scaled FP8 (apxml.com "硬件加速的考量", section "利用稀疏性和量化": FP8 weights and
+ * activations).  Element format OCP FP8 E4M3 (bias 7, largest finite 448, no infinities) or E5M2
+ * (bias 15, largest finite 57344); each row of an operand is cut along its reduction dimension K
+ * into blocks of 32 consecutive elements, and each block has one scale s = 2^(byte - 127) (an
+ * E8M0 byte): the smallest power of two with max|block| / s <= the format's largest finite
+ * value, s = 1 for an all-zero block, kept within 2^-127 .. 2^127.  Element codes are the nearest
+ * code to x / s, ties to even.  The GEMMs apply the block scales inside the MFMA
+ * (v_mfma_scale_f32_32x32x64_f8f6f4), so every product is exact before the fp32 accumulation.
+ * Scales are stored group-major: a group is the four blocks of 128 consecutive elements of a row,
+ * and groups are planes of one 4-byte word per row, so the scale byte of block b of row r in a
+ * matrix of `rows` rows is at byte (b / 4) * rows * 4 + r * 4 + b % 4 (the GEMMs load the words of
+ * 64 consecutive rows as one 256-byte access).  Bytes of blocks past K / 32 are unspecified. */
+typedef enum { MOE_FP8_E4M3 = 0, MOE_FP8_E5M2 = 1 } moe_fp8_format;
+
+/* Host: bytes of block scales for a rows x K matrix: ceil(K / 128) * rows * 4 (0 if invalid). */
+int64_t moe_mx_scale_bytes(int64_t rows, int64_t K);
+
+/* moe_quantize_mx — block-scaled quantisation of a rows x K matrix (K a multiple of 64, at most
+ * 65536).  src [rows, K] dtype (MOE_BF16 or MOE_F32), finite values; fmt a moe_fp8_format.
+ * codes [rows, K] uint8 and scales (moe_mx_scale_bytes(rows, K) bytes, group-major) overwritten.  Weights
+ * are quantised once with this call (W_gate / W_up as [E*n, d], W_down as [E*d, n]), tokens
+ * every step; moe_grouped_ffn_mx quantises its activation itself. */
+moe_status moe_quantize_mx(int64_t rows, int64_t K, int dtype, int fmt, const void* src, uint8_t* codes,
+                           uint8_t* scales, void* stream);
+
+/* moe_grouped_ffn_mx — the experts' SwiGLU FFN on block-scaled FP8 operands (format fmt for all
+ * of them) and gathered token rows.  dims.dtype must be MOE_BF16; T * d must be below 2^32.
+ *  Xq [T,d] + sx (scales of T rows of d);  Wg_q, Wu_q [E,n,d] + sg, su (scales of E*n rows of d);
+ *  Wd_q [E,d,n] + sd (scales of E*d rows of n); scales group-major as above.
+ *  The gate/up GEMM forms act = silu(G) U per row r (G, U accumulated in fp32 from exact block
+ *  products), rounds it to bf16 and quantises it in its epilogue, 32 columns to a block:
+ *    act   [R_max,n] bf16 or NULL (written when given: the activation before quantisation);
+ *    act_q [R_max,n] uint8 + sact (scales of R_max rows of n): its codes and scales;
+ *  then Y_perm [R_max,d] bf16: Y_r = act_q_r Wd_q[e]^T with both operands' block scales.
+ *  Rows r < R of the plan are written; rows past R are untouched.
+ *  ws: moe_workspace_bytes(dims, MOE_OP_FFN_MX) bytes. */
+moe_status moe_grouped_ffn_mx(const moe_dims* dims, const moe_plan* plan, int fmt, const uint8_t* Xq,
+                              const uint8_t* sx, const uint8_t* Wg_q, const uint8_t* sg, const uint8_t* Wu_q,
+                              const uint8_t* su, const uint8_t* Wd_q, const uint8_t* sd, void* act,
+                              uint8_t* act_q, uint8_t* sact, void* Y_perm, void* ws, size_t ws_bytes,
+                              void* stream);
 
 /* Stages of the layer, for the timing facility below.  Each stage is one kernel, except ROUTE
  * (top-K, counts, token rounding, offsets, placement) and DWR_GEMM (GEMM + slice reduction). */

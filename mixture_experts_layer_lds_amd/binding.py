@@ -5,7 +5,7 @@ becomes the hipStream_t, and non-zero status codes become ``MoEError``.  Every c
 in the library's HIP kernels; if the library is missing, the first call raises.
 The functions keep the C names: ``moe_route``, ``moe_permute``, ``moe_grouped_ffn``,
 ``moe_combine``, ``moe_forward``, ``moe_backward``, ``moe_decode``, ``moe_quantize_fp8``,
-``moe_grouped_ffn_fp8`` (plus sizing helpers).
+``moe_grouped_ffn_fp8``, ``moe_quantize_mx``, ``moe_grouped_ffn_mx`` (plus sizing helpers).
 """
 import ctypes
 import os
@@ -17,12 +17,14 @@ LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 
 MOE_F32, MOE_BF16 = 0, 1
 ROUND_NONE, ROUND_NEAREST, ROUND_UP, ROUND_DOWN, ROUND_STOCHASTIC = 0, 1, 2, 3, 4
-OP_ROUTE, OP_PERMUTE, OP_FFN, OP_COMBINE, OP_FORWARD, OP_BACKWARD, OP_DECODE, OP_FFN_FP8 = range(8)
+OP_ROUTE, OP_PERMUTE, OP_FFN, OP_COMBINE, OP_FORWARD, OP_BACKWARD, OP_DECODE, OP_FFN_FP8, OP_FFN_MX = range(9)
+FP8_E4M3, FP8_E5M2 = 0, 1
 STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ENOTSUP", -3: "MOE_EWORKSPACE", -4: "MOE_EHIP"}
 
 EXPORTS = ["moe_max_rows", "moe_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_ffn",
            "moe_combine", "moe_forward", "moe_backward", "moe_decode", "moe_decode_status",
-           "moe_route_noalloc", "moe_route_noalloc_max_bytes",
+           "moe_route_noalloc", "moe_route_noalloc_max_bytes", "moe_mx_scale_bytes", "moe_quantize_mx",
+           "moe_grouped_ffn_mx",
            "moe_decode_set_spin_limit", "moe_quantize_fp8",
            "moe_grouped_ffn_fp8", "moe_status_string", "moe_last_error",
            "moe_version", "moe_timing_enable", "moe_timing_read"]
@@ -83,8 +85,14 @@ def lib():
         L.moe_decode_set_spin_limit.restype = ctypes.c_longlong
         L.moe_quantize_fp8.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, vp, vp, vp, vp]
         L.moe_grouped_ffn_fp8.argtypes = [pd, pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_mx_scale_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64]
+        L.moe_mx_scale_bytes.restype = ctypes.c_int64
+        L.moe_quantize_mx.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp]
+        L.moe_grouped_ffn_mx.argtypes = [pd, pp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                         sz, vp]
         for f in ("moe_route", "moe_route_noalloc", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward",
-                  "moe_backward", "moe_decode", "moe_quantize_fp8", "moe_grouped_ffn_fp8"):
+                  "moe_backward", "moe_decode", "moe_quantize_fp8", "moe_grouped_ffn_fp8", "moe_quantize_mx",
+                  "moe_grouped_ffn_mx"):
             getattr(L, f).restype = st
         L.moe_status_string.argtypes, L.moe_status_string.restype = [ctypes.c_int], ctypes.c_char_p
         L.moe_last_error.argtypes, L.moe_last_error.restype = [], ctypes.c_char_p
@@ -245,6 +253,24 @@ def moe_grouped_ffn_fp8(dims, plan, Xq, sx, Wg_q, sg, Wu_q, su, Wd_q, sd, act, a
     _check(lib().moe_grouped_ffn_fp8(ctypes.byref(dims), plan.ref(), _p(Xq), _p(sx), _p(Wg_q), _p(sg),
                                      _p(Wu_q), _p(su), _p(Wd_q), _p(sd), _p(act), _p(act_q), _p(sact),
                                      _p(Y_perm), _p(ws), ws_bytes, _stream(stream)))
+
+
+def moe_mx_scale_bytes(rows, K):
+    return lib().moe_mx_scale_bytes(int(rows), int(K))
+
+
+def moe_quantize_mx(src, fmt, codes, scales, stream=None):
+    """Block-scaled FP8 codes and E8M0 scale bytes of a 2-D bf16 / fp32 tensor (rows x K)."""
+    rows, K = src.shape[0], src.shape[-1]
+    dtype = MOE_BF16 if src.dtype == torch.bfloat16 else MOE_F32
+    _check(lib().moe_quantize_mx(rows, K, dtype, int(fmt), _p(src), _p(codes), _p(scales), _stream(stream)))
+
+
+def moe_grouped_ffn_mx(dims, plan, fmt, Xq, sx, Wg_q, sg, Wu_q, su, Wd_q, sd, act, act_q, sact, Y_perm, ws, ws_bytes,
+                       stream=None):
+    _check(lib().moe_grouped_ffn_mx(ctypes.byref(dims), plan.ref(), int(fmt), _p(Xq), _p(sx), _p(Wg_q), _p(sg),
+                                    _p(Wu_q), _p(su), _p(Wd_q), _p(sd), _p(act), _p(act_q), _p(sact), _p(Y_perm),
+                                    _p(ws), ws_bytes, _stream(stream)))
 
 
 def moe_backward(dims, dY, X, W_r, W_gate, W_up, W_down, plan, H_cache, dX, dW_gate, dW_up, dW_down,

@@ -185,7 +185,7 @@ __global__ __launch_bounds__(GEMM8_THREADS, 1) void k_dact_w8(
   const char* wd = reinterpret_cast<const char*>(Wd) + ((int64_t)g.e * d * n + n0) * sizeof(bf16);
   auto lb = mn_rows_w8([=](int k) { return wd + (int64_t)k * n * sizeof(bf16); }, d, n0, n);
   AccW8 acc;
-  gemm_mainloop_w8(la, lb, d / Mma<bf16>::BK, acc, L, wm, [&](int j) { return j * 128 + wn * 32; });
+  gemm_mainloop_w8_rows(la, lb, d / Mma<bf16>::BK, acc, L, wm, [&](int j) { return j * 128 + wn * 32; }, g.mrows);
   dact_epilogue<bf16, GEMM8_THREADS, 2>(L, g, n0, n, nt, R_max, row_w, H, dH, wA, dS_part, [&](int half, auto frow) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -280,7 +280,7 @@ __global__ __launch_bounds__(GEMM8_THREADS, 1) void k_dx_w8(
                        2 * n, n0, d);
   auto bsub = [&](int j) { return bsub_w8(wn, j); };
   AccW8 acc;
-  gemm_mainloop_w8(la, lb, 2 * n / Mma<bf16>::BK, acc, L, wm, bsub);
+  gemm_mainloop_w8_rows(la, lb, 2 * n / Mma<bf16>::BK, acc, L, wm, bsub, g.mrows);
   const int valid = min(BN, d - n0);
   epi_stage_w8(L, wm, bsub, [&](int i, int j, int v) { return acc.c[i][j][v]; });
   __syncthreads();
@@ -311,16 +311,38 @@ hipError_t launch_dx_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mtil
 // staged as they lie and read with the transposing LDS load.  Experts without rows get zero
 // tiles.
 // ---------------------------------------------------------------------------------------------
+// Experts by decreasing row count (ties: lower id first): order[rank] = e.  The weight-gradient
+// GEMMs reduce over an expert's rows, so their tiles take time in proportion to its count; taking
+// the experts in this order starts the longest tiles first and leaves the short ones to fill the
+// end of the grid, instead of a hot expert's tiles forming the tail.  One block, E <= 1024.
+__global__ __launch_bounds__(1024) void k_expert_order(const int32_t* __restrict__ counts, int E,
+                                                       int32_t* __restrict__ order) {
+  __shared__ int c[1024];
+  const int e = threadIdx.x;
+  if (e < E) c[e] = counts[e];
+  __syncthreads();
+  if (e >= E) return;
+  const int ce = c[e];
+  int rank = 0;
+  for (int f = 0; f < E; ++f) rank += (c[f] > ce || (c[f] == ce && f < e)) ? 1 : 0;
+  order[rank] = e;
+}
+
+hipError_t launch_expert_order(const int32_t* counts, int E, int32_t* order, hipStream_t st) {
+  k_expert_order<<<1, 1024, 0, st>>>(counts, E, order);
+  return hipGetLastError();
+}
+
 template <typename T>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dw_down(
-    const int32_t* __restrict__ expert_off, const int32_t* __restrict__ row_token,
+    const int32_t* __restrict__ expert_off, const int32_t* __restrict__ order, const int32_t* __restrict__ row_token,
     const T* __restrict__ dY, const T* __restrict__ wA, T* __restrict__ dWd, int d, int n,
     int E, int MT, int NT, int T_) {
   MOE_GEMM_LDS(L);
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int per = MT * NT;
-  const int e = lin / per;
-  if (e >= E) return;
+  if (lin / per >= E) return;
+  const int e = order[lin / per];
   int mt, nt;
   raster_tile(lin % per, MT, NT, mt, nt);
   const int m0 = mt * BM, n0 = nt * BN;
@@ -349,14 +371,14 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dw_down(
 
 // bf16 dW_down on the eight-wave engine (same tiles, operands and bits as k_dw_down).
 __global__ __launch_bounds__(GEMM8_THREADS, 1) void k_dw_down_w8(
-    const int32_t* __restrict__ expert_off, const int32_t* __restrict__ row_token,
+    const int32_t* __restrict__ expert_off, const int32_t* __restrict__ order, const int32_t* __restrict__ row_token,
     const bf16* __restrict__ dY, const bf16* __restrict__ wA, bf16* __restrict__ dWd, int d, int n,
     int E, int MT, int NT, int T_) {
   MOE_GEMM_LDS(L);
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int per = MT * NT;
-  const int e = lin / per;
-  if (e >= E) return;
+  if (lin / per >= E) return;
+  const int e = order[lin / per];
   int mt, nt;
   raster_tile(lin % per, MT, NT, mt, nt);
   const int m0 = mt * BM, n0 = nt * BN;
@@ -379,15 +401,15 @@ __global__ __launch_bounds__(GEMM8_THREADS, 1) void k_dw_down_w8(
   epi_store_rows<GEMM8_THREADS>(L, 0, [&](int r) { return out + (int64_t)r * n; }, mrows, BN, valid);
 }
 
-hipError_t launch_dw_down_gemm(const Shape& s, const PlanPtrs& p, const void* dY, const void* wA,
-                               void* dW_down, hipStream_t st) {
+hipError_t launch_dw_down_gemm(const Shape& s, const PlanPtrs& p, const int32_t* order, const void* dY,
+                               const void* wA, void* dW_down, hipStream_t st) {
   const int MT = (int)cdiv(s.d, BM), NT = (int)cdiv(s.n, BN);
   const int grid = grid8((int64_t)s.E * MT * NT);
   if (s.bf16)
-    k_dw_down_w8<<<grid, GEMM8_THREADS, 0, st>>>(p.expert_off, p.row_token, (const bf16*)dY, (const bf16*)wA,
+    k_dw_down_w8<<<grid, GEMM8_THREADS, 0, st>>>(p.expert_off, order, p.row_token, (const bf16*)dY, (const bf16*)wA,
                                                  (bf16*)dW_down, (int)s.d, (int)s.n, s.E, MT, NT, (int)s.T);
   else
-    k_dw_down<float><<<grid, GEMM_THREADS, 0, st>>>(p.expert_off, p.row_token, (const float*)dY,
+    k_dw_down<float><<<grid, GEMM_THREADS, 0, st>>>(p.expert_off, order, p.row_token, (const float*)dY,
                                                     (const float*)wA, (float*)dW_down, (int)s.d,
                                                     (int)s.n, s.E, MT, NT, (int)s.T);
   return hipGetLastError();
@@ -395,14 +417,14 @@ hipError_t launch_dw_down_gemm(const Shape& s, const PlanPtrs& p, const void* dY
 
 template <typename T>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dw_gu(
-    const int32_t* __restrict__ expert_off, const int32_t* __restrict__ row_token,
+    const int32_t* __restrict__ expert_off, const int32_t* __restrict__ order, const int32_t* __restrict__ row_token,
     const T* __restrict__ dH, const T* __restrict__ X, T* __restrict__ dWg, T* __restrict__ dWu,
     int d, int n, int E, int MT, int NT, int T_) {
   MOE_GEMM_LDS(L);
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int per = MT * NT;
-  const int e = lin / per;
-  if (e >= E) return;
+  if (lin / per >= E) return;
+  const int e = order[lin / per];
   int mt, nt;
   raster_tile(lin % per, MT, NT, mt, nt);
   const int m0 = mt * BM, n0 = nt * BN;
@@ -434,14 +456,14 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dw_gu(
 
 // bf16 dW_gate | dW_up on the eight-wave engine (same tiles, operands and bits as k_dw_gu).
 __global__ __launch_bounds__(GEMM8_THREADS, 1) void k_dw_gu_w8(
-    const int32_t* __restrict__ expert_off, const int32_t* __restrict__ row_token,
+    const int32_t* __restrict__ expert_off, const int32_t* __restrict__ order, const int32_t* __restrict__ row_token,
     const bf16* __restrict__ dH, const bf16* __restrict__ X, bf16* __restrict__ dWg, bf16* __restrict__ dWu,
     int d, int n, int E, int MT, int NT, int T_) {
   MOE_GEMM_LDS(L);
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int per = MT * NT;
-  const int e = lin / per;
-  if (e >= E) return;
+  if (lin / per >= E) return;
+  const int e = order[lin / per];
   int mt, nt;
   raster_tile(lin % per, MT, NT, mt, nt);
   const int m0 = mt * BM, n0 = nt * BN;
@@ -466,16 +488,16 @@ __global__ __launch_bounds__(GEMM8_THREADS, 1) void k_dw_gu_w8(
   }, mrows, BN, valid);
 }
 
-hipError_t launch_dw_gu_gemm(const Shape& s, const PlanPtrs& p, const void* dH, const void* X,
-                             void* dW_gate, void* dW_up, hipStream_t st) {
+hipError_t launch_dw_gu_gemm(const Shape& s, const PlanPtrs& p, const int32_t* order, const void* dH,
+                             const void* X, void* dW_gate, void* dW_up, hipStream_t st) {
   const int MT = (int)cdiv(2 * s.n, BM), NT = (int)cdiv(s.d, BN);
   const int grid = grid8((int64_t)s.E * MT * NT);
   if (s.bf16)
-    k_dw_gu_w8<<<grid, GEMM8_THREADS, 0, st>>>(p.expert_off, p.row_token, (const bf16*)dH, (const bf16*)X,
+    k_dw_gu_w8<<<grid, GEMM8_THREADS, 0, st>>>(p.expert_off, order, p.row_token, (const bf16*)dH, (const bf16*)X,
                                                (bf16*)dW_gate, (bf16*)dW_up, (int)s.d, (int)s.n, s.E, MT, NT,
                                                (int)s.T);
   else
-    k_dw_gu<float><<<grid, GEMM_THREADS, 0, st>>>(p.expert_off, p.row_token, (const float*)dH,
+    k_dw_gu<float><<<grid, GEMM_THREADS, 0, st>>>(p.expert_off, order, p.row_token, (const float*)dH,
                                                   (const float*)X, (float*)dW_gate, (float*)dW_up,
                                                   (int)s.d, (int)s.n, s.E, MT, NT, (int)s.T);
   return hipGetLastError();
@@ -498,7 +520,7 @@ __device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ expert_
   return lo;
 }
 
-template <typename T>
+template <typename T, int CPL, int RB>
 __global__ __launch_bounds__(256) void k_router_bwd(
     const int32_t* __restrict__ tok_off, const int32_t* __restrict__ tok_row,
     const int32_t* __restrict__ expert_off, const float* __restrict__ row_w,
@@ -544,53 +566,80 @@ __global__ __launch_bounds__(256) void k_router_bwd(
     if (e < E) dLogits[(int64_t)t * E + e] = v;
     if (dLop) dLop[(int64_t)t * E_pad + e] = from_f32<T>(v);
   }
-  // dX[t]: lanes own 16-byte column chunks; the token's rows are taken four at a time, and all
-  // their dX_perm and W_r chunks are loaded before any is used, so that several loads are in
-  // flight per lane.
+  // dX[t]: a lane owns CPL 16-byte column chunks (lane + 64 j) of a pass over the row; the
+  // token's rows are taken RB at a time, and every dX_perm and W_r chunk of a batch is requested
+  // before any is used, so a wave reads whole rows at once.  Rows are added in ascending expert
+  // order.
   constexpr int VEC = 16 / sizeof(T);
   const int nch = d / VEC;
-  for (int ch = lane; ch < nch; ch += 64) {
-    float acc[VEC];
+  for (int c0 = 0; c0 < nch; c0 += 64 * CPL) {
+    float acc[CPL][VEC];
 #pragma unroll
-    for (int k = 0; k < VEC; ++k) acc[k] = 0.0f;
-    for (int i = 0; i < cnt; i += 4) {
-      u32x4 v[4], wv[4];
-      float dl[4];
+    for (int j = 0; j < CPL; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int k = 0; k < VEC; ++k) acc[j][k] = 0.0f;
+    bool ok[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) ok[j] = c0 + lane + 64 * j < nch;
+    for (int i = 0; i < cnt; i += RB) {
+      u32x4 v[RB][CPL], wv[RB][CPL];
+      float dl[RB];
+#pragma unroll
+      for (int q = 0; q < RB; ++q) {
         const bool live = i + q < cnt;
         const int r = live ? srow[i + q] : 0;
         const int e = live ? sexp[i + q] : 0;
         dl[q] = live ? sdl[e] : 0.0f;
-        v[q] = live ? ld16_nt(dXp + (int64_t)r * d + ch * VEC) : u32x4{0u, 0u, 0u, 0u};
-        wv[q] = (live && Wr) ? ld16(Wr + (int64_t)e * d + ch * VEC) : u32x4{0u, 0u, 0u, 0u};
+        const int64_t c = (int64_t)(c0 + lane) * VEC;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+          v[q][j] = (live && ok[j]) ? ld16_nt(dXp + (int64_t)r * d + c + 64 * j * VEC) : u32x4{0u, 0u, 0u, 0u};
+          wv[q][j] = (live && ok[j] && Wr) ? ld16(Wr + (int64_t)e * d + c + 64 * j * VEC) : u32x4{0u, 0u, 0u, 0u};
+        }
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float f[VEC], w[VEC];
-        unpack16<T>(v[q], f);
-        unpack16<T>(wv[q], w);
+      for (int q = 0; q < RB; ++q) {
+        if (i + q >= cnt) break;  // (uniform) the batch's rows past the token's last one add nothing
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) acc[k] += f[k] + dl[q] * w[k];
+        for (int j = 0; j < CPL; ++j) {
+          float f[VEC], w[VEC];
+          unpack16<T>(v[q][j], f);
+          unpack16<T>(wv[q][j], w);
+#pragma unroll
+          for (int k = 0; k < VEC; ++k) acc[j][k] += f[k] + dl[q] * w[k];
+        }
       }
     }
-    st16(dX + (int64_t)t * d + ch * VEC, pack16<T>(acc));
+#pragma unroll
+    for (int j = 0; j < CPL; ++j)
+      if (ok[j]) st16(dX + (int64_t)t * d + (int64_t)(c0 + lane + 64 * j) * VEC, pack16<T>(acc[j]));
   }
+}
+
+template <typename T, int CPL, int RB>
+static void router_bwd_for(const Shape& s, const PlanPtrs& p, const float* dS_part, int ntiles, const void* dX_perm,
+                           const void* W_r, float* dS, float* dLogits, void* dLop, int E_pad, void* dX,
+                           hipStream_t st) {
+  const int grid = (int)cdiv(s.T, 4);
+  const size_t lds = (size_t)4 * 3 * E_pad * sizeof(float);  // <= 48 KiB for E <= 1024
+  k_router_bwd<T, CPL, RB><<<grid, 256, lds, st>>>(p.tok_off, p.tok_row, p.expert_off, p.row_w, dS_part, ntiles,
+                                                   s.R_max, static_cast<const T*>(dX_perm), static_cast<const T*>(W_r),
+                                                   dS, dLogits, static_cast<T*>(dLop), E_pad, static_cast<T*>(dX),
+                                                   (int)s.T, (int)s.d, s.E);
 }
 
 hipError_t launch_router_bwd(const Shape& s, const PlanPtrs& p, const float* dS_part, int ntiles,
                              const void* dX_perm, const void* W_r, float* dS, float* dLogits,
                              void* dLop, int E_pad, void* dX, hipStream_t st) {
-  const int grid = (int)cdiv(s.T, 4);
-  const size_t lds = (size_t)4 * 3 * E_pad * sizeof(float);  // <= 48 KiB for E <= 1024
-  if (s.bf16)
-    k_router_bwd<bf16><<<grid, 256, lds, st>>>(p.tok_off, p.tok_row, p.expert_off, p.row_w, dS_part, ntiles,
-                                             s.R_max, (const bf16*)dX_perm, (const bf16*)W_r, dS, dLogits,
-                                             (bf16*)dLop, E_pad, (bf16*)dX, (int)s.T, (int)s.d, s.E);
-  else
-    k_router_bwd<float><<<grid, 256, lds, st>>>(p.tok_off, p.tok_row, p.expert_off, p.row_w, dS_part, ntiles,
-                                              s.R_max, (const float*)dX_perm, (const float*)W_r, dS, dLogits,
-                                              (float*)dLop, E_pad, (float*)dX, (int)s.T, (int)s.d, s.E);
+  // chunks per lane: the whole row in one pass up to 4 * 64 16-byte chunks, else passes of that
+  const int64_t nch = s.d / (s.bf16 ? 8 : 4);
+#define MOE_RBWD(TT)                                                                                    \
+  if (nch <= 64) router_bwd_for<TT, 1, 8>(s, p, dS_part, ntiles, dX_perm, W_r, dS, dLogits, dLop, E_pad, dX, st); \
+  else if (nch <= 128) router_bwd_for<TT, 2, 4>(s, p, dS_part, ntiles, dX_perm, W_r, dS, dLogits, dLop, E_pad, dX, st); \
+  else if (nch <= 192) router_bwd_for<TT, 3, 2>(s, p, dS_part, ntiles, dX_perm, W_r, dS, dLogits, dLop, E_pad, dX, st); \
+  else router_bwd_for<TT, 4, 2>(s, p, dS_part, ntiles, dX_perm, W_r, dS, dLogits, dLop, E_pad, dX, st);
+  if (s.bf16) { MOE_RBWD(bf16) } else { MOE_RBWD(float) }
+#undef MOE_RBWD
   return hipGetLastError();
 }
 
@@ -679,6 +728,54 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dwr(
     }
 }
 
+// bf16 on the eight-wave engine (same tiles, slices and bits as k_dwr; the four-wave kernel's
+// 256 accumulator registers left it reloading spilled registers inside the main loop).
+__global__ __launch_bounds__(GEMM8_THREADS, 1) void k_dwr_w8(
+    const bf16* __restrict__ dLop, int E_pad, const bf16* __restrict__ X, float* __restrict__ part,
+    bf16* __restrict__ dWr, int T_, int d, int E, int MT, int NT, int S, int TS) {
+  MOE_GEMM_LDS(L);
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int per = MT * NT;
+  const int sl = lin / per;
+  if (sl >= S) return;
+  int mt, nt;
+  raster_tile(lin % per, MT, NT, mt, nt);
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int t0 = sl * TS;
+  const int klen = min(TS, T_ - t0);
+  const char* ab = reinterpret_cast<const char*>(dLop) + m0 * sizeof(bf16);
+  const char* xb = reinterpret_cast<const char*>(X) + n0 * sizeof(bf16);
+  auto la = mn_rows_w8([=](int k) { return ab + (int64_t)(t0 + k) * E_pad * sizeof(bf16); }, klen, m0, E_pad);
+  auto lb = mn_rows_w8([=](int k) { return xb + (int64_t)(t0 + k) * d * sizeof(bf16); }, klen, n0, d);
+  auto bsub = [&](int j) { return bsub_w8(wn, j); };
+  AccW8 acc;
+  gemm_mainloop_w8_rows(la, lb, (int)cdiv(klen, Mma<bf16>::BK), acc, L, wm, bsub, E - m0);
+  // a lane's accumulators v = 4q .. 4q + 3 are four consecutive columns (d is a multiple of 64,
+  // so c < d implies c + 3 < d)
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = n0 + bsub(j) + acc_n(4 * q);
+      if (c >= d) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + acc_m(wm, i);
+        if (m >= E) continue;
+        if (S == 1) {
+          const u32x2 pk = {pack_bf16x2(acc.c[i][j][4 * q], acc.c[i][j][4 * q + 1]),
+                            pack_bf16x2(acc.c[i][j][4 * q + 2], acc.c[i][j][4 * q + 3])};
+          *reinterpret_cast<u32x2*>(dWr + (int64_t)m * d + c) = pk;
+        } else {
+          const f32x4 v4 = {acc.c[i][j][4 * q], acc.c[i][j][4 * q + 1], acc.c[i][j][4 * q + 2], acc.c[i][j][4 * q + 3]};
+          *reinterpret_cast<f32x4*>(part + ((int64_t)sl * E + m) * d + c) = v4;
+        }
+      }
+    }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_dwr_reduce(const float* __restrict__ part, int S,
                                                     int64_t n, T* __restrict__ dWr) {
@@ -696,8 +793,8 @@ hipError_t launch_dwr_gemm(const Shape& s, const void* dLop, int E_pad, const vo
   float* part = static_cast<float*>(ws);
   const int64_t nout = (int64_t)s.E * s.d;
   if (s.bf16) {
-    k_dwr<bf16><<<grid, GEMM_THREADS, 0, st>>>((const bf16*)dLop, E_pad, (const bf16*)X, part,
-                                               (bf16*)dW_r, (int)s.T, (int)s.d, s.E, q.MT, q.NT, q.S, q.TS);
+    k_dwr_w8<<<grid, GEMM8_THREADS, 0, st>>>((const bf16*)dLop, E_pad, (const bf16*)X, part, (bf16*)dW_r,
+                                             (int)s.T, (int)s.d, s.E, q.MT, q.NT, q.S, q.TS);
     if (q.S > 1) k_dwr_reduce<bf16><<<(int)cdiv(nout, 256), 256, 0, st>>>(part, q.S, nout, (bf16*)dW_r);
   } else {
     k_dwr<float><<<grid, GEMM_THREADS, 0, st>>>((const float*)dLop, E_pad, (const float*)X, part,

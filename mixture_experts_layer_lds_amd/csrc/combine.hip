@@ -55,11 +55,13 @@ hipError_t launch_permute(const Shape& s, const PlanPtrs& p, const void* X, void
   return hipGetLastError();
 }
 
-// out[t] = sum_{r in rows(t)} w_r Y[r].  Lanes own 16-byte column chunks; up to RB rows (a
-// token's K = 8 rows at once in the common case) are loaded before they are accumulated so that
-// several loads are in flight per lane.
-constexpr int RB = 8;
-template <typename T, bool WEIGHTED>
+// out[t] = sum_{r in rows(t)} w_r Y[r].  A wave owns a token; its lanes own CPL 16-byte column
+// chunks each (lane + 64 j), so one pass covers 64 * CPL chunks of the row (the whole row when
+// d is small enough; otherwise the row goes in several passes).  Per pass the rows are read in
+// batches of RBATCH: every chunk of every row of a batch is requested before any is used, so a
+// wave reads whole rows at once (RBATCH * CPL loads in flight per lane) instead of one chunk of
+// each row per round trip.  fp32 accumulation in ascending expert order, one rounding.
+template <typename T, bool WEIGHTED, int CPL, int RBATCH>
 __global__ __launch_bounds__(256) void k_combine(const int32_t* __restrict__ tok_off,
                                                  const int32_t* __restrict__ tok_row,
                                                  const float* __restrict__ row_w,
@@ -71,48 +73,64 @@ __global__ __launch_bounds__(256) void k_combine(const int32_t* __restrict__ tok
   const int base = tok_off[t], cnt = tok_off[t + 1] - base;
   constexpr int VEC = 16 / sizeof(T);
   const int nch = d / VEC;
-  for (int c = lane; c < nch; c += 64) {
-    float acc[VEC];
+  for (int c0 = 0; c0 < nch; c0 += 64 * CPL) {
+    float acc[CPL][VEC];
 #pragma unroll
-    for (int k = 0; k < VEC; ++k) acc[k] = 0.0f;
-    int i = 0;
-    for (; i + RB <= cnt; i += RB) {
-      u32x4 v[RB];
-      float w[RB];
+    for (int j = 0; j < CPL; ++j)
 #pragma unroll
-      for (int q = 0; q < RB; ++q) {
-        const int r = clamp_idx(tok_row[base + i + q], rmax);
-        v[q] = ld16_nt(Y + (int64_t)r * d + c * VEC);
-        w[q] = WEIGHTED ? row_w[r] : 1.0f;
+      for (int k = 0; k < VEC; ++k) acc[j][k] = 0.0f;
+    bool ok[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) ok[j] = c0 + lane + 64 * j < nch;
+    for (int i = 0; i < cnt; i += RBATCH) {
+      u32x4 v[RBATCH][CPL];
+      float w[RBATCH];
+#pragma unroll
+      for (int q = 0; q < RBATCH; ++q) {
+        const bool live = i + q < cnt;
+        const int r = live ? clamp_idx(tok_row[base + i + q], rmax) : 0;
+        w[q] = live ? (WEIGHTED ? row_w[r] : 1.0f) : 0.0f;
+        const T* y = Y + (int64_t)r * d + (int64_t)(c0 + lane) * VEC;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+          v[q][j] = (live && ok[j]) ? ld16_nt(y + 64 * j * VEC) : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
-      for (int q = 0; q < RB; ++q) {
-        float f[VEC];
-        unpack16<T>(v[q], f);
+      for (int q = 0; q < RBATCH; ++q) {
+        if (i + q >= cnt) break;  // (uniform) the batch's rows past the token's last one add nothing
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) acc[k] += w[q] * f[k];
+        for (int j = 0; j < CPL; ++j) {
+          float f[VEC];
+          unpack16<T>(v[q][j], f);
+#pragma unroll
+          for (int k = 0; k < VEC; ++k) acc[j][k] += w[q] * f[k];
+        }
       }
     }
-    for (; i < cnt; ++i) {
-      const int r = clamp_idx(tok_row[base + i], rmax);
-      const float w = WEIGHTED ? row_w[r] : 1.0f;
-      float f[VEC];
-      unpack16<T>(ld16_nt(Y + (int64_t)r * d + c * VEC), f);
 #pragma unroll
-      for (int k = 0; k < VEC; ++k) acc[k] += w * f[k];
-    }
-    st16(out + (int64_t)t * d + c * VEC, pack16<T>(acc));
+    for (int j = 0; j < CPL; ++j)
+      if (ok[j]) st16(out + (int64_t)t * d + (int64_t)(c0 + lane + 64 * j) * VEC, pack16<T>(acc[j]));
   }
+}
+
+template <typename T, bool W>
+static void combine_for(const Shape& s, const PlanPtrs& p, const void* Y_perm, void* out, hipStream_t st) {
+  const int grid = (int)cdiv(s.T, 4);
+  const int64_t nch = s.d / (16 / (int)sizeof(T));
+  const T* Y = static_cast<const T*>(Y_perm);
+  T* o = static_cast<T*>(out);
+  // chunks per lane: the whole row in one pass up to 4 * 64 chunks (bf16 d <= 2048), else passes
+  // of 4 * 64 chunks; rows per batch keep RBATCH * CPL at 8 to 16 loads in flight per lane
+  if (nch <= 64) k_combine<T, W, 1, 8><<<grid, 256, 0, st>>>(p.tok_off, p.tok_row, p.row_w, Y, o, (int)s.T, (int)s.d, (int)s.R_max);
+  else if (nch <= 128) k_combine<T, W, 2, 8><<<grid, 256, 0, st>>>(p.tok_off, p.tok_row, p.row_w, Y, o, (int)s.T, (int)s.d, (int)s.R_max);
+  else if (nch <= 192) k_combine<T, W, 3, 4><<<grid, 256, 0, st>>>(p.tok_off, p.tok_row, p.row_w, Y, o, (int)s.T, (int)s.d, (int)s.R_max);
+  else k_combine<T, W, 4, 4><<<grid, 256, 0, st>>>(p.tok_off, p.tok_row, p.row_w, Y, o, (int)s.T, (int)s.d, (int)s.R_max);
 }
 
 hipError_t launch_combine(const Shape& s, const PlanPtrs& p, const void* Y_perm, bool weighted,
                           void* out, hipStream_t st) {
-  const int grid = (int)cdiv(s.T, 4);
-#define MOE_COMB(TT, W) k_combine<TT, W><<<grid, 256, 0, st>>>(p.tok_off, p.tok_row, p.row_w, \
-      (const TT*)Y_perm, (TT*)out, (int)s.T, (int)s.d, (int)s.R_max)
-  if (s.bf16) { if (weighted) MOE_COMB(bf16, true); else MOE_COMB(bf16, false); }
-  else { if (weighted) MOE_COMB(float, true); else MOE_COMB(float, false); }
-#undef MOE_COMB
+  if (s.bf16) { if (weighted) combine_for<bf16, true>(s, p, Y_perm, out, st); else combine_for<bf16, false>(s, p, Y_perm, out, st); }
+  else { if (weighted) combine_for<float, true>(s, p, Y_perm, out, st); else combine_for<float, false>(s, p, Y_perm, out, st); }
   return hipGetLastError();
 }
 

@@ -492,7 +492,8 @@ __device__ __forceinline__ void gemm_mainloop_dma(AL& la, BL& lb, int nkt, WaveA
 // row are 64 elements, so K-major loading (KDma) is unchanged and a stage is one k-step of 16
 // v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales; per-row scales are applied by the
 // epilogue).  A lane's fragment is 32 consecutive k of its row (lane half h: k 32 h .. 32 h + 31);
-// A and B use the same placement, which is all the product needs.
+// A and B use the same placement, which is all a product with unit block scales needs (the
+// instruction's own k order differs; the block-scaled path follows it, see frag8_mx).
 // ===============================================================================================
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -994,44 +995,46 @@ __device__ __forceinline__ void mma_range_w8(const FragW8& F, AccW8& acc) {
 //      beside the other 7 MFMAs.
 // Stages past the end repeat the last one, so the count of DMA instructions per step, and with
 // it every wait, stays fixed.
-template <int P, class AL, class BL, class BSub>
+// MMA = false: the same DMA issue, waits and barriers with no fragment reads and no MFMAs, for a
+// wave whose 128 tile rows are all past the valid ones (see gemm_mainloop_w8_rows).
+template <int P, bool MMA, class AL, class BL, class BSub>
 __device__ __forceinline__ void dma_step_w8(AL& la, BL& lb, int s, int nkt, const char* cur, const char* next,
                                             char* half2, char* refill, FragW8& F0, FragW8& F1, AccW8& acc, int wm,
                                             BSub bsub) {
   const int r2 = min(s + 2, nkt - 1), r3 = min(s + 3, nkt - 1);
-  mma_range_w8<0, 1>(F0, acc);
+  if constexpr (MMA) mma_range_w8<0, 1>(F0, acc);
   __builtin_amdgcn_sched_barrier(0);
-  load_frags_w8<AL, BL>(cur, 1, wm, bsub, F1);
+  if constexpr (MMA) load_frags_w8<AL, BL>(cur, 1, wm, bsub, F1);
   la.template fetch<P ^ 1>(r3);
   lb.template fetch<P ^ 1>(r3);
   __builtin_amdgcn_sched_barrier(0);
   la.template prepare_q<P>(r2, 1);
   la.issue_q(1, half2);
-  mma_range_w8<1, 4>(F0, acc);
+  if constexpr (MMA) mma_range_w8<1, 4>(F0, acc);
   __builtin_amdgcn_sched_barrier(0);
   lb.template prepare_q<P>(r2, 1);
   lb.issue_q(1, half2 + DMA_B_OFF);
-  mma_range_w8<4, 8>(F0, acc);
+  if constexpr (MMA) mma_range_w8<4, 8>(F0, acc);
   __builtin_amdgcn_sched_barrier(0);
   wait_vmcnt<4>();
   ring_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  mma_range_w8<0, 1>(F1, acc);
+  if constexpr (MMA) mma_range_w8<0, 1>(F1, acc);
   __builtin_amdgcn_sched_barrier(0);
-  load_frags_w8<AL, BL>(next, 0, wm, bsub, F0);
+  if constexpr (MMA) load_frags_w8<AL, BL>(next, 0, wm, bsub, F0);
   __builtin_amdgcn_sched_barrier(0);
   la.template prepare_q<P ^ 1>(r3, 0);
   la.issue_q(0, refill);
-  mma_range_w8<1, 4>(F1, acc);
+  if constexpr (MMA) mma_range_w8<1, 4>(F1, acc);
   __builtin_amdgcn_sched_barrier(0);
   lb.template prepare_q<P ^ 1>(r3, 0);
   lb.issue_q(0, refill + DMA_B_OFF);
-  mma_range_w8<4, 8>(F1, acc);
+  if constexpr (MMA) mma_range_w8<4, 8>(F1, acc);
   __builtin_amdgcn_sched_barrier(0);
 }
 
 // The eight-wave main loop over nkt stages (accumulating from zero; ends with the LDS free).
-template <class AL, class BL, class BSub>
+template <bool MMA = true, class AL, class BL, class BSub>
 __device__ __forceinline__ void gemm_mainloop_w8(AL& la, BL& lb, int nkt, AccW8& acc, LdsBufs L, int wm, BSub bsub) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -1069,18 +1072,30 @@ __device__ __forceinline__ void gemm_mainloop_w8(AL& la, BL& lb, int nkt, AccW8&
   wait_vmcnt<6>();  // stage 0 has landed: stage 1 (4) and half of stage 2 (2) came after it
   ring_barrier();
   FragW8 F0, F1;
-  load_frags_w8<AL, BL>(L.b[0], 0, wm, bsub, F0);
+  if constexpr (MMA) load_frags_w8<AL, BL>(L.b[0], 0, wm, bsub, F0);
   int s = 0;
   for (; s + 4 <= nkt; s += 4) {
-    dma_step_w8<0>(la, lb, s, nkt, L.b[0], L.b[1], L.b[2], L.b[3], F0, F1, acc, wm, bsub);
-    dma_step_w8<1>(la, lb, s + 1, nkt, L.b[1], L.b[2], L.b[3], L.b[0], F0, F1, acc, wm, bsub);
-    dma_step_w8<0>(la, lb, s + 2, nkt, L.b[2], L.b[3], L.b[0], L.b[1], F0, F1, acc, wm, bsub);
-    dma_step_w8<1>(la, lb, s + 3, nkt, L.b[3], L.b[0], L.b[1], L.b[2], F0, F1, acc, wm, bsub);
+    dma_step_w8<0, MMA>(la, lb, s, nkt, L.b[0], L.b[1], L.b[2], L.b[3], F0, F1, acc, wm, bsub);
+    dma_step_w8<1, MMA>(la, lb, s + 1, nkt, L.b[1], L.b[2], L.b[3], L.b[0], F0, F1, acc, wm, bsub);
+    dma_step_w8<0, MMA>(la, lb, s + 2, nkt, L.b[2], L.b[3], L.b[0], L.b[1], F0, F1, acc, wm, bsub);
+    dma_step_w8<1, MMA>(la, lb, s + 3, nkt, L.b[3], L.b[0], L.b[1], L.b[2], F0, F1, acc, wm, bsub);
   }
-  if (s < nkt) dma_step_w8<0>(la, lb, s, nkt, L.b[0], L.b[1], L.b[2], L.b[3], F0, F1, acc, wm, bsub);
-  if (s + 1 < nkt) dma_step_w8<1>(la, lb, s + 1, nkt, L.b[1], L.b[2], L.b[3], L.b[0], F0, F1, acc, wm, bsub);
-  if (s + 2 < nkt) dma_step_w8<0>(la, lb, s + 2, nkt, L.b[2], L.b[3], L.b[0], L.b[1], F0, F1, acc, wm, bsub);
+  if (s < nkt) dma_step_w8<0, MMA>(la, lb, s, nkt, L.b[0], L.b[1], L.b[2], L.b[3], F0, F1, acc, wm, bsub);
+  if (s + 1 < nkt) dma_step_w8<1, MMA>(la, lb, s + 1, nkt, L.b[1], L.b[2], L.b[3], L.b[0], F0, F1, acc, wm, bsub);
+  if (s + 2 < nkt) dma_step_w8<0, MMA>(la, lb, s + 2, nkt, L.b[2], L.b[3], L.b[0], L.b[1], F0, F1, acc, wm, bsub);
   __syncthreads();  // drains the trailing loads; the LDS is free for the epilogue
+}
+
+// The eight-wave main loop for a tile with `mrows` valid rows: a wave whose 128 rows all lie past
+// them (wave row 1 of a tile with at most 128 valid rows, e.g. an expert's last tile after token
+// rounding to 128) still issues its share of every stage's DMA and meets every barrier, but reads
+// no fragments and issues no MFMAs, so the wave row 0 wave on the same SIMD has the matrix unit
+// to itself.  Its accumulators stay zero and its rows are never stored.
+template <class AL, class BL, class BSub>
+__device__ __forceinline__ void gemm_mainloop_w8_rows(AL& la, BL& lb, int nkt, AccW8& acc, LdsBufs L, int wm,
+                                                      BSub bsub, int mrows) {
+  if (wm * 128 < mrows) gemm_mainloop_w8<true>(la, lb, nkt, acc, L, wm, bsub);
+  else gemm_mainloop_w8<false>(la, lb, nkt, acc, L, wm, bsub);
 }
 
 // Column block j of wave column wn (plain layout): 64 columns per wave column.
@@ -1270,6 +1285,196 @@ __device__ __forceinline__ void gemm_mainloop_h(const KDmaH<4>& la, const BL& lb
   __syncthreads();  // drains the trailing loads; the LDS is free for the epilogue
 }
 
+// ---------------------------------------------------------------------------------------------
+// Block-scaled FP8 on the half-width engine: E4M3 (FMT 0) or E5M2 (FMT 1) codes with one E8M0
+// scale byte per 32 consecutive k of each row, applied by v_mfma_scale_f32_32x32x64_f8f6f4 itself.
+// Scales are stored group-major, [K / 128][rows][4 bytes]: a group holds the four blocks of 128
+// consecutive k of a row, so stage s (64 k) uses bytes 2 (s & 1) and 2 (s & 1) + 1 of the row's
+// word in group s / 2, and the words of consecutive rows are contiguous (a wave loads 64 rows'
+// words as 256 contiguous bytes).  Each ring slot gets a 2 KB scale area after its codes:
+// A words [256 rows][4 B], then B words [128 rows][4 B] twice (see ScaleDmaH).
+// ---------------------------------------------------------------------------------------------
+constexpr int H_SLOT_MX = H_SLOT + 2048;
+constexpr int MX_SA_OFF = H_SLOT;         // A operand scales in a slot
+constexpr int MX_SB_OFF = H_SLOT + 1024;  // B operand scales in a slot
+
+// The block-scaled loop's loaders keep, per lane, a 32-bit byte offset from a wave-uniform base
+// (one register per instruction instead of a 64-bit pointer and a step), which keeps the loop
+// within the 256 registers of two workgroups per CU.  Rows past the valid ones are given the offset
+// of a valid row by the caller: their products land in accumulator rows or columns that are never
+// stored, so no zero-page select is needed.
+// Codes, K-major (layout as KDma): instruction q fills tile rows (4 q + w) * 16 .. + 15 from
+// base[q] + off[q] + 64 s (each instruction's rows lie in one source array, so its base is uniform).
+template <int NQ>
+struct KDmaHU {
+  const char* base[NQ];
+  uint32_t off[NQ];
+  template <class Base, class RowOff>
+  __device__ void init(Base base_of, RowOff row_off) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int chunk = (lane & 3) ^ (lane >> 4);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      base[q] = base_of(q);
+      off[q] = row_off((4 * q + w) * 16 + (lane >> 2)) + chunk * 16;
+    }
+  }
+  // the stage index goes through readfirstlane, which the compiler cannot see through, so it
+  // forms each address when the instruction issues instead of keeping a 64-bit induction pointer
+  // per instruction live across the loop
+  __device__ void issue(int q, int s, char* dst) const {
+    const int w = threadIdx.x >> 6;
+    const uint32_t so = (uint32_t)__builtin_amdgcn_readfirstlane(s) * 64u;
+    dma16(base[q] + (off[q] + so), dst + (4 * q + w) * 1024);
+  }
+};
+
+// Scale words of one operand: wave w loads, for the 64 tile rows (w % NG) * 64 + lane, the word
+// of stage s's group, straight into LDS at [row][4 B] (global_load_lds_dword: lane l writes 4
+// bytes at the wave's destination + 4 l); the group's plane is `plane` bytes past the previous
+// one.  NG = 4 for the 256 A rows; NG = 2 for the 128 B rows, where waves 2 and 3 load the rows
+// of waves 0 and 1 again into a second copy, so that every wave issues exactly one instruction
+// per operand and stage and the waits stay exact.
+template <int NG>
+struct ScaleDmaH {
+  const char* base;
+  int64_t plane;
+  uint32_t off;
+  template <class Base, class RowOff>
+  __device__ void init(Base base_of_wave, int64_t plane_bytes, RowOff row_off) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    base = base_of_wave(w % NG);
+    plane = plane_bytes;
+    off = row_off((w % NG) * 64 + lane);
+  }
+  __device__ void issue(int s, char* area) const {
+    const int w = threadIdx.x >> 6;
+    const int64_t so = (int64_t)__builtin_amdgcn_readfirstlane(s >> 1) * plane;
+    __builtin_amdgcn_global_load_lds((gmem_void*)(base + so + off), (lds_void*)(area + w * 256), 4, 0, 0);
+  }
+};
+
+// Fragment of the block-scaled MFMA (measured on gfx950 with one-hot inputs and distinct scales):
+// of the 64 k of a 32x32x64 step, lane l (h = l / 32) holds k 16 h .. 16 h + 15 in its bytes 0-15
+// and k 32 + 16 h .. 32 + 16 h + 15 in bytes 16-31; k 0-31 form scale block 0, whose byte comes
+// from lane l % 32, and k 32-63 block 1, from lane l % 32 + 32.  So lane h reads 16-byte chunks h
+// and 2 + h of the row's 64-byte stage: then block 0 is the stage's bytes 0-31 and block 1 its
+// bytes 32-63, the two 32-element blocks the scales were computed on.
+__device__ __forceinline__ i32x8 frag8_mx(const char* t, int row0) {
+  const int lane = threadIdx.x & 63;
+  const int r = row0 + (lane & 31), h = lane >> 5, sw = (r >> 2) & 3;
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(t + r * 64 + (h ^ sw) * 16);
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(t + r * 64 + ((2 + h) ^ sw) * 16);
+  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+// One ring step of the block-scaled loop (as step_h with F8, eight DMA instructions per wave and
+// stage: four A and two B code loads, one A and one B scale load).
+template <int FMT, class BL, class BSub>
+__device__ __forceinline__ void step_h_mx(const KDmaHU<4>& la, const BL& lb, const ScaleDmaH<4>& sa,
+                                          const ScaleDmaH<2>& sb, int s, int nkt, const char* cur, char* refill,
+                                          AccW8& acc, int wm, BSub bsub) {
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<8>();
+  ring_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  const int r = min(s + 2, nkt - 1);
+  const int lane = threadIdx.x & 63;
+  const int byte = 2 * (s & 1) + (lane >> 5);  // the scale this lane supplies: block 2 s + lane / 32
+  // the lane's scale bytes, packed: byte i of ka for A block i, byte j of kb for B block j (the
+  // MFMA's scale op-select picks the byte)
+  FragH8 F;
+  uint32_t ka = 0, kb = 0;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    F.b[j] = frag8_mx(cur + DMA_B_OFF, bsub(j));
+    kb |= (uint32_t)*reinterpret_cast<const uint8_t*>(cur + MX_SB_OFF + (bsub(j) + (lane & 31)) * 4 + byte) << (8 * j);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    F.a[i] = frag8_mx(cur, wm * 128 + i * 32);
+    ka |= (uint32_t)*reinterpret_cast<const uint8_t*>(cur + MX_SA_OFF + (wm * 128 + i * 32 + (lane & 31)) * 4 + byte)
+          << (8 * i);
+  }
+  auto mma = [&](auto P) {
+    constexpr int p = decltype(P)::value;
+    acc.c[p >> 1][p & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+        F.b[p & 1], F.a[p >> 1], acc.c[p >> 1][p & 1], FMT, FMT, p & 1, (int)kb, p >> 1, (int)ka);
+  };
+  __builtin_amdgcn_sched_barrier(0);
+  la.issue(0, r, refill);
+  __builtin_amdgcn_sched_barrier(0);
+  mma(std::integral_constant<int, 0>{});
+  __builtin_amdgcn_sched_barrier(0);
+  la.issue(1, r, refill);
+  __builtin_amdgcn_sched_barrier(0);
+  mma(std::integral_constant<int, 1>{});
+  __builtin_amdgcn_sched_barrier(0);
+  la.issue(2, r, refill);
+  __builtin_amdgcn_sched_barrier(0);
+  mma(std::integral_constant<int, 2>{});
+  __builtin_amdgcn_sched_barrier(0);
+  la.issue(3, r, refill);
+  __builtin_amdgcn_sched_barrier(0);
+  mma(std::integral_constant<int, 3>{});
+  __builtin_amdgcn_sched_barrier(0);
+  lb.issue(0, r, refill + DMA_B_OFF);
+  __builtin_amdgcn_sched_barrier(0);
+  mma(std::integral_constant<int, 4>{});
+  __builtin_amdgcn_sched_barrier(0);
+  lb.issue(1, r, refill + DMA_B_OFF);
+  __builtin_amdgcn_sched_barrier(0);
+  mma(std::integral_constant<int, 5>{});
+  __builtin_amdgcn_sched_barrier(0);
+  sa.issue(r, refill + MX_SA_OFF);
+  __builtin_amdgcn_sched_barrier(0);
+  mma(std::integral_constant<int, 6>{});
+  __builtin_amdgcn_sched_barrier(0);
+  sb.issue(r, refill + MX_SB_OFF);
+  __builtin_amdgcn_sched_barrier(0);
+  mma(std::integral_constant<int, 7>{});
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// The block-scaled main loop over nkt stages of 64 k (accumulating from zero; ends with the LDS
+// free).  The slots are H_SLOT_MX bytes each.
+template <int FMT, class BL, class BSub>
+__device__ __forceinline__ void gemm_mainloop_h_mx(const KDmaHU<4>& la, const BL& lb, const ScaleDmaH<4>& sa,
+                                                   const ScaleDmaH<2>& sb, int nkt, AccW8& acc, char* b0, char* b1,
+                                                   char* b2, int wm, BSub bsub) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc.c[i][j][v] = 0.0f;
+  if (nkt <= 0) return;
+  const int r1 = min(1, nkt - 1);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) la.issue(q, 0, b0);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) lb.issue(q, 0, b0 + DMA_B_OFF);
+  sa.issue(0, b0 + MX_SA_OFF);
+  sb.issue(0, b0 + MX_SB_OFF);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) la.issue(q, r1, b1);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) lb.issue(q, r1, b1 + DMA_B_OFF);
+  sa.issue(r1, b1 + MX_SA_OFF);
+  sb.issue(r1, b1 + MX_SB_OFF);
+  int s = 0;
+  for (; s + 3 <= nkt; s += 3) {
+    step_h_mx<FMT>(la, lb, sa, sb, s, nkt, b0, b2, acc, wm, bsub);
+    step_h_mx<FMT>(la, lb, sa, sb, s + 1, nkt, b1, b0, acc, wm, bsub);
+    step_h_mx<FMT>(la, lb, sa, sb, s + 2, nkt, b2, b1, acc, wm, bsub);
+  }
+  if (s < nkt) {
+    step_h_mx<FMT>(la, lb, sa, sb, s, nkt, b0, b2, acc, wm, bsub);
+    if (s + 1 < nkt) step_h_mx<FMT>(la, lb, sa, sb, s + 1, nkt, b1, b0, acc, wm, bsub);
+  }
+  __syncthreads();  // drains the trailing loads; the LDS is free for the epilogue
+}
+
 // Epilogue of a half-width tile: val(i, j, v) of every accumulator staged in bf16, H_EPI_ROWS rows
 // to a slot, then stored as 16-byte chunks (rows < mrows, columns < valid) through row_ptr(r).
 __device__ __forceinline__ char* epi_row_h(char* b0, char* b1, char* b2, int r) {
@@ -1354,6 +1559,11 @@ __device__ __forceinline__ bool find_group_tile(int lin, int NT, const int32_t* 
   __shared__ __attribute__((aligned(1024))) char L##_2[LDS_BUF];     \
   __shared__ __attribute__((aligned(1024))) char L##_3[LDS_BUF];     \
   const LdsBufs L{{L##_0, L##_1, L##_2, L##_3}}
+
+#define MOE_GEMM_LDS_HMX(L)                                          \
+  __shared__ __attribute__((aligned(1024))) char L##_0[H_SLOT_MX];   \
+  __shared__ __attribute__((aligned(1024))) char L##_1[H_SLOT_MX];   \
+  __shared__ __attribute__((aligned(1024))) char L##_2[H_SLOT_MX]
 
 #define MOE_GEMM_LDS_H(L)                                            \
   __shared__ __attribute__((aligned(1024))) char L##_0[H_SLOT];      \

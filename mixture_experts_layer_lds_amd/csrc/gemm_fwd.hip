@@ -283,7 +283,7 @@ __global__ __launch_bounds__(GEMM8_THREADS, 1) void k_up_w8(
   });
   auto bsub = [&](int j) { return j * 128 + wn * 32; };
   AccW8 acc;
-  gemm_mainloop_w8(la, lb, d / Mma<bf16>::BK, acc, L, wm, bsub);
+  gemm_mainloop_w8_rows(la, lb, d / Mma<bf16>::BK, acc, L, wm, bsub, g.mrows);
   const int valid = min(128, n - j0);
   epi_stage_w8(L, wm, [&](int j) { return j == 0 ? wn * 32 : -1; }, [&](int i, int, int v) {
     const float gv = acc.c[i][0][v], uv = acc.c[i][1][v];

@@ -62,6 +62,22 @@ hipError_t launch_up_fp8(const Shape& s, const PlanPtrs& p, const int32_t* mtile
 hipError_t launch_down_fp8(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off, const uint8_t* Aq,
                            const float* sa, const uint8_t* Wdq, const float* sd, void* Y, hipStream_t st);
 
+// ---- block-scaled FP8 expert FFN (fp8.hip): E4M3 (fmt 0) or E5M2 (fmt 1) codes, one E8M0 scale
+// byte per 32 elements along K, scales group-major [ceil(K / 128)][rows][4 bytes] ----
+int64_t mx_scale_bytes(int64_t rows, int64_t K);
+hipError_t launch_quant_mx(const void* src, bool is_bf16, int fmt, int64_t rows, int64_t K, uint8_t* codes,
+                           uint8_t* scales, hipStream_t st);
+// sxp = the token scales in routed-row order ([groups of d][R_max][4 B])
+hipError_t launch_gather_mx_scales(const Shape& s, const PlanPtrs& p, const uint8_t* sx, uint8_t* sxp,
+                                   hipStream_t st);
+// act_q / sact ([groups of n][R_max][4 B]): the activation quantised in the gate/up epilogue;
+// act (bf16) optional
+hipError_t launch_up_mx(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off, int fmt, const uint8_t* Xq,
+                        const uint8_t* sxp, const uint8_t* Wgq, const uint8_t* sg, const uint8_t* Wuq,
+                        const uint8_t* su, void* act, uint8_t* act_q, uint8_t* sact, hipStream_t st);
+hipError_t launch_down_mx(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off, int fmt, const uint8_t* Aq,
+                          const uint8_t* sa, const uint8_t* Wdq, const uint8_t* sd, void* Y, hipStream_t st);
+
 // ---- permute / combine (combine.hip) ----
 hipError_t launch_permute(const Shape& s, const PlanPtrs& p, const void* X, void* X_perm, hipStream_t st);
 hipError_t launch_combine(const Shape& s, const PlanPtrs& p, const void* Y_perm, bool weighted,
@@ -79,12 +95,15 @@ int dact_ntiles(int64_t n);
 hipError_t launch_dx_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off,
                           const void* dH, const void* W_gate, const void* W_up, void* dX_perm,
                           hipStream_t st);
-// dW_down[e] = (w dY[rows])^T A = dY[rows]^T wA
-hipError_t launch_dw_down_gemm(const Shape& s, const PlanPtrs& p, const void* dY, const void* wA,
-                               void* dW_down, hipStream_t st);
-// dW_gate[e] | dW_up[e] = dH^T X[rows]
-hipError_t launch_dw_gu_gemm(const Shape& s, const PlanPtrs& p, const void* dH, const void* X,
-                             void* dW_gate, void* dW_up, hipStream_t st);
+// order[E]: experts by decreasing row count, ties to the lower id (the weight-gradient GEMMs'
+// expert order, longest tiles first)
+hipError_t launch_expert_order(const int32_t* counts, int E, int32_t* order, hipStream_t st);
+// dW_down[e] = (w dY[rows])^T A = dY[rows]^T wA, experts taken in `order`
+hipError_t launch_dw_down_gemm(const Shape& s, const PlanPtrs& p, const int32_t* order, const void* dY,
+                               const void* wA, void* dW_down, hipStream_t st);
+// dW_gate[e] | dW_up[e] = dH^T X[rows], experts taken in `order`
+hipError_t launch_dw_gu_gemm(const Shape& s, const PlanPtrs& p, const int32_t* order, const void* dH,
+                             const void* X, void* dW_gate, void* dW_up, hipStream_t st);
 // Router backward + dX gather-sum, one wave per token:
 //   dS[r] = sum of partials; dL = w (dS - <w, dS>); dLogits row; dLop[t][e] (GEMM operand);
 //   dX[t] = sum_r dX_perm[r] (+ sum_r dL_r W_r[e_r] if W_r)

@@ -158,6 +158,7 @@ FfnWs carve_ffn(Carve& c, const moe_dims* dm) {
 
 struct BwdWs {
   int32_t* mtile_off;
+  int32_t* order;
   void* H;
   void* dH;
   void* wA;
@@ -171,6 +172,7 @@ BwdWs carve_bwd(Carve& c, const moe_dims* dm) {
   const size_t es = esize(dm);
   BwdWs w;
   w.mtile_off = static_cast<int32_t*>(c.take((size_t)(dm->E + 1) * 4));
+  w.order = static_cast<int32_t*>(c.take((size_t)dm->E * 4));
   w.H = c.take((size_t)s.R_max * 2 * dm->n * es);
   w.dH = c.take((size_t)s.R_max * 2 * dm->n * es);
   w.wA = c.take((size_t)s.R_max * dm->n * es);
@@ -197,6 +199,10 @@ size_t ws_bytes_for(const moe_dims* dm, int op) {
     case MOE_OP_BACKWARD: carve_bwd(c, dm); return c.off;
     case MOE_OP_DECODE: return decode_workspace_bytes(dm->T, dm->d, dm->n, dm->E, dm->K);
     case MOE_OP_FFN_FP8: c.take((size_t)(dm->E + 1) * 4); return c.off;
+    case MOE_OP_FFN_MX:  // tile offsets, the token scales in routed-row order
+      c.take((size_t)(dm->E + 1) * 4);
+      c.take((size_t)mx_scale_bytes(max_rows(dm), dm->d));
+      return c.off;
     default: return 0;
   }
 }
@@ -297,7 +303,7 @@ int64_t moe_max_rows(const moe_dims* dims) {
 
 size_t moe_workspace_bytes(const moe_dims* dims, int op) {
   if (check_dims(dims) != MOE_OK) return 0;
-  if (op < MOE_OP_ROUTE || op > MOE_OP_FFN_FP8) {
+  if (op < MOE_OP_ROUTE || op > MOE_OP_FFN_MX) {
     fail(MOE_EINVAL, "unknown op %d", op);
     return 0;
   }
@@ -458,6 +464,65 @@ moe_status moe_decode(const moe_dims* dims, const void* X, const void* W_r, cons
   return MOE_OK;
 }
 
+int64_t moe_mx_scale_bytes(int64_t rows, int64_t K) { return rows >= 0 && K > 0 ? mx_scale_bytes(rows, K) : 0; }
+
+moe_status moe_quantize_mx(int64_t rows, int64_t K, int dtype, int fmt, const void* src, uint8_t* codes,
+                           uint8_t* scales, void* stream) {
+  if (rows < 0 || rows > ((int64_t)1 << 31)) return fail(MOE_EINVAL, "rows=%lld out of range", (long long)rows);
+  if (K < 64 || K > 65536 || K % 64) return fail(MOE_EINVAL, "K=%lld must be a multiple of 64 in [64, 65536]", (long long)K);
+  if (dtype != MOE_BF16 && dtype != MOE_F32) return fail(MOE_ENOTSUP, "dtype %d not supported", dtype);
+  if (fmt != MOE_FP8_E4M3 && fmt != MOE_FP8_E5M2) return fail(MOE_EINVAL, "fp8 format %d invalid", fmt);
+  if (rows == 0) return MOE_OK;
+  MOE_TRY(need_ptr(src, "src"));
+  MOE_TRY(need_ptr(codes, "codes"));
+  MOE_TRY(need_ptr(scales, "scales"));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  MOE_STAGE(MOE_STAGE_FP8_QUANT, st, launch_quant_mx(src, dtype == MOE_BF16, fmt, rows, K, codes, scales, st),
+            "block-scaled fp8 quantisation");
+  return MOE_OK;
+}
+
+moe_status moe_grouped_ffn_mx(const moe_dims* dims, const moe_plan* plan, int fmt, const uint8_t* Xq,
+                              const uint8_t* sx, const uint8_t* Wg_q, const uint8_t* sg, const uint8_t* Wu_q,
+                              const uint8_t* su, const uint8_t* Wd_q, const uint8_t* sd, void* act,
+                              uint8_t* act_q, uint8_t* sact, void* Y_perm, void* ws, size_t ws_bytes,
+                              void* stream) {
+  MOE_TRY(check_dims(dims));
+  if (dims->dtype != MOE_BF16) return fail(MOE_ENOTSUP, "moe_grouped_ffn_mx needs dtype MOE_BF16");
+  if (fmt != MOE_FP8_E4M3 && fmt != MOE_FP8_E5M2) return fail(MOE_EINVAL, "fp8 format %d invalid", fmt);
+  if (dims->T * dims->d >= ((int64_t)1 << 32))
+    return fail(MOE_ENOTSUP, "moe_grouped_ffn_mx needs T * d < 2^32 (T=%lld, d=%lld)", (long long)dims->T,
+                (long long)dims->d);
+  MOE_TRY(check_plan(plan));
+  MOE_TRY(need_ptr(Xq, "Xq"));
+  MOE_TRY(need_ptr(sx, "sx"));
+  MOE_TRY(need_ptr(Wg_q, "Wg_q"));
+  MOE_TRY(need_ptr(sg, "sg"));
+  MOE_TRY(need_ptr(Wu_q, "Wu_q"));
+  MOE_TRY(need_ptr(su, "su"));
+  MOE_TRY(need_ptr(Wd_q, "Wd_q"));
+  MOE_TRY(need_ptr(sd, "sd"));
+  MOE_TRY(opt_ptr(act, "act"));
+  MOE_TRY(need_ptr(act_q, "act_q"));
+  MOE_TRY(need_ptr(sact, "sact"));
+  MOE_TRY(need_ptr(Y_perm, "Y_perm"));
+  MOE_TRY(check_ws(dims, MOE_OP_FFN_MX, ws, ws_bytes));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const Shape s = shape_of(dims);
+  const PlanPtrs p = plan_ptrs(plan);
+  Carve c(ws);
+  int32_t* mtile_off = static_cast<int32_t*>(c.take((size_t)(dims->E + 1) * 4));
+  uint8_t* sxp = static_cast<uint8_t*>(c.take((size_t)mx_scale_bytes(s.R_max, dims->d)));
+  MOE_STAGE(MOE_STAGE_TILES, st, launch_tile_offsets(p.counts, dims->E, mtile_off, st), "tile offsets");
+  MOE_STAGE(MOE_STAGE_FP8_QUANT, st, launch_gather_mx_scales(s, p, sx, sxp, st), "token scale gather");
+  MOE_STAGE(MOE_STAGE_FP8_UP, st,
+            launch_up_mx(s, p, mtile_off, fmt, Xq, sxp, Wg_q, sg, Wu_q, su, act, act_q, sact, st),
+            "block-scaled fp8 gate/up GEMM");
+  MOE_STAGE(MOE_STAGE_FP8_DOWN, st, launch_down_mx(s, p, mtile_off, fmt, act_q, sact, Wd_q, sd, Y_perm, st),
+            "block-scaled fp8 down GEMM");
+  return MOE_OK;
+}
+
 moe_status moe_decode_status(void* stream) {
   int failed = 0;
   MOE_HIP(decode_read_status(static_cast<hipStream_t>(stream), &failed), "moe_decode_status");
@@ -538,8 +603,10 @@ moe_status moe_backward(const moe_dims* dims, const void* dY, const void* X, con
   }
   MOE_STAGE(MOE_STAGE_DACT_GEMM, st,
             launch_dact_gemm(s, p, w.mtile_off, dY, W_down, H, w.dH, w.wA, w.dS_part, st), "dAct GEMM");
-  MOE_STAGE(MOE_STAGE_DW_DOWN_GEMM, st, launch_dw_down_gemm(s, p, dY, w.wA, dW_down, st), "dW_down GEMM");
-  MOE_STAGE(MOE_STAGE_DW_GU_GEMM, st, launch_dw_gu_gemm(s, p, w.dH, X, dW_gate, dW_up, st), "dW_gate/up GEMM");
+  MOE_HIP(launch_expert_order(p.counts, dims->E, w.order, st), "expert order");
+  MOE_STAGE(MOE_STAGE_DW_DOWN_GEMM, st, launch_dw_down_gemm(s, p, w.order, dY, w.wA, dW_down, st), "dW_down GEMM");
+  MOE_STAGE(MOE_STAGE_DW_GU_GEMM, st, launch_dw_gu_gemm(s, p, w.order, w.dH, X, dW_gate, dW_up, st),
+            "dW_gate/up GEMM");
   MOE_STAGE(MOE_STAGE_DX_GEMM, st, launch_dx_gemm(s, p, w.mtile_off, w.dH, W_gate, W_up, w.dX_perm, st),
             "dX GEMM");
   MOE_STAGE(MOE_STAGE_ROUTER_BWD, st,

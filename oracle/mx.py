@@ -78,14 +78,13 @@ def max_finite(fmt):
 
 def block_scale_exponent(amax, fmt):
     """log2 of the smallest power of two s with amax / s <= max_finite(fmt), clamped to the E8M0
-    range [-127, 127]; 0 for amax = 0."""
-    amax = float(amax)
-    if amax == 0.0:
-        return 0
-    f, ex = np.frexp(amax)            # amax = f 2^ex; max_finite = 0.875 2^E with E = 9 or 16
+    range [-127, 127]; 0 for amax = 0.  Elementwise over an array of block maxima."""
+    a = np.asarray(amax, np.float64)
+    f, ex = np.frexp(a)               # amax = f 2^ex; max_finite = 0.875 2^E with E = 9 or 16
     E = 9 if fmt == "e4m3" else 16
-    k = int(ex) - E + (1 if f > 0.875 else 0)
-    return max(-127, min(127, k))
+    k = ex.astype(np.int64) - E + (f > 0.875).astype(np.int64)
+    k = np.where(a == 0.0, 0, np.clip(k, -127, 127))
+    return int(k) if k.ndim == 0 else k
 
 
 def quantize_blocks(X, fmt):
@@ -95,16 +94,10 @@ def quantize_blocks(X, fmt):
     rows, K = X.shape
     if K % BLOCK:
         raise ValueError("K must be a multiple of 32")
-    nb = K // BLOCK
-    scales = np.zeros((rows, nb), np.uint8)
-    codes = np.zeros((rows, K), np.uint8)
-    for r in range(rows):
-        for b in range(nb):
-            blk = X[r, b * BLOCK:(b + 1) * BLOCK]
-            k = block_scale_exponent(np.max(np.abs(blk)), fmt)
-            scales[r, b] = k + 127
-            codes[r, b * BLOCK:(b + 1) * BLOCK] = encode(blk / 2.0 ** k, fmt)
-    return codes, scales
+    blocks = X.reshape(rows, K // BLOCK, BLOCK)
+    k = block_scale_exponent(np.max(np.abs(blocks), axis=2), fmt)      # [rows, K / 32]
+    codes = encode(blocks / np.power(2.0, k)[:, :, None], fmt).reshape(rows, K)
+    return codes, (k + 127).astype(np.uint8)
 
 
 def dequantize_blocks(codes, scales, fmt):
