@@ -533,6 +533,127 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_down_mx_h(
         [&](int r) { return out + (int64_t)r * d; }, g.mrows, vrows);
 }
 
+// Gate/up with block scales on the four-wave engine, for d > UP_H_MAX_D_FP8: tile 256 rows x 128
+// act columns (B: W_gate rows j0 .. j0 + 127 over W_up rows j0 .. j0 + 127, halved block layout,
+// so G and U of a (row, column) sit in accumulator blocks j and j + 2 of one lane).  Wave column
+// wn holds act columns j0 + 64 wn .. + 63, two scale blocks (j = 0, 1), each split between lanes l
+// and l + 32 as in k_up_mx_h.  Staging: the bf16 act in bytes 0-255 of each epilogue row, the codes
+// in bytes 256-383.
+template <int FMT>
+__global__ __launch_bounds__(GEMM_THREADS, 1) void k_up_mx(
+    const int32_t* __restrict__ mtile_off, const int32_t* __restrict__ expert_off,
+    const int32_t* __restrict__ row_token, const uint8_t* __restrict__ Xq, const uint8_t* __restrict__ sx,
+    const uint8_t* __restrict__ Wgq, const uint8_t* __restrict__ sg, const uint8_t* __restrict__ Wuq,
+    const uint8_t* __restrict__ su, bf16* __restrict__ act, uint8_t* __restrict__ act_q,
+    uint8_t* __restrict__ sact, int d, int n, int E, int NT, int64_t R_max, int T_) {
+  MOE_GEMM_LDS(L);
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  GroupTile g;
+  if (!find_group_tile(lin, NT, mtile_off, expert_off, E, g)) return;
+  const int j0 = g.nt * 128;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int valid = min(128, n - j0);  // 64 or 128 (n is a multiple of 64)
+  // rows and columns past the valid ones read the last valid one (never stored); gathered code
+  // offsets fit in 32 bits (checked on the host: T * d < 2^32)
+  auto rowi = [&](int i) { return g.m0 + min(i, g.mrows - 1); };
+  KDmaHU<4> la;
+  la.init([&](int) { return reinterpret_cast<const char*>(Xq); },
+          [&](int i) { return (uint32_t)clamp_idx(row_token[rowi(i)], T_) * (uint32_t)d; });
+  ScaleDmaH<4> sa;
+  sa.init([&](int) { return reinterpret_cast<const char*>(sx); }, R_max * 4, [&](int i) { return (uint32_t)rowi(i) * 4u; });
+  const int64_t wrow0 = (int64_t)g.e * n + j0;
+  KDmaHU<4> lb;  // instructions 0, 1: W_gate rows; 2, 3: W_up rows
+  lb.init([&](int q) { return reinterpret_cast<const char*>(q < 2 ? Wgq : Wuq) + wrow0 * d; },
+          [&](int i) { return (uint32_t)min(i & 127, valid - 1) * (uint32_t)d; });
+  ScaleDmaH<4> sb;  // waves 0, 1: W_gate rows; 2, 3: W_up rows
+  sb.init([&](int w) { return reinterpret_cast<const char*>(w < 2 ? sg : su) + wrow0 * 4; }, (int64_t)E * n * 4,
+          [&](int i) { return (uint32_t)min(i & 127, valid - 1) * 4u; });
+  auto bsub = [&](int j) { return bsub_halved(wn, j); };
+  WaveAcc acc;
+  gemm_mainloop_f8_mx<FMT>(la, lb, sa, sb, d / 64, acc, L, wm, bsub);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = acc_m(wm, i);
+    char* row = epi_row(L, r);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c0 = bsub(j);  // wn * 64 + 32 j
+      float a[16];
+      float amax = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float gv = acc.c[i][j][v], uv = acc.c[i][j + 2][v];
+        a[v] = (float)(bf16)(gv * sigmoid_f32(gv) * uv);  // the activation in the element type
+        amax = fmaxf(amax, fabsf(a[v]));
+      }
+      amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+      const int k = mx_exponent<FMT>(amax);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = c0 + acc_n(4 * q);
+        const int lo = mx_cvt2<FMT, false>(ldexpf(a[4 * q], -k), ldexpf(a[4 * q + 1], -k), 0);
+        const int w = mx_cvt2<FMT, true>(ldexpf(a[4 * q + 2], -k), ldexpf(a[4 * q + 3], -k), lo);
+        *reinterpret_cast<int*>(row + 256 + c) = w;
+        if (act) {
+          const u32x2 pk = {pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3])};
+          *reinterpret_cast<u32x2*>(row + c * 2) = pk;
+        }
+      }
+      const int blk = (j0 + c0) >> 5;
+      if (lane < 32 && r < g.mrows && c0 < valid)
+        sact[((int64_t)(blk >> 2) * R_max + g.m0 + r) * 4 + (blk & 3)] = (uint8_t)(k + 127);
+    }
+  }
+  __syncthreads();
+  // codes: 256 rows x 128 bytes = 2048 chunks of 16 bytes, eight per thread
+  const int cvalid = valid / 16;
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const int c = threadIdx.x + b * GEMM_THREADS;
+    const int r = c >> 3, ch = c & 7;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(epi_row(L, r) + 256 + ch * 16);
+    if (r < g.mrows && ch < cvalid) st16_nt(act_q + (int64_t)(g.m0 + r) * n + j0 + ch * 16, v);
+  }
+  if (act) epi_store_bf16(L, 0, act + (int64_t)g.m0 * n + j0, n, g.mrows, 128, valid);
+}
+
+// Down with block scales on the four-wave engine, for n > DOWN_H_MAX_N_FP8: tile 256 rows x 256
+// columns of d.
+template <int FMT>
+__global__ __launch_bounds__(GEMM_THREADS, 1) void k_down_mx(
+    const int32_t* __restrict__ mtile_off, const int32_t* __restrict__ expert_off,
+    const uint8_t* __restrict__ Aq, const uint8_t* __restrict__ sa_, const uint8_t* __restrict__ Wdq,
+    const uint8_t* __restrict__ sd, bf16* __restrict__ Y, int d, int n, int E, int NT, int64_t R_max) {
+  MOE_GEMM_LDS(L);
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  GroupTile g;
+  if (!find_group_tile(lin, NT, mtile_off, expert_off, E, g)) return;
+  const int n0 = g.nt * BN;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int vrows = min(BN, d - n0);
+  KDmaHU<4> la;
+  la.init([&](int) { return reinterpret_cast<const char*>(Aq) + (int64_t)g.m0 * n; },
+          [&](int i) { return (uint32_t)min(i, g.mrows - 1) * (uint32_t)n; });
+  ScaleDmaH<4> sa;
+  sa.init([&](int) { return reinterpret_cast<const char*>(sa_); }, R_max * 4,
+          [&](int i) { return (uint32_t)(g.m0 + min(i, g.mrows - 1)) * 4u; });
+  const int64_t wrow0 = (int64_t)g.e * d + n0;
+  KDmaHU<4> lb;
+  lb.init([&](int) { return reinterpret_cast<const char*>(Wdq) + wrow0 * n; },
+          [&](int i) { return (uint32_t)min(i, vrows - 1) * (uint32_t)n; });
+  ScaleDmaH<4> sb;
+  sb.init([&](int) { return reinterpret_cast<const char*>(sd) + wrow0 * 4; }, (int64_t)E * d * 4,
+          [&](int i) { return (uint32_t)min(i, vrows - 1) * 4u; });
+  auto bsub = [&](int j) { return bsub_plain(wn, j); };
+  WaveAcc acc;
+  gemm_mainloop_f8_mx<FMT>(la, lb, sa, sb, n / 64, acc, L, wm, bsub);
+  epi_stage_bf16(L, wm, bsub, [&](int i, int j, int v) { return acc.c[i][j][v]; });
+  __syncthreads();
+  epi_store_bf16(L, 0, Y + (int64_t)g.m0 * d + n0, d, g.mrows, BN, vrows);
+}
+
 static inline int grid8f(int64_t n) { return (int)((n + 7) / 8 * 8); }
 
 hipError_t launch_up_fp8(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off, const uint8_t* Xq,
@@ -577,24 +698,26 @@ hipError_t launch_gather_mx_scales(const Shape& s, const PlanPtrs& p, const uint
 hipError_t launch_up_mx(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off, int fmt, const uint8_t* Xq,
                         const uint8_t* sxp, const uint8_t* Wgq, const uint8_t* sg, const uint8_t* Wuq,
                         const uint8_t* su, void* act, uint8_t* act_q, uint8_t* sact, hipStream_t st) {
-  const int NT = (int)cdiv(s.n, UP8H_COLS);
+  const bool half = s.d <= UP_H_MAX_D_FP8;
+  const int NT = (int)cdiv(s.n, half ? UP8H_COLS : 128);
   const int grid = grid8f(max_mtiles(s.R_max, s.E) * NT);
-#define MOE_UPMX(F) k_up_mx_h<F><<<grid, GEMM_THREADS, 0, st>>>(mtile_off, p.expert_off, p.row_token, Xq, sxp, Wgq, sg, \
+#define MOE_UPMX(K, F) K<F><<<grid, GEMM_THREADS, 0, st>>>(mtile_off, p.expert_off, p.row_token, Xq, sxp, Wgq, sg, \
       Wuq, su, static_cast<bf16*>(act), act_q, sact, (int)s.d, (int)s.n, s.E, NT, s.R_max, (int)s.T)
-  if (fmt == 0) MOE_UPMX(0);
-  else MOE_UPMX(1);
+  if (half) { if (fmt == 0) MOE_UPMX(k_up_mx_h, 0); else MOE_UPMX(k_up_mx_h, 1); }
+  else { if (fmt == 0) MOE_UPMX(k_up_mx, 0); else MOE_UPMX(k_up_mx, 1); }
 #undef MOE_UPMX
   return hipGetLastError();
 }
 
 hipError_t launch_down_mx(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off, int fmt, const uint8_t* Aq,
                           const uint8_t* sa, const uint8_t* Wdq, const uint8_t* sd, void* Y, hipStream_t st) {
-  const int NT = (int)cdiv(s.d, HBN);
+  const bool half = s.n <= DOWN_H_MAX_N_FP8;
+  const int NT = (int)cdiv(s.d, half ? HBN : BN);
   const int grid = grid8f(max_mtiles(s.R_max, s.E) * NT);
-#define MOE_DNMX(F) k_down_mx_h<F><<<grid, GEMM_THREADS, 0, st>>>(mtile_off, p.expert_off, Aq, sa, Wdq, sd, \
+#define MOE_DNMX(K, F) K<F><<<grid, GEMM_THREADS, 0, st>>>(mtile_off, p.expert_off, Aq, sa, Wdq, sd, \
       static_cast<bf16*>(Y), (int)s.d, (int)s.n, s.E, NT, s.R_max)
-  if (fmt == 0) MOE_DNMX(0);
-  else MOE_DNMX(1);
+  if (half) { if (fmt == 0) MOE_DNMX(k_down_mx_h, 0); else MOE_DNMX(k_down_mx_h, 1); }
+  else { if (fmt == 0) MOE_DNMX(k_down_mx, 0); else MOE_DNMX(k_down_mx, 1); }
 #undef MOE_DNMX
   return hipGetLastError();
 }

@@ -1368,14 +1368,19 @@ __device__ __forceinline__ i32x8 frag8_mx(const char* t, int row0) {
   return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 
-// One ring step of the block-scaled loop (as step_h with F8, eight DMA instructions per wave and
-// stage: four A and two B code loads, one A and one B scale load).
-template <int FMT, class BL, class BSub>
+// One ring step of the block-scaled loop (as step_h with F8: four A and two B code loads per wave
+// and stage).  A scale word covers two stages, so only even stages load scales (one A and one B
+// load more: eight instructions, six for odd stages) and an odd stage reads its scale bytes from
+// the previous stage's slot `sc`: that slot's refill (an odd stage, so codes only) leaves its
+// scale area alone, and the next scale load into it comes three steps later.  ODD = s & 1, known
+// at compile time in the unrolled loop, fixes the wait count.
+template <int FMT, bool ODD, class BL, class BSub>
 __device__ __forceinline__ void step_h_mx(const KDmaHU<4>& la, const BL& lb, const ScaleDmaH<4>& sa,
-                                          const ScaleDmaH<2>& sb, int s, int nkt, const char* cur, char* refill,
-                                          AccW8& acc, int wm, BSub bsub) {
+                                          const ScaleDmaH<2>& sb, int s, int nkt, const char* cur, const char* sc,
+                                          char* refill, AccW8& acc, int wm, BSub bsub) {
+  constexpr bool refill_scales = !ODD;  // stage s + 2 is even
   __builtin_amdgcn_sched_barrier(0);
-  wait_vmcnt<8>();
+  wait_vmcnt<ODD ? 8 : 6>();  // stage s + 1 is in flight
   ring_barrier();
   __builtin_amdgcn_sched_barrier(0);
   const int r = min(s + 2, nkt - 1);
@@ -1388,12 +1393,12 @@ __device__ __forceinline__ void step_h_mx(const KDmaHU<4>& la, const BL& lb, con
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     F.b[j] = frag8_mx(cur + DMA_B_OFF, bsub(j));
-    kb |= (uint32_t)*reinterpret_cast<const uint8_t*>(cur + MX_SB_OFF + (bsub(j) + (lane & 31)) * 4 + byte) << (8 * j);
+    kb |= (uint32_t)*reinterpret_cast<const uint8_t*>(sc + MX_SB_OFF + (bsub(j) + (lane & 31)) * 4 + byte) << (8 * j);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     F.a[i] = frag8_mx(cur, wm * 128 + i * 32);
-    ka |= (uint32_t)*reinterpret_cast<const uint8_t*>(cur + MX_SA_OFF + (wm * 128 + i * 32 + (lane & 31)) * 4 + byte)
+    ka |= (uint32_t)*reinterpret_cast<const uint8_t*>(sc + MX_SA_OFF + (wm * 128 + i * 32 + (lane & 31)) * 4 + byte)
           << (8 * i);
   }
   auto mma = [&](auto P) {
@@ -1426,11 +1431,11 @@ __device__ __forceinline__ void step_h_mx(const KDmaHU<4>& la, const BL& lb, con
   __builtin_amdgcn_sched_barrier(0);
   mma(std::integral_constant<int, 5>{});
   __builtin_amdgcn_sched_barrier(0);
-  sa.issue(r, refill + MX_SA_OFF);
+  if (refill_scales) sa.issue(r, refill + MX_SA_OFF);
   __builtin_amdgcn_sched_barrier(0);
   mma(std::integral_constant<int, 6>{});
   __builtin_amdgcn_sched_barrier(0);
-  sb.issue(r, refill + MX_SB_OFF);
+  if (refill_scales) sb.issue(r, refill + MX_SB_OFF);
   __builtin_amdgcn_sched_barrier(0);
   mma(std::integral_constant<int, 7>{});
   __builtin_amdgcn_sched_barrier(0);
@@ -1460,18 +1465,164 @@ __device__ __forceinline__ void gemm_mainloop_h_mx(const KDmaHU<4>& la, const BL
   for (int q = 0; q < 4; ++q) la.issue(q, r1, b1);
 #pragma unroll
   for (int q = 0; q < 2; ++q) lb.issue(q, r1, b1 + DMA_B_OFF);
-  sa.issue(r1, b1 + MX_SA_OFF);
-  sb.issue(r1, b1 + MX_SB_OFF);
+  // slots: stage s in b[s % 3]; an odd stage's scales in the previous stage's slot
   int s = 0;
-  for (; s + 3 <= nkt; s += 3) {
-    step_h_mx<FMT>(la, lb, sa, sb, s, nkt, b0, b2, acc, wm, bsub);
-    step_h_mx<FMT>(la, lb, sa, sb, s + 1, nkt, b1, b0, acc, wm, bsub);
-    step_h_mx<FMT>(la, lb, sa, sb, s + 2, nkt, b2, b1, acc, wm, bsub);
+  for (; s + 6 <= nkt; s += 6) {
+    step_h_mx<FMT, false>(la, lb, sa, sb, s, nkt, b0, b0, b2, acc, wm, bsub);
+    step_h_mx<FMT, true>(la, lb, sa, sb, s + 1, nkt, b1, b0, b0, acc, wm, bsub);
+    step_h_mx<FMT, false>(la, lb, sa, sb, s + 2, nkt, b2, b2, b1, acc, wm, bsub);
+    step_h_mx<FMT, true>(la, lb, sa, sb, s + 3, nkt, b0, b2, b2, acc, wm, bsub);
+    step_h_mx<FMT, false>(la, lb, sa, sb, s + 4, nkt, b1, b1, b0, acc, wm, bsub);
+    step_h_mx<FMT, true>(la, lb, sa, sb, s + 5, nkt, b2, b1, b1, acc, wm, bsub);
   }
-  if (s < nkt) {
-    step_h_mx<FMT>(la, lb, sa, sb, s, nkt, b0, b2, acc, wm, bsub);
-    if (s + 1 < nkt) step_h_mx<FMT>(la, lb, sa, sb, s + 1, nkt, b1, b0, acc, wm, bsub);
+  if (s < nkt) step_h_mx<FMT, false>(la, lb, sa, sb, s, nkt, b0, b0, b2, acc, wm, bsub);
+  if (s + 1 < nkt) step_h_mx<FMT, true>(la, lb, sa, sb, s + 1, nkt, b1, b0, b0, acc, wm, bsub);
+  if (s + 2 < nkt) step_h_mx<FMT, false>(la, lb, sa, sb, s + 2, nkt, b2, b2, b1, acc, wm, bsub);
+  if (s + 3 < nkt) step_h_mx<FMT, true>(la, lb, sa, sb, s + 3, nkt, b0, b2, b2, acc, wm, bsub);
+  if (s + 4 < nkt) step_h_mx<FMT, false>(la, lb, sa, sb, s + 4, nkt, b1, b1, b0, acc, wm, bsub);
+  __syncthreads();  // drains the trailing loads; the LDS is free for the epilogue
+}
+
+// ---------------------------------------------------------------------------------------------
+// Block-scaled FP8 on the four-wave engine (256 x 256 tiles, the ring of gemm_mainloop_f8), for
+// long K where the larger tile's operand reuse wins: each slot holds the codes (A 16 KB, B 16 KB)
+// and then the A and B scale words ([256 rows][4 B] each).  Per wave and stage: four A and four B
+// code loads, and on even stages one A and one B scale load.
+// ---------------------------------------------------------------------------------------------
+constexpr int F4_SA_OFF = 32768;
+constexpr int F4_SB_OFF = 33792;
+static_assert(F4_SB_OFF + 1024 <= LDS_BUF, "scale words fit a four-wave slot");
+
+struct FragSet8S {
+  i32x8 a[4], b[4];
+  uint32_t ra[4], rb[4];  // the lane's scale byte of A block i / B block j, as read
+  uint32_t ka, kb;        // the same packed: byte i of ka, byte j of kb
+};
+
+// Fragments of stage s from a four-wave slot and its scale bytes from `sslot` (layouts as in
+// step_h_mx).  The bytes are packed by pack_scales8s, which the ring step runs after the stage's last MFMAs: packing
+// here would make the wave wait for these LDS reads before its next MFMAs.
+template <class BSub>
+__device__ __forceinline__ void load_frags8s(const char* slot, const char* sslot, int s, int wm, BSub bsub,
+                                             FragSet8S& F) {
+  const int lane = threadIdx.x & 63;
+  const int byte = 2 * (s & 1) + (lane >> 5);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    F.b[j] = frag8_mx(slot + DMA_B_OFF, bsub(j));
+    F.rb[j] = *reinterpret_cast<const uint8_t*>(sslot + F4_SB_OFF + (bsub(j) + (lane & 31)) * 4 + byte);
   }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    F.a[i] = frag8_mx(slot, wm * 128 + i * 32);
+    F.ra[i] = *reinterpret_cast<const uint8_t*>(sslot + F4_SA_OFF + (wm * 128 + i * 32 + (lane & 31)) * 4 + byte);
+  }
+}
+
+__device__ __forceinline__ void pack_scales8s(FragSet8S& F) {
+  F.ka = F.ra[0] | (F.ra[1] << 8) | (F.ra[2] << 16) | (F.ra[3] << 24);
+  F.kb = F.rb[0] | (F.rb[1] << 8) | (F.rb[2] << 16) | (F.rb[3] << 24);
+}
+
+// Blocks p = FROM .. TO-1, block p = (i, j) = (p / 4, p % 4), B first as in mma8_range, with the
+// blocks' scale bytes selected from the packed words.
+template <int FMT, int P>
+__device__ __forceinline__ void mma8s_one(const FragSet8S& F, WaveAcc& acc) {
+  acc.c[P >> 2][P & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+      F.b[P & 3], F.a[P >> 2], acc.c[P >> 2][P & 3], FMT, FMT, P & 3, (int)F.kb, P >> 2, (int)F.ka);
+}
+template <int FMT, int FROM, int TO>
+__device__ __forceinline__ void mma8s_range(const FragSet8S& F, WaveAcc& acc) {
+  if constexpr (FROM < TO) {
+    mma8s_one<FMT, FROM>(F, acc);
+    mma8s_range<FMT, FROM + 1, TO>(F, acc);
+  }
+}
+
+// One ring step for stage s (as dma_step_f8): the first eight blocks of stage s; the wait for
+// stage s + 1 (only stage s + 2 was issued after it) and the barrier; stage s + 1's fragments and
+// scales into F1; the refill of stage s + 3 into the slot stage s - 1 used, its instructions
+// between pairs of the last eight blocks.  A scale word covers two stages (a group of four
+// 32-element blocks), so only even stages load scales (ten instructions per wave, eight for odd
+// ones) and an odd stage reads them from the previous stage's slot: that slot is refilled one step
+// later, after the barrier that follows every wave's reads.  ODD = s & 1, known at compile time
+// in the unrolled loop, fixes each step's wait count.
+template <int FMT, bool ODD, class BSub>
+__device__ __forceinline__ void dma_step_f8_mx(const KDmaHU<4>& la, const KDmaHU<4>& lb, const ScaleDmaH<4>& sa,
+                                               const ScaleDmaH<4>& sb, int s, int nkt, const char* cur,
+                                               const char* next, char* refill, FragSet8S& F0, FragSet8S& F1,
+                                               WaveAcc& acc, int wm, BSub bsub) {
+  constexpr bool refill_scales = ODD;  // stage s + 3 is even
+  const int r = min(s + 3, nkt - 1);
+  mma8s_range<FMT, 0, 8>(F0, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<ODD ? 8 : 10>();  // stage s + 2 (even when s is) is in flight
+  ring_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  load_frags8s(next, ODD ? next : cur, s + 1, wm, bsub, F1);
+  __builtin_amdgcn_sched_barrier(0);
+  la.issue(0, r, refill);
+  lb.issue(0, r, refill + DMA_B_OFF);
+  __builtin_amdgcn_sched_barrier(0);
+  mma8s_range<FMT, 8, 10>(F0, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  la.issue(1, r, refill);
+  lb.issue(1, r, refill + DMA_B_OFF);
+  __builtin_amdgcn_sched_barrier(0);
+  mma8s_range<FMT, 10, 12>(F0, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  la.issue(2, r, refill);
+  lb.issue(2, r, refill + DMA_B_OFF);
+  if (refill_scales) sa.issue(r, refill + F4_SA_OFF);
+  __builtin_amdgcn_sched_barrier(0);
+  mma8s_range<FMT, 12, 14>(F0, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  la.issue(3, r, refill);
+  lb.issue(3, r, refill + DMA_B_OFF);
+  if (refill_scales) sb.issue(r, refill + F4_SB_OFF);
+  __builtin_amdgcn_sched_barrier(0);
+  mma8s_range<FMT, 14, 16>(F0, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  pack_scales8s(F1);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// The four-wave block-scaled main loop over nkt stages of 64 k (stages 0-2 issued first; ends
+// with the LDS free).
+template <int FMT, class BSub>
+__device__ __forceinline__ void gemm_mainloop_f8_mx(const KDmaHU<4>& la, const KDmaHU<4>& lb, const ScaleDmaH<4>& sa,
+                                                    const ScaleDmaH<4>& sb, int nkt, WaveAcc& acc, LdsBufs L, int wm,
+                                                    BSub bsub) {
+  zero_acc(acc);
+  if (nkt <= 0) return;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int r = min(i, nkt - 1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      la.issue(q, r, L.b[i]);
+      lb.issue(q, r, L.b[i] + DMA_B_OFF);
+    }
+    if (i != 1) {
+      sa.issue(r, L.b[i] + F4_SA_OFF);
+      sb.issue(r, L.b[i] + F4_SB_OFF);
+    }
+  }
+  FragSet8S F0, F1;
+  wait_vmcnt<18>();  // stage 0 has landed: stages 1 (8) and 2 (10) came after it
+  ring_barrier();
+  load_frags8s(L.b[0], L.b[0], 0, wm, bsub, F0);
+  pack_scales8s(F0);
+  int s = 0;
+  for (; s + 4 <= nkt; s += 4) {
+    dma_step_f8_mx<FMT, false>(la, lb, sa, sb, s, nkt, L.b[0], L.b[1], L.b[3], F0, F1, acc, wm, bsub);
+    dma_step_f8_mx<FMT, true>(la, lb, sa, sb, s + 1, nkt, L.b[1], L.b[2], L.b[0], F1, F0, acc, wm, bsub);
+    dma_step_f8_mx<FMT, false>(la, lb, sa, sb, s + 2, nkt, L.b[2], L.b[3], L.b[1], F0, F1, acc, wm, bsub);
+    dma_step_f8_mx<FMT, true>(la, lb, sa, sb, s + 3, nkt, L.b[3], L.b[0], L.b[2], F1, F0, acc, wm, bsub);
+  }
+  if (s < nkt) dma_step_f8_mx<FMT, false>(la, lb, sa, sb, s, nkt, L.b[0], L.b[1], L.b[3], F0, F1, acc, wm, bsub);
+  if (s + 1 < nkt) dma_step_f8_mx<FMT, true>(la, lb, sa, sb, s + 1, nkt, L.b[1], L.b[2], L.b[0], F1, F0, acc, wm, bsub);
+  if (s + 2 < nkt) dma_step_f8_mx<FMT, false>(la, lb, sa, sb, s + 2, nkt, L.b[2], L.b[3], L.b[1], F0, F1, acc, wm, bsub);
   __syncthreads();  // drains the trailing loads; the LDS is free for the epilogue
 }
 

@@ -133,7 +133,16 @@ def run_ffn_mx(cfg, inp, fmt):
                 sd=by_row(sd, E * d, n).reshape(E, d, -1), act=act, act_q=act_q, sact=by_row(sact, R, n), Y=Y)
 
 
-def check_ffn_mx(cfg, inp, out, experts, fmt):
+def sample_rows(r0, r1, max_rows):
+    """Rows r0 .. r1 - 1 of an expert, or max_rows of them spread evenly (first and last kept)."""
+    if max_rows is None or r1 - r0 <= max_rows:
+        return np.arange(r0, r1)
+    return np.unique(np.linspace(r0, r1 - 1, max_rows).round().astype(np.int64))
+
+
+def check_ffn_mx(cfg, inp, out, experts, fmt, max_rows=None):
+    """Codes and scales of X and of every checked expert's weights bit for bit; then, on the
+    expert's rows (or max_rows of them), the activation, its codes and scales, and Y."""
     name = FMT[fmt]
     d, n = cfg.d, cfg.n
     plan_ref = oracle.build_plan(f64(out["logits"]), cfg.K)
@@ -155,25 +164,29 @@ def check_ffn_mx(cfg, inp, out, experts, fmt):
             w[q], w[sc] = {e: c}, {e: s}
         if r1 == r0:
             continue
-        _, _, A = M.ffn_mx_up(Xq, sx, w["Wgq"], w["sg"], w["Wuq"], w["su"], tok, off, e, name)
-        a_gpu = f64(out["act"][r0:r1])
+        rows = sample_rows(r0, r1, max_rows)
+        # the sampled rows as a one-expert plan (expert e renumbered 0)
+        sub_off = np.array([0, len(rows)])
+        sub = {k: {0: v[e]} for k, v in w.items()}
+        idx = torch.from_numpy(rows).to(out["act"].device)
+        _, _, A = M.ffn_mx_up(Xq, sx, sub["Wgq"], sub["sg"], sub["Wuq"], sub["su"], tok[rows], sub_off, 0, name)
+        a_gpu = f64(out["act"].index_select(0, idx))
         worst["act"] = max(worst.get("act", 0), assert_close("act e%d" % e, a_gpu, A, TOL8))
         ac, asc = M.quantize_blocks(a_gpu, name)
-        assert np.array_equal(out["act_q"][r0:r1].cpu().numpy(), ac), "act codes e%d" % e
-        assert np.array_equal(out["sact"][r0:r1], asc), "act scales e%d" % e
-        R = int(off[-1])
-        Aq = np.zeros((R, n), np.uint8)
-        sa = np.full((R, n // 32), 127, np.uint8)
-        Aq[r0:r1], sa[r0:r1] = ac, asc
-        Y = M.ffn_mx_down(Aq, sa, w["Wdq"], w["sd"], off, e, name)
-        worst["Y"] = max(worst.get("Y", 0), assert_close("Y e%d" % e, f64(out["Y"][r0:r1]), Y, TOL8))
+        assert np.array_equal(out["act_q"].index_select(0, idx).cpu().numpy(), ac), "act codes e%d" % e
+        assert np.array_equal(out["sact"][rows], asc), "act scales e%d" % e
+        Y = M.ffn_mx_down(ac, asc, sub["Wdq"], sub["sd"], sub_off, 0, name)
+        worst["Y"] = max(worst.get("Y", 0), assert_close("Y e%d" % e, f64(out["Y"].index_select(0, idx)), Y, TOL8))
     return worst
 
 
-# d = 2112 gives an odd number of 64-wide k-stages and n = 64 a scale stride with padding
+# d <= 2048 runs the gate/up GEMM and n <= 2048 the down GEMM on the half-width engine, d or n =
+# 2112 (an odd number of 64-wide k-stages) on the four-wave one; there n = 192 leaves the last
+# 128-column gate/up tile half empty and d = 192 the down tile's last 64 columns; n = 64 gives a
+# scale stride with padding
 @pytest.mark.parametrize("fmt", [B.FP8_E4M3, B.FP8_E5M2])
 @pytest.mark.parametrize("T,d,n,E,K", [(700, 320, 192, 6, 2), (129, 256, 64, 4, 4), (1000, 512, 320, 8, 2),
-                                       (300, 192, 2112, 4, 2), (200, 2112, 128, 3, 2)])
+                                       (300, 192, 2112, 4, 2), (200, 2112, 128, 3, 2), (260, 2112, 192, 3, 2)])
 def test_grouped_ffn_mx_small(T, d, n, E, K, fmt):
     cfg = wl.small_shape(T=T, d=d, E=E, K=K, n=n, dtype="bf16", backward=False, seed=T + d + fmt)
     inp = wl.make_inputs(cfg, device="cuda")
@@ -190,3 +203,13 @@ def test_grouped_ffn_mx_fine_grained_sampled(fmt):
     inp = wl.make_inputs(cfg, device="cuda")
     out = run_ffn_mx(cfg, inp, fmt)
     print(check_ffn_mx(cfg, inp, out, [0, 57, 127], fmt))
+
+
+@pytest.mark.slow
+def test_grouped_ffn_mx_mixtral_sampled():
+    """The coarse layer (T=8192, d=4096, n=14336, E=8, K=2): both GEMMs on the four-wave engine
+    (K = 4096 and 14336); experts 0 and 7, 48 rows of each."""
+    cfg = wl.BY_NAME["mixtral_coarse"].with_(backward=False)
+    inp = wl.make_inputs(cfg, device="cuda")
+    out = run_ffn_mx(cfg, inp, B.FP8_E4M3)
+    print(check_ffn_mx(cfg, inp, out, [0, 7], B.FP8_E4M3, max_rows=48))
