@@ -262,7 +262,7 @@ __global__ __launch_bounds__(GEMM8_THREADS, 1) void k_dx_w8(
     const bf16* __restrict__ dH, const bf16* __restrict__ Wg, const bf16* __restrict__ Wu,
     bf16* __restrict__ dXp, int d, int n, int E, int NT) {
   MOE_GEMM_LDS(L);
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int lin = xcd_remap<64>(blockIdx.x, gridDim.x);
   GroupTile g;
   if (!find_group_tile(lin, NT, mtile_off, expert_off, E, g)) return;
   const int n0 = g.nt * BN;

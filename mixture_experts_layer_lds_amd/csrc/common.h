@@ -117,19 +117,23 @@ __host__ __device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return 
 __device__ __forceinline__ int clamp_idx(int i, int n) { return min(max(i, 0), n - 1); }
 
 // XCD-aware remap of a 1-D grid: hardware hands consecutive workgroups to the 8 XCDs in turn,
-// each with its own L2.  The logical tiles are cut into chunks of XCD_CHUNK consecutive tiles
-// (one per CU of an XCD) and the chunks are dealt to the XCDs in turn, so that the tiles an XCD
-// runs side by side are neighbours (they share operands in its L2) while every XCD still gets an
-// even share of the whole range (tiles late in the list can carry more work than early ones).
-// The tail that does not fill a chunk per XCD is split evenly.  `n` must be a multiple of 8; the
-// map is a bijection of [0, n).
+// each with its own L2.  The logical tiles are cut into chunks of CHUNK consecutive tiles and the
+// chunks are dealt to the XCDs in turn, so that the tiles an XCD runs side by side are neighbours
+// (they share operands in its L2) while every XCD still gets an even share of the whole range
+// (tiles late in the list can carry more work than early ones).  The tail that does not fill a
+// chunk per XCD is split evenly.  `n` must be a multiple of 8; the map is a bijection of [0, n).
+// The default chunk is one tile per CU of an XCD; a kernel whose tile groups (RASTER_M m-tiles x
+// its n-tiles) are larger takes a chunk that keeps more of a group on one XCD (measured per
+// kernel on the fine-grained layer: the half-width down GEMM, 12 n-tiles, 0.394 -> 0.379 ms at
+// 96; the dX GEMM, 6 n-tiles, 0.612 -> 0.601 ms at 64; the others best at 32).
 constexpr int XCD_CHUNK = 32;
+template <int CHUNK = XCD_CHUNK>
 __host__ __device__ __forceinline__ int xcd_remap(int bid, int n) {
-  const int per = n >> 3;           // workgroups per XCD
+  const int per = n >> 3;        // workgroups per XCD
   const int xcd = bid & 7, j = bid >> 3;
-  const int full = per / XCD_CHUNK; // whole chunks per XCD
-  if (j < full * XCD_CHUNK) return ((j / XCD_CHUNK) * 8 + xcd) * XCD_CHUNK + j % XCD_CHUNK;
-  const int rem = per - full * XCD_CHUNK;
-  return full * 8 * XCD_CHUNK + xcd * rem + (j - full * XCD_CHUNK);
+  const int full = per / CHUNK;  // whole chunks per XCD
+  if (j < full * CHUNK) return ((j / CHUNK) * 8 + xcd) * CHUNK + j % CHUNK;
+  const int rem = per - full * CHUNK;
+  return full * 8 * CHUNK + xcd * rem + (j - full * CHUNK);
 }
 }  // namespace moe

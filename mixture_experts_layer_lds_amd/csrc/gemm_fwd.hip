@@ -365,7 +365,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_down_h(
     const bf16* __restrict__ act, const bf16* __restrict__ Wd, bf16* __restrict__ Y, int d, int n, int E,
     int NT) {
   MOE_GEMM_LDS_H(L);
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int lin = xcd_remap<96>(blockIdx.x, gridDim.x);
   GroupTile g;
   if (!find_group_tile(lin, NT, mtile_off, expert_off, E, g)) return;
   const int n0 = g.nt * HBN;
