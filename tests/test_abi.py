@@ -190,3 +190,30 @@ def test_route_noalloc_rejects_layers_beyond_its_buffer(lib):
     plan = B.PlanStruct(*([FAKE] * 9))
     st = lib.moe_route_noalloc(ctypes.byref(big), None, None, None, FAKE, ctypes.byref(plan), None)
     assert st == -3 and b"static buffer" in lib.moe_last_error()
+
+
+def test_mx_argument_checks(lib):
+    """moe_quantize_mx: K a multiple of 64, bf16 / fp32 sources, a known format, required
+    pointers, nothing to do for rows = 0; moe_mx_scale_bytes: the group-major size, 0 for invalid
+    sizes.  moe_grouped_ffn_mx: bf16 layers only, a known format, T * d below 2^32 (the
+    gathered code offsets are 32-bit), required pointers (act optional), its workspace."""
+    assert B.moe_mx_scale_bytes(10, 128) == 40 and B.moe_mx_scale_bytes(10, 192) == 80
+    assert B.moe_mx_scale_bytes(0, 128) == 0 and B.moe_mx_scale_bytes(-1, 128) == 0
+    q = lambda rows, K, dt=1, fmt=B.FP8_E4M3, src=FAKE, sc=FAKE: lib.moe_quantize_mx(rows, K, dt, fmt, src, FAKE, sc, None)
+    assert q(4, 96) == -1 and q(4, 0) == -1 and q(-1, 128) == -1
+    assert q(4, 128, dt=7) == -2
+    assert q(4, 128, fmt=5) == -1
+    assert q(4, 128, src=None) == -1 and q(4, 128, sc=None) == -1
+    assert q(0, 128, src=None) == 0
+    plan = B.PlanStruct(*([FAKE] * 9))
+    ffn = lambda d, fmt=B.FP8_E4M3, ws=1 << 40, act_q=FAKE: lib.moe_grouped_ffn_mx(
+        ctypes.byref(d), ctypes.byref(plan), fmt, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, act_q,
+        FAKE, FAKE, FAKE, ws, None)
+    assert ffn(dims(dtype="f32")) == -2
+    assert ffn(dims(), fmt=9) == -1
+    assert ffn(dims(T=1 << 22, d=1024)) == -2 and b"2^32" in lib.moe_last_error()
+    assert ffn(dims(), act_q=None) == -1
+    need = B.moe_workspace_bytes(dims(), B.OP_FFN_MX)
+    R = B.moe_max_rows(dims())
+    assert need >= B.moe_mx_scale_bytes(R, 128)
+    assert ffn(dims(), ws=need - 1) == -3
