@@ -96,15 +96,20 @@ TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic_counters.json")
 
 
 def kernel_source_digest():
-    """sha256 over the HIP/C++ sources of the library (file names and contents, sorted)."""
+    """sha256 over the HIP/C++ sources of the library (file names and code, sorted), with comments
+    and blank lines stripped, so that a record stays valid across edits of comments only."""
     import hashlib
+    import re
     src = os.path.join(HERE, "mixture_experts_layer_lds_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(src)):
         if f.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(src, f), encoding="utf-8") as fh:
+                text = fh.read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            lines = [re.sub(r"//.*$", "", l).rstrip() for l in text.splitlines()]
             h.update(f.encode())
-            with open(os.path.join(src, f), "rb") as fh:
-                h.update(fh.read())
+            h.update("\n".join(l for l in lines if l.strip()).encode())
     return h.hexdigest()
 
 

@@ -36,6 +36,11 @@
 // threads, 128 x 64 per wave, two waves per SIMD) and the half-width engine (256 x 128 tiles of
 // four such waves, a three-slot ring, two workgroups per CU); see their sections below.
 //
+// FP8 operands (OCP E4M3 or E5M2) go through the four-wave and half-width rings with one-byte
+// elements: a stage's 64 bytes per row are one k-step of v_mfma_scale_f32_32x32x64_f8f6f4, with
+// the block scales either held at 1.0 (per-row scales, applied in the epilogue) or loaded beside
+// the codes, one E8M0 byte per 32 elements (block-scaled); see the FP8 sections below.
+//
 // fp32 path (small fp32 layers only) — register-staged double buffer: stage j uses buffers
 // 2j (A) and 2j+1 (B) as [256][128 B + 16 B pad]; MN-major fp32 operands are transposed in
 // registers while staged.
