@@ -74,6 +74,19 @@ def test_single_expert_and_all_experts():
     full_check(wl.small_shape(T=200, d=128, E=4, K=4, n=64, dtype="f32", seed=6))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_limits_of_the_abi(dtype):
+    """The largest expert count and top-K the library accepts (E = 1024, K = 16: sixteen
+    candidates per lane in top-K, a 48 KiB router-backward row cache), a single token, and the
+    smallest width (d = n = 64), forward and backward against the oracle."""
+    _, ref, errs = full_check(wl.small_shape(T=300, d=64, E=1024, K=16, n=64, dtype=dtype, seed=11))
+    assert int(ref["counts"].sum()) == 300 * 16
+    print(errs)
+    _, ref, errs = full_check(wl.small_shape(T=1, d=64, E=8, K=2, n=64, dtype=dtype, seed=12))
+    assert int(ref["counts"].sum()) == 2
+    print(errs)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_empty_experts(dtype):
     cfg = wl.small_shape(T=400, d=128, E=8, K=2, n=128, dtype=dtype, bias="normal", seed=7)
