@@ -81,13 +81,15 @@ def stage_flops(stage, R, T, d, n, E):
 def stage_bytes(stage, R, T, d, n, E, es, K=None):
     """Algorithmic HBM bytes of one launch of a streaming stage.  Routing reads the fp32 logits
     and writes the plan: top-K ids and weights, expert-major rows (token, weight) and the
-    token-major inverse (offsets, rows)."""
+    token-major inverse (offsets, rows).  The router backward reads each row's dX_perm row, index,
+    weight and dS partial, writes dS, the fp32 dLogits, the router weight gradient's dL operand
+    and dX (the router weights it reads stay in the L2)."""
     K = K if K is not None else max(1, R // max(T, 1))
     return {
         "route": T * E * 4 + T * K * 8 + R * 12 + (T + 1) * 4,
         "permute": R * d * es + T * d * es + R * 4,
         "combine": R * d * es + T * d * es + R * 8 + (T + 1) * 4,
-        "router_bwd": R * d * es + T * d * es + T * E * 4 + R * 16,
+        "router_bwd": R * d * es + T * d * es + T * E * (4 + es) + R * 16 + (T + 1) * 4,
     }.get(stage)
 
 
