@@ -55,65 +55,107 @@ __device__ __forceinline__ void dact_epilogue(LdsBufs L, const GroupTile& g, int
     col = half * 128 + ch * VEC;
     return row < g.mrows && col < valid;
   };
-  u32x4 gv[PF][UNR], uv[PF][UNR];
-  float wv[PF][UNR];
-  auto load_group = [&](int half, int b0) {
-#pragma unroll
-    for (int pb = 0; pb < PF; ++pb)
-#pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        int row, ch, col;
-        if (chunk_at(half, b0 + pb, u, row, ch, col)) {
-          const int64_t r = g.m0 + row;
-          gv[pb][u] = ld16(H + r * 2 * n + n0 + col);
-          uv[pb][u] = ld16(H + r * 2 * n + n + n0 + col);
-          wv[pb][u] = row_w[r];
-        }
-      }
+  // G, U and the row weight of UNR chunks; H is read once and the outputs are not read again by
+  // this kernel, so both go around the caches' retention (non-temporal)
+  struct Grp {
+    u32x4 g[UNR], u[UNR];
+    float w[UNR];
   };
+  // Every thread issues the same number of loads whatever its chunks' validity (an invalid chunk
+  // reads the tile's last valid row and column chunk, and its values go unused), so the waits
+  // that follow can count them.
+  auto load_grp = [&](int half, int b, Grp& q) {
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    load_group(half, 0);
-    dump(half, frow);
-    __syncthreads();
-#pragma unroll 1
-    for (int b0 = 0; b0 < NB; b0 += PF) {
-      if (b0 > 0) load_group(half, b0);
-#pragma unroll
-      for (int pb = 0; pb < PF; ++pb)
-#pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-          int row, ch, col;
-          float p = 0.0f;
-          if (chunk_at(half, b0 + pb, u, row, ch, col)) {
-            const int64_t r = g.m0 + row;
-            const float w = wv[pb][u];
-            float dAp[VEC], G[VEC], U[VEC], oG[VEC], oU[VEC], oA[VEC];
-#pragma unroll
-            for (int k = 0; k < VEC; ++k) dAp[k] = *reinterpret_cast<const float*>(frow(row) + (ch * VEC + k) * 4);
-            unpack16<T>(gv[pb][u], G);
-            unpack16<T>(uv[pb][u], U);
-#pragma unroll
-            for (int k = 0; k < VEC; ++k) {
-              const float sg = sigmoid_f32(G[k]);
-              const float silu = G[k] * sg;
-              const float A = silu * U[k];
-              p += dAp[k] * A;
-              const float dA = w * dAp[k];
-              oG[k] = dA * U[k] * sg * (1.0f + G[k] * (1.0f - sg));
-              oU[k] = dA * silu;
-              oA[k] = w * A;
-            }
-            st16(dH + r * 2 * n + n0 + col, pack16<T>(oG));
-            st16(dH + r * 2 * n + n + n0 + col, pack16<T>(oU));
-            st16(wA + r * n + n0 + col, pack16<T>(oA));
-          }
-#pragma unroll
-          for (int o = 1; o < CPR; o <<= 1) p += __shfl_xor(p, o, 64);
-          if (ch == 0) red[row] = half == 0 ? p : red[row] + p;
-        }
+    for (int u = 0; u < UNR; ++u) {
+      int row, ch, col;
+      chunk_at(half, b, u, row, ch, col);
+      const int64_t r = g.m0 + min(row, g.mrows - 1);
+      const int c = min(col, valid - VEC);
+      q.g[u] = ld16_nt(H + r * 2 * n + n0 + c);
+      q.u[u] = ld16_nt(H + r * 2 * n + n + n0 + c);
+      q.w[u] = row_w[r];
     }
+  };
+  // The arithmetic runs for every chunk (an invalid one on the stand-in values above and the
+  // zero rows of the staged tile), so that the loaded values are used on every path and the
+  // compiler keeps the loads where they are issued; only the stores and the dS term are masked.
+  auto run_grp = [&](int half, int b, const Grp& q) {
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      int row, ch, col;
+      const bool ok = chunk_at(half, b, u, row, ch, col);
+      const int64_t r = g.m0 + row;
+      const float w = q.w[u];
+      float p = 0.0f;
+      float dAp[VEC], G[VEC], U[VEC], oG[VEC], oU[VEC], oA[VEC];
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) dAp[k] = *reinterpret_cast<const float*>(frow(row) + (ch * VEC + k) * 4);
+      unpack16<T>(q.g[u], G);
+      unpack16<T>(q.u[u], U);
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) {
+        const float sg = sigmoid_f32(G[k]);
+        const float silu = G[k] * sg;
+        const float A = silu * U[k];
+        p += dAp[k] * A;
+        const float dA = w * dAp[k];
+        oG[k] = dA * U[k] * sg * (1.0f + G[k] * (1.0f - sg));
+        oU[k] = dA * silu;
+        oA[k] = w * A;
+      }
+      if (ok) {
+        st16_nt(dH + r * 2 * n + n0 + col, pack16<T>(oG));
+        st16_nt(dH + r * 2 * n + n + n0 + col, pack16<T>(oU));
+        st16_nt(wA + r * n + n0 + col, pack16<T>(oA));
+      }
+      p = ok ? p : 0.0f;
+#pragma unroll
+      for (int o = 1; o < CPR; o <<= 1) p += __shfl_xor(p, o, 64);
+      if (ch == 0) red[row] = half == 0 ? p : red[row] + p;
+    }
+  };
+  if constexpr (NB == 2 && PF == 2) {
+    // two batches per half (eight waves): the second half's loads go out while the first half is
+    // finished -- the first batch's right after the first dump, the second's once the first
+    // half's first batch has freed its registers -- so that they are not queued behind the first
+    // half's stores and the second half costs no memory round trip of its own
+    // (scheduling barriers keep the loads in this order: the waits count them in issue order)
+    Grp a0, a1, b0, b1;
+    load_grp(0, 0, a0);
+    __builtin_amdgcn_sched_barrier(0);
+    dump(0, frow);
+    __builtin_amdgcn_sched_barrier(0);
+    load_grp(0, 1, a1);
+    load_grp(1, 0, b0);
     __syncthreads();
+    run_grp(0, 0, a0);
+    run_grp(0, 1, a1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_grp(1, 1, b1);
+    __syncthreads();
+    dump(1, frow);
+    __syncthreads();
+    run_grp(1, 0, b0);
+    run_grp(1, 1, b1);
+    __syncthreads();
+  } else {
+    Grp q[PF];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int pb = 0; pb < PF; ++pb) load_grp(half, pb, q[pb]);
+      dump(half, frow);
+      __syncthreads();
+#pragma unroll 1
+      for (int b0 = 0; b0 < NB; b0 += PF) {
+        if (b0 > 0)
+#pragma unroll
+          for (int pb = 0; pb < PF; ++pb) load_grp(half, b0 + pb, q[pb]);
+#pragma unroll
+        for (int pb = 0; pb < PF; ++pb) run_grp(half, b0 + pb, q[pb]);
+      }
+      __syncthreads();
+    }
   }
   if (threadIdx.x < 256 && (int)threadIdx.x < g.mrows)
     dS_part[(int64_t)nt * R_max + g.m0 + threadIdx.x] = red[threadIdx.x];
