@@ -818,14 +818,26 @@ __global__ __launch_bounds__(GEMM8_THREADS, 1) void k_dwr_w8(
     }
 }
 
+// Sums the S slices in slice order, four consecutive outputs per thread (n is a multiple of 4);
+// the slices' loads are issued eight at a time.
 template <typename T>
 __global__ __launch_bounds__(256) void k_dwr_reduce(const float* __restrict__ part, int S,
                                                     int64_t n, T* __restrict__ dWr) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= n) return;
-  float s = 0.0f;
-  for (int q = 0; q < S; ++q) s += part[(int64_t)q * n + i];
-  dWr[i] = from_f32<T>(s);
+  f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+  int q = 0;
+  for (; q + 8 <= S; q += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      v[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(part + (int64_t)(q + k) * n + i));
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s += v[k];
+  }
+  for (; q < S; ++q) s += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(part + (int64_t)q * n + i));
+#pragma unroll
+  for (int k = 0; k < 4; ++k) dWr[i + k] = from_f32<T>(s[k]);
 }
 
 hipError_t launch_dwr_gemm(const Shape& s, const void* dLop, int E_pad, const void* X, void* dW_r,
@@ -837,11 +849,11 @@ hipError_t launch_dwr_gemm(const Shape& s, const void* dLop, int E_pad, const vo
   if (s.bf16) {
     k_dwr_w8<<<grid, GEMM8_THREADS, 0, st>>>((const bf16*)dLop, E_pad, (const bf16*)X, part, (bf16*)dW_r,
                                              (int)s.T, (int)s.d, s.E, q.MT, q.NT, q.S, q.TS);
-    if (q.S > 1) k_dwr_reduce<bf16><<<(int)cdiv(nout, 256), 256, 0, st>>>(part, q.S, nout, (bf16*)dW_r);
+    if (q.S > 1) k_dwr_reduce<bf16><<<(int)cdiv(nout / 4, 256), 256, 0, st>>>(part, q.S, nout, (bf16*)dW_r);
   } else {
     k_dwr<float><<<grid, GEMM_THREADS, 0, st>>>((const float*)dLop, E_pad, (const float*)X, part,
                                                 (float*)dW_r, (int)s.T, (int)s.d, s.E, q.MT, q.NT, q.S, q.TS);
-    if (q.S > 1) k_dwr_reduce<float><<<(int)cdiv(nout, 256), 256, 0, st>>>(part, q.S, nout, (float*)dW_r);
+    if (q.S > 1) k_dwr_reduce<float><<<(int)cdiv(nout / 4, 256), 256, 0, st>>>(part, q.S, nout, (float*)dW_r);
   }
   return hipGetLastError();
 }

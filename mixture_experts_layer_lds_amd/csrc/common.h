@@ -9,6 +9,8 @@ namespace moe {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -100,13 +102,16 @@ template <> __device__ __forceinline__ u32x4 pack16<float>(const float* f) {
   for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(f[i]);
   return v;
 }
+// Two floats to two bf16 (round to nearest even) in one 32-bit word, lo in the low half: a
+// two-element vector conversion, which gfx950 does in one instruction (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
 template <> __device__ __forceinline__ u32x4 pack16<bf16>(const float* f) {
   u32x4 v;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    bf16 lo = (bf16)f[2 * i], hi = (bf16)f[2 * i + 1];
-    v[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-  }
+  for (int i = 0; i < 4; ++i) v[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
   return v;
 }
 

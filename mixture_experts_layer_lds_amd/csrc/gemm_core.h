@@ -780,10 +780,6 @@ __device__ __forceinline__ char* epi_buf(LdsBufs L, int r) {
 }
 __device__ __forceinline__ char* epi_row(LdsBufs L, int r) { return epi_buf(L, r) + (r & 63) * EPI_ROW; }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)hi) << 16);
-}
-
 template <class Col, class Val>
 __device__ __forceinline__ void epi_stage_bf16(LdsBufs L, int wm, Col col, Val val) {
 #pragma unroll
