@@ -552,11 +552,12 @@ hipError_t launch_dw_gu_gemm(const Shape& s, const PlanPtrs& p, const int32_t* o
 //   padded to E_pad columns, the operand of the router weight gradient)
 //   dX[t] = sum_r dX_perm[r] + dL_r W_r[e_r]      (rows in ascending expert order)
 // ---------------------------------------------------------------------------------------------
-__device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ expert_off, int E, int r) {
-  int lo = 0, hi = E;  // expert_off[lo] <= r < expert_off[hi]
+// The expert of row r: a binary search over the block's LDS copy of expert_off.
+__device__ __forceinline__ int expert_of_row(const int32_t* soff, int E, int r) {
+  int lo = 0, hi = E;  // soff[lo] <= r < soff[hi]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (expert_off[mid] <= r) lo = mid;
+    if (soff[mid] <= r) lo = mid;
     else hi = mid;
   }
   return lo;
@@ -569,36 +570,53 @@ __global__ __launch_bounds__(256) void k_router_bwd(
     const float* __restrict__ dS_part, int ntiles, int64_t R_max, const T* __restrict__ dXp,
     const T* __restrict__ Wr, float* __restrict__ dS, float* __restrict__ dLogits,
     T* __restrict__ dLop, int E_pad, T* __restrict__ dX, int T_, int d, int E) {
-  // per wave: the dense dL row [E_pad], the token's rows and their experts (at most E of each)
+  // per wave: the dense dL row [E_pad], the token's rows and their experts (at most E of each);
+  // per block: expert_off [E + 1]
   extern __shared__ char rb_lds[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
+  int* soff = reinterpret_cast<int*>(rb_lds) + (size_t)4 * 3 * E_pad;
+  for (int e = threadIdx.x; e <= E; e += 256) soff[e] = expert_off[e];
+  __syncthreads();
   if (t >= T_) return;
   const int base = tok_off[t], cnt = tok_off[t + 1] - base;
   float* sdl = reinterpret_cast<float*>(rb_lds) + (size_t)wave * 3 * E_pad;
   int* srow = reinterpret_cast<int*>(sdl + E_pad);
   int* sexp = srow + E_pad;
   for (int e = lane; e < E_pad; e += 64) sdl[e] = 0.0f;
-  // pass 1: s = sum_r w_r dS_r
-  float part = 0.0f;
+  // pass 1: s = sum_r w_r dS_r; a lane keeps its first row's index, dS and weight for pass 2
   const int rmax = (int)R_max;
-  for (int i = lane; i < cnt; i += 64) {
-    const int r = clamp_idx(tok_row[base + i], rmax);
-    float ds = 0.0f;
+  auto row_ds = [&](int i, int& r, float& ds, float& w) {
+    r = clamp_idx(tok_row[base + i], rmax);
+    ds = 0.0f;
     for (int q = 0; q < ntiles; ++q) ds += dS_part[(int64_t)q * R_max + r];
-    part += row_w[r] * ds;
+    w = row_w[r];
+  };
+  int r0 = 0;
+  float ds0 = 0.0f, w0 = 0.0f;
+  if (lane < cnt) row_ds(lane, r0, ds0, w0);
+  float part = w0 * ds0;
+  for (int i = lane + 64; i < cnt; i += 64) {
+    int r;
+    float ds, w;
+    row_ds(i, r, ds, w);
+    part += w * ds;
   }
   const float ssum = wave_sum(part);
   // pass 2: dL per row, dS out, dense dL row in LDS; each row's expert resolved once
-  for (int i = lane; i < cnt; i += 64) {
-    const int r = clamp_idx(tok_row[base + i], rmax);
-    float ds = 0.0f;
-    for (int q = 0; q < ntiles; ++q) ds += dS_part[(int64_t)q * R_max + r];
+  auto put = [&](int i, int r, float ds, float w) {
     dS[r] = ds;
-    const int e = expert_of_row(expert_off, E, r);
-    sdl[e] = row_w[r] * (ds - ssum);
+    const int e = expert_of_row(soff, E, r);
+    sdl[e] = w * (ds - ssum);
     srow[i] = r;
     sexp[i] = e;
+  };
+  if (lane < cnt) put(lane, r0, ds0, w0);
+  for (int i = lane + 64; i < cnt; i += 64) {
+    int r;
+    float ds, w;
+    row_ds(i, r, ds, w);
+    put(i, r, ds, w);
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -663,7 +681,7 @@ static void router_bwd_for(const Shape& s, const PlanPtrs& p, const float* dS_pa
                            const void* W_r, float* dS, float* dLogits, void* dLop, int E_pad, void* dX,
                            hipStream_t st) {
   const int grid = (int)cdiv(s.T, 4);
-  const size_t lds = (size_t)4 * 3 * E_pad * sizeof(float);  // <= 48 KiB for E <= 1024
+  const size_t lds = ((size_t)4 * 3 * E_pad + s.E + 1) * sizeof(float);  // <= 53 KiB for E <= 1024
   k_router_bwd<T, CPL, RB><<<grid, 256, lds, st>>>(p.tok_off, p.tok_row, p.expert_off, p.row_w, dS_part, ntiles,
                                                    s.R_max, static_cast<const T*>(dX_perm), static_cast<const T*>(W_r),
                                                    dS, dLogits, static_cast<T*>(dLop), E_pad, static_cast<T*>(dX),

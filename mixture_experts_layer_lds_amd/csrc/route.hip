@@ -470,8 +470,23 @@ __global__ __launch_bounds__(256) void k_place(const float* __restrict__ logits,
 #pragma unroll
   for (int k = 0; k < KM; ++k) ids[k] = k < K ? topk_idx[(int64_t)t * K + k] : INT_MAX;
   bitonic_sort_i32(ids);
+  // every load below is issued for all KM slots (slots k >= K read expert 0 and are ignored), so
+  // that they go out together instead of one dependent round trip per slot
+  int rows[KM];
 #pragma unroll
-  for (int k = 0; k < KM; ++k) lv[k] = k < K ? L[ids[k]] : -INFINITY;
+  for (int k = 0; k < KM; ++k) {
+    const int e = k < K ? ids[k] : 0;
+    lv[k] = L[e];
+    rows[k] = expert_off[e] + wprefix[(int64_t)e * W + w] + __popc(bits[(int64_t)e * W + w] & below);
+  }
+  // (an empty asm that takes the rows and logits keeps the compiler from sinking their loads
+  // towards their conditional uses below, one round trip each)
+  if constexpr (KM <= 8) {  // (at 16 slots the pinned values crowd the registers)
+#pragma unroll
+    for (int k = 0; k < KM; ++k) asm volatile("" : "+v"(rows[k]), "+v"(lv[k]));
+  }
+#pragma unroll
+  for (int k = 0; k < KM; ++k) lv[k] = k < K ? lv[k] : -INFINITY;
   float m = lv[0];
 #pragma unroll
   for (int k = 1; k < KM; ++k)
@@ -484,8 +499,7 @@ __global__ __launch_bounds__(256) void k_place(const float* __restrict__ logits,
 #pragma unroll
   for (int k = 0; k < KM; ++k) {
     if (k >= K) break;
-    const int e = ids[k];
-    const int row = expert_off[e] + wprefix[(int64_t)e * W + w] + __popc(bits[(int64_t)e * W + w] & below);
+    const int row = rows[k];
     row_token[row] = t;
     row_w[row] = __expf(lv[k] - m) * inv;
     tok_row[base + k] = row;
