@@ -44,12 +44,13 @@ __device__ __forceinline__ float wave_max(float v) {
 // Maximum of v over the 64 lanes, returned in every lane.  Within each row of 16 lanes, row
 // shifts by 1, 2, 3, 4 (lanes 4-15) and 8 (lanes 8-15) leave the row's maximum in its lane 15;
 // row broadcasts of lane 15 (into rows 1 and 3) and of lane 31 (into rows 2 and 3) then leave the
-// wave's maximum in lane 63.  Lanes whose DPP source is off the row or masked keep their own
-// value, which a maximum ignores.
+// wave's maximum in lane 63.  Lanes whose DPP source is off the row or masked read 0, the
+// identity of an unsigned maximum, which lets the compiler fold each move into the maximum
+// (one v_max_u32 with a DPP operand per step).
 __device__ __forceinline__ uint32_t dpp_max_step(uint32_t v, uint32_t x) { return v > x ? v : x; }
 template <int CTRL, int ROWS, int BANKS>
 __device__ __forceinline__ uint32_t dpp_src(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWS, BANKS, false);
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, BANKS, true);
 }
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   v = dpp_max_step(v, dpp_src<0x111, 0xf, 0xf>(v));  // row_shr:1
