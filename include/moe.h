@@ -232,9 +232,10 @@ moe_status moe_backward(const moe_dims* dims, const void* dY, const void* X, con
  * weighted combine.  apxml.com "自定义核与核融合" (the five steps fused into one kernel) and
  * "条件参数加载" (only the selected experts' weights are read, each once per 48 routed tokens).
  * Plain top-K only (round_mode must be MOE_ROUND_NONE, else MOE_ENOTSUP); T <= 1024.  The
- * launch is cooperative (one workgroup per CU, all resident, phases separated by grid-wide
- * barriers), so the call fails with MOE_EHIP rather than run if the device cannot host the
- * grid.  The barriers count arrivals in the call's workspace, which a small kernel clears right
+ * grid is one workgroup per CU, phases separated by grid-wide barriers, so the whole grid must
+ * be resident at once: it is on a device that runs nothing else; if other work (other streams)
+ * holds CUs for longer than the barrier bound below, the call fails as described there instead
+ * of hanging.  The barriers count arrivals in the call's workspace, which a small kernel clears right
  * before the launch, so calls share no device state: calls that may overlap (other streams) need
  * only their own workspaces.  A barrier wait is bounded (about a second of polling; see
  * moe_decode_set_spin_limit); a workgroup that reaches the bound leaves the kernel and sets the
@@ -244,9 +245,10 @@ moe_status moe_backward(const moe_dims* dims, const void* dY, const void* X, con
  * activation is rounded to dtype between the projections, as in moe_forward); routing is the
  * same function of the logits, ties to the lower expert id.  It pays off while few experts
  * see each a few tokens and their weights are large (on MI355X it beats moe_forward at T = 1
- * and T = 8 on the layer shapes with large experts); once most experts are routed with several
- * tokens each (T = 64 on those shapes), or when the experts are small (the fine-grained shape:
- * d = 1536, n = 256, at any T tried), moe_forward is as fast or faster.
+ * and T = 8 on the layer shapes with large experts, and at T = 1 on the fine-grained shape:
+ * d = 1536, n = 256); once most experts are routed with several tokens each (T = 64 on the
+ * large-expert shapes), or at T >= 8 on the fine-grained shape, moe_forward is as fast or
+ * faster.
  *  X [T,d], W_r [E,d], bias [E] fp32 or NULL, W_gate/W_up [E,n,d], W_down [E,d,n] dtype.
  *  Outputs (overwritten): logits [T,E] fp32, topk_idx [T,K] int32, topk_w [T,K] fp32 (as in the
  *  plan of moe_route), out [T,d] dtype.

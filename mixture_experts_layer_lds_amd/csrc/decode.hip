@@ -17,9 +17,9 @@
 // most one tile ahead), never through a workgroup barrier; with W = 1 the wave does the whole
 // tile alone.  Every result is deterministic.
 //
-// One cooperative kernel, one workgroup of 16 waves per CU, phases separated by grid-wide
-// barriers (every workgroup walks every phase with grid-stride loops, so each reaches every
-// barrier).  The barrier is a release fence, one relaxed arrival on a 64-bit counter, relaxed
+// One kernel, one workgroup of 16 waves per CU (the whole grid resident at once), phases
+// separated by grid-wide barriers (every workgroup walks every phase with grid-stride loops, so
+// each reaches every barrier).  The barrier is a release fence, one relaxed arrival on a 64-bit counter, relaxed
 // polling and an acquire fence: cache maintenance happens once per workgroup and barrier, not
 // once per poll.  The counter lives in the call's workspace and a one-workgroup kernel clears it
 // (with the per-expert counters) right before the launch, so calls share no device state and
@@ -38,6 +38,8 @@
 //   E. combine: out[t] = sum over the token's experts, in ascending expert order, of w y.
 // Routing is plain top-K (no token rounding); results match moe_forward up to the order of the
 // fp32 accumulations.
+#include <atomic>
+
 #include "internal.h"
 
 namespace moe {
@@ -337,9 +339,9 @@ __device__ __forceinline__ bool dec_grid_barrier(unsigned long long* ctr, long l
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const unsigned long long v = __hip_atomic_fetch_add(ctr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const unsigned long long target = (v / nb + 1) * nb;
-    // bounded wait: under a cooperative launch every workgroup is resident and arrives, so the
-    // limit is only reached if that guarantee fails; then the call reports an error instead of
-    // hanging or finishing with wrong results
+    // bounded wait: with the grid resident every workgroup arrives, so the limit is only reached
+    // if part of the grid could not be placed (other work holding CUs past the bound); then the
+    // call reports an error instead of hanging or finishing with wrong results
     int ok = 0;
     for (long long spin = 0; spin < spin_limit; ++spin) {
       if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) {
@@ -577,6 +579,9 @@ size_t decode_workspace_bytes(int64_t T, int64_t d, int64_t n, int E, int K) {
 }
 
 static long long g_dec_spin_limit = 1ll << 20;  // about a second of polling
+// Grid size per device and dtype (0 until the first call on that device computes it).
+constexpr int DEC_MAX_DEVICES = 64;
+static std::atomic<int> g_dec_grid[DEC_MAX_DEVICES][2];
 
 long long decode_set_spin_limit(long long limit) {
   const long long prev = g_dec_spin_limit;
@@ -618,22 +623,34 @@ hipError_t launch_decode(const Shape& s, const void* X, const void* W_r, const f
   a.spin_limit = g_dec_spin_limit;
   const void* fn = s.bf16 ? reinterpret_cast<const void*>(&k_decode<bf16>)
                           : reinterpret_cast<const void*>(&k_decode<float>);
-  int dev = 0, cus = 0, per_cu = 0;
+  int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, DEC_THREADS, 0);
-  if (e != hipSuccess) return e;
-  if (per_cu < 1) return hipErrorInvalidConfiguration;
-  // every workgroup must be resident at once for the grid barriers: the cooperative launch
-  // refuses a larger grid
-  const int grid = cus * per_cu;
+  // every workgroup must be resident at once for the grid barriers: the grid is the device's CU
+  // count times the kernel's occupancy, queried once per device and dtype
+  if (dev < 0 || dev >= DEC_MAX_DEVICES) return hipErrorInvalidDevice;
+  std::atomic<int>& cached = g_dec_grid[dev][s.bf16 ? 1 : 0];
+  int grid = cached.load(std::memory_order_relaxed);
+  if (grid == 0) {
+    int cus = 0, per_cu = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, DEC_THREADS, 0);
+    if (e != hipSuccess) return e;
+    if (per_cu < 1 || cus < 1) return hipErrorInvalidConfiguration;
+    grid = cus * per_cu;
+    cached.store(grid, std::memory_order_relaxed);
+  }
   k_dec_clear<<<1, 256, 0, st>>>(a.bar, a.cnt, s.E);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // A plain launch: a grid of at most one full CU's worth of workgroups per CU is placed whole on
+  // a device that runs nothing else, and the barriers' bounded wait turns the case where it
+  // cannot be (other work holding CUs past the bound) into a reported failure.  The
+  // cooperative launch gives the same guarantee up front but costs about 20 us more per call,
+  // a third of a small decode step.
   void* params[] = {&a};
-  return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(DEC_THREADS), params, 0u, st);
+  return hipLaunchKernel(fn, dim3(grid), dim3(DEC_THREADS), params, 0u, st);
 }
 
 }  // namespace moe
