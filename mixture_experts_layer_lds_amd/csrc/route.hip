@@ -108,6 +108,107 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const float* __restrict__
 }
 
 // ---------------------------------------------------------------------------------------------
+// top-K for E <= 256: four tokens per wave, one 16-lane row of the wave per token (the same 64
+// tokens and 16 waves per block).  Lane i of a row holds the order keys of experts e = i + 16 j,
+// j < EPG.  A round takes the row's largest live key (rotations by 1, 2, 4 and 8 lanes within the
+// row leave the maximum in every lane, one v_max_u32 with a DPP operand each), then the lowest
+// expert id holding it (the same with minima over each lane's lowest candidate) -- the same
+// order as the wave-per-token kernel, with a quarter of its instructions per token.
+// ---------------------------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ uint32_t row_ror_max(uint32_t v) {
+  const uint32_t x = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, true);
+  return v > x ? v : x;
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t row_ror_min(uint32_t v) {
+  const uint32_t x = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, CTRL, 0xf, 0xf, true);
+  return v < x ? v : x;
+}
+__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
+  v = row_ror_max<0x121>(v);  // row_ror:1
+  v = row_ror_max<0x122>(v);  // row_ror:2
+  v = row_ror_max<0x124>(v);  // row_ror:4
+  return row_ror_max<0x128>(v);  // row_ror:8
+}
+__device__ __forceinline__ uint32_t row16_min(uint32_t v) {
+  v = row_ror_min<0x121>(v);
+  v = row_ror_min<0x122>(v);
+  v = row_ror_min<0x124>(v);
+  return row_ror_min<0x128>(v);
+}
+
+template <int EPG>
+__global__ __launch_bounds__(TOPK_THREADS) void k_topk_g(const float* __restrict__ logits, int T, int E,
+                                                         int K, int W, int32_t* __restrict__ topk_idx,
+                                                         float* __restrict__ topk_w,
+                                                         uint32_t* __restrict__ bits,
+                                                         uint32_t* __restrict__ keysT) {
+  extern __shared__ uint32_t sbits[];  // [E][2], then (keysT staged) [E][65] keys
+  uint32_t* skeys = sbits + 2 * E;
+  const bool stage = keysT && E <= TOPK_STAGE_E;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = lane & 15;
+  const int tt = wave * 4 + (lane >> 4);  // the row's token within the block
+  const int t0 = blockIdx.x * TOPK_TOKENS_PER_BLOCK;
+  const int t = t0 + tt;
+  for (int x = threadIdx.x; x < 2 * E; x += blockDim.x) sbits[x] = 0u;
+  __syncthreads();
+  if (t < T) {  // uniform over the row, so every DPP source lane is active
+    const float* row = logits + (int64_t)t * E;
+    uint32_t key[EPG];
+    uint32_t alive = 0;  // bit j: candidate e = i + 16 j still in play
+#pragma unroll
+    for (int j = 0; j < EPG; ++j) {
+      const int e = i + 16 * j;
+      key[j] = e < E ? order_key(row[e]) : 0u;
+      alive |= e < E ? (1u << j) : 0u;
+      if (keysT && e < E) {
+        if (stage) skeys[e * 65 + tt] = key[j];
+        else keysT[(int64_t)e * T + t] = key[j];
+      }
+    }
+    int my_e = 0;
+    for (int k = 0; k < K; ++k) {
+      uint32_t lm = 0;  // NaN keys are 0 too; ties at 0 are settled below among live candidates
+#pragma unroll
+      for (int j = 0; j < EPG; ++j)
+        if ((alive >> j) & 1u) lm = key[j] > lm ? key[j] : lm;
+      const uint32_t kmax = row16_max(lm);
+      uint32_t cand = 0xffffffffu;  // this lane's lowest expert id holding kmax
+#pragma unroll
+      for (int j = EPG - 1; j >= 0; --j)
+        if (((alive >> j) & 1u) && key[j] == kmax) cand = (uint32_t)(i + 16 * j);
+      const int win = (int)row16_min(cand);
+      if (i == (win & 15)) alive &= ~(1u << (win >> 4));
+      if (i == k) my_e = win;
+    }
+    const float my_v = i < K ? row[my_e] : 0.0f;
+    const float vmax = __shfl(my_v, lane & ~15, 64);
+    const float ex = i < K ? __expf(my_v - vmax) : 0.0f;
+    float s = ex;
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);  // the same sum in every lane of the row
+    if (i < K) {
+      topk_idx[(int64_t)t * K + i] = my_e;
+      topk_w[(int64_t)t * K + i] = ex / s;
+      atomicOr(&sbits[my_e * 2 + (tt >> 5)], 1u << (tt & 31));
+    }
+  }
+  __syncthreads();
+  const int w0 = blockIdx.x * 2;
+  for (int x = threadIdx.x; x < 2 * E; x += blockDim.x) {
+    const int e = x >> 1, w = w0 + (x & 1);
+    if (w < W) bits[(int64_t)e * W + w] = sbits[x];
+  }
+  if (stage)
+    for (int x = threadIdx.x; x < E * 64; x += blockDim.x) {
+      const int e = x >> 6, c = x & 63;
+      if (t0 + c < T) keysT[(int64_t)e * T + t0 + c] = skeys[e * 65 + c];
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
 // Block-wide exclusive scan helper (256 threads).  Returns the exclusive prefix of `x` and the
 // block total.
 // ---------------------------------------------------------------------------------------------
@@ -632,11 +733,15 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int K, int round_
   const int nblk = (int)cdiv(T, TOPK_TOKENS_PER_BLOCK);
   const size_t lds = (size_t)E * 2 * sizeof(uint32_t) + (rounded && E <= TOPK_STAGE_E ? (size_t)E * 65 * 4 : 0);
 #define MOE_TOPK(EPL) k_topk<EPL><<<nblk, TOPK_THREADS, lds, st>>>(logits, (int)T, E, K, W, p.topk_idx, p.topk_w, bits, keysT)
-  if (E <= 64) MOE_TOPK(1);
-  else if (E <= 128) MOE_TOPK(2);
-  else if (E <= 256) MOE_TOPK(4);
+#define MOE_TOPK_G(EPG) k_topk_g<EPG><<<nblk, TOPK_THREADS, lds, st>>>(logits, (int)T, E, K, W, p.topk_idx, p.topk_w, bits, keysT)
+  if (E <= 16) MOE_TOPK_G(1);
+  else if (E <= 32) MOE_TOPK_G(2);
+  else if (E <= 64) MOE_TOPK_G(4);
+  else if (E <= 128) MOE_TOPK_G(8);
+  else if (E <= 256) MOE_TOPK_G(16);
   else if (E <= 512) MOE_TOPK(8);
   else MOE_TOPK(16);
+#undef MOE_TOPK_G
 #undef MOE_TOPK
   k_count<<<E, 256, 0, st>>>(bits, W, wprefix, p.counts);
   if (rounded) {
