@@ -353,28 +353,11 @@ hipError_t launch_dx_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mtil
 // staged as they lie and read with the transposing LDS load.  Experts without rows get zero
 // tiles.
 // ---------------------------------------------------------------------------------------------
-// Experts by decreasing row count (ties: lower id first): order[rank] = e.  The weight-gradient
-// GEMMs reduce over an expert's rows, so their tiles take time in proportion to its count; taking
-// the experts in this order starts the longest tiles first and leaves the short ones to fill the
-// end of the grid, instead of a hot expert's tiles forming the tail.  One block, E <= 1024.
-__global__ __launch_bounds__(1024) void k_expert_order(const int32_t* __restrict__ counts, int E,
-                                                       int32_t* __restrict__ order) {
-  __shared__ int c[1024];
-  const int e = threadIdx.x;
-  if (e < E) c[e] = counts[e];
-  __syncthreads();
-  if (e >= E) return;
-  const int ce = c[e];
-  int rank = 0;
-  for (int f = 0; f < E; ++f) rank += (c[f] > ce || (c[f] == ce && f < e)) ? 1 : 0;
-  order[rank] = e;
-}
-
-hipError_t launch_expert_order(const int32_t* counts, int E, int32_t* order, hipStream_t st) {
-  k_expert_order<<<1, 1024, 0, st>>>(counts, E, order);
-  return hipGetLastError();
-}
-
+// The expert order of these GEMMs (order[rank] = e, decreasing row count, ties to the lower id) is
+// computed with the tile offsets (k_tile_offsets).  The weight-gradient GEMMs reduce over an
+// expert's rows, so their tiles take time in proportion to its count; taking the experts in this
+// order starts the longest tiles first and leaves the short ones to fill the end of the grid,
+// instead of a hot expert's tiles forming the tail.
 template <typename T>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dw_down(
     const int32_t* __restrict__ expert_off, const int32_t* __restrict__ order, const int32_t* __restrict__ row_token,

@@ -11,12 +11,18 @@
 
 namespace moe {
 
-// mtile_off[E+1]: exclusive scan over experts of ceil(counts[e] / BM).  One block, E <= 1024.
+// mtile_off[E+1]: exclusive scan over experts of ceil(counts[e] / BM).  With order non-null also
+// order[E]: the experts by decreasing row count, ties to the lower id (the weight-gradient GEMMs'
+// tile order), so that the backward gets both tables from one launch.  One block, E <= 1024.
 __global__ __launch_bounds__(1024) void k_tile_offsets(const int32_t* __restrict__ counts, int E,
-                                                       int32_t* __restrict__ mtile_off) {
+                                                       int32_t* __restrict__ mtile_off,
+                                                       int32_t* __restrict__ order) {
   __shared__ int sh[16];
+  __shared__ int c[1024];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int x = threadIdx.x < E ? (counts[threadIdx.x] + BM - 1) / BM : 0;
+  const int ce = threadIdx.x < E ? counts[threadIdx.x] : 0;
+  if (order && threadIdx.x < E) c[threadIdx.x] = ce;
+  const int x = (ce + BM - 1) / BM;
   int inc = x;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -32,10 +38,16 @@ __global__ __launch_bounds__(1024) void k_tile_offsets(const int32_t* __restrict
   }
   if (threadIdx.x < E) mtile_off[threadIdx.x] = base + inc - x;
   if (threadIdx.x == 0) mtile_off[E] = tot;
+  if (order && (int)threadIdx.x < E) {
+    const int e = threadIdx.x;
+    int rank = 0;
+    for (int f = 0; f < E; ++f) rank += (c[f] > ce || (c[f] == ce && f < e)) ? 1 : 0;
+    order[rank] = e;
+  }
 }
 
-hipError_t launch_tile_offsets(const int32_t* counts, int E, int32_t* mtile_off, hipStream_t st) {
-  k_tile_offsets<<<1, 1024, 0, st>>>(counts, E, mtile_off);
+hipError_t launch_tile_offsets(const int32_t* counts, int E, int32_t* mtile_off, int32_t* order, hipStream_t st) {
+  k_tile_offsets<<<1, 1024, 0, st>>>(counts, E, mtile_off, order);
   return hipGetLastError();
 }
 

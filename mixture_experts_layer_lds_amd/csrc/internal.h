@@ -36,8 +36,10 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int K, int round_
                         const uint32_t* round_rand, const PlanPtrs& p, void* ws, hipStream_t st);
 
 // ---- grouped GEMM tile schedule (gemm_fwd.hip) ----
-// mtile_off[E+1] = exclusive scan over experts of ceil(counts[e] / 256).
-hipError_t launch_tile_offsets(const int32_t* counts, int E, int32_t* mtile_off, hipStream_t st);
+// mtile_off[E+1] = exclusive scan over experts of ceil(counts[e] / 256); with order non-null also
+// order[E]: experts by decreasing row count, ties to the lower id (the weight-gradient GEMMs'
+// expert order, longest tiles first).
+hipError_t launch_tile_offsets(const int32_t* counts, int E, int32_t* mtile_off, int32_t* order, hipStream_t st);
 int64_t max_mtiles(int64_t R_max, int E);
 
 // ---- forward GEMMs (gemm_fwd.hip) ----
@@ -95,9 +97,6 @@ int dact_ntiles(int64_t n);
 hipError_t launch_dx_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off,
                           const void* dH, const void* W_gate, const void* W_up, void* dX_perm,
                           hipStream_t st);
-// order[E]: experts by decreasing row count, ties to the lower id (the weight-gradient GEMMs'
-// expert order, longest tiles first)
-hipError_t launch_expert_order(const int32_t* counts, int E, int32_t* order, hipStream_t st);
 // dW_down[e] = (w dY[rows])^T A = dY[rows]^T wA, experts taken in `order`
 hipError_t launch_dw_down_gemm(const Shape& s, const PlanPtrs& p, const int32_t* order, const void* dY,
                                const void* wA, void* dW_down, hipStream_t st);

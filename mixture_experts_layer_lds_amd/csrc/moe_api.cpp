@@ -259,7 +259,7 @@ moe_status do_ffn(const moe_dims* dm, const moe_plan* plan, const void* A_in, bo
                   hipStream_t st) {
   const Shape s = shape_of(dm);
   const PlanPtrs p = plan_ptrs(plan);
-  MOE_STAGE(MOE_STAGE_TILES, st, launch_tile_offsets(p.counts, dm->E, w.mtile_off, st), "tile offsets");
+  MOE_STAGE(MOE_STAGE_TILES, st, launch_tile_offsets(p.counts, dm->E, w.mtile_off, nullptr, st), "tile offsets");
   MOE_STAGE(MOE_STAGE_UP_GEMM, st, launch_up_gemm(s, p, w.mtile_off, A_in, gathered, Wg, Wu, w.act, H, st),
             "gate/up GEMM");
   MOE_STAGE(MOE_STAGE_DOWN_GEMM, st, launch_down_gemm(s, p, w.mtile_off, w.act, Wd, Y, st), "down GEMM");
@@ -427,7 +427,7 @@ moe_status moe_grouped_ffn_fp8(const moe_dims* dims, const moe_plan* plan, const
   const Shape s = shape_of(dims);
   const PlanPtrs p = plan_ptrs(plan);
   int32_t* mtile_off = static_cast<int32_t*>(ws);
-  MOE_STAGE(MOE_STAGE_TILES, st, launch_tile_offsets(p.counts, dims->E, mtile_off, st), "tile offsets");
+  MOE_STAGE(MOE_STAGE_TILES, st, launch_tile_offsets(p.counts, dims->E, mtile_off, nullptr, st), "tile offsets");
   MOE_STAGE(MOE_STAGE_FP8_UP, st, launch_up_fp8(s, p, mtile_off, Xq, sx, Wg_q, sg, Wu_q, su, act, st),
             "fp8 gate/up GEMM");
   MOE_STAGE(MOE_STAGE_FP8_QUANT, st, launch_quant_fp8(act, true, s.R_max, dims->n, p.meta, act_q, sact, st),
@@ -513,7 +513,7 @@ moe_status moe_grouped_ffn_mx(const moe_dims* dims, const moe_plan* plan, int fm
   Carve c(ws);
   int32_t* mtile_off = static_cast<int32_t*>(c.take((size_t)(dims->E + 1) * 4));
   uint8_t* sxp = static_cast<uint8_t*>(c.take((size_t)mx_scale_bytes(s.R_max, dims->d)));
-  MOE_STAGE(MOE_STAGE_TILES, st, launch_tile_offsets(p.counts, dims->E, mtile_off, st), "tile offsets");
+  MOE_STAGE(MOE_STAGE_TILES, st, launch_tile_offsets(p.counts, dims->E, mtile_off, nullptr, st), "tile offsets");
   MOE_STAGE(MOE_STAGE_FP8_QUANT, st, launch_gather_mx_scales(s, p, sx, sxp, st), "token scale gather");
   MOE_STAGE(MOE_STAGE_FP8_UP, st,
             launch_up_mx(s, p, mtile_off, fmt, Xq, sxp, Wg_q, sg, Wu_q, su, act, act_q, sact, st),
@@ -594,7 +594,8 @@ moe_status moe_backward(const moe_dims* dims, const void* dY, const void* X, con
   const PlanPtrs p = plan_ptrs(plan);
   Carve c(ws);
   const BwdWs w = carve_bwd(c, dims);
-  MOE_STAGE(MOE_STAGE_TILES, st, launch_tile_offsets(p.counts, dims->E, w.mtile_off, st), "tile offsets");
+  MOE_STAGE(MOE_STAGE_TILES, st, launch_tile_offsets(p.counts, dims->E, w.mtile_off, w.order, st),
+            "tile offsets and expert order");
   const void* H = H_cache;
   if (!H) {  // recompute [G | U] from X; the SwiGLU output goes to wA, which dAct overwrites
     MOE_STAGE(MOE_STAGE_UP_GEMM, st, launch_up_gemm(s, p, w.mtile_off, X, true, W_gate, W_up, w.wA, w.H, st),
@@ -603,7 +604,6 @@ moe_status moe_backward(const moe_dims* dims, const void* dY, const void* X, con
   }
   MOE_STAGE(MOE_STAGE_DACT_GEMM, st,
             launch_dact_gemm(s, p, w.mtile_off, dY, W_down, H, w.dH, w.wA, w.dS_part, st), "dAct GEMM");
-  MOE_HIP(launch_expert_order(p.counts, dims->E, w.order, st), "expert order");
   MOE_STAGE(MOE_STAGE_DW_DOWN_GEMM, st, launch_dw_down_gemm(s, p, w.order, dY, w.wA, dW_down, st), "dW_down GEMM");
   MOE_STAGE(MOE_STAGE_DW_GU_GEMM, st, launch_dw_gu_gemm(s, p, w.order, w.dH, X, dW_gate, dW_up, st),
             "dW_gate/up GEMM");

@@ -475,12 +475,6 @@ __global__ __launch_bounds__(256) void k_tok_count(const uint32_t* __restrict__ 
   if ((threadIdx.x & 31) == 0 && t < T) grp[(t >> 5) + 1] = c;
 }
 
-// Plain top-K: every token has K rows.
-__global__ __launch_bounds__(256) void k_tok_fill(int T, int K, int32_t* __restrict__ tok_off) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t <= T) tok_off[t] = t * K;
-}
-
 // In-place scan: tok_off[1..T] holds counts; afterwards tok_off[t] = sum of counts before t.
 // One block of 1024 threads, sequential over chunks of 1024 * 8 tokens.
 __global__ __launch_bounds__(1024) void k_tok_scan(int T, int32_t* __restrict__ tok_off) {
@@ -556,13 +550,15 @@ __global__ __launch_bounds__(256) void k_place(const float* __restrict__ logits,
                                                const uint32_t* __restrict__ bits,
                                                const int32_t* __restrict__ wprefix,
                                                const int32_t* __restrict__ expert_off,
-                                               const int32_t* __restrict__ tok_off,
+                                               int32_t* __restrict__ tok_off,
                                                int32_t* __restrict__ row_token,
                                                float* __restrict__ row_w,
                                                int32_t* __restrict__ tok_row) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= T) return;
-  const int base = tok_off[t];
+  const int base = t * K;  // plain top-K: every token has K rows
+  tok_off[t] = base;
+  if (t == T - 1) tok_off[T] = T * K;
   const float* L = logits + (int64_t)t * E;
   const int w = t >> 5;
   const uint32_t below = (1u << (t & 31)) - 1u;
@@ -762,7 +758,6 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int K, int round_
     k_place_rounded<<<W, 256, (size_t)E * 4, st>>>(logits, (int)T, E, W, bits, wprefix, p.expert_off, grp,
                                                    p.tok_off, p.row_token, p.row_w, p.tok_row);
   } else {
-    k_tok_fill<<<(int)cdiv(T + 1, 256), 256, 0, st>>>((int)T, K, p.tok_off);
 #define MOE_PLACE(KM) k_place<KM><<<(int)cdiv(T, 256), 256, 0, st>>>(logits, (int)T, E, K, W, p.topk_idx, bits, \
       wprefix, p.expert_off, p.tok_off, p.row_token, p.row_w, p.tok_row)
     if (K <= 2) MOE_PLACE(2);
