@@ -146,7 +146,9 @@ size_t moe_workspace_bytes(const moe_dims* dims, int op);
  * cloud.baidu.com "工作原理" steps 1 (gate_network, top_k); apxml.com fused steps 1-2; SonicMoE
  * optimization 3 (token rounding).
  *  X      [T,d] dtype, W_r [E,d] dtype, bias [E] fp32 or NULL: if X != NULL, the library computes
- *         logits = X W_r^T + bias (fp32 accumulation) and writes them to `logits`.
+ *         logits = X W_r^T + bias (fp32 accumulation) and writes them to `logits`; a bf16 layer
+ *         with fewer than 256 tiles of 256 tokens x 128 experts sums d in 2 or 4 slices, added
+ *         in slice order (a fixed order: the result does not depend on the schedule).
  *         If X == NULL, `logits` is an INPUT: caller-computed fp32 logits (bias already added).
  *  logits [T,E] fp32.  NaN ranks below every number (so a token still gets K distinct experts).
  *  plan   all arrays written (see moe_plan).

@@ -15,7 +15,7 @@ SOURCES = ["route.hip", "gemm_fwd.hip", "backward.hip", "combine.hip", "decode.h
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wshadow", "-Wno-unused-function",
     # no packed-fp32 instructions: their generated forms are avoided on this hardware
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]

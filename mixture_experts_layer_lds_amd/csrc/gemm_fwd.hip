@@ -113,30 +113,37 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_router(const T* __restrict_
 }
 
 // bf16 router GEMM on the half-width engine: tile 256 tokens x 128 experts (the four-wave
-// 256 x 256 tile would leave half its columns empty at E = 128), two workgroups per CU.
+// 256 x 256 tile would leave half its columns empty at E = 128), two workgroups per CU.  With
+// SK > 1 workgroup (tile, ks) reduces over columns ks d / SK .. (ks + 1) d / SK only: at E = 128 a
+// layer of 32768 tokens has 128 tiles, which alone would leave half the CUs idle.
 __global__ __launch_bounds__(GEMM_THREADS, 2) void k_router_h(const bf16* __restrict__ X, const bf16* __restrict__ Wr,
                                                               const float* __restrict__ bias,
-                                                              float* __restrict__ logits, int T_, int d, int E,
-                                                              int NT) {
+                                                              float* __restrict__ logits, float* __restrict__ part,
+                                                              int T_, int d, int E, int NT, int SK) {
   MOE_GEMM_LDS_H(L);
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int mt = lin / NT, nt = lin % NT;
+  const int tiles = (int)cdiv(T_, BM) * NT;
+  const int ks = lin / tiles, tl = lin % tiles;  // reduction slice, output tile
+  if (ks >= SK) return;
+  const int mt = tl / NT, nt = tl % NT;
   const int m0 = mt * BM, n0 = nt * HBN;
-  if (m0 >= T_) return;
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t rowb = (int64_t)d * sizeof(bf16);
+  const int klen = d / SK;
+  const int64_t k0b = (int64_t)ks * klen * sizeof(bf16);
   KDmaH<4> la;
   la.init([&](int i) -> const char* {
-    return m0 + i < T_ ? reinterpret_cast<const char*>(X) + (m0 + i) * rowb : nullptr;
+    return m0 + i < T_ ? reinterpret_cast<const char*>(X) + (m0 + i) * rowb + k0b : nullptr;
   });
   KDmaH<2> lb;
   lb.init([&](int i) -> const char* {
-    return n0 + i < E ? reinterpret_cast<const char*>(Wr) + (n0 + i) * rowb : nullptr;
+    return n0 + i < E ? reinterpret_cast<const char*>(Wr) + (n0 + i) * rowb + k0b : nullptr;
   });
   auto bsub = [&](int j) { return bsub_w8(wn, j); };
   AccW8 acc;
-  gemm_mainloop_h<false>(la, lb, d / Mma<bf16>::BK, acc, L_0, L_1, L_2, wm, bsub);
+  gemm_mainloop_h<false>(la, lb, klen / Mma<bf16>::BK, acc, L_0, L_1, L_2, wm, bsub);
+  float* dst = ks == 0 ? logits : part + (int64_t)(ks - 1) * T_ * E;
   // as in k_router: a lane's v = 4q .. 4q + 3 are four consecutive experts of one token
 #pragma unroll
   for (int j = 0; j < 2; ++j)
@@ -145,7 +152,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_router_h(const bf16* __rest
       const int n = n0 + bsub(j) + acc_n(4 * q);
       if (n >= E) continue;
       f32x4 b = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (bias) {
+      if (bias && ks == 0) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) b[u] = n + u < E ? bias[n + u] : 0.0f;
       }
@@ -153,7 +160,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_router_h(const bf16* __rest
       for (int i = 0; i < 4; ++i) {
         const int m = m0 + acc_m(wm, i);
         if (m >= T_) continue;
-        float* o = logits + (int64_t)m * E + n;
+        float* o = dst + (int64_t)m * E + n;
         const f32x4 v4 = {acc.c[i][j][4 * q] + b[0], acc.c[i][j][4 * q + 1] + b[1], acc.c[i][j][4 * q + 2] + b[2],
                           acc.c[i][j][4 * q + 3] + b[3]};
         if ((E & 3) == 0) {
@@ -167,12 +174,26 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_router_h(const bf16* __rest
     }
 }
 
+// Slices of the router GEMM's reduction: enough that the tiles fill the 256 CUs, at most 4, and
+// each slice a whole number of k-steps, at least two.
+int router_split(const Shape& s) {
+  if (!s.bf16) return 1;
+  const int64_t tiles = cdiv(s.T, BM) * cdiv(s.E, HBN);
+  constexpr int BK = Mma<bf16>::BK;
+  int sk = 1;
+  while (sk < 4 && tiles * sk < 256 && s.d % (2 * sk * BK) == 0 && s.d / (2 * sk) >= 2 * BK) sk *= 2;
+  return sk;
+}
+
+size_t router_part_bytes(const Shape& s) { return (size_t)(router_split(s) - 1) * s.T * s.E * sizeof(float); }
+
 hipError_t launch_router_gemm(const Shape& s, const void* X, const void* W_r, const float* bias,
-                              float* logits, hipStream_t st) {
+                              float* logits, float* part, hipStream_t st) {
   if (s.bf16) {
     const int NT = (int)cdiv(s.E, HBN);
-    k_router_h<<<grid8(cdiv(s.T, BM) * NT), GEMM_THREADS, 0, st>>>((const bf16*)X, (const bf16*)W_r, bias, logits,
-                                                                  (int)s.T, (int)s.d, s.E, NT);
+    const int SK = router_split(s);
+    k_router_h<<<grid8(cdiv(s.T, BM) * NT * SK), GEMM_THREADS, 0, st>>>((const bf16*)X, (const bf16*)W_r, bias,
+                                                                       logits, part, (int)s.T, (int)s.d, s.E, NT, SK);
   } else {
     const int NT = (int)cdiv(s.E, BN);
     k_router<float><<<grid8(cdiv(s.T, BM) * NT), GEMM_THREADS, 0, st>>>((const float*)X, (const float*)W_r, bias,

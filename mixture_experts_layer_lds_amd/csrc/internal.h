@@ -32,8 +32,10 @@ struct Shape {
 
 // ---- routing (route.hip) ----
 size_t route_workspace_bytes(int64_t T, int E, bool rounded);
-hipError_t launch_route(const float* logits, int64_t T, int E, int K, int round_mode, int tile_m,
-                        const uint32_t* round_rand, const PlanPtrs& p, void* ws, hipStream_t st);
+// part: null, or the SK - 1 partial products [SK-1][T][E] of a split router GEMM, which top-K adds
+// to logits (in slice order) and writes back as the final logits before selecting.
+hipError_t launch_route(float* logits, const float* part, int SK, int64_t T, int E, int K, int round_mode,
+                        int tile_m, const uint32_t* round_rand, const PlanPtrs& p, void* ws, hipStream_t st);
 
 // ---- grouped GEMM tile schedule (gemm_fwd.hip) ----
 // mtile_off[E+1] = exclusive scan over experts of ceil(counts[e] / 256); with order non-null also
@@ -43,9 +45,13 @@ hipError_t launch_tile_offsets(const int32_t* counts, int E, int32_t* mtile_off,
 int64_t max_mtiles(int64_t R_max, int E);
 
 // ---- forward GEMMs (gemm_fwd.hip) ----
-// logits[T,E] (fp32) = X[T,d] W_r[E,d]^T + bias
+// logits[T,E] (fp32) = X[T,d] W_r[E,d]^T + bias.  With router_split(s) = SK > 1 (bf16 layers
+// whose tiles would fill less than the chip) the reduction over d is cut into SK slices: slice 0
+// (with the bias) goes to logits, slice q > 0 to part[q-1][T][E], and top-K adds them up.
+int router_split(const Shape& s);
+size_t router_part_bytes(const Shape& s);
 hipError_t launch_router_gemm(const Shape& s, const void* X, const void* W_r, const float* bias,
-                              float* logits, hipStream_t st);
+                              float* logits, float* part, hipStream_t st);
 // Act[R,n] = silu(G) * U with [G|U] = X[rows] [W_gate|W_up]^T; H[R,2n] optional
 hipError_t launch_up_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mtile_off,
                           const void* A_in, bool gathered, const void* W_gate, const void* W_up,

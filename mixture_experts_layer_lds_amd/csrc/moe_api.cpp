@@ -186,14 +186,15 @@ BwdWs carve_bwd(Carve& c, const moe_dims* dm) {
 size_t ws_bytes_for(const moe_dims* dm, int op) {
   Carve c(nullptr);
   switch (op) {
-    case MOE_OP_ROUTE: return route_workspace_bytes(dm->T, dm->E, dm->round_mode != 0);
+    case MOE_OP_ROUTE:  // (+ the partial products of a split router GEMM)
+      return route_workspace_bytes(dm->T, dm->E, dm->round_mode != 0) + router_part_bytes(shape_of(dm));
     case MOE_OP_PERMUTE: return 0;
     case MOE_OP_COMBINE: return 0;
     case MOE_OP_FFN: carve_ffn(c, dm); return c.off;
     case MOE_OP_FORWARD: {
       carve_ffn(c, dm);
       c.take((size_t)max_rows(dm) * dm->d * esize(dm));  // Y_perm
-      const size_t r = route_workspace_bytes(dm->T, dm->E, dm->round_mode != 0);
+      const size_t r = route_workspace_bytes(dm->T, dm->E, dm->round_mode != 0) + router_part_bytes(shape_of(dm));
       return c.off > r ? c.off : r;
     }
     case MOE_OP_BACKWARD: carve_bwd(c, dm); return c.off;
@@ -243,12 +244,18 @@ moe_status check_ws(const moe_dims* dm, int op, void* ws, size_t ws_bytes) {
 }
 
 // The routing stage shared by moe_route and moe_forward (arguments already validated).
+// With X the router GEMM runs first; when it splits its reduction (router_split), the partial
+// products go to the end of the routing workspace and top-K adds them into logits.
 moe_status do_route(const moe_dims* dm, const void* X, const void* W_r, const float* bias,
                     float* logits, const moe_plan* plan, void* ws, hipStream_t st) {
   const Shape s = shape_of(dm);
-  if (X) MOE_STAGE(MOE_STAGE_ROUTER_GEMM, st, launch_router_gemm(s, X, W_r, bias, logits, st), "router GEMM");
+  const int SK = X ? router_split(s) : 1;
+  float* part = SK > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                                  route_workspace_bytes(dm->T, dm->E, dm->round_mode != 0))
+                       : nullptr;
+  if (X) MOE_STAGE(MOE_STAGE_ROUTER_GEMM, st, launch_router_gemm(s, X, W_r, bias, logits, part, st), "router GEMM");
   MOE_STAGE(MOE_STAGE_ROUTE, st,
-            launch_route(logits, dm->T, dm->E, dm->K, dm->round_mode, dm->tile_m, dm->round_rand,
+            launch_route(logits, part, SK, dm->T, dm->E, dm->K, dm->round_mode, dm->tile_m, dm->round_rand,
                          plan_ptrs(plan), ws, st),
             "routing");
   return MOE_OK;

@@ -33,13 +33,32 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   const uint32_t u = __float_as_uint(x == 0.0f ? 0.0f : x);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+// The float an order key came from: exact for every number (-0.0 comes back as +0.0, which no
+// difference or exponential below tells apart); key 0 comes back as a NaN.
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Logit e of token t: logits[t][e], plus, after a split router GEMM, its SK - 1 partial products
+// in slice order; the sum is written back so that the logits output holds the final values.
+__device__ __forceinline__ float token_logit(float* __restrict__ logits, const float* __restrict__ part, int SK,
+                                            int T, int E, int t, int e) {
+  const int64_t i = (int64_t)t * E + e;
+  float v = logits[i];
+  if (SK > 1) {
+    for (int q = 0; q < SK - 1; ++q) v += part[(int64_t)q * T * E + i];
+    logits[i] = v;
+  }
+  return v;
+}
 
 // keysT (token rounding only, else null): the order keys transposed, keysT[e][t], for the rounding
 // kernel's per-expert scans.  With E <= TOPK_STAGE_E the block's keys are staged in LDS
 // ([e][65], conflict-free) and written out as 64-token rows; otherwise each lane stores its own.
 constexpr int TOPK_STAGE_E = 192;  // E * (2 + 65) words stay within the default 64 KiB of dynamic LDS
 template <int EPL>
-__global__ __launch_bounds__(TOPK_THREADS) void k_topk(const float* __restrict__ logits, int T, int E,
+__global__ __launch_bounds__(TOPK_THREADS) void k_topk(float* __restrict__ logits, const float* __restrict__ part,
+                                                       int SK, int T, int E,
                                                        int K, int W, int32_t* __restrict__ topk_idx,
                                                        float* __restrict__ topk_w,
                                                        uint32_t* __restrict__ bits,
@@ -54,13 +73,12 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const float* __restrict__
   for (int tt = wave; tt < TOPK_TOKENS_PER_BLOCK; tt += TOPK_THREADS / 64) {
     const int t = t0 + tt;
     if (t >= T) break;
-    const float* row = logits + (int64_t)t * E;
     uint32_t key[EPL];
     uint32_t alive = 0;  // bit j: candidate e = lane + 64 j still in play
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
       const int e = lane + 64 * j;
-      key[j] = e < E ? order_key(row[e]) : 0u;
+      key[j] = e < E ? order_key(token_logit(logits, part, SK, T, E, t, e)) : 0u;
       alive |= e < E ? (1u << j) : 0u;
       if (keysT && e < E) {
         if (stage) skeys[e * 65 + tt] = key[j];
@@ -68,12 +86,14 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const float* __restrict__
       }
     }
     int my_e = 0;
+    uint32_t my_key = 0;
     for (int k = 0; k < K; ++k) {
       uint32_t lm = 0;  // NaN keys are 0 too; ties at 0 are settled below among live candidates
 #pragma unroll
       for (int j = 0; j < EPL; ++j)
         if ((alive >> j) & 1u) lm = key[j] > lm ? key[j] : lm;
       const uint32_t kmax = wave_max_u32(lm);
+      if (lane == k) my_key = kmax;
       int win = -1;  // lowest expert id holding kmax (uniform)
 #pragma unroll
       for (int j = 0; j < EPL; ++j) {
@@ -84,7 +104,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const float* __restrict__
       if (lane == (win & 63)) alive &= ~(1u << (win >> 6));
       if (lane == k) my_e = win;
     }
-    const float my_v = lane < K ? row[my_e] : 0.0f;
+    const float my_v = lane < K ? key_value(my_key) : 0.0f;  // the winner's logit, from its key
     const float vmax = __shfl(my_v, 0, 64);
     const float ex = lane < K ? __expf(my_v - vmax) : 0.0f;
     const float s = wave_sum(ex);
@@ -139,7 +159,8 @@ __device__ __forceinline__ uint32_t row16_min(uint32_t v) {
 }
 
 template <int EPG>
-__global__ __launch_bounds__(TOPK_THREADS) void k_topk_g(const float* __restrict__ logits, int T, int E,
+__global__ __launch_bounds__(TOPK_THREADS) void k_topk_g(float* __restrict__ logits, const float* __restrict__ part,
+                                                         int SK, int T, int E,
                                                          int K, int W, int32_t* __restrict__ topk_idx,
                                                          float* __restrict__ topk_w,
                                                          uint32_t* __restrict__ bits,
@@ -155,13 +176,12 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk_g(const float* __restrict
   for (int x = threadIdx.x; x < 2 * E; x += blockDim.x) sbits[x] = 0u;
   __syncthreads();
   if (t < T) {  // uniform over the row, so every DPP source lane is active
-    const float* row = logits + (int64_t)t * E;
     uint32_t key[EPG];
     uint32_t alive = 0;  // bit j: candidate e = i + 16 j still in play
 #pragma unroll
     for (int j = 0; j < EPG; ++j) {
       const int e = i + 16 * j;
-      key[j] = e < E ? order_key(row[e]) : 0u;
+      key[j] = e < E ? order_key(token_logit(logits, part, SK, T, E, t, e)) : 0u;
       alive |= e < E ? (1u << j) : 0u;
       if (keysT && e < E) {
         if (stage) skeys[e * 65 + tt] = key[j];
@@ -169,12 +189,14 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk_g(const float* __restrict
       }
     }
     int my_e = 0;
+    uint32_t my_key = 0;
     for (int k = 0; k < K; ++k) {
       uint32_t lm = 0;  // NaN keys are 0 too; ties at 0 are settled below among live candidates
 #pragma unroll
       for (int j = 0; j < EPG; ++j)
         if ((alive >> j) & 1u) lm = key[j] > lm ? key[j] : lm;
       const uint32_t kmax = row16_max(lm);
+      if (i == k) my_key = kmax;
       uint32_t cand = 0xffffffffu;  // this lane's lowest expert id holding kmax
 #pragma unroll
       for (int j = EPG - 1; j >= 0; --j)
@@ -183,7 +205,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk_g(const float* __restrict
       if (i == (win & 15)) alive &= ~(1u << (win >> 4));
       if (i == k) my_e = win;
     }
-    const float my_v = i < K ? row[my_e] : 0.0f;
+    const float my_v = i < K ? key_value(my_key) : 0.0f;  // the winner's logit, from its key
     const float vmax = __shfl(my_v, lane & ~15, 64);
     const float ex = i < K ? __expf(my_v - vmax) : 0.0f;
     float s = ex;
@@ -717,8 +739,8 @@ size_t route_workspace_bytes(int64_t T, int E, bool rounded) {
          (rounded ? align_up((size_t)E * T * 4, 256) : 0);
 }
 
-hipError_t launch_route(const float* logits, int64_t T, int E, int K, int round_mode, int tile_m,
-                        const uint32_t* round_rand, const PlanPtrs& p, void* ws, hipStream_t st) {
+hipError_t launch_route(float* logits, const float* part, int SK, int64_t T, int E, int K, int round_mode,
+                        int tile_m, const uint32_t* round_rand, const PlanPtrs& p, void* ws, hipStream_t st) {
   const int W = (int)cdiv(T, 32);
   uint32_t* bits = static_cast<uint32_t*>(ws);
   int32_t* wprefix = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + align_up((size_t)E * W * 4, 256));
@@ -728,8 +750,8 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int K, int round_
                             : nullptr;
   const int nblk = (int)cdiv(T, TOPK_TOKENS_PER_BLOCK);
   const size_t lds = (size_t)E * 2 * sizeof(uint32_t) + (rounded && E <= TOPK_STAGE_E ? (size_t)E * 65 * 4 : 0);
-#define MOE_TOPK(EPL) k_topk<EPL><<<nblk, TOPK_THREADS, lds, st>>>(logits, (int)T, E, K, W, p.topk_idx, p.topk_w, bits, keysT)
-#define MOE_TOPK_G(EPG) k_topk_g<EPG><<<nblk, TOPK_THREADS, lds, st>>>(logits, (int)T, E, K, W, p.topk_idx, p.topk_w, bits, keysT)
+#define MOE_TOPK(EPL) k_topk<EPL><<<nblk, TOPK_THREADS, lds, st>>>(logits, part, SK, (int)T, E, K, W, p.topk_idx, p.topk_w, bits, keysT)
+#define MOE_TOPK_G(EPG) k_topk_g<EPG><<<nblk, TOPK_THREADS, lds, st>>>(logits, part, SK, (int)T, E, K, W, p.topk_idx, p.topk_w, bits, keysT)
   if (E <= 16) MOE_TOPK_G(1);
   else if (E <= 32) MOE_TOPK_G(2);
   else if (E <= 64) MOE_TOPK_G(4);

@@ -99,6 +99,25 @@ def test_route_workspace_grows_with_token_rounding():
     assert B.moe_workspace_bytes(dims(T=T, E=E, round_mode=1), B.OP_FORWARD) >= rounded
 
 
+def test_route_workspace_holds_split_router_partials():
+    """A bf16 layer whose router GEMM has fewer than 256 tiles of 256 tokens x 128 experts splits
+    its reduction over d: the partial products of the slices after the first ([SK-1][T][E] fp32)
+    sit after the routing workspace proper.  32768 tokens x 128 experts is 128 tiles: two slices;
+    512 tokens x 8 experts at d = 4096 is 2 tiles: four slices; fp32 layers never split."""
+    def base(T, E):
+        W = (T + 31) // 32
+        r = lambda x: (x + 255) // 256 * 256
+        return 2 * r(E * W * 4) + r((W + 1) * 4)
+
+    T, E = 32768, 128
+    assert B.moe_workspace_bytes(dims(T=T, E=E, d=1536), B.OP_ROUTE) == base(T, E) + T * E * 4
+    assert B.moe_workspace_bytes(dims(T=T, E=E, d=1536, dtype="f32"), B.OP_ROUTE) == base(T, E)
+    T, E = 512, 8
+    assert B.moe_workspace_bytes(dims(T=T, E=E, d=4096), B.OP_ROUTE) == base(T, E) + 3 * T * E * 4
+    T, E = 65536, 128  # 256 tiles: no split
+    assert B.moe_workspace_bytes(dims(T=T, E=E, d=1536), B.OP_ROUTE) == base(T, E)
+
+
 def test_decode_argument_checks(lib):
     """moe_decode: plain top-K only, T <= 1024, its own workspace size, required pointers."""
     call = lambda d, ws=1 << 40, out=FAKE: lib.moe_decode(
