@@ -57,6 +57,19 @@ def test_ragged_multi_tile(shape):
     print(errs)
 
 
+@pytest.mark.parametrize("shape", [
+    dict(T=300, d=512, E=200, K=4, n=128),  # 2 x 2 ragged router tiles: d summed in 4 slices
+    dict(T=520, d=192, E=136, K=2, n=64),   # 3 x 2 tiles: 2 slices of 3 k-steps each
+])
+def test_split_router_with_bias(shape):
+    """bf16 layers whose router GEMM has few tiles split its reduction over d; the slices are
+    added by top-K, which writes the final logits.  With a per-expert bias (added once, in the
+    first slice), ragged token and expert tiles, and top-K over 16-lane rows (E <= 256)."""
+    cfg = wl.small_shape(**shape, dtype="bf16", bias="normal", seed=37)
+    _, _, errs = full_check(cfg)
+    print(errs)
+
+
 @pytest.mark.parametrize("mode,tile_m,dtype", [
     (1, 128, "f32"), (1, 32, "bf16"), (2, 16, "bf16"), (3, 64, "f32"), (2, 128, "f32"), (3, 8, "bf16"),
     (4, 128, "bf16"), (4, 16, "f32"),
