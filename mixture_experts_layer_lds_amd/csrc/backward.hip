@@ -115,11 +115,12 @@ __device__ __forceinline__ void dact_epilogue(LdsBufs L, const GroupTile& g, int
     }
   };
   if constexpr (NB == 2 && PF == 2) {
-    // two batches per half (eight waves): the second half's loads go out while the first half is
-    // finished -- the first batch's right after the first dump, the second's once the first
-    // half's first batch has freed its registers -- so that they are not queued behind the first
-    // half's stores and the second half costs no memory round trip of its own
-    // (scheduling barriers keep the loads in this order: the waits count them in issue order)
+    // two batches per half (eight waves): the first half's first batch goes out before its dump,
+    // its second batch and the second half's first batch right after the dump, and the second
+    // half's second batch once the first half is done (before its stores drain), so that the
+    // second half's loads are not queued behind the first half's stores; the registers of both
+    // halves' batches do not fit at once.  Scheduling barriers keep the loads in this order,
+    // which the waits count on.
     Grp a0, a1, b0, b1;
     load_grp(0, 0, a0);
     __builtin_amdgcn_sched_barrier(0);

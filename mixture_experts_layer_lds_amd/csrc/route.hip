@@ -3,7 +3,8 @@
 //
 // Pages: cloud.baidu.com "工作原理" (gate network, top_k), apxml.com "自定义核与核融合" steps 1-2,
 // SonicMoE page optimization 3 (token rounding), ThunderEP article section 2.2.2 (int32 row index
-// lists).  Design for gfx950: one 64-lane wave per token for selection; the membership of every
+// lists).  Design for gfx950: selection by DPP reductions within a 16-lane row per token (E <= 256)
+// or a whole wave per token (larger E), no LDS round trips; the membership of every
 // (token, expert) pair lives in a bitmap bits[E][ceil(T/32)] built in LDS per block, so that
 // per-expert counts, in-expert ranks (rows ordered by token id) and token rounding are popcounts
 // and scans over 32-bit words; no atomics touch global memory and every result is deterministic.
