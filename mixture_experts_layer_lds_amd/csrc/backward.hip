@@ -172,7 +172,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dact(
   MOE_GEMM_LDS(L);
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   GroupTile g;
-  if (!find_group_tile(lin, NT, mtile_off, expert_off, E, g)) return;
+  if (!find_group_tile<true>(lin, NT, mtile_off, expert_off, E, g)) return;
   const int nt = g.nt;
   const int n0 = nt * BN;
   const int wave = threadIdx.x >> 6;
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(GEMM8_THREADS, 1) void k_dact_w8(
   MOE_GEMM_LDS(L);
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   GroupTile g;
-  if (!find_group_tile(lin, NT, mtile_off, expert_off, E, g)) return;
+  if (!find_group_tile<true>(lin, NT, mtile_off, expert_off, E, g)) return;
   const int nt = g.nt;
   const int n0 = nt * BN;
   const int wave = threadIdx.x >> 6;

@@ -1666,11 +1666,16 @@ __device__ __forceinline__ void epi_h(Val val, char* b0, char* b1, char* b2, int
   }
 }
 
-// Grouped tiles.  The experts' ceil(rows / BM) m-tiles are concatenated (mtile_off is their
-// exclusive scan), and each m-tile has NT n-tiles.  Tile `lin` is found expert by expert; inside
-// an expert the tiles run in groups of RASTER_M m-tiles, n-tile outer and m-tile inner, so that
-// the workgroups an XCD runs side by side (consecutive `lin`, see xcd_remap) share both their
-// weight columns (same n-tile) and their token rows (same group) through that XCD's L2.
+// Grouped tiles.  The tile table (3 E + 3 ints, written by k_tile_offsets) orders the experts'
+// ceil(rows / BM) m-tiles, each with NT n-tiles, in one of two ways.  TAIL_LAST = false: expert by
+// expert, table[0..E] being the exclusive scan of the m-tiles per expert.  TAIL_LAST = true: first
+// the head tiles, i.e. every m-tile except a last m-tile with 1..BM/2 rows ("light": the
+// eight-wave kernels skip the MFMAs of its empty 128-row half), expert by expert (scan in
+// table[E + 1 .. 2 E + 1]); then the light tails, table[2 E + 2] of them, of experts
+// table[2 E + 3 ..] in ascending order, so that light tiles fill the grid's last round.  Inside an
+// expert the tiles run in groups of RASTER_M m-tiles, n-tile outer and m-tile inner, so that the
+// workgroups an XCD runs side by side (consecutive `lin`, see xcd_remap) share both their weight
+// columns (same n-tile) and their token rows (same group) through that XCD's L2.
 struct GroupTile {
   int e, m0, mrows, nt;
 };
@@ -1685,19 +1690,32 @@ __device__ __forceinline__ void raster_tile(int local, int MT, int NT, int& mt, 
   nt = idx / gm;
 }
 
-__device__ __forceinline__ bool find_group_tile(int lin, int NT, const int32_t* __restrict__ mtile_off,
+template <bool TAIL_LAST = false>
+__device__ __forceinline__ bool find_group_tile(int lin, int NT, const int32_t* __restrict__ table,
                                                 const int32_t* __restrict__ expert_off, int E,
                                                 GroupTile& g) {
-  if (lin >= mtile_off[E] * NT) return false;
-  int lo = 0, hi = E;  // mtile_off[lo] * NT <= lin < mtile_off[hi] * NT
+  const int32_t* scan = TAIL_LAST ? table + E + 1 : table;
+  const int heads = scan[E] * NT;
+  if (lin >= heads) {
+    if (!TAIL_LAST) return false;
+    const int k = (lin - heads) / NT;  // light tail k: expert tail[k], its last m-tile
+    if (k >= table[2 * E + 2]) return false;
+    const int e = table[2 * E + 3 + k];
+    g.e = e;
+    g.nt = (lin - heads) - k * NT;
+    g.m0 = expert_off[e] + (scan[e + 1] - scan[e]) * BM;
+    g.mrows = expert_off[e + 1] - g.m0;
+    return true;
+  }
+  int lo = 0, hi = E;  // scan[lo] * NT <= lin < scan[hi] * NT
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (mtile_off[mid] * NT <= lin) lo = mid;
+    if (scan[mid] * NT <= lin) lo = mid;
     else hi = mid;
   }
-  const int me = mtile_off[lo + 1] - mtile_off[lo];  // >= 1: tile lin lies in this expert
+  const int me = scan[lo + 1] - scan[lo];  // >= 1: tile lin lies in this expert('s head)
   int mt;
-  raster_tile(lin - mtile_off[lo] * NT, me, NT, mt, g.nt);
+  raster_tile(lin - scan[lo] * NT, me, NT, mt, g.nt);
   g.e = lo;
   g.m0 = expert_off[lo] + mt * BM;
   g.mrows = min(BM, expert_off[lo + 1] - g.m0);

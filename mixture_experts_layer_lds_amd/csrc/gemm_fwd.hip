@@ -11,33 +11,52 @@
 
 namespace moe {
 
-// mtile_off[E+1]: exclusive scan over experts of ceil(counts[e] / BM).  With order non-null also
-// order[E]: the experts by decreasing row count, ties to the lower id (the weight-gradient GEMMs'
-// tile order), so that the backward gets both tables from one launch.  One block, E <= 1024.
+// The tile table of the grouped GEMMs (see find_group_tile): table[0..E] = exclusive scan of
+// ceil(counts[e] / BM); table[E + 1 .. 2 E + 1] = the same without the light tails (a last m-tile
+// of 1..BM/2 rows); table[2 E + 2] = the number of light tails, table[2 E + 3 ..] = their experts
+// in ascending order.  With order non-null also order[E]: the experts by decreasing row count,
+// ties to the lower id (the weight-gradient GEMMs' tile order), so that the backward gets both
+// tables from one launch.  One block, E <= 1024.
 __global__ __launch_bounds__(1024) void k_tile_offsets(const int32_t* __restrict__ counts, int E,
-                                                       int32_t* __restrict__ mtile_off,
+                                                       int32_t* __restrict__ table,
                                                        int32_t* __restrict__ order) {
-  __shared__ int sh[16];
+  __shared__ int sh[3][16];
   __shared__ int c[1024];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ce = threadIdx.x < E ? counts[threadIdx.x] : 0;
   if (order && threadIdx.x < E) c[threadIdx.x] = ce;
-  const int x = (ce + BM - 1) / BM;
-  int inc = x;
+  const int rem = ce % BM;
+  const int light = (rem > 0 && rem <= BM / 2) ? 1 : 0;
+  const int x[3] = {(ce + BM - 1) / BM, (ce + BM - 1) / BM - light, light};
+  int inc[3] = {x[0], x[1], x[2]};
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(inc, o, 64);
-    if (lane >= o) inc += y;
-  }
-  if (lane == 63) sh[wave] = inc;
+  for (int o = 1; o < 64; o <<= 1)
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int y = __shfl_up(inc[q], o, 64);
+      if (lane >= o) inc[q] += y;
+    }
+  if (lane == 63)
+#pragma unroll
+    for (int q = 0; q < 3; ++q) sh[q][wave] = inc[q];
   __syncthreads();
-  int base = 0, tot = 0;
-  for (int w = 0; w < 16; ++w) {
-    base += (w < wave) ? sh[w] : 0;
-    tot += sh[w];
+  int base[3] = {0, 0, 0}, tot[3] = {0, 0, 0};
+  for (int w = 0; w < 16; ++w)
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      base[q] += (w < wave) ? sh[q][w] : 0;
+      tot[q] += sh[q][w];
+    }
+  if ((int)threadIdx.x < E) {
+    table[threadIdx.x] = base[0] + inc[0] - x[0];
+    table[E + 1 + threadIdx.x] = base[1] + inc[1] - x[1];
+    if (light) table[2 * E + 3 + base[2] + inc[2] - 1] = threadIdx.x;
   }
-  if (threadIdx.x < E) mtile_off[threadIdx.x] = base + inc - x;
-  if (threadIdx.x == 0) mtile_off[E] = tot;
+  if (threadIdx.x == 0) {
+    table[E] = tot[0];
+    table[2 * E + 1] = tot[1];
+    table[2 * E + 2] = tot[2];
+  }
   if (order && (int)threadIdx.x < E) {
     const int e = threadIdx.x;
     int rank = 0;

@@ -38,9 +38,11 @@ hipError_t launch_route(float* logits, const float* part, int SK, int64_t T, int
                         int tile_m, const uint32_t* round_rand, const PlanPtrs& p, void* ws, hipStream_t st);
 
 // ---- grouped GEMM tile schedule (gemm_fwd.hip) ----
-// mtile_off[E+1] = exclusive scan over experts of ceil(counts[e] / 256); with order non-null also
-// order[E]: experts by decreasing row count, ties to the lower id (the weight-gradient GEMMs'
-// expert order, longest tiles first).
+// The grouped GEMMs' tile table [tile_table_ints(E)]: the m-tiles per expert (scanned), and the
+// same with the light tails (a last m-tile of 1..128 rows) listed apart so that a kernel can run
+// them last (see find_group_tile); with order non-null also order[E]: experts by decreasing row
+// count, ties to the lower id (the weight-gradient GEMMs' expert order, longest tiles first).
+inline int tile_table_ints(int E) { return 3 * E + 3; }
 hipError_t launch_tile_offsets(const int32_t* counts, int E, int32_t* mtile_off, int32_t* order, hipStream_t st);
 int64_t max_mtiles(int64_t R_max, int E);
 

@@ -151,7 +151,7 @@ struct FfnWs {
 };
 FfnWs carve_ffn(Carve& c, const moe_dims* dm) {
   FfnWs w;
-  w.mtile_off = static_cast<int32_t*>(c.take((size_t)(dm->E + 1) * 4));
+  w.mtile_off = static_cast<int32_t*>(c.take((size_t)tile_table_ints(dm->E) * 4));
   w.act = c.take((size_t)max_rows(dm) * dm->n * esize(dm));
   return w;
 }
@@ -171,7 +171,7 @@ BwdWs carve_bwd(Carve& c, const moe_dims* dm) {
   const Shape s = shape_of(dm);
   const size_t es = esize(dm);
   BwdWs w;
-  w.mtile_off = static_cast<int32_t*>(c.take((size_t)(dm->E + 1) * 4));
+  w.mtile_off = static_cast<int32_t*>(c.take((size_t)tile_table_ints(dm->E) * 4));
   w.order = static_cast<int32_t*>(c.take((size_t)dm->E * 4));
   w.H = c.take((size_t)s.R_max * 2 * dm->n * es);
   w.dH = c.take((size_t)s.R_max * 2 * dm->n * es);
@@ -199,9 +199,9 @@ size_t ws_bytes_for(const moe_dims* dm, int op) {
     }
     case MOE_OP_BACKWARD: carve_bwd(c, dm); return c.off;
     case MOE_OP_DECODE: return decode_workspace_bytes(dm->T, dm->d, dm->n, dm->E, dm->K);
-    case MOE_OP_FFN_FP8: c.take((size_t)(dm->E + 1) * 4); return c.off;
-    case MOE_OP_FFN_MX:  // tile offsets, the token scales in routed-row order
-      c.take((size_t)(dm->E + 1) * 4);
+    case MOE_OP_FFN_FP8: c.take((size_t)tile_table_ints(dm->E) * 4); return c.off;
+    case MOE_OP_FFN_MX:  // tile table, the token scales in routed-row order
+      c.take((size_t)tile_table_ints(dm->E) * 4);
       c.take((size_t)mx_scale_bytes(max_rows(dm), dm->d));
       return c.off;
     default: return 0;
@@ -518,7 +518,7 @@ moe_status moe_grouped_ffn_mx(const moe_dims* dims, const moe_plan* plan, int fm
   const Shape s = shape_of(dims);
   const PlanPtrs p = plan_ptrs(plan);
   Carve c(ws);
-  int32_t* mtile_off = static_cast<int32_t*>(c.take((size_t)(dims->E + 1) * 4));
+  int32_t* mtile_off = static_cast<int32_t*>(c.take((size_t)tile_table_ints(dims->E) * 4));
   uint8_t* sxp = static_cast<uint8_t*>(c.take((size_t)mx_scale_bytes(s.R_max, dims->d)));
   MOE_STAGE(MOE_STAGE_TILES, st, launch_tile_offsets(p.counts, dims->E, mtile_off, nullptr, st), "tile offsets");
   MOE_STAGE(MOE_STAGE_FP8_QUANT, st, launch_gather_mx_scales(s, p, sx, sxp, st), "token scale gather");
