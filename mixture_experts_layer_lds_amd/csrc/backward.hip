@@ -172,7 +172,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_dact(
   MOE_GEMM_LDS(L);
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   GroupTile g;
-  if (!find_group_tile<true>(lin, NT, mtile_off, expert_off, E, g)) return;
+  if (!find_group_tile(lin, NT, mtile_off, expert_off, E, g)) return;
   const int nt = g.nt;
   const int n0 = nt * BN;
   const int wave = threadIdx.x >> 6;
@@ -210,11 +210,13 @@ __global__ __launch_bounds__(GEMM8_THREADS, 1) void k_dact_w8(
     const int32_t* __restrict__ row_token, const float* __restrict__ row_w,
     const bf16* __restrict__ dY, const bf16* __restrict__ Wd, const bf16* __restrict__ H,
     bf16* __restrict__ dH, bf16* __restrict__ wA, float* __restrict__ dS_part, int64_t R_max, int d,
-    int n, int E, int NT, int T_) {
+    int n, int E, int NT, int T_, int light_last) {
   MOE_GEMM_LDS(L);
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   GroupTile g;
-  if (!find_group_tile<true>(lin, NT, mtile_off, expert_off, E, g)) return;
+  const bool found = light_last ? find_group_tile<true>(lin, NT, mtile_off, expert_off, E, g)
+                                : find_group_tile<false>(lin, NT, mtile_off, expert_off, E, g);
+  if (!found) return;
   const int nt = g.nt;
   const int n0 = nt * BN;
   const int wave = threadIdx.x >> 6;
@@ -247,11 +249,16 @@ hipError_t launch_dact_gemm(const Shape& s, const PlanPtrs& p, const int32_t* mt
                             const void* dY, const void* W_down, const void* H, void* dH, void* wA,
                             float* dS_part, hipStream_t st) {
   const int NT = dact_ntiles(s.n);
-  const int grid = grid8(max_mtiles(s.R_max, s.E) * NT);
+  const int64_t tiles = max_mtiles(s.R_max, s.E) * NT;
+  const int grid = grid8(tiles);
+  // Light tails last pays while the grid is a few rounds (its last partial round is then a large
+  // share of the kernel); with many rounds their weight slices, read again far from the rest of
+  // their expert, cost more (measured at 4 and 43 rounds of 256 workgroups).
+  const int light_last = tiles <= 8 * 256 ? 1 : 0;
   if (s.bf16)
     k_dact_w8<<<grid, GEMM8_THREADS, 0, st>>>(mtile_off, p.expert_off, p.row_token, p.row_w, (const bf16*)dY,
                                               (const bf16*)W_down, (const bf16*)H, (bf16*)dH, (bf16*)wA, dS_part,
-                                              s.R_max, (int)s.d, (int)s.n, s.E, NT, (int)s.T);
+                                              s.R_max, (int)s.d, (int)s.n, s.E, NT, (int)s.T, light_last);
   else
     k_dact<float><<<grid, GEMM_THREADS, 0, st>>>(mtile_off, p.expert_off, p.row_token, p.row_w,
                                                  (const float*)dY, (const float*)W_down, (const float*)H,
