@@ -50,6 +50,8 @@ def test_tiny_fp32_layer_forward_backward():
     dict(T=333, d=256, E=16, K=4, n=128, dtype="bf16"),
     dict(T=129, d=64, E=3, K=1, n=64, dtype="f32"),
     dict(T=400, d=192, E=3, K=2, n=576, dtype="bf16"),  # n > 512: the four-wave bf16 down GEMM
+    dict(T=1500, d=320, E=6, K=2, n=256, dtype="bf16"),  # down GEMM with LDS-held rows: 2 n-tiles, the last 64 wide
+    dict(T=250, d=64, E=3, K=2, n=128, dtype="bf16"),    # the same with n = 128: one n-tile, 64 columns of 256
 ])
 def test_ragged_multi_tile(shape):
     cfg = wl.small_shape(**shape, seed=31)
